@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the Domino draft-head path.
+
+This module only draws random numbers and packs them into arrays. It holds
+none of the method's arithmetic: both the HIP path (through the Python
+binding) and the CPU oracle receive the same arrays from here.
+
+Workloads stand in for the pages' datasets and trained checkpoints, which are
+not available: the path's cost depends only on shapes, so weights and hidden
+states are Gaussian draws with the shapes of the Qwen3 draft heads that the
+pages describe (block 16, GRU hidden 1024, rank 256; page
+"完全开源的语言模型学习记录--推理加速Domino", section 二.1(2) and 三.1).
+
+Generation recipe (fixed so that every caller sees the same values):
+  * numpy ``default_rng(seed)`` (PCG64); float32 standard normals scaled by the
+    tensor's standard deviation; bf16 tensors are rounded to nearest-even from
+    those float32 values and stored as raw ``uint16`` bit patterns.
+  * draw order: lm_head, embed (skipped when tied), w_ih, w_hh, b_ih, b_hh,
+    w1, b1, w2, b2, hidden, x_t.
+  * hidden states N(0, 1); x_t uniform on [0, V).
+  * accept-length targets (``make_targets``): a separate generator seeded 1;
+    each position copies the draft token with probability p (0.9), otherwise
+    takes a uniform token on [0, V).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "get_workload",
+    "make_head",
+    "make_block_inputs",
+    "make_workload",
+    "make_targets",
+    "make_tokens",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "head_param_count",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int  # B: draft blocks per call
+    block: int  # K: positions per block
+    d: int  # hidden size of the backbone / LM head input
+    vocab: int  # V
+    gru_hidden: int  # H
+    rank: int  # r
+    dtype: str  # "f32" or "bf16" for weights and hidden states
+    tied: bool  # embedding table is the LM head matrix
+    temperature: float  # 0 = greedy
+    init: str = "small"  # "small": every parameter N(0, 0.02); "fanin": N(0, 1/sqrt(fan_in))
+    accept: bool = False  # the workload also scores the draft with accept_len
+    seed: int = 0
+    philox_seed: int = 0
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# Workloads named by what they are.  The Qwen3 hidden sizes (4096 for 8B,
+# 2560 for 4B) and vocabulary (151936) are the public model shapes; block 16,
+# GRU hidden 1024 and rank 256 are the pages' head shapes.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32_b1", 1, 16, 256, 4096, 128, 32, "f32", False, 0.0),
+        Workload("qwen3_8b_b1_greedy", 1, 16, 4096, 151936, 1024, 256, "bf16", False, 0.0),
+        Workload("qwen3_8b_b32_t1", 32, 16, 4096, 151936, 1024, 256, "bf16", False, 1.0),
+        Workload("qwen3_4b_b8_tied", 8, 16, 2560, 151936, 1024, 256, "bf16", True, 0.0),
+        Workload("qwen3_8b_b128_accept", 128, 16, 4096, 151936, 1024, 256, "bf16", False, 0.0,
+                 accept=True),
+        # test-only: fan-in scaled weights make the GRU signal O(1) so that a
+        # wrong recurrence moves the logits far beyond the tolerance.
+        Workload("tiny_stress_b4", 4, 16, 256, 4096, 128, 32, "f32", False, 0.0, init="fanin"),
+    ]
+}
+
+
+def get_workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.reshape(-1).view(np.uint32)
+    flat_out = out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        u = flat_in[s:s + step].astype(np.uint32)
+        bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+        flat_out[s:s + step] = ((u + bias) >> 16).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def _std(w: Workload, kind: str, fan_in: int) -> float:
+    if w.init == "small":
+        return 0.02
+    if kind == "embed":
+        return 1.0
+    return 1.0 / math.sqrt(fan_in)
+
+
+def make_head(w: Workload, rng: np.random.Generator) -> dict:
+    """Draw every head parameter in the fixed order; bf16 tensors come back as uint16 bits."""
+    d, V, H, r, dt = w.d, w.vocab, w.gru_hidden, w.rank, w.dtype
+    head = {}
+    head["lm_head"] = _normal(rng, (V, d), _std(w, "linear", d), dt)
+    head["embed"] = head["lm_head"] if w.tied else _normal(rng, (V, d), _std(w, "embed", d), dt)
+    head["w_ih"] = _normal(rng, (3 * H, d), _std(w, "linear", d), dt)
+    head["w_hh"] = _normal(rng, (3 * H, H), _std(w, "linear", H), dt)
+    head["b_ih"] = _normal(rng, (3 * H,), _std(w, "linear", d), dt)
+    head["b_hh"] = _normal(rng, (3 * H,), _std(w, "linear", H), dt)
+    head["w1"] = _normal(rng, (r, d + H), _std(w, "linear", d + H), dt)
+    head["b1"] = _normal(rng, (r,), _std(w, "linear", d + H), dt)
+    head["w2"] = _normal(rng, (V, r), _std(w, "linear", r), dt)
+    head["b2"] = _normal(rng, (V,), _std(w, "linear", r), dt)
+    return head
+
+
+def make_block_inputs(w: Workload, rng: np.random.Generator, batch: int | None = None) -> dict:
+    B = w.batch if batch is None else batch
+    hidden = _normal(rng, (B, w.block, w.d), 1.0, w.dtype)
+    x_t = rng.integers(0, w.vocab, size=(B,), dtype=np.int64).astype(np.int32)
+    return {"hidden": hidden, "x_t": x_t}
+
+
+def make_workload(w: Workload, batch: int | None = None):
+    """Head parameters and one batch of block inputs, drawn from one seeded stream."""
+    rng = np.random.default_rng(w.seed)
+    head = make_head(w, rng)
+    inputs = make_block_inputs(w, rng, batch)
+    return head, inputs
+
+
+def make_tokens(shape, vocab: int, seed: int) -> np.ndarray:
+    """Uniform token ids (teacher sequences, synthetic drafts)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, vocab, size=shape, dtype=np.int64).astype(np.int32)
+
+
+def make_targets(draft: np.ndarray, vocab: int, p: float = 0.9, seed: int = 1) -> np.ndarray:
+    """Synthetic verification targets: copy the draft token w.p. ``p``, else a uniform token."""
+    rng = np.random.default_rng(seed)
+    keep = rng.random(size=draft.shape) < p
+    other = rng.integers(0, vocab, size=draft.shape, dtype=np.int64).astype(np.int32)
+    return np.where(keep, draft, other).astype(np.int32)
+
+
+def head_param_count(w: Workload, biases: bool = True) -> int:
+    """Number of trainable head parameters (GRU + W1 + W2), excluding the frozen LM head/embedding."""
+    d, V, H, r = w.d, w.vocab, w.gru_hidden, w.rank
+    n = 3 * H * d + 3 * H * H + r * (d + H) + V * r
+    if biases:
+        n += 3 * H + 3 * H + r + V
+    return n

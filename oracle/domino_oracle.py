@@ -1,0 +1,285 @@
+"""Plain, slow, obviously-correct CPU oracle of the Domino draft-head hot path.
+
+TEST INFRASTRUCTURE.  Nothing on the product path imports, calls or links this
+module: only the test suite, the smoke check and the benchmark's CPU-baseline
+leg do.  It shares no code, header, table or helper with the HIP library.
+
+Every value is computed in float64 with numpy; bf16 inputs are widened
+exactly.  Each function writes out the plain definition the pages give, in
+the pages' order, with one library primitive (a matrix product) per step and
+no blocking, fusion or reordering.
+
+Pages cited (by title and section):
+  [notes]     "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn news article)
+  [explainer] the yhxrc.cn article on the Domino paper (Traditional Chinese,
+              sections 一 … 七 and a Q&A)
+  [abstract]  "Домино: отделение каузального моделирования от
+              авторегрессивного формирования черновика …" (chatpaper.ai;
+              Russian abstract with the English original)
+  [chapter]   "大三本科生一作，交出7.92倍加速的投机解码新答卷！DeepSeek和阶跃星辰双双引用"
+              (ai-engineering-6yk.pages.dev, Ch01.1513)
+
+Readings of points the pages leave open (each is also listed with its reason
+in the design notes):
+  * GRU cell: PyTorch ``GRUCell`` convention, gate rows ordered r|z|n, reset
+    gate applied to (W_hn g + b_hn), new state (1-z)*n + z*g.
+  * GRU input: the frozen input-embedding row of the token, no scaling.
+  * GRU starts from a zero state; its first input is x_t; position i uses the
+    state after reading x_t, y_0 … y_{i-1}.  All K positions are drafted.
+  * W1 input is [h_i ; g_i] (hidden state first).
+  * Residual L_i = L_i^base + ΔL_i with no scale.
+  * Biases are present in the GRU, W1 and W2; the LM head has none.
+  * Sampler: greedy argmax at T = 0, Gumbel-max argmax(L/T + G) at T > 0 with
+    G from a Philox4x32-10 counter generator (counter = (v>>2, i, b, offset),
+    key = (seed lo32, seed hi32), word = output[v & 3],
+    U = ((word >> 9) + 1/2) * 2^-23, G = -ln(-ln U)).
+  * The token decision is taken on the score rounded to float32 (the
+    kernel's precision); ties go to the lowest vocabulary index.
+  * Acceptance length: the bare length of the longest matching prefix.
+
+Pins: every function here is checked by ``tests/test_oracle_pins.py``
+against something other than itself (closed forms, brute force, invariants,
+torch / rocRAND library routines, statistics).  No function is parity
+unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "as_f64",
+    "base_logits",
+    "sigmoid",
+    "silu",
+    "gru_cell",
+    "correction_logits",
+    "philox4x32_10",
+    "philox_words",
+    "gumbel_noise",
+    "sampling_scores",
+    "pick_token",
+    "draft_block",
+    "accept_len",
+    "top2_margin",
+]
+
+_MASK32 = np.uint64(0xFFFFFFFF)
+
+
+def as_f64(x) -> np.ndarray:
+    """Widen an input to float64: uint16 arrays are bf16 bit patterns (exact widening)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def base_logits(hidden: np.ndarray, lm_head: np.ndarray) -> np.ndarray:
+    """L^base = h W_lm^T for every block position at once.
+
+    [notes] §二.1(1): the backbone emits hidden states for every position of
+    the block in one forward, and the frozen target LM head turns them into
+    base logits; [explainer] §三 (second paragraph) says the same.
+    hidden [..., d], lm_head [V, d] -> [..., V].
+    """
+    return as_f64(hidden) @ as_f64(lm_head).T
+
+
+def sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x) ([explainer] §四, the correction head's activation)."""
+    return x * sigmoid(x)
+
+
+def gru_cell(x, g, w_ih, w_hh, b_ih, b_hh):
+    """One GRU update g' = GRU(x, g) in the PyTorch GRUCell convention.
+
+    [notes] §二.1(2) item 1 and [explainer] §四: a GRU with hidden size 1024
+    reads the embeddings of the already-sampled tokens one position at a time
+    and keeps a running summary state.  The pages name only "GRU"; the gate
+    equations below are the standard cell (rows r|z|n):
+        a = W_ih x + b_ih,  c = W_hh g + b_hh
+        r = σ(a_r + c_r),   z = σ(a_z + c_z),   n = tanh(a_n + r ⊙ c_n)
+        g' = (1 - z) ⊙ n + z ⊙ g
+    x [..., d_in], g [..., H].
+    """
+    H = g.shape[-1]
+    a = x @ w_ih.T + b_ih
+    c = g @ w_hh.T + b_hh
+    r = sigmoid(a[..., 0:H] + c[..., 0:H])
+    z = sigmoid(a[..., H:2 * H] + c[..., H:2 * H])
+    n = np.tanh(a[..., 2 * H:3 * H] + r * c[..., 2 * H:3 * H])
+    return (1.0 - z) * n + z * g
+
+
+def correction_logits(h_i, g, w1, b1, w2, b2):
+    """ΔL_i = W2 SiLU(W1 [h_i ; g] + b1) + b2.
+
+    [notes] §二.1(2) item 2 and [explainer] §四 (low-rank correction head):
+    concatenate the base hidden state with the causal (GRU) state, project to
+    the rank-256 bottleneck with W1, apply SiLU, project to the vocabulary
+    with W2.  h_i [..., d], g [..., H] -> [..., V].
+    """
+    z = np.concatenate([h_i, g], axis=-1)
+    u = silu(z @ w1.T + b1)
+    return u @ w2.T + b2
+
+
+# ---------------------------------------------------------------------------
+# Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+# as 1, 2, 3", SC'11).  The pages do not name a sampler; the Gumbel noise of
+# the T > 0 sampler is drawn from this counter-based generator.
+# ---------------------------------------------------------------------------
+_PHILOX_M0 = np.uint64(0xD2511F53)
+_PHILOX_M1 = np.uint64(0xCD9E8D57)
+_PHILOX_W0 = np.uint64(0x9E3779B9)
+_PHILOX_W1 = np.uint64(0xBB67AE85)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Ten Philox-4x32 rounds on counter (c0..c3) with key (k0, k1).
+
+    Each round multiplies c0 and c2 by the two round multipliers into 64-bit
+    products and forms the new counter (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the
+    key is advanced by the two Weyl constants between rounds.  Arguments are
+    array-likes of 32-bit values; returns four uint64 arrays holding 32-bit words.
+    """
+    c0, c1, c2, c3, k0, k1 = (np.asarray(v, dtype=np.uint64) & _MASK32
+                              for v in (c0, c1, c2, c3, k0, k1))
+    for rnd in range(10):
+        if rnd > 0:
+            k0 = (k0 + _PHILOX_W0) & _MASK32
+            k1 = (k1 + _PHILOX_W1) & _MASK32
+        p0 = _PHILOX_M0 * c0
+        p1 = _PHILOX_M1 * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return c0, c1, c2, c3
+
+
+def philox_words(seed: int, offset: int, b, i, v) -> np.ndarray:
+    """The 32-bit random word for vocabulary entry v of position i of block b.
+
+    Counter = (v >> 2, i, b, offset), key = (seed low 32 bits, seed high 32
+    bits); the word is output lane v & 3.  Arguments broadcast.
+    """
+    v = np.asarray(v, dtype=np.uint64)
+    b = np.asarray(b, dtype=np.uint64)
+    i = np.asarray(i, dtype=np.uint64)
+    off = np.asarray(offset, dtype=np.uint64)
+    seed = int(seed)
+    k0 = np.uint64(seed & 0xFFFFFFFF)
+    k1 = np.uint64((seed >> 32) & 0xFFFFFFFF)
+    shape = np.broadcast_shapes(v.shape, b.shape, i.shape, off.shape)
+    c0 = np.broadcast_to(v >> np.uint64(2), shape)
+    out = philox4x32_10(c0, np.broadcast_to(i, shape), np.broadcast_to(b, shape),
+                        np.broadcast_to(off, shape), k0, k1)
+    lane = np.broadcast_to(v & np.uint64(3), shape)
+    word = np.choose(lane.astype(np.int64), out)
+    return word.astype(np.uint32)
+
+
+def gumbel_noise(seed: int, offset: int, b, i, v) -> np.ndarray:
+    """G = -ln(-ln U) with U = ((word >> 9) + 1/2) * 2^-23, strictly inside (0, 1)."""
+    w = philox_words(seed, offset, b, i, v).astype(np.float64)
+    u = (np.floor(w / 512.0) + 0.5) * 2.0 ** -23
+    return -np.log(-np.log(u))
+
+
+def sampling_scores(logits, temperature: float, seed: int, offset: int, b: int, i: int):
+    """Scores whose argmax is the drafted token.
+
+    T = 0: the logits themselves (greedy decoding).  T > 0: Gumbel-max,
+    L / T + G, which draws from softmax(L / T).  The pages report greedy
+    (T = 0) and sampled (T = 1) decoding ([notes] §三.2(1); [explainer] §六)
+    without naming the sampler.
+    """
+    if temperature < 0:
+        raise ValueError("temperature must be >= 0")
+    if temperature == 0.0:
+        return np.asarray(logits, dtype=np.float64)
+    V = logits.shape[-1]
+    return logits / temperature + gumbel_noise(seed, offset, b, i, np.arange(V))
+
+
+def pick_token(scores) -> int:
+    """First index of the maximum, decided on the float32-rounded score."""
+    s32 = np.asarray(scores, dtype=np.float64).astype(np.float32)
+    return int(np.argmax(s32))
+
+
+def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
+                seed: int = 0, offset: int = 0, base=None):
+    """One draft block per batch row, position by position.
+
+    [notes] §二.1 and [explainer] §三–§四, in their order:
+      1. base logits for all K positions from the frozen LM head (one pass);
+      2. for i = 0 … K-1: the GRU reads the embedding of the previous token
+         (x_t for i = 0, then y_{i-1}; in teacher-forced mode teacher[b, i-1]),
+         starting from a zero state;
+      3. ΔL_i = W2 SiLU(W1 [h_i ; g_i] + b1) + b2 and L_i = L_i^base + ΔL_i;
+      4. the token y_i is picked from L_i.
+    Teacher forcing follows [notes] §二.2(1) / [explainer] §五 (the causal
+    encoder is fed the reference tokens instead of the sampled ones).
+
+    head: dict with lm_head, embed, w_ih, w_hh, b_ih, b_hh, w1, b1, w2, b2
+    (float64 or bf16 bits).  hidden [B, K, d]; x_t [B]; teacher [B, K] or None.
+    Returns dict(tokens [B, K] int32, logits [B, K, V], states [B, K, H],
+    scores [B, K, V], base [B, K, V]).
+    """
+    f = {k: as_f64(v) for k, v in head.items()}
+    hidden = as_f64(hidden)
+    x_t = np.asarray(x_t)
+    B, K, _ = hidden.shape
+    V = f["lm_head"].shape[0]
+    H = f["w_hh"].shape[1]
+    if base is None:
+        base = base_logits(hidden, f["lm_head"])
+    base = np.asarray(base, dtype=np.float64)
+    tokens = np.zeros((B, K), dtype=np.int32)
+    logits = np.zeros((B, K, V))
+    states = np.zeros((B, K, H))
+    scores = np.zeros((B, K, V))
+    for b in range(B):
+        g = np.zeros(H)
+        prev = int(x_t[b])
+        for i in range(K):
+            g = gru_cell(f["embed"][prev], g, f["w_ih"], f["w_hh"], f["b_ih"], f["b_hh"])
+            states[b, i] = g
+            dl = correction_logits(hidden[b, i], g, f["w1"], f["b1"], f["w2"], f["b2"])
+            logits[b, i] = base[b, i] + dl
+            scores[b, i] = sampling_scores(logits[b, i], temperature, seed, offset, b, i)
+            tokens[b, i] = pick_token(scores[b, i])
+            prev = int(teacher[b, i]) if teacher is not None else int(tokens[b, i])
+    return {"tokens": tokens, "logits": logits, "states": states, "scores": scores,
+            "base": base}
+
+
+def accept_len(draft, target) -> np.ndarray:
+    """τ per row: how many leading draft tokens equal the target's.
+
+    [notes] §一.1 item 1: the acceptance length is the number of draft tokens
+    one verification accepts in a row.  Returns the bare prefix length 0 … K.
+    """
+    draft = np.asarray(draft)
+    target = np.asarray(target)
+    out = np.zeros(draft.shape[0], dtype=np.int32)
+    for b in range(draft.shape[0]):
+        n = 0
+        while n < draft.shape[1] and draft[b, n] == target[b, n]:
+            n += 1
+        out[b] = n
+    return out
+
+
+def top2_margin(scores) -> np.ndarray:
+    """Gap between the largest and second-largest score along the last axis."""
+    s = np.sort(np.asarray(scores, dtype=np.float64), axis=-1)
+    if s.shape[-1] < 2:
+        return np.full(s.shape[:-1], np.inf)
+    return s[..., -1] - s[..., -2]
