@@ -11,11 +11,16 @@ pages describe (block 16, GRU hidden 1024, rank 256; page
 "完全开源的语言模型学习记录--推理加速Domino", section 二.1(2) and 三.1).
 
 Generation recipe (fixed so that every caller sees the same values):
-  * numpy ``default_rng(seed)`` (PCG64); float32 standard normals scaled by the
-    tensor's standard deviation; bf16 tensors are rounded to nearest-even from
-    those float32 values and stored as raw ``uint16`` bit patterns.
-  * draw order: lm_head, embed (skipped when tied), w_ih, w_hh, b_ih, b_hh,
-    w1, b1, w2, b2, hidden, x_t.
+  * every tensor has its own numpy PCG64 stream: tensor number t of the fixed
+    order below draws from ``SeedSequence(seed, spawn_key=(t, chunk))`` for
+    each consecutive chunk of 2^22 elements (chunks are filled in parallel;
+    the values do not depend on the thread count);
+  * float32 standard normals scaled by the tensor's standard deviation; bf16
+    tensors are rounded to nearest-even from those float32 values and stored
+    as raw ``uint16`` bit patterns;
+  * order: lm_head, embed (skipped when tied), w_ih, w_hh, b_ih, b_hh, w1, b1,
+    w2, b2, hidden, x_t (x_t uses ``default_rng(SeedSequence(seed,
+    spawn_key=(11,)))``).
   * hidden states N(0, 1); x_t uniform on [0, V).
   * accept-length targets (``make_targets``): a separate generator seeded 1;
     each position copies the draft token with probability p (0.9), otherwise
@@ -25,8 +30,13 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
+
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 __all__ = [
     "Workload",
@@ -40,6 +50,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "head_param_count",
+    "to_torch",
 ]
 
 
@@ -106,13 +117,26 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x)
-    return x
+def _normal(seed: int, tensor_id: int, shape, std: float, dtype: str) -> np.ndarray:
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor_id, c))))
+        x = rng.standard_normal(size=hi - lo, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    chunks = range((n + _CHUNK - 1) // _CHUNK)
+    if len(chunks) > 1:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for c in chunks:
+            fill(c)
+    return out.reshape(shape)
 
 
 def _std(w: Workload, kind: str, fan_in: int) -> float:
@@ -123,36 +147,34 @@ def _std(w: Workload, kind: str, fan_in: int) -> float:
     return 1.0 / math.sqrt(fan_in)
 
 
-def make_head(w: Workload, rng: np.random.Generator) -> dict:
-    """Draw every head parameter in the fixed order; bf16 tensors come back as uint16 bits."""
-    d, V, H, r, dt = w.d, w.vocab, w.gru_hidden, w.rank, w.dtype
+def make_head(w: Workload) -> dict:
+    """Draw every head parameter; bf16 tensors come back as uint16 bits."""
+    d, V, H, r, dt, sd = w.d, w.vocab, w.gru_hidden, w.rank, w.dtype, w.seed
     head = {}
-    head["lm_head"] = _normal(rng, (V, d), _std(w, "linear", d), dt)
-    head["embed"] = head["lm_head"] if w.tied else _normal(rng, (V, d), _std(w, "embed", d), dt)
-    head["w_ih"] = _normal(rng, (3 * H, d), _std(w, "linear", d), dt)
-    head["w_hh"] = _normal(rng, (3 * H, H), _std(w, "linear", H), dt)
-    head["b_ih"] = _normal(rng, (3 * H,), _std(w, "linear", d), dt)
-    head["b_hh"] = _normal(rng, (3 * H,), _std(w, "linear", H), dt)
-    head["w1"] = _normal(rng, (r, d + H), _std(w, "linear", d + H), dt)
-    head["b1"] = _normal(rng, (r,), _std(w, "linear", d + H), dt)
-    head["w2"] = _normal(rng, (V, r), _std(w, "linear", r), dt)
-    head["b2"] = _normal(rng, (V,), _std(w, "linear", r), dt)
+    head["lm_head"] = _normal(sd, 0, (V, d), _std(w, "linear", d), dt)
+    head["embed"] = head["lm_head"] if w.tied else _normal(sd, 1, (V, d), _std(w, "embed", d), dt)
+    head["w_ih"] = _normal(sd, 2, (3 * H, d), _std(w, "linear", d), dt)
+    head["w_hh"] = _normal(sd, 3, (3 * H, H), _std(w, "linear", H), dt)
+    head["b_ih"] = _normal(sd, 4, (3 * H,), _std(w, "linear", d), dt)
+    head["b_hh"] = _normal(sd, 5, (3 * H,), _std(w, "linear", H), dt)
+    head["w1"] = _normal(sd, 6, (r, d + H), _std(w, "linear", d + H), dt)
+    head["b1"] = _normal(sd, 7, (r,), _std(w, "linear", d + H), dt)
+    head["w2"] = _normal(sd, 8, (V, r), _std(w, "linear", r), dt)
+    head["b2"] = _normal(sd, 9, (V,), _std(w, "linear", r), dt)
     return head
 
 
-def make_block_inputs(w: Workload, rng: np.random.Generator, batch: int | None = None) -> dict:
+def make_block_inputs(w: Workload, batch: int | None = None) -> dict:
     B = w.batch if batch is None else batch
-    hidden = _normal(rng, (B, w.block, w.d), 1.0, w.dtype)
+    hidden = _normal(w.seed, 10, (B, w.block, w.d), 1.0, w.dtype)
+    rng = np.random.default_rng(np.random.SeedSequence(w.seed, spawn_key=(11,)))
     x_t = rng.integers(0, w.vocab, size=(B,), dtype=np.int64).astype(np.int32)
     return {"hidden": hidden, "x_t": x_t}
 
 
 def make_workload(w: Workload, batch: int | None = None):
-    """Head parameters and one batch of block inputs, drawn from one seeded stream."""
-    rng = np.random.default_rng(w.seed)
-    head = make_head(w, rng)
-    inputs = make_block_inputs(w, rng, batch)
-    return head, inputs
+    """Head parameters and one batch of block inputs."""
+    return make_head(w), make_block_inputs(w, batch)
 
 
 def make_tokens(shape, vocab: int, seed: int) -> np.ndarray:
@@ -167,6 +189,17 @@ def make_targets(draft: np.ndarray, vocab: int, p: float = 0.9, seed: int = 1) -
     keep = rng.random(size=draft.shape) < p
     other = rng.integers(0, vocab, size=draft.shape, dtype=np.int64).astype(np.int32)
     return np.where(keep, draft, other).astype(np.int32)
+
+
+def to_torch(a: np.ndarray, device=None):
+    """Host array -> torch tensor: uint16 arrays are bf16 bit patterns (reinterpreted, not converted)."""
+    import torch
+
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device) if device is not None else t
 
 
 def head_param_count(w: Workload, biases: bool = True) -> int:

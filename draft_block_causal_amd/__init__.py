@@ -1,0 +1,22 @@
+"""Domino draft-head engine for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library libdomino.so (C ABI in include/domino.h);
+this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    DOMINO_BF16,
+    DOMINO_F32,
+    EXPORTED,
+    LIB_PATH,
+    DominoError,
+    DominoHeadStruct,
+    Head,
+    domino_accept_len,
+    domino_base_logits,
+    domino_check_head,
+    domino_debug_philox,
+    domino_draft_block,
+    domino_version,
+    domino_workspace_size,
+    load_library,
+)

@@ -1,0 +1,247 @@
+"""ctypes binding of libdomino.so.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their pointers and the current HIP stream are handed to the
+C ABI declared in include/domino.h.  Every step of the path runs in the HIP
+library; there is no other implementation behind these functions, and they
+raise if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdomino.so")
+
+DOMINO_F32 = 0
+DOMINO_BF16 = 1
+
+_STATUS = {
+    0: "DOMINO_OK",
+    -1: "DOMINO_ERR_NULL",
+    -2: "DOMINO_ERR_SHAPE",
+    -3: "DOMINO_ERR_DTYPE",
+    -4: "DOMINO_ERR_ALIGN",
+    -5: "DOMINO_ERR_ARG",
+    -6: "DOMINO_ERR_WORKSPACE",
+    -7: "DOMINO_ERR_HIP",
+    -8: "DOMINO_ERR_UNSUPPORTED",
+}
+
+EXPORTED = [
+    "domino_version",
+    "domino_status_string",
+    "domino_check_head",
+    "domino_workspace_size",
+    "domino_base_logits",
+    "domino_draft_block",
+    "domino_accept_len",
+    "domino_debug_philox",
+]
+
+
+class DominoError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class DominoHeadStruct(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("gru_hidden", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("lm_head", ctypes.c_void_p),
+        ("embed", ctypes.c_void_p),
+        ("w_ih", ctypes.c_void_p),
+        ("w_hh", ctypes.c_void_p),
+        ("b_ih", ctypes.c_void_p),
+        ("b_hh", ctypes.c_void_p),
+        ("w1", ctypes.c_void_p),
+        ("b1", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("b2", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdomino.so (built in-tree by draft_block_causal_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m draft_block_causal_amd.build` "
+                           "(the Domino engine has no other implementation)")
+    lib = ctypes.CDLL(path)
+    P, I32, U32, U64, SZ, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64,
+                               ctypes.c_size_t, ctypes.c_float)
+    HP = ctypes.POINTER(DominoHeadStruct)
+    sig = {
+        "domino_version": (ctypes.c_int, []),
+        "domino_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "domino_check_head": (ctypes.c_int, [HP]),
+        "domino_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
+        "domino_base_logits": (ctypes.c_int, [HP, I32, P, P, P]),
+        "domino_draft_block": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P, SZ, P]),
+        "domino_accept_len": (ctypes.c_int, [I32, I32, P, P, P, P]),
+        "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        text = load_library().domino_status_string(status).decode()
+        raise DominoError(fn, status, text)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+class Head:
+    """A Domino head whose parameters are device tensors (the caller owns them)."""
+
+    NAMES = ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2")
+
+    def __init__(self, tensors: dict, block: int = 16):
+        lm = tensors["lm_head"]
+        self.dtype = lm.dtype
+        if self.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("head tensors must be float32 or bfloat16")
+        self.device = lm.device
+        self.vocab, self.d = lm.shape
+        self.gru_hidden = tensors["w_hh"].shape[1]
+        self.rank = tensors["w1"].shape[0]
+        self.block = int(block)
+        V, d, H, r = self.vocab, self.d, self.gru_hidden, self.rank
+        shapes = {"lm_head": (V, d), "embed": (V, d), "w_ih": (3 * H, d), "w_hh": (3 * H, H),
+                  "b_ih": (3 * H,), "b_hh": (3 * H,), "w1": (r, d + H), "b1": (r,), "w2": (V, r), "b2": (V,)}
+        self.tensors = {}
+        for k in self.NAMES:
+            t = tensors.get(k)
+            if t is None and k in ("b_ih", "b_hh", "b1", "b2"):
+                self.tensors[k] = None
+                continue
+            _need(t, k, self.dtype, shapes[k], self.device)
+            self.tensors[k] = t
+        self.struct = DominoHeadStruct(
+            d, V, H, r, self.block, DOMINO_BF16 if self.dtype == torch.bfloat16 else DOMINO_F32,
+            *[_ptr(self.tensors[k]) for k in self.NAMES])
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def domino_version() -> int:
+    return load_library().domino_version()
+
+
+def domino_check_head(head: Head) -> None:
+    _check("domino_check_head", load_library().domino_check_head(head.ref))
+
+
+def domino_workspace_size(head: Head, batch: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("domino_workspace_size", load_library().domino_workspace_size(head.ref, int(batch), ctypes.byref(out)))
+    return out.value
+
+
+def domino_base_logits(head: Head, hidden: torch.Tensor, base_logits: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    B = hidden.shape[0]
+    _need(hidden, "hidden", head.dtype, (B, head.block, head.d), head.device)
+    if base_logits is None:
+        base_logits = torch.empty((B, head.block, head.vocab), dtype=torch.float32, device=head.device)
+    _need(base_logits, "base_logits", torch.float32, (B, head.block, head.vocab), head.device)
+    _check("domino_base_logits", load_library().domino_base_logits(
+        head.ref, B, _ptr(hidden), _ptr(base_logits), _stream_ptr(stream)))
+    return base_logits
+
+
+def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: torch.Tensor, x_t: torch.Tensor,
+                       teacher: Optional[torch.Tensor] = None, temperature: float = 0.0, seed: int = 0,
+                       offset: int = 0, tokens: Optional[torch.Tensor] = None,
+                       logits: Optional[torch.Tensor] = None, gru_states: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B, K, dev = hidden.shape[0], head.block, head.device
+    _need(hidden, "hidden", head.dtype, (B, K, head.d), dev)
+    _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
+    _need(x_t, "x_t", torch.int32, (B,), dev)
+    if teacher is not None:
+        _need(teacher, "teacher", torch.int32, (B, K), dev)
+    if tokens is None:
+        tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _need(tokens, "tokens", torch.int32, (B, K), dev)
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (B, K, head.vocab), dev)
+    if gru_states is not None:
+        _need(gru_states, "gru_states", torch.float32, (B, K, head.gru_hidden), dev)
+    need = domino_workspace_size(head, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    _check("domino_draft_block", load_library().domino_draft_block(
+        head.ref, B, _ptr(hidden), _ptr(base_logits), _ptr(x_t), _ptr(teacher), float(temperature),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(tokens), _ptr(logits), _ptr(gru_states),
+        _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return tokens
+
+
+def domino_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    B, K = draft.shape
+    _need(draft, "draft", torch.int32, (B, K), draft.device)
+    _need(target, "target", torch.int32, (B, K), draft.device)
+    if accept is None:
+        accept = torch.empty((B,), dtype=torch.int32, device=draft.device)
+    _need(accept, "accept", torch.int32, (B,), draft.device)
+    _check("domino_accept_len", load_library().domino_accept_len(
+        B, K, _ptr(draft), _ptr(target), _ptr(accept), _stream_ptr(stream)))
+    return accept
+
+
+def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,
+                        out: Optional[torch.Tensor] = None, device="cuda", stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int32, device=device)
+    _need(out, "out", torch.int32, (n,), out.device)
+    _check("domino_debug_philox", load_library().domino_debug_philox(
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, b, pos, v0, n, _ptr(out), _stream_ptr(stream)))
+    return out

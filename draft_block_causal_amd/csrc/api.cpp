@@ -1,0 +1,107 @@
+// C ABI entry points of the Domino engine: validate on the host, then enqueue
+// the kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "kernels.h"
+#include "validate.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+int device_cu_count() {
+  static int cu[kMaxDevices] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cu[dev] = n;
+  }
+  return cu[dev];
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DOMINO_OK : DOMINO_ERR_HIP; }
+
+}  // namespace
+
+extern "C" int domino_base_logits(const domino_head* h, int32_t batch, const void* hidden, float* base_logits,
+                                  void* stream) {
+  int st = domino::check_base_args(h, batch, hidden, base_logits);
+  if (st != DOMINO_OK || batch == 0) return st;
+  const int num_cu = device_cu_count();
+  if (num_cu <= 0) return DOMINO_ERR_HIP;
+  const int M = batch * h->block;
+  return hip_status(domino::launch_panel_gemm(h->dtype, hidden, h->d, M, h->lm_head, h->d, h->vocab, h->d,
+                                              nullptr, base_logits, h->vocab, num_cu,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const void* hidden,
+                                  const float* base_logits, const int32_t* x_t, const int32_t* teacher,
+                                  float temperature, uint64_t seed, uint32_t offset, int32_t* tokens,
+                                  float* logits, float* gru_states, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  int st = domino::check_draft_args(h, batch, hidden, base_logits, x_t, temperature, tokens, logits, gru_states,
+                                    workspace, workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  const int num_cu = device_cu_count();
+  if (num_cu <= 0) return DOMINO_ERR_HIP;
+  const domino::WorkspaceLayout w = domino::workspace_layout(h, batch);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  domino::LoopArgs a{};
+  a.dtype = h->dtype;
+  a.B = batch;
+  a.K = h->block;
+  a.d = h->d;
+  a.V = h->vocab;
+  a.H = h->gru_hidden;
+  a.r = h->rank;
+  a.embed = h->embed;
+  a.w_ih = h->w_ih;
+  a.w_hh = h->w_hh;
+  a.b_ih = h->b_ih;
+  a.b_hh = h->b_hh;
+  a.w1 = h->w1;
+  a.b1 = h->b1;
+  a.w2 = h->w2;
+  a.b2 = h->b2;
+  a.hidden = hidden;
+  a.base = base_logits;
+  a.x_t = x_t;
+  a.teacher = teacher;
+  a.sampled = temperature > 0.f ? 1 : 0;
+  a.inv_temp = temperature > 0.f ? 1.0f / temperature : 0.f;
+  a.seed = seed;
+  a.offset = offset;
+  a.tokens = tokens;
+  a.logits = logits;
+  a.states = gru_states ? gru_states : reinterpret_cast<float*>(ws + w.states);
+  a.keys = reinterpret_cast<unsigned long long*>(ws + w.keys);
+  a.P = reinterpret_cast<float*>(ws + w.P);
+  a.part_ih = reinterpret_cast<float*>(ws + w.part_ih);
+  a.part_hh = reinterpret_cast<float*>(ws + w.part_hh);
+  a.u = reinterpret_cast<float*>(ws + w.u);
+  a.ks = w.ks;
+  a.num_cu = num_cu;
+  return hip_status(domino::launch_draft_loop(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int domino_accept_len(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
+                                 int32_t* accept, void* stream) {
+  int st = domino::check_accept_args(batch, block, draft, target, accept);
+  if (st != DOMINO_OK || batch == 0) return st;
+  return hip_status(domino::launch_accept_len(batch, block, draft, target, accept, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int domino_debug_philox(uint64_t seed, uint32_t offset, int32_t b, int32_t pos, int32_t v0, int32_t n,
+                                   uint32_t* out, void* stream) {
+  if (n < 0 || n > (1 << 26) || b < 0 || pos < 0 || v0 < 0) return DOMINO_ERR_SHAPE;
+  if (n == 0) return DOMINO_OK;
+  if (!out) return DOMINO_ERR_NULL;
+  return hip_status(domino::launch_debug_philox(seed, offset, b, pos, v0, n, out, static_cast<hipStream_t>(stream)));
+}

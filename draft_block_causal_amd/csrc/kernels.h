@@ -1,0 +1,49 @@
+// Host-side launchers of the Domino kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace domino {
+
+// C[m, n] = sum_k A[m, k] W[n, k] (+ bias[n]) for m < M, n < N, in float32.
+// dtype 0 = f32, 1 = bf16 for A, W and bias.  K * elem_size must be a multiple
+// of 64 and at most 8192 bytes.  Pointers 16-byte aligned, lda/ldw rows too.
+hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
+                             const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
+
+struct LoopArgs {
+  int dtype;
+  int B, K, d, V, H, r;
+  const void *embed, *w_ih, *w_hh, *b_ih, *b_hh, *w1, *b1, *w2, *b2;
+  const void* hidden;
+  const float* base;
+  const int32_t* x_t;
+  const int32_t* teacher;
+  float inv_temp;
+  int sampled;
+  uint64_t seed;
+  uint32_t offset;
+  int32_t* tokens;
+  float* logits;
+  float* states;  // [B, K, H]
+  // workspace pieces
+  unsigned long long* keys;  // [K, B]
+  float* P;                  // [B, K, r]
+  float* part_ih;            // [KS, B, 3H]
+  float* part_hh;            // [B, 3H]
+  float* u;                  // [B, r]
+  int ks;
+  int num_cu;
+};
+
+hipError_t launch_draft_loop(const LoopArgs& a, hipStream_t s);
+
+hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
+                             hipStream_t s);
+
+hipError_t launch_debug_philox(uint64_t seed, uint32_t offset, int b, int pos, int v0, int n, uint32_t* out,
+                               hipStream_t s);
+
+}  // namespace domino

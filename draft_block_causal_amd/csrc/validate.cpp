@@ -1,0 +1,129 @@
+// Host-only argument validation and workspace layout of the Domino C ABI.
+// Pure C++ (no HIP calls), so it can also be built and sanitised on a CPU.
+#include "validate.h"
+
+#include <cmath>
+
+namespace domino {
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) { return dtype == DOMINO_BF16 ? 2 : 4; }
+
+int check_head(const domino_head* h) {
+  if (!h) return DOMINO_ERR_NULL;
+  if (h->dtype != DOMINO_F32 && h->dtype != DOMINO_BF16) return DOMINO_ERR_DTYPE;
+  if (h->d <= 0 || h->vocab <= 0 || h->gru_hidden <= 0 || h->rank <= 0 || h->block <= 0) return DOMINO_ERR_SHAPE;
+  if (h->d % 32 || h->gru_hidden % 32 || h->rank % 32) return DOMINO_ERR_SHAPE;
+  if (h->block > kMaxBlock) return DOMINO_ERR_SHAPE;
+  if (!h->lm_head || !h->embed || !h->w_ih || !h->w_hh || !h->w1 || !h->w2) return DOMINO_ERR_NULL;
+  const void* mats[] = {h->lm_head, h->embed, h->w_ih, h->w_hh, h->w1, h->w2};
+  for (const void* p : mats)
+    if (!aligned16(p)) return DOMINO_ERR_ALIGN;
+  const long es = elem_size(h->dtype);
+  if ((long)h->d * es > kMaxRowBytes) return DOMINO_ERR_UNSUPPORTED;
+  if (h->gru_hidden > kMaxGruHidden || h->rank > kMaxRank) return DOMINO_ERR_UNSUPPORTED;
+  if ((long)h->vocab * h->d > 0x7FFFFFFFL * 8L) return DOMINO_ERR_UNSUPPORTED;
+  return DOMINO_OK;
+}
+
+// ks: K-split of the W_ih e product, so that one 16-row tile of W_ih is shared
+// by several waves; the slice must stay a multiple of 32 elements.
+int gru_ksplit(int d) {
+  for (int ks : {4, 2})
+    if (d % (32 * ks) == 0) return ks;
+  return 1;
+}
+
+static size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
+  WorkspaceLayout w{};
+  const size_t B = (size_t)batch, K = (size_t)h->block, H = (size_t)h->gru_hidden, r = (size_t)h->rank;
+  const size_t ks = (size_t)gru_ksplit(h->d);
+  size_t off = 0;
+  w.keys = off;
+  off += up256(K * B * sizeof(unsigned long long));
+  w.P = off;
+  off += up256(B * K * r * sizeof(float));
+  w.part_ih = off;
+  off += up256(ks * B * 3 * H * sizeof(float));
+  w.part_hh = off;
+  off += up256(B * 3 * H * sizeof(float));
+  w.u = off;
+  off += up256(B * r * sizeof(float));
+  w.states = off;
+  off += up256(B * K * H * sizeof(float));
+  w.total = off;
+  w.ks = (int)ks;
+  return w;
+}
+
+int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                     const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
+                     const float* gru_states, const void* workspace, size_t workspace_bytes) {
+  int st = check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  if (!std::isfinite(temperature) || temperature < 0.f) return DOMINO_ERR_ARG;
+  if (batch == 0) return DOMINO_OK;
+  if (!hidden || !base_logits || !x_t || !tokens) return DOMINO_ERR_NULL;
+  if (!aligned16(hidden) || !aligned16(base_logits) || !aligned16(tokens)) return DOMINO_ERR_ALIGN;
+  if ((logits && !aligned16(logits)) || (gru_states && !aligned16(gru_states))) return DOMINO_ERR_ALIGN;
+  const WorkspaceLayout w = workspace_layout(h, batch);
+  if (!workspace) return DOMINO_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DOMINO_ERR_WORKSPACE;
+  if (workspace_bytes < w.total) return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
+int check_base_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits) {
+  int st = check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  if (batch == 0) return DOMINO_OK;
+  if (!hidden || !base_logits) return DOMINO_ERR_NULL;
+  if (!aligned16(hidden) || !aligned16(base_logits)) return DOMINO_ERR_ALIGN;
+  return DOMINO_OK;
+}
+
+int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
+                      const int32_t* accept) {
+  if (batch < 0 || block <= 0 || block > 1024) return DOMINO_ERR_SHAPE;
+  if (batch == 0) return DOMINO_OK;
+  if (!draft || !target || !accept) return DOMINO_ERR_NULL;
+  return DOMINO_OK;
+}
+
+}  // namespace domino
+
+extern "C" const char* domino_status_string(int status) {
+  switch (status) {
+    case DOMINO_OK: return "ok";
+    case DOMINO_ERR_NULL: return "a required pointer is NULL";
+    case DOMINO_ERR_SHAPE: return "a size is out of range or not a multiple of 32";
+    case DOMINO_ERR_DTYPE: return "unknown dtype code";
+    case DOMINO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case DOMINO_ERR_ARG: return "invalid scalar argument";
+    case DOMINO_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case DOMINO_ERR_HIP: return "HIP runtime error";
+    case DOMINO_ERR_UNSUPPORTED: return "request outside this build's limits";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int domino_version(void) { return 100; }
+
+extern "C" int domino_check_head(const domino_head* head) { return domino::check_head(head); }
+
+extern "C" int domino_workspace_size(const domino_head* head, int32_t batch, size_t* bytes) {
+  if (!bytes) return DOMINO_ERR_NULL;
+  int st = domino::check_head(head);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > domino::kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  *bytes = domino::workspace_layout(head, batch).total;
+  return DOMINO_OK;
+}

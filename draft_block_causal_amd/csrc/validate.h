@@ -1,0 +1,33 @@
+// Host-only validation and workspace layout (internal).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/domino.h"
+
+namespace domino {
+
+constexpr int kMaxBlock = 64;
+constexpr int kMaxBatch = 128;
+constexpr long kMaxRowBytes = 8192;
+constexpr int kMaxGruHidden = 4096;
+constexpr int kMaxRank = 1024;
+
+struct WorkspaceLayout {
+  size_t keys, P, part_ih, part_hh, u, states, total;
+  int ks;
+};
+
+int elem_size(int dtype);
+int check_head(const domino_head* h);
+int gru_ksplit(int d);
+WorkspaceLayout workspace_layout(const domino_head* h, int batch);
+int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                     const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
+                     const float* gru_states, const void* workspace, size_t workspace_bytes);
+int check_base_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits);
+int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
+                      const int32_t* accept);
+
+}  // namespace domino

@@ -1,0 +1,175 @@
+/*
+ * domino.h — C ABI of the Domino draft-head engine for AMD Instinct MI355X (gfx950).
+ *
+ * The engine turns the hidden states that a parallel draft backbone produces
+ * for a block of K positions into a K-token draft, as the Domino head does:
+ * frozen LM head -> base logits for every position in one pass; then, position
+ * by position, a GRU causal encoder over the previously chosen tokens, a
+ * low-rank logit correction added to the base logits, and a token pick.
+ * A separate call scores a draft against verification targets.
+ *
+ * Sources (pages on the Domino paper, cited by title and section):
+ *   [notes]     "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn)
+ *   [explainer] the yhxrc.cn article on the Domino paper (sections 一 … 七, Q&A)
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is caller-owned DEVICE memory, contiguous and
+ *     row-major, unless stated otherwise.  The library keeps no pointer after
+ *     a call returns and allocates no device memory of its own.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  Nothing synchronises the host.
+ *   - Argument errors are reported as a negative domino_status before any work
+ *     is enqueued.  A failed kernel launch returns DOMINO_ERR_HIP.  No call
+ *     throws across this interface.
+ *   - Preconditions not checked on the host: token ids lie in [0, vocab);
+ *     every floating-point input is finite.  Violations give unspecified
+ *     results (never out-of-bounds accesses for token ids: the kernels clamp).
+ *   - Thread safety: calls may be made from several host threads on different
+ *     streams; each concurrent draft_block call needs its own workspace.
+ */
+#ifndef DOMINO_H_
+#define DOMINO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DOMINO_OK = 0,
+  DOMINO_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  DOMINO_ERR_SHAPE = -2,       /* a size is out of range or not a multiple of 32  */
+  DOMINO_ERR_DTYPE = -3,       /* unknown dtype code                              */
+  DOMINO_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                */
+  DOMINO_ERR_ARG = -5,         /* a scalar argument is invalid (e.g. T < 0, NaN)  */
+  DOMINO_ERR_WORKSPACE = -6,   /* workspace missing, too small or not 256-aligned */
+  DOMINO_ERR_HIP = -7,         /* the HIP runtime reported an error               */
+  DOMINO_ERR_UNSUPPORTED = -8  /* valid request outside this build's limits       */
+} domino_status;
+
+typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
+
+/*
+ * The Domino head: frozen LM head and input embedding of the target model,
+ * and the trained GRU + low-rank correction parameters ([notes] §二.1(2);
+ * [explainer] §四).  Weight layouts are [out, in], row-major.
+ *
+ *   d          hidden size of the backbone / LM head input      (multiple of 32)
+ *   vocab      V, vocabulary size                               (>= 1)
+ *   gru_hidden H, GRU state size (1024 in the pages)             (multiple of 32)
+ *   rank       r, correction bottleneck (256 in the pages)       (multiple of 32)
+ *   block      K, positions per draft block (16 in the pages)    (1 … 64)
+ *   dtype      element type of every weight, bias and hidden state
+ *
+ *   lm_head [V, d]      frozen LM head (no bias)
+ *   embed   [V, d]      token embedding read by the GRU; may equal lm_head (tied)
+ *   w_ih    [3H, d]     GRU input weights, gate rows ordered r | z | n
+ *   w_hh    [3H, H]     GRU recurrent weights, rows r | z | n
+ *   b_ih, b_hh [3H]     GRU biases (NULL = zero)
+ *   w1      [r, d + H]  first correction projection; columns 0 … d-1 multiply
+ *                       the hidden state, columns d … d+H-1 the GRU state
+ *   b1      [r]         (NULL = zero)
+ *   w2      [V, r]      second correction projection to the vocabulary
+ *   b2      [V]         (NULL = zero)
+ *
+ * Limits of this build: d * sizeof(element) <= 8192 bytes (bf16: d <= 4096,
+ * f32: d <= 2048); H <= 4096; r <= 1024; batch <= 128.
+ */
+typedef struct {
+  int32_t d;
+  int32_t vocab;
+  int32_t gru_hidden;
+  int32_t rank;
+  int32_t block;
+  int32_t dtype; /* domino_dtype */
+  const void *lm_head;
+  const void *embed;
+  const void *w_ih;
+  const void *w_hh;
+  const void *b_ih;
+  const void *b_hh;
+  const void *w1;
+  const void *b1;
+  const void *w2;
+  const void *b2;
+} domino_head;
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int domino_version(void);
+
+/* Static text for a domino_status code. */
+const char *domino_status_string(int status);
+
+/* Host-only check of a head descriptor (sizes, dtype, pointers, alignment).
+ * Touches no device memory and makes no HIP call. */
+int domino_check_head(const domino_head *head);
+
+/* Bytes of device workspace that domino_draft_block needs for `batch` blocks. */
+int domino_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);
+
+/*
+ * Base logits of every position of every block, in one pass over the frozen
+ * LM head ([notes] §二.1(1); [explainer] §三):
+ *     base_logits[b, i, v] = sum_k hidden[b, i, k] * lm_head[v, k]
+ * hidden      [batch, K, d] (head dtype), 16-byte aligned
+ * base_logits [batch, K, V] float32 (output)
+ * Products are accumulated in float32.  batch == 0 is a no-op.
+ */
+int domino_base_logits(const domino_head *head, int32_t batch, const void *hidden,
+                       float *base_logits, void *stream);
+
+/*
+ * One draft block per batch row: the Domino head's serial causal-correction
+ * loop ([notes] §二.1(2) items 1-3; [explainer] §四):
+ *   g_{-1} = 0;  for i = 0 … K-1:
+ *     g_i  = GRU(embed[prev_i], g_{i-1})      prev_0 = x_t[b];
+ *                                              prev_i = tokens[b, i-1], or
+ *                                              teacher[b, i-1] when teacher != NULL
+ *     L_i  = base_logits[b, i] + W2 SiLU(W1 [hidden[b, i] ; g_i] + b1) + b2
+ *     tokens[b, i] = argmax_v L_i[v]                      (temperature == 0)
+ *                  = argmax_v L_i[v] / T + G[b, i, v]     (temperature T > 0)
+ *   Ties go to the lowest index.  G = -ln(-ln U) with U from Philox4x32-10:
+ *   counter (v >> 2, i, b, offset), key (seed low 32 bits, seed high 32 bits),
+ *   word = output lane (v & 3), U = ((word >> 9) + 0.5) * 2^-23.
+ *
+ * hidden      [batch, K, d] head dtype          base_logits [batch, K, V] float32
+ * x_t         [batch] int32                     teacher     [batch, K] int32 or NULL
+ * tokens      [batch, K] int32 (output)
+ * logits      [batch, K, V] float32 or NULL (output: the corrected logits L_i)
+ * gru_states  [batch, K, H] float32 or NULL (output: g_i)
+ * workspace   device scratch of at least domino_workspace_size() bytes,
+ *             256-byte aligned; its contents are overwritten.
+ * Arithmetic: float32 throughout; bf16 weights are multiplied in bf16 by the
+ * matrix cores with float32 accumulation, and float32 activations are fed to
+ * them as a bf16 (high, low) pair so they keep about 16 significant bits.
+ */
+int domino_draft_block(const domino_head *head, int32_t batch, const void *hidden,
+                       const float *base_logits, const int32_t *x_t, const int32_t *teacher,
+                       float temperature, uint64_t seed, uint32_t offset, int32_t *tokens,
+                       float *logits, float *gru_states, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Acceptance length of each draft row ([notes] §一.1 item 1): the number of
+ * leading positions j with draft[b, j] == target[b, j], in 0 … block.
+ * draft, target [batch, block] int32; accept [batch] int32 (output).
+ * block in 1 … 1024; batch == 0 is a no-op.
+ */
+int domino_accept_len(int32_t batch, int32_t block, const int32_t *draft, const int32_t *target,
+                      int32_t *accept, void *stream);
+
+/*
+ * Test hook: out[j] = the Philox word that domino_draft_block uses for
+ * vocabulary entry v0 + j of position pos of block b (see above).
+ * out: device buffer of n uint32.  n in 0 … 2^26.
+ */
+int domino_debug_philox(uint64_t seed, uint32_t offset, int32_t b, int32_t pos, int32_t v0, int32_t n,
+                        uint32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DOMINO_H_ */

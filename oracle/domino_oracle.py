@@ -214,7 +214,7 @@ def pick_token(scores) -> int:
 
 
 def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
-                seed: int = 0, offset: int = 0, base=None):
+                seed: int = 0, offset: int = 0, base=None, batch_index=None):
     """One draft block per batch row, position by position.
 
     [notes] §二.1 and [explainer] §三–§四, in their order:
@@ -229,6 +229,9 @@ def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
 
     head: dict with lm_head, embed, w_ih, w_hh, b_ih, b_hh, w1, b1, w2, b2
     (float64 or bf16 bits).  hidden [B, K, d]; x_t [B]; teacher [B, K] or None.
+    batch_index [B] (optional): the block index b that keys the sampler's
+    random stream for each row (default 0 … B-1), so that a subset of a
+    larger batch can be recomputed.
     Returns dict(tokens [B, K] int32, logits [B, K, V], states [B, K, H],
     scores [B, K, V], base [B, K, V]).
     """
@@ -245,6 +248,7 @@ def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
     logits = np.zeros((B, K, V))
     states = np.zeros((B, K, H))
     scores = np.zeros((B, K, V))
+    rows = np.arange(B) if batch_index is None else np.asarray(batch_index)
     for b in range(B):
         g = np.zeros(H)
         prev = int(x_t[b])
@@ -253,7 +257,7 @@ def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
             states[b, i] = g
             dl = correction_logits(hidden[b, i], g, f["w1"], f["b1"], f["w2"], f["b2"])
             logits[b, i] = base[b, i] + dl
-            scores[b, i] = sampling_scores(logits[b, i], temperature, seed, offset, b, i)
+            scores[b, i] = sampling_scores(logits[b, i], temperature, seed, offset, int(rows[b]), i)
             tokens[b, i] = pick_token(scores[b, i])
             prev = int(teacher[b, i]) if teacher is not None else int(tokens[b, i])
     return {"tokens": tokens, "logits": logits, "states": states, "scores": scores,

@@ -1,0 +1,156 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side validation returns the documented status codes (no GPU call is
+made for rejected arguments; accepted arguments fail cleanly without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import draft_block_causal_amd as D
+from draft_block_causal_amd._lib import DominoHeadStruct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "domino.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_ARG, E_WS, E_HIP, E_UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return D.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(domino_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(D.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.domino_version() >= 100
+    for code in range(-8, 1):
+        assert lib.domino_status_string(code)
+    assert lib.domino_status_string(-99) == b"unknown status"
+
+
+def fake_head(**kw):
+    base = 0x10000
+    f = dict(d=256, vocab=4096, gru_hidden=128, rank=32, block=16, dtype=1)
+    f.update({k: v for k, v in kw.items() if k in f})
+    ptrs = {k: base * (i + 1) for i, k in enumerate(
+        ["lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2"])}
+    ptrs.update({k: v for k, v in kw.items() if k in ptrs})
+    return DominoHeadStruct(f["d"], f["vocab"], f["gru_hidden"], f["rank"], f["block"], f["dtype"],
+                            *[ptrs[k] for k in ["lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1",
+                                                "w2", "b2"]])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK),
+    ({"dtype": 0}, OK),
+    ({"dtype": 7}, E_DTYPE),
+    ({"d": 0}, E_SHAPE),
+    ({"d": 100}, E_SHAPE),
+    ({"gru_hidden": 48}, E_SHAPE),
+    ({"rank": 20}, E_SHAPE),
+    ({"block": 0}, E_SHAPE),
+    ({"block": 65}, E_SHAPE),
+    ({"vocab": 0}, E_SHAPE),
+    ({"lm_head": 0}, E_NULL),
+    ({"w2": 0}, E_NULL),
+    ({"b_ih": 0, "b_hh": 0, "b1": 0, "b2": 0}, OK),
+    ({"w1": 0x10008}, E_ALIGN),
+    ({"d": 4096}, OK),
+    ({"d": 4128}, E_UNSUP),
+    ({"d": 4096, "dtype": 0}, E_UNSUP),
+    ({"d": 2048, "dtype": 0}, OK),
+])
+def test_check_head(lib, kw, code):
+    h = fake_head(**kw)
+    assert lib.domino_check_head(ctypes.byref(h)) == code
+    assert lib.domino_check_head(None) == E_NULL
+
+
+def test_workspace_size(lib):
+    h = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=256)
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_workspace_size(ctypes.byref(h), 1, ctypes.byref(sz)) == OK
+    one = sz.value
+    assert one > 0 and one % 256 == 0
+    assert lib.domino_workspace_size(ctypes.byref(h), 128, ctypes.byref(sz)) == OK
+    assert sz.value > one
+    assert lib.domino_workspace_size(ctypes.byref(h), -1, ctypes.byref(sz)) == E_SHAPE
+    assert lib.domino_workspace_size(ctypes.byref(h), 129, ctypes.byref(sz)) == E_UNSUP
+    assert lib.domino_workspace_size(ctypes.byref(h), 1, None) == E_NULL
+
+
+def _draft(lib, h, batch=1, hidden=0x20000, base=0x30000, x_t=0x40000, teacher=None, temp=0.0, tokens=0x50000,
+           logits=None, states=None, ws=0x100000, ws_bytes=1 << 30):
+    return lib.domino_draft_block(ctypes.byref(h), batch, hidden, base, x_t, teacher, temp, 0, 0, tokens, logits,
+                                  states, ws, ws_bytes, None)
+
+
+def test_draft_block_validation(lib):
+    h = fake_head()
+    assert _draft(lib, h, batch=-1) == E_SHAPE
+    assert _draft(lib, h, batch=129) == E_UNSUP
+    assert _draft(lib, h, temp=-1.0) == E_ARG
+    assert _draft(lib, h, temp=float("nan")) == E_ARG
+    assert _draft(lib, h, temp=float("inf")) == E_ARG
+    assert _draft(lib, h, hidden=None) == E_NULL
+    assert _draft(lib, h, x_t=None) == E_NULL
+    assert _draft(lib, h, tokens=None) == E_NULL
+    assert _draft(lib, h, hidden=0x20004) == E_ALIGN
+    assert _draft(lib, h, logits=0x60008) == E_ALIGN
+    assert _draft(lib, h, ws=None) == E_WS
+    assert _draft(lib, h, ws=0x100010) == E_WS
+    assert _draft(lib, h, ws_bytes=1024) == E_WS
+    assert _draft(lib, h, batch=0) == OK  # empty batch: nothing to do, no GPU needed
+    bad = fake_head(d=100)
+    assert _draft(lib, bad) == E_SHAPE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour without a GPU")
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    h = fake_head()
+    assert _draft(lib, h) == E_HIP
+    assert lib.domino_base_logits(ctypes.byref(h), 1, 0x20000, 0x30000, None) == E_HIP
+    assert lib.domino_accept_len(4, 16, 0x1000, 0x2000, 0x3000, None) == E_HIP
+
+
+def test_base_logits_and_accept_validation(lib):
+    h = fake_head()
+    assert lib.domino_base_logits(ctypes.byref(h), -1, 0x20000, 0x30000, None) == E_SHAPE
+    assert lib.domino_base_logits(ctypes.byref(h), 1, None, 0x30000, None) == E_NULL
+    assert lib.domino_base_logits(ctypes.byref(h), 1, 0x20002, 0x30000, None) == E_ALIGN
+    assert lib.domino_base_logits(ctypes.byref(h), 0, None, None, None) == OK
+    assert lib.domino_accept_len(-1, 16, 0x1000, 0x2000, 0x3000, None) == E_SHAPE
+    assert lib.domino_accept_len(4, 0, 0x1000, 0x2000, 0x3000, None) == E_SHAPE
+    assert lib.domino_accept_len(4, 16, None, 0x2000, 0x3000, None) == E_NULL
+    assert lib.domino_accept_len(0, 16, None, None, None, None) == OK
+    assert lib.domino_debug_philox(0, 0, 0, 0, 0, -1, 0x1000, None) == E_SHAPE
+    assert lib.domino_debug_philox(0, 0, 0, 0, 0, 0, None, None) == OK
+    assert lib.domino_debug_philox(0, 0, 0, 0, 0, 5, None, None) == E_NULL
+
+
+def test_binding_rejects_bad_tensors():
+    t = {"lm_head": torch.zeros(64, 32), "embed": torch.zeros(64, 32), "w_ih": torch.zeros(96, 32),
+         "w_hh": torch.zeros(96, 32), "b_ih": torch.zeros(96), "b_hh": torch.zeros(96),
+         "w1": torch.zeros(32, 64), "b1": torch.zeros(32), "w2": torch.zeros(64, 32), "b2": torch.zeros(64)}
+    h = D.Head(t, block=4)
+    assert (h.vocab, h.d, h.gru_hidden, h.rank) == (64, 32, 32, 32)
+    bad = dict(t, w2=torch.zeros(64, 31))
+    with pytest.raises(ValueError):
+        D.Head(bad)
+    with pytest.raises(TypeError):
+        D.Head(dict(t, w1=t["w1"].double()))

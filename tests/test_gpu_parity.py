@@ -1,0 +1,277 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Every input is seeded and synthetic (domino_synth).  Rules:
+  * base logits, teacher-forced logits: max-abs error <= 2e-2;
+  * GRU states: max-abs error <= 1e-3;
+  * free-running tokens: identical to the oracle re-run teacher-forced on the
+    GPU's own tokens, except where that oracle's top-2 margin is below 2e-2
+    (the GPU token must then score within 2e-2 of the maximum);
+  * accept lengths and Philox words: bit-exact.
+Full-size workloads are checked in full on a few blocks and on sampled
+outputs for the rest.
+"""
+import numpy as np
+import pytest
+import torch
+
+import domino_synth as S
+import oracle as O
+from _helpers import LOGIT_TOL, STATE_TOL, check_replay, device_head, head_f64, log, workload_arrays
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import draft_block_causal_amd as D
+
+    D.load_library()
+    return torch.device("cuda:0")
+
+
+def _t(a, dev):
+    return S.to_torch(np.ascontiguousarray(a), dev)
+
+
+def _gpu_block(D, head, hidden_t, base, x_t, teacher_t, w, dev):
+    B, K, V, H = hidden_t.shape[0], w.block, w.vocab, w.gru_hidden
+    logits = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    states = torch.empty((B, K, H), dtype=torch.float32, device=dev)
+    tok = D.domino_draft_block(head, hidden_t, base, x_t, teacher=teacher_t, temperature=w.temperature,
+                               seed=w.philox_seed, offset=0, logits=logits, gru_states=states)
+    return tok, logits, states
+
+
+def _sampled_checks(w, f, inp, teacher, base_gpu, logits_tf, states_tf, n=4096, seed=123):
+    """Oracle values at random (b, i, v) for every block, one definition at a time."""
+    rng = np.random.default_rng(seed)
+    B, K, V = inp["hidden"].shape[0], w.block, w.vocab
+    hid = O.as_f64(inp["hidden"])
+    bs, is_, vs = rng.integers(0, B, n), rng.integers(0, K, n), rng.integers(0, V, n)
+    base_o = np.einsum("nk,nk->n", hid[bs, is_], f["lm_head"][vs])
+    err = np.abs(base_gpu[bs, is_, vs] - base_o).max()
+    assert err <= LOGIT_TOL, f"sampled base logits err {err}"
+    # teacher-forced GRU states for every block, batched over blocks
+    g = np.zeros((B, w.gru_hidden))
+    prev = inp["x_t"].astype(np.int64)
+    states = np.zeros((B, K, w.gru_hidden))
+    for i in range(K):
+        g = O.gru_cell(f["embed"][prev], g, f["w_ih"], f["w_hh"], f["b_ih"], f["b_hh"])
+        states[:, i] = g
+        prev = teacher[:, i].astype(np.int64)
+    serr = np.abs(states_tf - states).max()
+    assert serr <= STATE_TOL, f"teacher-forced GRU states err {serr}"
+    uniq = np.unique(vs)
+    dl = O.correction_logits(hid, states, f["w1"], f["b1"], f["w2"][uniq], f["b2"][uniq])
+    col = np.searchsorted(uniq, vs)
+    L = base_o + dl[bs, is_, col]
+    lerr = np.abs(logits_tf[bs, is_, vs] - L).max()
+    assert lerr <= LOGIT_TOL, f"sampled teacher-forced logits err {lerr}"
+    return err, serr, lerr
+
+
+def _parity(w, dev, check_blocks=None, sampled=False):
+    import draft_block_causal_amd as D
+
+    log(f"{w.name}: generating inputs")
+    head_np, inp = workload_arrays(w)
+    f = head_f64(w)
+    head = device_head(w, dev)
+    B, K, V = inp["hidden"].shape[0], w.block, w.vocab
+    hidden_t = _t(inp["hidden"], dev)
+    x_t = _t(inp["x_t"], dev)
+    teacher = S.make_tokens((B, K), V, seed=7)
+    teacher_t = _t(teacher, dev)
+    log(f"{w.name}: GPU base logits + teacher-forced + free-running")
+    base = D.domino_base_logits(head, hidden_t)
+    tok_tf, log_tf, st_tf = _gpu_block(D, head, hidden_t, base, x_t, teacher_t, w, dev)
+    tok_fr, log_fr, st_fr = _gpu_block(D, head, hidden_t, base, x_t, None, w, dev)
+    torch.cuda.synchronize()
+    base_g = base.cpu().numpy()
+    tok_tf, log_tf, st_tf = tok_tf.cpu().numpy(), log_tf.cpu().numpy(), st_tf.cpu().numpy()
+    tok_fr, log_fr, st_fr = tok_fr.cpu().numpy(), log_fr.cpu().numpy(), st_fr.cpu().numpy()
+    assert tok_fr.min() >= 0 and tok_fr.max() < V
+
+    sel = np.arange(B) if check_blocks is None else np.asarray(check_blocks)
+    log(f"{w.name}: oracle on blocks {sel.tolist()}")
+    hid = O.as_f64(inp["hidden"][sel])
+    base_o = O.base_logits(hid, f["lm_head"])
+    berr = np.abs(base_g[sel] - base_o).max()
+    assert berr <= LOGIT_TOL, f"base logits err {berr}"
+    o_tf = O.draft_block(f, hid, inp["x_t"][sel], teacher=teacher[sel], temperature=w.temperature,
+                         seed=w.philox_seed, base=base_o, batch_index=sel)
+    terr = np.abs(log_tf[sel] - o_tf["logits"]).max()
+    serr = np.abs(st_tf[sel] - o_tf["states"]).max()
+    assert terr <= LOGIT_TOL, f"teacher-forced logits err {terr}"
+    assert serr <= STATE_TOL, f"teacher-forced GRU state err {serr}"
+    ties_tf, _ = check_replay(tok_tf[sel], o_tf)
+    o_fr = O.draft_block(f, hid, inp["x_t"][sel], teacher=tok_fr[sel], temperature=w.temperature,
+                         seed=w.philox_seed, base=base_o, batch_index=sel)
+    ferr = np.abs(log_fr[sel] - o_fr["logits"]).max()
+    fserr = np.abs(st_fr[sel] - o_fr["states"]).max()
+    assert ferr <= LOGIT_TOL, f"free-running replay logits err {ferr}"
+    assert fserr <= STATE_TOL, f"free-running replay GRU state err {fserr}"
+    ties_fr, npos = check_replay(tok_fr[sel], o_fr)
+    log(f"{w.name}: base {berr:.2e}  tf-logits {terr:.2e}  states {serr:.2e}  fr-logits {ferr:.2e}  "
+        f"near-ties tf {ties_tf}/{npos} fr {ties_fr}/{npos}")
+    if sampled:
+        e = _sampled_checks(w, f, inp, teacher, base_g, log_tf, st_tf)
+        log(f"{w.name}: sampled over all blocks: base {e[0]:.2e} states {e[1]:.2e} logits {e[2]:.2e}")
+    return tok_fr
+
+
+# ----------------------------------------------------------------- workloads
+def test_tiny_f32_b1(dev):
+    _parity(S.get_workload("tiny_f32_b1"), dev)
+
+
+def test_tiny_stress_b4_greedy(dev):
+    _parity(S.get_workload("tiny_stress_b4"), dev)
+
+
+def test_tiny_stress_b4_sampled(dev):
+    _parity(S.get_workload("tiny_stress_b4").with_(temperature=1.0, philox_seed=0x1234_5678_9ABC), dev)
+
+
+def test_qwen3_8b_b1_greedy(dev):
+    _parity(S.get_workload("qwen3_8b_b1_greedy"), dev)
+
+
+def test_qwen3_8b_b32_t1(dev):
+    _parity(S.get_workload("qwen3_8b_b32_t1"), dev, check_blocks=[0, 31], sampled=True)
+
+
+def test_qwen3_4b_b8_tied(dev):
+    _parity(S.get_workload("qwen3_4b_b8_tied"), dev, check_blocks=[0, 7], sampled=True)
+
+
+def test_qwen3_8b_b128_accept(dev):
+    import draft_block_causal_amd as D
+
+    w = S.get_workload("qwen3_8b_b128_accept")
+    _parity(w, dev, check_blocks=[0, 127], sampled=True)
+    draft = S.make_tokens((w.batch, w.block), w.vocab, seed=11)
+    target = S.make_targets(draft, w.vocab, p=0.9, seed=1)
+    acc = D.domino_accept_len(_t(draft, dev), _t(target, dev)).cpu().numpy()
+    np.testing.assert_array_equal(acc, O.accept_len(draft, target))
+
+
+# ---------------------------------------------------------------- edge cases
+def _small(dtype="bf16", **kw):
+    base = dict(name="small", batch=3, block=5, d=64, vocab=1000, gru_hidden=32, rank=32, dtype=dtype,
+                tied=False, temperature=0.0, init="fanin")
+    base.update(kw)
+    return S.Workload(**base)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_vocab_and_block(dev, dtype):
+    # V = 1000 is not a multiple of the 16-row tile; K = 5 is odd
+    _parity(_small(dtype), dev)
+
+
+@pytest.mark.parametrize("batch", [16, 17, 33, 65])
+def test_batch_tile_boundaries(dev, batch):
+    _parity(_small("bf16", batch=batch, vocab=777, block=3, d=96, gru_hidden=64), dev)
+
+
+def test_sampled_small_temperature_and_ties(dev):
+    _parity(_small("bf16", temperature=0.37, philox_seed=99), dev)
+
+
+def test_all_equal_logits_pick_lowest_index(dev):
+    import draft_block_causal_amd as D
+
+    w = _small("bf16", batch=2)
+    head_np, inp = S.make_workload(w)
+    head_np = dict(head_np)
+    for k in ("lm_head", "w2", "b2"):
+        head_np[k] = np.zeros_like(head_np[k])
+    t = {k: _t(v, dev) for k, v in head_np.items()}
+    head = D.Head(t, block=w.block)
+    hidden = _t(inp["hidden"], dev)
+    base = D.domino_base_logits(head, hidden)
+    tok = D.domino_draft_block(head, hidden, base, _t(inp["x_t"], dev))
+    assert (tok.cpu().numpy() == 0).all()
+
+
+def test_empty_batch_is_noop(dev):
+    import draft_block_causal_amd as D
+
+    w = _small("bf16")
+    head_np, inp = S.make_workload(w, batch=0)
+    head = D.Head({k: _t(v, dev) for k, v in head_np.items()}, block=w.block)
+    hidden = _t(inp["hidden"], dev)
+    base = D.domino_base_logits(head, hidden)
+    tok = D.domino_draft_block(head, hidden, base, _t(inp["x_t"], dev))
+    assert tok.shape == (0, w.block)
+    acc = D.domino_accept_len(torch.zeros((0, 16), dtype=torch.int32, device=dev),
+                              torch.zeros((0, 16), dtype=torch.int32, device=dev))
+    assert acc.shape == (0,)
+
+
+def test_teacher_last_position_is_unused(dev):
+    import draft_block_causal_amd as D
+
+    w = _small("bf16")
+    head_np, inp = S.make_workload(w)
+    head = D.Head({k: _t(v, dev) for k, v in head_np.items()}, block=w.block)
+    hidden = _t(inp["hidden"], dev)
+    base = D.domino_base_logits(head, hidden)
+    teacher = S.make_tokens((w.batch, w.block), w.vocab, seed=3)
+    outs = []
+    for last in (0, w.vocab - 1):
+        teacher[:, -1] = last
+        lg = torch.empty((w.batch, w.block, w.vocab), device=dev)
+        tok = D.domino_draft_block(head, hidden, base, _t(inp["x_t"], dev), teacher=_t(teacher, dev), logits=lg)
+        outs.append((tok.cpu().numpy(), lg.cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_determinism_qwen3_8b_b1(dev):
+    import draft_block_causal_amd as D
+
+    w = S.get_workload("qwen3_8b_b1_greedy")
+    _, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    hidden, x_t = _t(inp["hidden"], dev), _t(inp["x_t"], dev)
+    runs = []
+    for _ in range(2):
+        base = D.domino_base_logits(head, hidden)
+        lg = torch.empty((1, w.block, w.vocab), device=dev)
+        st = torch.empty((1, w.block, w.gru_hidden), device=dev)
+        tok = D.domino_draft_block(head, hidden, base, x_t, logits=lg, gru_states=st)
+        runs.append([x.cpu().numpy() for x in (base, tok, lg, st)])
+    for a, b in zip(*runs):
+        np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------- bit-exact
+@pytest.mark.parametrize("seed,offset,b,pos,v0,n", [
+    (0, 0, 0, 0, 0, 4096),
+    (0x0123_4567_89AB_CDEF, 7, 31, 15, 151000, 936),
+    (2 ** 64 - 1, 2 ** 32 - 1, 127, 63, 3, 1001),
+])
+def test_philox_words_bit_exact(dev, seed, offset, b, pos, v0, n):
+    import draft_block_causal_amd as D
+
+    got = D.domino_debug_philox(seed, offset, b, pos, v0, n, device=dev).cpu().numpy().view(np.uint32)
+    want = O.philox_words(seed, offset, b, pos, np.arange(v0, v0 + n))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_accept_len_bit_exact_edges(dev):
+    import draft_block_causal_amd as D
+
+    rng = np.random.default_rng(5)
+    for B, K in [(1, 1), (7, 16), (128, 16), (300, 33)]:
+        draft = rng.integers(0, 5, size=(B, K)).astype(np.int32)
+        target = np.where(rng.random((B, K)) < 0.8, draft, rng.integers(0, 5, size=(B, K))).astype(np.int32)
+        target[0] = draft[0]  # a full match
+        if B > 1:
+            target[1, 0] = draft[1, 0] + 1  # an immediate mismatch
+        got = D.domino_accept_len(_t(draft, dev), _t(target, dev)).cpu().numpy()
+        np.testing.assert_array_equal(got, O.accept_len(draft, target))
