@@ -2,6 +2,8 @@
 // the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "kernels.h"
@@ -26,6 +28,16 @@ int device_cu_count() {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DOMINO_OK : DOMINO_ERR_HIP; }
+
+// DOMINO_LOOP=persistent | multi selects the loop schedule (default: three
+// kernels per position).
+int loop_mode() {
+  const char* m = std::getenv("DOMINO_LOOP");
+  if (!m) return 0;
+  if (std::strcmp(m, "persistent") == 0) return 1;
+  if (std::strcmp(m, "multi") == 0) return 2;
+  return 0;
+}
 
 }  // namespace
 
@@ -86,9 +98,12 @@ extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const voi
   a.part_ih = reinterpret_cast<float*>(ws + w.part_ih);
   a.part_hh = reinterpret_cast<float*>(ws + w.part_hh);
   a.u = reinterpret_cast<float*>(ws + w.u);
+  a.xpart = reinterpret_cast<unsigned long long*>(ws + w.xchg);
+  a.xwords = w.xwords;
+  a.max_wg = domino::kMaxLoopWorkgroups;
   a.ks = w.ks;
   a.num_cu = num_cu;
-  return hip_status(domino::launch_draft_loop(a, static_cast<hipStream_t>(stream)));
+  return hip_status(domino::launch_draft_loop(a, loop_mode(), static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int domino_accept_len(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,

@@ -13,6 +13,10 @@ namespace domino {
 hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                              const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
 
+// Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 64 == 0 (else hipErrorNotSupported).
+hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
+                               float* C, int ldc, hipStream_t s);
+
 struct LoopArgs {
   int dtype;
   int B, K, d, V, H, r;
@@ -29,16 +33,25 @@ struct LoopArgs {
   float* logits;
   float* states;  // [B, K, H]
   // workspace pieces
-  unsigned long long* keys;  // [K, B]
+  unsigned long long* keys;  // [K, B], followed by 2 u64 of loop control (barrier counter, status)
   float* P;                  // [B, K, r]
   float* part_ih;            // [KS, B, 3H]
   float* part_hh;            // [B, 3H]
   float* u;                  // [B, r]
+  // persistent schedule: tagged exchange words (xpart, xg, xu, xkey back to back)
+  unsigned long long* xpart;
+  size_t xwords;
+  int max_wg;
   int ks;
   int num_cu;
 };
 
-hipError_t launch_draft_loop(const LoopArgs& a, hipStream_t s);
+// Runs the K-position loop.  mode: 0 = default (three kernels per position),
+// 1 = one persistent cooperative kernel (B <= 32), 2 = three kernels per position.
+hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s);
+
+hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
+hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s);

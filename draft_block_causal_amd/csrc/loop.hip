@@ -1,0 +1,718 @@
+// The Domino head's serial loop on gfx950 ([notes] §二.1(2) items 1-3;
+// [explainer] §四): for each of the K positions, the GRU reads the embedding
+// of the previous token, the low-rank correction is added to the base logits,
+// and the next token is picked.
+//
+// Pages: [notes] "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn);
+//        [explainer] the yhxrc.cn article on the Domino paper.
+//
+// Each position has three phases, written once as device functions:
+//   1. gru_partial_job  - GRU pre-activations W_ih e(prev) (split over K) and
+//                         W_hh g on the matrix cores, one 16-row tile per wave;
+//   2. gates_u_tile     - GRU gates -> new state; u = SiLU(P + W1[:, d:] g);
+//   3. w2_sample_block  - L = L_base + W2 u + b2 (+ Gumbel noise), vocabulary
+//                         argmax as a 64-bit key max.
+// Two schedules run them:
+//   * three kernels per position (Plain exchange: ordinary stores, kernel
+//     boundaries order the phases);
+//   * one persistent cooperative kernel (Tagged exchange): every value that
+//     crosses workgroups is a 64-bit word {tag, payload} written and read with
+//     relaxed agent-scope atomics; a consumer spins (bounded) until each word
+//     carries the tag of the current position.  No grid barrier and no memory
+//     fence is needed: each word validates itself.  Exchange buffers are
+//     double-buffered by position parity and cleared before every call.
+//     Reuse is safe because the phases form a chain: a buffer of parity q is
+//     rewritten at position i + 2 only after every reader of position i has
+//     produced an input that position i + 1 waits for.
+#include <algorithm>
+#include <cstdlib>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace domino {
+
+struct Plain {
+  static constexpr bool kTagged = false;
+};
+struct Tagged {
+  static constexpr bool kTagged = true;
+};
+
+template <class T>
+struct DevLoop {
+  using E = typename T::elem;
+  int B, K, d, V, H, r, KS;
+  const E *embed, *w_ih, *w_hh, *b_ih, *b_hh, *w1, *w2, *b2;
+  const float* base;
+  const int32_t *x_t, *teacher;
+  float inv_temp;
+  int sampled;
+  uint64_t seed;
+  uint32_t offset;
+  float *logits, *states, *P, *part_ih, *part_hh, *u;
+  unsigned long long* keys;  // [K, B]  (three-kernel schedule)
+  unsigned int* ctrl;        // [1]: non-zero once a persistent-kernel wait gave up
+  int32_t* tokens;
+  // persistent schedule: tagged exchange buffers, each [2 (parity)][...]
+  unsigned long long* xpart;  // [2][KS + 1][B][3H]: W_ih slices, then W_hh
+  unsigned long long* xg;     // [2][B][H]
+  unsigned long long* xu;     // [2][B][r]
+  unsigned long long* xkey;   // [2][G][B]
+};
+
+// ---------------------------------------------------------------------------
+// tagged words
+// ---------------------------------------------------------------------------
+constexpr unsigned int kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ void put_word(unsigned long long* p, unsigned long long w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void put_f32(unsigned long long* p, float v, uint32_t tag) {
+  put_word(p, ((unsigned long long)tag << 32) | __float_as_uint(v));
+}
+
+__device__ __forceinline__ bool gave_up(const unsigned int* status) {
+  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+// Bounded wait until *p carries `tag` in its high 32 bits.  Returns false when
+// the wait gives up (too many polls, or another workgroup already gave up).
+__device__ __forceinline__ bool wait_f32(const unsigned long long* p, uint32_t tag, const unsigned int* status,
+                                         float& v) {
+  unsigned int spins = 0;
+  for (;;) {
+    const unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == tag) {
+      v = __uint_as_float((uint32_t)w);
+      return true;
+    }
+    if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
+      v = 0.f;
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Tagged argmax key: ordered score (32) | tag (8) | 0xFFFFFF - v (24).  Among
+// keys of one position the order is (score, lower index); the reader checks
+// the tag.  Requires V < 2^24.
+__device__ __forceinline__ unsigned long long tagged_key(float s, uint32_t v, uint32_t tag) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | ((unsigned long long)(tag & 0xFFu) << 24) |
+         (unsigned long long)(0xFFFFFFu - v);
+}
+
+__device__ __forceinline__ bool key_has_tag(unsigned long long k, uint32_t tag) {
+  return k != 0ull && ((uint32_t)(k >> 24) & 0xFFu) == (tag & 0xFFu);
+}
+
+__device__ __forceinline__ int tagged_key_token(unsigned long long k) {
+  return (int)(0xFFFFFFu - (uint32_t)(k & 0xFFFFFFull));
+}
+
+__device__ __forceinline__ int gru_jobs(int H, int KS, int step) {
+  const int T3 = (3 * H) >> 4;
+  return T3 * KS + (step > 0 ? T3 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1, one wave job over 16-row tiles of the stacked gate rows (3H):
+//   job < T3*KS : tile t, K-slice ks of W_ih e(tok)   -> slice ks
+//   otherwise   : tile t of W_hh g_{step-1}           -> slice KS
+// tok[b] (LDS) is the token each batch row feeds to the GRU at this step.
+// Batch rows are the matrix-core M dimension (MT tiles of 16).
+// ---------------------------------------------------------------------------
+template <class T, int MT, class X>
+__device__ bool gru_partial_job(const DevLoop<T>& p, int step, int job, const int* tok) {
+  using E = typename T::elem;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int H = p.H, d = p.d, B = p.B;
+  const int T3 = (3 * H) >> 4;
+  const int n_ih = T3 * p.KS;
+  const int G3 = 3 * H;
+  const uint32_t tag = step + 1;
+  const int par = step & 1;
+  bool ok = true;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int slice, n;
+  if (job < n_ih) {
+    const int ks = job / T3, t = job - ks * T3;
+    slice = ks;
+    const int kc = d / p.KS;
+    n = t * 16 + col;
+    const unsigned char* wrow =
+        reinterpret_cast<const unsigned char*>(p.w_ih + (size_t)n * d + (size_t)ks * kc) + grp * 16;
+    const unsigned char* erow[MT];
+    bool live[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int b = mt * 16 + col;
+      live[mt] = b < B;
+      const int tk = live[mt] ? tok[b] : 0;
+      erow[mt] = reinterpret_cast<const unsigned char*>(p.embed + (size_t)tk * d + (size_t)ks * kc) + grp * 16;
+    }
+    const int bytes = kc * (int)sizeof(E);
+#pragma unroll 4
+    for (int kb = 0; kb < bytes; kb += 64) {
+      const u32x4 w = ld16(wrow + kb);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 a = live[mt] ? ld16(erow[mt] + kb) : u32x4{0, 0, 0, 0};
+        acc[mt] = mma16<T>(acc[mt], a, w);
+      }
+    }
+  } else {
+    const int t = job - n_ih;
+    slice = p.KS;
+    n = t * 16 + col;
+    const unsigned char* wrow = reinterpret_cast<const unsigned char*>(p.w_hh + (size_t)n * H) + grp * 16;
+    constexpr int EPF = T::kPer16B;  // k elements per lane per fragment
+#pragma unroll 2
+    for (int k0 = 0; k0 < H; k0 += 4 * EPF) {
+      const u32x4 w = ld16(wrow + (size_t)k0 * sizeof(E));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int b = mt * 16 + col;
+        ActFrag<T> a;
+        if (b < B) {
+          float x[EPF];
+          if constexpr (X::kTagged) {
+            const unsigned long long* src = p.xg + ((size_t)(par ^ 1) * B + b) * H + k0 + grp * EPF;
+#pragma unroll
+            for (int e = 0; e < EPF; ++e) ok &= wait_f32(src + e, step, p.ctrl, x[e]);
+          } else {
+            const float* src = p.states + ((size_t)b * p.K + step - 1) * H + k0 + grp * EPF;
+#pragma unroll
+            for (int e = 0; e < EPF; e += 4) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+              x[e] = v[0];
+              x[e + 1] = v[1];
+              x[e + 2] = v[2];
+              x[e + 3] = v[3];
+            }
+          }
+          a.from_f32(x);
+        } else {
+          a.zero();
+        }
+        acc[mt] = a.mma(acc[mt], w);
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = mt * 16 + grp * 4 + j;
+      if (b < B) {
+        if constexpr (X::kTagged) {
+          put_f32(p.xpart + (((size_t)par * (p.KS + 1) + slice) * B + b) * G3 + n, acc[mt][j], tag);
+        } else if (slice < p.KS) {
+          p.part_ih[((size_t)slice * B + b) * G3 + n] = acc[mt][j];
+        } else {
+          p.part_hh[(size_t)b * G3 + n] = acc[mt][j];
+        }
+      }
+    }
+  return ok;
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2 for bottleneck rows 16t..16t+15 (one 256-thread workgroup).  For each
+// slice of 16 batch rows it recomputes the new GRU state of those rows (every
+// participating workgroup computes identical values; t == 0 stores them),
+// then u = SiLU(P + W1[:, d:] g).  LDS: 16 x (H + 4) floats + 4 KB.
+// ---------------------------------------------------------------------------
+template <class T, class X>
+__device__ bool gates_u_tile(const DevLoop<T>& p, int step, int t, unsigned char* smem) {
+  using E = typename T::elem;
+  const int H = p.H, B = p.B, G3 = 3 * H, KS = p.KS;
+  float* gt = reinterpret_cast<float*>(smem);  // [16][H + 4]
+  const int gstride = H + 4;
+  float* red = gt + 16 * gstride;  // [4][16][16]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int ldw1 = p.d + H;
+  constexpr int EPF = T::kPer16B;
+  const uint32_t tag = step + 1;
+  const int par = step & 1;
+  bool ok = true;
+
+  for (int m0 = 0; m0 < B; m0 += 16) {
+    for (int idx = threadIdx.x; idx < 16 * H; idx += blockDim.x) {
+      const int rr = idx / H, j = idx - rr * H;
+      const int b = m0 + rr;
+      float g = 0.f;
+      if (b < B) {
+        float a3[3] = {0.f, 0.f, 0.f}, c3[3] = {0.f, 0.f, 0.f}, gp = 0.f;
+        for (int q = 0; q < 3; ++q) {
+          for (int ks = 0; ks < KS; ++ks) {
+            float x;
+            if constexpr (X::kTagged) {
+              ok &= wait_f32(p.xpart + (((size_t)par * (KS + 1) + ks) * B + b) * G3 + q * H + j, tag, p.ctrl, x);
+            } else {
+              x = p.part_ih[((size_t)ks * B + b) * G3 + q * H + j];
+            }
+            a3[q] += x;
+          }
+          if (step > 0) {
+            if constexpr (X::kTagged) {
+              ok &= wait_f32(p.xpart + (((size_t)par * (KS + 1) + KS) * B + b) * G3 + q * H + j, tag, p.ctrl, c3[q]);
+            } else {
+              c3[q] = p.part_hh[(size_t)b * G3 + q * H + j];
+            }
+          }
+          if (p.b_ih) a3[q] += T::to_f32(p.b_ih[q * H + j]);
+          if (p.b_hh) c3[q] += T::to_f32(p.b_hh[q * H + j]);
+        }
+        if (step > 0) {
+          if constexpr (X::kTagged) {
+            ok &= wait_f32(p.xg + ((size_t)(par ^ 1) * B + b) * H + j, step, p.ctrl, gp);
+          } else {
+            gp = p.states[((size_t)b * p.K + step - 1) * H + j];
+          }
+        }
+        const float rg = sigmoidf_(a3[0] + c3[0]);
+        const float zg = sigmoidf_(a3[1] + c3[1]);
+        const float ng = tanhf(a3[2] + rg * c3[2]);
+        g = (1.f - zg) * ng + zg * gp;
+        if (t == 0) {
+          p.states[((size_t)b * p.K + step) * H + j] = g;
+          if constexpr (X::kTagged) put_f32(p.xg + ((size_t)par * B + b) * H + j, g, tag);
+        }
+      }
+      gt[rr * gstride + j] = g;
+    }
+    if constexpr (X::kTagged) {
+      if (__syncthreads_or(!ok)) return false;
+    } else {
+      __syncthreads();
+    }
+
+    // u rows t*16 + col; the four waves take interleaved 64-byte K chunks
+    const int row = t * 16 + col;
+    const unsigned char* wrow =
+        reinterpret_cast<const unsigned char*>(p.w1 + (size_t)row * ldw1 + p.d) + grp * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = wave * 4 * EPF; k0 < H; k0 += 16 * EPF) {
+      const u32x4 w = ld16(wrow + (size_t)k0 * sizeof(E));
+      ActFrag<T> a;
+      a.from_f32(gt + col * gstride + k0 + grp * EPF);
+      acc = a.mma(acc, w);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[(wave * 16 + grp * 4 + j) * 16 + col] = acc[j];
+    __syncthreads();
+    {
+      const int rr = threadIdx.x >> 4, c = threadIdx.x & 15;
+      const int b = m0 + rr;
+      if (b < B) {
+        const float s = red[(0 * 16 + rr) * 16 + c] + red[(1 * 16 + rr) * 16 + c] +
+                        red[(2 * 16 + rr) * 16 + c] + red[(3 * 16 + rr) * 16 + c];
+        const int q = t * 16 + c;
+        const float pre = p.P[((size_t)b * p.K + step) * p.r + q] + s;
+        const float uv = pre * sigmoidf_(pre);
+        if constexpr (X::kTagged)
+          put_f32(p.xu + ((size_t)par * B + b) * p.r + q, uv, tag);
+        else
+          p.u[(size_t)b * p.r + q] = uv;
+      }
+    }
+    __syncthreads();
+  }
+  return true;
+}
+
+template <class T>
+__host__ __device__ constexpr int act_parts() {
+  return (int)(sizeof(ActFrag<T>) / 16);  // bf16 weights: (hi, lo) pair; f32: one
+}
+
+template <class T>
+__host__ __device__ inline size_t w2_lds_bytes(int r, int rows) {
+  return (size_t)act_parts<T>() * rows * (r * sizeof(typename T::elem) + 16) + 4 * rows * sizeof(unsigned long long);
+}
+
+__host__ __device__ inline size_t gates_lds_bytes(int H) { return 16 * (size_t)(H + 4) * sizeof(float) + 4096; }
+
+// ---------------------------------------------------------------------------
+// Phase 3 for batch rows m0 .. m0 + 16*MT - 1 and vocabulary tiles
+// bx, bx + nbx, ... (one 256-thread workgroup).  u is staged in LDS as
+// matrix-core operands; each wave streams 16-row tiles of W2, adds b2 and the
+// base logits, optionally stores the logits, draws Gumbel noise, and keeps a
+// running argmax key per batch row; keys are reduced across lanes and waves.
+// Plain: merged into keys[step][b] with a 64-bit atomic max.  Tagged: the
+// workgroup's key is published in xkey[parity][bx][b].
+// ---------------------------------------------------------------------------
+template <class T, int MT, class X>
+__device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, int m0, unsigned char* smem) {
+  using E = typename T::elem;
+  constexpr int EPF = T::kPer16B;
+  constexpr int NPARTS = act_parts<T>();
+  const int B = p.B, V = p.V, r = p.r;
+  const int row_bytes = r * (int)sizeof(E);
+  const int lds_stride = row_bytes + 16;
+  constexpr int rows = 16 * MT;
+  const uint32_t tag = step + 1;
+  const int par = step & 1;
+  unsigned long long* kred = reinterpret_cast<unsigned long long*>(smem + NPARTS * rows * lds_stride);
+  bool ok = true;
+
+  for (int idx = threadIdx.x; idx < rows * (r / EPF); idx += blockDim.x) {
+    const int rr = idx / (r / EPF), c = idx - rr * (r / EPF);
+    const int b = m0 + rr;
+    ActFrag<T> a;
+    if (b < B) {
+      float x[EPF];
+      if constexpr (X::kTagged) {
+        const unsigned long long* src = p.xu + ((size_t)par * B + b) * r + c * EPF;
+#pragma unroll
+        for (int e = 0; e < EPF; ++e) ok &= wait_f32(src + e, tag, p.ctrl, x[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPF; ++e) x[e] = p.u[(size_t)b * r + c * EPF + e];
+      }
+      a.from_f32(x);
+    } else {
+      a.zero();
+    }
+    const u32x4* parts = reinterpret_cast<const u32x4*>(&a);
+#pragma unroll
+    for (int q = 0; q < NPARTS; ++q) st16(smem + (q * rows + rr) * lds_stride + c * 16, parts[q]);
+  }
+  if constexpr (X::kTagged) {
+    if (__syncthreads_or(!ok)) return false;
+  } else {
+    __syncthreads();
+  }
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int ntiles = (V + 15) >> 4;
+  unsigned long long best[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) best[mt][j] = 0ull;
+
+  for (int t = bx * 4 + wave; t < ntiles; t += nbx * 4) {
+    const int v = t * 16 + col;
+    const unsigned char* wrow = reinterpret_cast<const unsigned char*>(p.w2 + (size_t)min(v, V - 1) * r) + grp * 16;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kb = 0; kb < row_bytes; kb += 64) {
+      const u32x4 w = ld16(wrow + kb);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < NPARTS; ++q) {
+          const u32x4 a = ld16(smem + (q * rows + mt * 16 + col) * lds_stride + grp * 16 + kb);
+          acc[mt] = mma16<T>(acc[mt], a, w);
+        }
+    }
+    if (v < V) {
+      const float bv = p.b2 ? T::to_f32(p.b2[v]) : 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int b = m0 + mt * 16 + grp * 4 + j;
+          if (b < B) {
+            const size_t o = ((size_t)b * p.K + step) * V + v;
+            const float L = p.base[o] + (acc[mt][j] + bv);
+            if (p.logits) p.logits[o] = L;
+            float s = L;
+            if (p.sampled) s = L * p.inv_temp + gumbel_from_word(philox_word(p.seed, p.offset, b, step, v));
+            const unsigned long long k = X::kTagged ? tagged_key(s, v, tag) : argmax_key(s, v);
+            best[mt][j] = k > best[mt][j] ? k : best[mt][j];
+          }
+        }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned long long k = best[mt][j];
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) {
+        const unsigned long long o = __shfl_xor(k, sh, 64);
+        k = o > k ? o : k;
+      }
+      best[mt][j] = k;
+    }
+  if (col == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kred[wave * rows + mt * 16 + grp * 4 + j] = best[mt][j];
+  }
+  __syncthreads();
+  for (int rr = threadIdx.x; rr < rows; rr += blockDim.x) {
+    unsigned long long k = kred[rr];
+    for (int w = 1; w < 4; ++w) k = kred[w * rows + rr] > k ? kred[w * rows + rr] : k;
+    const int b = m0 + rr;
+    if (b < B) {
+      if constexpr (X::kTagged) {
+        // a workgroup without vocabulary tiles still publishes a tagged (lowest) key
+        if (k == 0ull) k = (unsigned long long)(tag & 0xFFu) << 24;
+        put_word(p.xkey + ((size_t)par * nbx + bx) * B + b, k);
+      } else if (k != 0ull) {
+        atomicMax(p.keys + (size_t)step * B + b, k);
+      }
+    }
+  }
+  __syncthreads();  // LDS is reused by the caller
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// three-kernels-per-position schedule
+// ---------------------------------------------------------------------------
+template <class T, int MT>
+__global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step) {
+  __shared__ int tok[16 * MT];
+  for (int b = threadIdx.x; b < p.B && b < 16 * MT; b += blockDim.x) {
+    int tk;
+    if (step == 0)
+      tk = p.x_t[b];
+    else if (p.teacher)
+      tk = p.teacher[(size_t)b * p.K + step - 1];
+    else
+      tk = key_token(p.keys[(size_t)(step - 1) * p.B + b]);
+    tok[b] = min(max(tk, 0), p.V - 1);
+  }
+  __syncthreads();
+  const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (job < gru_jobs(p.H, p.KS, step)) gru_partial_job<T, MT, Plain>(p, step, job, tok);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) gates_u_kernel(DevLoop<T> p, int step) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  gates_u_tile<T, Plain>(p, step, blockIdx.x, smem);
+}
+
+template <class T, int MT>
+__global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  w2_sample_block<T, MT, Plain>(p, step, blockIdx.x, gridDim.x, blockIdx.y * 16 * MT, smem);
+}
+
+// ---------------------------------------------------------------------------
+// persistent schedule
+// ---------------------------------------------------------------------------
+
+// Reduce the tagged keys that all G workgroups published for position `step`
+// (tag step + 1) into picked[b].  Runs on one wave.
+template <class T>
+__device__ bool reduce_keys(const DevLoop<T>& p, int step, int G, int* picked) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t tag = step + 1;
+  const int par = step & 1;
+  bool ok = true;
+  for (int b = 0; b < p.B; ++b) {
+    unsigned long long best = 0ull;
+    for (int w = lane; w < G; w += 64) {
+      const unsigned long long* src = p.xkey + ((size_t)par * G + w) * p.B + b;
+      unsigned long long k = 0ull;
+      unsigned int spins = 0;
+      for (;;) {
+        k = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (key_has_tag(k, tag)) break;
+        if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(p.ctrl))) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const unsigned long long o = __shfl_xor(best, sh, 64);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) picked[b] = tagged_key_token(best);
+  }
+  return ok;
+}
+
+template <class T>
+__device__ void loop_failed(const DevLoop<T>& p) {
+  if (threadIdx.x == 0) atomicOr(p.ctrl, 1u);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < p.B * p.K; i += gridDim.x * blockDim.x) p.tokens[i] = -1;
+}
+
+template <class T, int MT>
+__global__ void __launch_bounds__(256) draft_loop_persistent_kernel(DevLoop<T> p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int picked[16 * MT];
+  __shared__ int tok[16 * MT];
+  const int G = gridDim.x;
+  const int wave = threadIdx.x >> 6;
+  const int n_u_tiles = p.r >> 4;
+  for (int step = 0; step < p.K; ++step) {
+    const int jobs = gru_jobs(p.H, p.KS, step);
+    if (blockIdx.x * 4 < jobs) {
+      // tokens picked at step - 1: every workgroup with GRU work reduces the keys itself
+      bool ok = true;
+      if (step > 0 && wave == 0) ok = reduce_keys(p, step - 1, G, picked);
+      if (__syncthreads_or(!ok)) return loop_failed(p);
+      for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
+        if (step > 0 && blockIdx.x == 0) p.tokens[(size_t)b * p.K + step - 1] = picked[b];
+        const int tk = step == 0 ? p.x_t[b] : (p.teacher ? p.teacher[(size_t)b * p.K + step - 1] : picked[b]);
+        tok[b] = min(max(tk, 0), p.V - 1);
+      }
+      __syncthreads();
+      for (int job = blockIdx.x * 4 + wave; job < jobs; job += G * 4)
+        ok &= gru_partial_job<T, MT, Tagged>(p, step, job, tok);
+      if (__syncthreads_or(!ok)) return loop_failed(p);
+    }
+    for (int t = blockIdx.x; t < n_u_tiles; t += G)
+      if (!gates_u_tile<T, Tagged>(p, step, t, smem)) return loop_failed(p);
+    if (!w2_sample_block<T, MT, Tagged>(p, step, blockIdx.x, G, 0, smem)) return loop_failed(p);
+  }
+  if (blockIdx.x == 0) {
+    bool ok = true;
+    if (wave == 0) ok = reduce_keys(p, p.K - 1, G, picked);
+    if (__syncthreads_or(!ok)) return loop_failed(p);
+    for (int b = threadIdx.x; b < p.B; b += blockDim.x) p.tokens[(size_t)b * p.K + p.K - 1] = picked[b];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <class K>
+static hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <class T>
+static DevLoop<T> make_dev(const LoopArgs& a) {
+  using E = typename T::elem;
+  DevLoop<T> p{};
+  p.B = a.B;
+  p.K = a.K;
+  p.d = a.d;
+  p.V = a.V;
+  p.H = a.H;
+  p.r = a.r;
+  p.KS = a.ks;
+  p.embed = static_cast<const E*>(a.embed);
+  p.w_ih = static_cast<const E*>(a.w_ih);
+  p.w_hh = static_cast<const E*>(a.w_hh);
+  p.b_ih = static_cast<const E*>(a.b_ih);
+  p.b_hh = static_cast<const E*>(a.b_hh);
+  p.w1 = static_cast<const E*>(a.w1);
+  p.w2 = static_cast<const E*>(a.w2);
+  p.b2 = static_cast<const E*>(a.b2);
+  p.base = a.base;
+  p.x_t = a.x_t;
+  p.teacher = a.teacher;
+  p.inv_temp = a.inv_temp;
+  p.sampled = a.sampled;
+  p.seed = a.seed;
+  p.offset = a.offset;
+  p.logits = a.logits;
+  p.states = a.states;
+  p.P = a.P;
+  p.part_ih = a.part_ih;
+  p.part_hh = a.part_hh;
+  p.u = a.u;
+  p.keys = a.keys;
+  p.ctrl = reinterpret_cast<unsigned int*>(a.keys + (size_t)a.K * a.B);
+  p.tokens = a.tokens;
+  p.xpart = a.xpart;
+  p.xg = a.xpart + 2 * (size_t)(a.ks + 1) * a.B * 3 * a.H;
+  p.xu = p.xg + 2 * (size_t)a.B * a.H;
+  p.xkey = p.xu + 2 * (size_t)a.B * a.r;
+  return p;
+}
+
+template <class T, int MT>
+static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t s) {
+  hipError_t e;
+  const size_t lds_g = gates_lds_bytes(p.H);
+  if ((e = allow_lds(gates_u_kernel<T>, lds_g)) != hipSuccess) return e;
+  constexpr int MW = MT > 2 ? 2 : MT;  // w2 rows per workgroup: 16 * MW
+  const size_t lds_w = w2_lds_bytes<T>(p.r, 16 * MW);
+  if ((e = allow_lds(w2_sample_kernel<T, MW>, lds_w)) != hipSuccess) return e;
+  const int ntiles = (p.V + 15) / 16;
+  const dim3 wgrid(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW));
+  for (int step = 0; step < p.K; ++step) {
+    const int jobs = (3 * p.H / 16) * p.KS + (step > 0 ? 3 * p.H / 16 : 0);
+    hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((jobs + 3) / 4), dim3(256), 0, s, p, step);
+    hipLaunchKernelGGL(gates_u_kernel<T>, dim3(p.r / 16), dim3(256), lds_g, s, p, step);
+    hipLaunchKernelGGL((w2_sample_kernel<T, MW>), wgrid, dim3(256), lds_w, s, p, step);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return launch_finalize_tokens(p.B, p.K, p.keys, p.tokens, s);
+}
+
+// Returns an error when the grid cannot be co-resident (the caller falls back).
+template <class T, int MT>
+static hipError_t persistent_loop(const DevLoop<T>& p, int num_cu, int max_wg, hipStream_t s) {
+  auto kern = draft_loop_persistent_kernel<T, MT>;
+  const size_t lds = std::max(gates_lds_bytes(p.H), w2_lds_bytes<T>(p.r, 16 * MT));
+  hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 256, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
+  const int G = std::min(num_cu * std::min(per_cu, 2), max_wg);
+  DevLoop<T> pp = p;
+  void* args[] = {&pp};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(G), dim3(256), args, (unsigned)lds, s);
+}
+
+template <class T, int MT>
+static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
+  const DevLoop<T> p = make_dev<T>(a);
+  // keys [K, B] and the control words start at zero on every call
+  hipError_t e = launch_fill_u64(a.keys, a.K * a.B + 1, s);
+  if (e != hipSuccess) return e;
+  // loop-invariant hidden half of the first correction projection (+ b1)
+  e = launch_panel_gemm(a.dtype, a.hidden, a.d, a.B * a.K, a.w1, a.d + a.H, a.r, a.d, a.b1, a.P, a.r, a.num_cu, s);
+  if (e != hipSuccess) return e;
+  if constexpr (MT <= 2) {
+    if (mode == 1) {
+      // the tagged exchange buffers start at zero (no valid tag) on every call
+      e = launch_fill_u64(a.xpart, (int)a.xwords, s);
+      if (e != hipSuccess) return e;
+      return persistent_loop<T, MT>(p, a.num_cu, a.max_wg, s);
+    }
+  }
+  return multi_kernel_loop<T, MT>(p, a.num_cu, s);
+}
+
+template <class T>
+static hipError_t loop_t(const LoopArgs& a, int mode, hipStream_t s) {
+  if (a.B <= 16) return run_loop<T, 1>(a, mode, s);
+  if (a.B <= 32) return run_loop<T, 2>(a, mode, s);
+  if (a.B <= 64) return run_loop<T, 4>(a, mode, s);
+  return run_loop<T, 8>(a, mode, s);
+}
+
+hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s) {
+  if (a.dtype == 1) return loop_t<Bf16>(a, mode, s);
+  return loop_t<F32>(a, mode, s);
+}
+
+}  // namespace domino

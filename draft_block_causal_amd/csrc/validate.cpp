@@ -23,7 +23,7 @@ int check_head(const domino_head* h) {
   const long es = elem_size(h->dtype);
   if ((long)h->d * es > kMaxRowBytes) return DOMINO_ERR_UNSUPPORTED;
   if (h->gru_hidden > kMaxGruHidden || h->rank > kMaxRank) return DOMINO_ERR_UNSUPPORTED;
-  if ((long)h->vocab * h->d > 0x7FFFFFFFL * 8L) return DOMINO_ERR_UNSUPPORTED;
+  if (h->vocab > kMaxVocab) return DOMINO_ERR_UNSUPPORTED;
   return DOMINO_OK;
 }
 
@@ -43,7 +43,7 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   const size_t ks = (size_t)gru_ksplit(h->d);
   size_t off = 0;
   w.keys = off;
-  off += up256(K * B * sizeof(unsigned long long));
+  off += up256((K * B + 2) * sizeof(unsigned long long));  // keys + loop control words
   w.P = off;
   off += up256(B * K * r * sizeof(float));
   w.part_ih = off;
@@ -54,6 +54,11 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   off += up256(B * r * sizeof(float));
   w.states = off;
   off += up256(B * K * H * sizeof(float));
+  // tagged exchange words of the persistent loop: partials, GRU state, u, keys,
+  // each double-buffered by position parity
+  w.xwords = 2 * ((ks + 1) * B * 3 * H + B * H + B * r + (size_t)kMaxLoopWorkgroups * B);
+  w.xchg = off;
+  off += up256(w.xwords * sizeof(unsigned long long));
   w.total = off;
   w.ks = (int)ks;
   return w;

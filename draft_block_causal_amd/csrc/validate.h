@@ -13,9 +13,12 @@ constexpr int kMaxBatch = 128;
 constexpr long kMaxRowBytes = 8192;
 constexpr int kMaxGruHidden = 4096;
 constexpr int kMaxRank = 1024;
+constexpr int kMaxVocab = (1 << 24) - 1;  // the persistent loop's argmax keys hold a 24-bit index
+constexpr int kMaxLoopWorkgroups = 1024;  // persistent loop grid cap (sizes the key exchange buffer)
 
 struct WorkspaceLayout {
-  size_t keys, P, part_ih, part_hh, u, states, total;
+  size_t keys, P, part_ih, part_hh, u, states, xchg, total;
+  size_t xwords;  // 64-bit words in the exchange region
   int ks;
 };
 

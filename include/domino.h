@@ -57,7 +57,7 @@ typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
  * [explainer] §四).  Weight layouts are [out, in], row-major.
  *
  *   d          hidden size of the backbone / LM head input      (multiple of 32)
- *   vocab      V, vocabulary size                               (>= 1)
+ *   vocab      V, vocabulary size                               (1 … 2^24 - 1)
  *   gru_hidden H, GRU state size (1024 in the pages)             (multiple of 32)
  *   rank       r, correction bottleneck (256 in the pages)       (multiple of 32)
  *   block      K, positions per draft block (16 in the pages)    (1 … 64)

@@ -127,19 +127,30 @@ def test_tiny_f32_b1(dev):
     _parity(S.get_workload("tiny_f32_b1"), dev)
 
 
-def test_tiny_stress_b4_greedy(dev):
+LOOP_MODES = ["persistent", "multi"]
+
+
+@pytest.mark.parametrize("mode", LOOP_MODES)
+def test_tiny_stress_b4_greedy(dev, mode, monkeypatch):
+    monkeypatch.setenv("DOMINO_LOOP", mode)
     _parity(S.get_workload("tiny_stress_b4"), dev)
 
 
-def test_tiny_stress_b4_sampled(dev):
+@pytest.mark.parametrize("mode", LOOP_MODES)
+def test_tiny_stress_b4_sampled(dev, mode, monkeypatch):
+    monkeypatch.setenv("DOMINO_LOOP", mode)
     _parity(S.get_workload("tiny_stress_b4").with_(temperature=1.0, philox_seed=0x1234_5678_9ABC), dev)
 
 
-def test_qwen3_8b_b1_greedy(dev):
+@pytest.mark.parametrize("mode", LOOP_MODES)
+def test_qwen3_8b_b1_greedy(dev, mode, monkeypatch):
+    monkeypatch.setenv("DOMINO_LOOP", mode)
     _parity(S.get_workload("qwen3_8b_b1_greedy"), dev)
 
 
-def test_qwen3_8b_b32_t1(dev):
+@pytest.mark.parametrize("mode", LOOP_MODES)
+def test_qwen3_8b_b32_t1(dev, mode, monkeypatch):
+    monkeypatch.setenv("DOMINO_LOOP", mode)
     _parity(S.get_workload("qwen3_8b_b32_t1"), dev, check_blocks=[0, 31], sampled=True)
 
 
@@ -173,7 +184,9 @@ def test_ragged_vocab_and_block(dev, dtype):
 
 
 @pytest.mark.parametrize("batch", [16, 17, 33, 65])
-def test_batch_tile_boundaries(dev, batch):
+@pytest.mark.parametrize("mode", LOOP_MODES)
+def test_batch_tile_boundaries(dev, batch, mode, monkeypatch):
+    monkeypatch.setenv("DOMINO_LOOP", mode if batch <= 32 else "multi")
     _parity(_small("bf16", batch=batch, vocab=777, block=3, d=96, gru_hidden=64), dev)
 
 
