@@ -96,6 +96,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_b1_greedy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-table", action="store_true",
+                    help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
+                         "by W_ih at every position")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -128,6 +131,15 @@ def main() -> int:
     tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
     accept = torch.empty((B,), dtype=torch.int32, device=dev)
     ws = torch.empty(D.domino_workspace_size(head, B), dtype=torch.uint8, device=dev)
+    prepare_ms = None
+    if not args.no_table:
+        # one-time, per-head preparation (outside the timed region): T = W_ih E^T + b_ih
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        D.domino_prepare_gru_table(head)
+        e1.record()
+        torch.cuda.synchronize()
+        prepare_ms = e0.elapsed_time(e1)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -185,7 +197,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian weights and hidden states; no datasets or checkpoints)",
         "config": {"workload": w.name, "batch": B, "block": K, "d": d, "vocab": V, "gru_hidden": H,
-                   "rank": w.rank, "temperature": w.temperature, "tied": w.tied, "parallelism": "none (1 GPU)"},
+                   "rank": w.rank, "temperature": w.temperature, "tied": w.tied, "parallelism": "none (1 GPU)",
+                   "gru_input_table": not args.no_table},
+        "gru_table_prepare_ms": prepare_ms,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     domino_check_head,
     domino_debug_philox,
     domino_draft_block,
+    domino_gru_table_size,
+    domino_prepare_gru_table,
     domino_version,
     domino_workspace_size,
     load_library,

@@ -36,6 +36,8 @@ EXPORTED = [
     "domino_version",
     "domino_status_string",
     "domino_check_head",
+    "domino_gru_table_size",
+    "domino_prepare_gru_table",
     "domino_workspace_size",
     "domino_base_logits",
     "domino_draft_block",
@@ -68,6 +70,7 @@ class DominoHeadStruct(ctypes.Structure):
         ("b1", ctypes.c_void_p),
         ("w2", ctypes.c_void_p),
         ("b2", ctypes.c_void_p),
+        ("gru_input_table", ctypes.c_void_p),
     ]
 
 
@@ -90,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_version": (ctypes.c_int, []),
         "domino_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "domino_check_head": (ctypes.c_int, [HP]),
+        "domino_gru_table_size": (ctypes.c_int, [HP, ctypes.POINTER(SZ)]),
+        "domino_prepare_gru_table": (ctypes.c_int, [HP, P, P]),
         "domino_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
         "domino_base_logits": (ctypes.c_int, [HP, I32, P, P, P]),
         "domino_draft_block": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P, SZ, P]),
@@ -138,7 +143,7 @@ class Head:
 
     NAMES = ("lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1", "w2", "b2")
 
-    def __init__(self, tensors: dict, block: int = 16):
+    def __init__(self, tensors: dict, block: int = 16, gru_input_table: Optional[torch.Tensor] = None):
         lm = tensors["lm_head"]
         self.dtype = lm.dtype
         if self.dtype not in (torch.float32, torch.bfloat16):
@@ -159,9 +164,19 @@ class Head:
                 continue
             _need(t, k, self.dtype, shapes[k], self.device)
             self.tensors[k] = t
+        self.table = None
         self.struct = DominoHeadStruct(
             d, V, H, r, self.block, DOMINO_BF16 if self.dtype == torch.bfloat16 else DOMINO_F32,
-            *[_ptr(self.tensors[k]) for k in self.NAMES])
+            *[_ptr(self.tensors[k]) for k in self.NAMES], None)
+        if gru_input_table is not None:
+            self.set_gru_input_table(gru_input_table)
+
+    def set_gru_input_table(self, table: Optional[torch.Tensor]) -> None:
+        """Attach (or detach, with None) the [V, 3H] float32 GRU input table."""
+        if table is not None:
+            _need(table, "gru_input_table", torch.float32, (self.vocab, 3 * self.gru_hidden), self.device)
+        self.table = table
+        self.struct.gru_input_table = _ptr(table)
 
     @property
     def ref(self):
@@ -180,6 +195,25 @@ def domino_workspace_size(head: Head, batch: int) -> int:
     out = ctypes.c_size_t(0)
     _check("domino_workspace_size", load_library().domino_workspace_size(head.ref, int(batch), ctypes.byref(out)))
     return out.value
+
+
+def domino_gru_table_size(head: Head) -> int:
+    out = ctypes.c_size_t(0)
+    _check("domino_gru_table_size", load_library().domino_gru_table_size(head.ref, ctypes.byref(out)))
+    return out.value
+
+
+def domino_prepare_gru_table(head: Head, table: Optional[torch.Tensor] = None, attach: bool = True,
+                             stream=None) -> torch.Tensor:
+    """Compute T = W_ih E^T + b_ih ([V, 3H] float32) on the device; by default attach it to the head."""
+    if table is None:
+        table = torch.empty((head.vocab, 3 * head.gru_hidden), dtype=torch.float32, device=head.device)
+    _need(table, "table", torch.float32, (head.vocab, 3 * head.gru_hidden), head.device)
+    _check("domino_prepare_gru_table", load_library().domino_prepare_gru_table(
+        head.ref, _ptr(table), _stream_ptr(stream)))
+    if attach:
+        head.set_gru_input_table(table)
+    return table
 
 
 def domino_base_logits(head: Head, hidden: torch.Tensor, base_logits: Optional[torch.Tensor] = None,

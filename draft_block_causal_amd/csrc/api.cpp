@@ -98,12 +98,26 @@ extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const voi
   a.part_ih = reinterpret_cast<float*>(ws + w.part_ih);
   a.part_hh = reinterpret_cast<float*>(ws + w.part_hh);
   a.u = reinterpret_cast<float*>(ws + w.u);
+  a.table = h->gru_input_table;
   a.xpart = reinterpret_cast<unsigned long long*>(ws + w.xchg);
   a.xwords = w.xwords;
   a.max_wg = domino::kMaxLoopWorkgroups;
   a.ks = w.ks;
   a.num_cu = num_cu;
   return hip_status(domino::launch_draft_loop(a, loop_mode(), static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int domino_prepare_gru_table(const domino_head* h, float* table, void* stream) {
+  int st = domino::check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (!table) return DOMINO_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(table) & 15u) != 0) return DOMINO_ERR_ALIGN;
+  const int num_cu = device_cu_count();
+  if (num_cu <= 0) return DOMINO_ERR_HIP;
+  // T[v] = W_ih E[v] + b_ih for every vocabulary entry: C[V][3H] = E W_ih^T + b_ih
+  return hip_status(domino::launch_panel_gemm(h->dtype, h->embed, h->d, h->vocab, h->w_ih, h->d,
+                                              3 * h->gru_hidden, h->d, h->b_ih, table, 3 * h->gru_hidden,
+                                              num_cu, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int domino_accept_len(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,

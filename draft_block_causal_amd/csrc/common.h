@@ -43,6 +43,12 @@ struct F32 {
   __device__ __forceinline__ static float to_f32(elem e) { return e; }
 };
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+// Branches on it then compile to scalar branches: a matrix-core instruction
+// must not sit in a branch that the compiler lowers with a per-lane EXEC mask,
+// which is what happens when the wave index is left in a vector register.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

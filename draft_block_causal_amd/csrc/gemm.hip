@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(kGThreads, 2)
   if (nl >= n_per_xcd || nt >= num_n) return;
   const int m0 = mt * kGBM, n0 = nt * kGBN;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
 

@@ -38,7 +38,8 @@ struct LoopArgs {
   float* part_ih;            // [KS, B, 3H]
   float* part_hh;            // [B, 3H]
   float* u;                  // [B, r]
-  // persistent schedule: tagged exchange words (xpart, xg, xu, xkey back to back)
+  const float* table;  // [V, 3H] = W_ih E^T + b_ih, or nullptr
+  // persistent schedules: tagged exchange words
   unsigned long long* xpart;
   size_t xwords;
   int max_wg;
@@ -49,6 +50,11 @@ struct LoopArgs {
 // Runs the K-position loop.  mode: 0 = default (three kernels per position),
 // 1 = one persistent cooperative kernel (B <= 32), 2 = three kernels per position.
 hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s);
+
+// The B = 1 persistent loop with on-chip weights; hipErrorNotSupported when the
+// shape, dtype or device does not fit it (the caller then uses another schedule).
+hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s);
+size_t b1_exchange_words(int H, int r, int max_wg);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kPanelWaves * 64)
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int ntiles = (N + 15) >> 4;
   const unsigned char* arow = smem + col * lds_stride + grp * 16;
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
                        const typename T::elem* __restrict__ W, int ldw, int N,
                        const typename T::elem* __restrict__ bias, float* __restrict__ C, int ldc) {
   __shared__ float red[kSplitWaves][16][17];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int m0 = blockIdx.y * 16;
   const size_t kbyte0 = (size_t)wave * KW * 64 + grp * 16;

@@ -240,7 +240,7 @@ __device__ bool gates_u_tile(const DevLoop<T>& p, int step, int t, unsigned char
   float* gt = reinterpret_cast<float*>(smem);  // [16][H + 4]
   const int gstride = H + 4;
   float* red = gt + 16 * gstride;  // [4][16][16]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int ldw1 = p.d + H;
   constexpr int EPF = T::kPer16B;
@@ -396,7 +396,7 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
     __syncthreads();
   }
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
   const int ntiles = (V + 15) >> 4;
   unsigned long long best[MT][4];
@@ -495,7 +495,7 @@ __global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step
     tok[b] = min(max(tk, 0), p.V - 1);
   }
   __syncthreads();
-  const int job = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int job = blockIdx.x * 4 + wave_id();
   if (job < gru_jobs(p.H, p.KS, step)) gru_partial_job<T, MT, Plain>(p, step, job, tok);
 }
 
@@ -562,7 +562,7 @@ __global__ void __launch_bounds__(256) draft_loop_persistent_kernel(DevLoop<T> p
   __shared__ int picked[16 * MT];
   __shared__ int tok[16 * MT];
   const int G = gridDim.x;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int n_u_tiles = p.r >> 4;
   for (int step = 0; step < p.K; ++step) {
     const int jobs = gru_jobs(p.H, p.KS, step);
@@ -691,6 +691,16 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
   // loop-invariant hidden half of the first correction projection (+ b1)
   e = launch_panel_gemm(a.dtype, a.hidden, a.d, a.B * a.K, a.w1, a.d + a.H, a.r, a.d, a.b1, a.P, a.r, a.num_cu, s);
   if (e != hipSuccess) return e;
+  if constexpr (MT == 1) {
+    if (mode != 2 && a.B == 1 && a.table) {
+      // on-chip-weight loop for a single block (needs the GRU input table)
+      e = launch_fill_u64(a.xpart, (int)a.xwords, s);
+      if (e != hipSuccess) return e;
+      e = launch_draft_b1(a, s);
+      if (e != hipErrorNotSupported) return e;
+      (void)hipGetLastError();
+    }
+  }
   if constexpr (MT <= 2) {
     if (mode == 1) {
       // the tagged exchange buffers start at zero (no valid tag) on every call

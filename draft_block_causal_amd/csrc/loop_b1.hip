@@ -4,29 +4,31 @@
 // Pages: [notes] "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn);
 //        [explainer] the yhxrc.cn article on the Domino paper.
 //
-// One cooperative launch of G = #CU workgroups (256 threads each) runs the
-// whole K-position loop.  Re-reading W2, W_ih, W_hh and W1 from HBM at every
-// position would cost ~110 MB per position; instead each workgroup loads its
+// One cooperative launch of G = #CU workgroups (512 threads, 8 waves each)
+// runs the whole K-position loop.  Re-reading W2 and W_hh from HBM at every
+// position would cost ~85 MB per position; each workgroup instead loads its
 // share once and keeps it resident:
-//   * W_ih: a contiguous range of U_ih "k-steps" (16 gate rows x 32 inputs,
-//     1 KB) of the stacked [3H, d] matrix, in LDS;
-//   * W_hh: a contiguous range of U_hh k-steps of [3H, H], in registers;
-//   * W2:   a contiguous range of 16-row vocabulary tiles, 4*NR in registers
-//     (NR per wave) and the rest in LDS;
-//   * W1[:, d:] (the GRU half of the first correction projection): workgroups
-//     0..kUnitWGs-1 each hold the columns of their H/kUnitWGs GRU units.
-// Per position i (tags are i + 1; every exchanged word is {tag, payload}
-// written and polled with relaxed agent-scope atomics, double-buffered by the
-// parity of i):
-//   A1. W_hh g_{i-1} partials of each workgroup's k-range       -> x_hh
-//   A2. token y_{i-1} from the G argmax keys, the token's embedding
-//       row staged in LDS, W_ih e partials                       -> x_ih
-//   B.  unit workgroups: gate pre-activations from the partials,
-//       new GRU state for their units (-> states, x_g) and their
-//       share of W1[:, d:] g                                      -> x_pu
-//   C.  every workgroup: u = SiLU(P_i + sum of the shares), its W2 tiles on
-//       the matrix cores, + b2 + base logits (+ Gumbel), argmax   -> x_key
-// A1 runs while the keys of position i-1 are still arriving.
+//   * W2:   a contiguous range of 16-row vocabulary tiles, NR per wave in
+//           registers and the rest in LDS;
+//   * W_hh: a contiguous range of U_hh "k-steps" (16 gate rows x 32 inputs)
+//           of the stacked [3H, H] matrix, in registers;
+//   * W1[:, d:] (the GRU half of the first correction projection): the
+//           kUnitWGs "unit" workgroups hold the columns of their H / kUnitWGs
+//           GRU units in LDS, in place of some of their W2 tiles.
+// The GRU input term W_ih e(y) + b_ih is read from the per-head table
+// T[y] = W_ih E[y] + b_ih (domino_prepare_gru_table): one row gather per
+// position instead of a 25 MB matrix-vector product.
+//
+// Per position i (every exchanged word is {tag = i + 1, payload}, written and
+// polled with relaxed agent-scope atomics, double-buffered by the parity of i):
+//   A. every workgroup: W_hh g_{i-1} partials of its k-range         -> x_hh
+//   B. unit workgroups: y_{i-1} from the G argmax keys, T[y_{i-1}] for their
+//      units, gates, new state (-> states, x_g), their share of
+//      W1[:, d:] g                                                    -> x_pu
+//   C. every workgroup: u = SiLU(P_i + sum of the shares), its W2 tiles on the
+//      matrix cores, + b2 + base logits (+ Gumbel), argmax            -> x_key
+// Every wait is bounded: a workgroup that gives up records it in `status`
+// and all others leave at their next poll; the tokens are then -1.
 #include <algorithm>
 
 #include "common.h"
@@ -35,18 +37,22 @@
 namespace domino {
 namespace b1 {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 constexpr int kUnitWGs = 8;
+constexpr int kUnitMax = 128;  // GRU units per unit workgroup (H <= 1024)
 constexpr unsigned int kSpinLimit = 1u << 20;
 
 struct Params {
   int d, V, H, r, K;
-  int KI, KH;      // 32-element k-steps per gate row: d / 32, H / 32
-  int U_ih, U_hh;  // k-steps of W_ih / W_hh per workgroup (multiples of kWaves)
-  int ntiles;      // ceil(V / 16)
-  int nl;          // W2 tiles per workgroup kept in LDS (capacity)
-  const uint16_t *embed, *w_ih, *w_hh, *b_ih, *b_hh, *w1, *w2, *b2;
+  int KH;      // 32-element k-steps per W_hh row: H / 32
+  int U_hh;    // W_hh k-steps per workgroup (multiple of kWaves)
+  int ntiles;  // ceil(V / 16)
+  int nl;      // W2 tiles kept in LDS by an ordinary workgroup
+  int nl_unit; // ... by a unit workgroup (the rest of its LDS pool holds its W1 columns)
+  int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
+  const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
+  const float* table;     // [V][3H]: W_ih E[v] + b_ih
   const float *base, *P;  // base [K][V], P [K][r] (includes b1)
   const int32_t *x_t, *teacher;
   float inv_temp;
@@ -56,10 +62,10 @@ struct Params {
   float *logits, *states;
   int32_t* tokens;
   unsigned int* status;
-  unsigned long long *x_ih, *x_hh;  // [2][G][2 segments][16]
-  unsigned long long* x_g;          // [2][H]
-  unsigned long long* x_pu;         // [2][kUnitWGs][r]
-  unsigned long long* x_key;        // [2][G]
+  unsigned long long* x_hh;   // [2][G][2 segments][16]
+  unsigned long long* x_g;    // [2][H]
+  unsigned long long* x_pu;   // [2][kUnitWGs][r]
+  unsigned long long* x_key;  // [2][G]
 };
 
 __device__ __forceinline__ unsigned long long ld_word(const unsigned long long* p) {
@@ -71,24 +77,23 @@ __device__ __forceinline__ void put_word(unsigned long long* p, unsigned long lo
 __device__ __forceinline__ void put_f32(unsigned long long* p, float v, uint32_t tag) {
   put_word(p, ((unsigned long long)tag << 32) | __float_as_uint(v));
 }
-__device__ __forceinline__ bool has_tag(unsigned long long w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ bool gave_up(const unsigned int* status) {
+  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
 
-// Polls *p until it carries `tag` (bounded); w holds the last value read.
+// Polls *p until it carries `tag` in its high word (bounded); w is the last value read.
 __device__ __forceinline__ bool settle(const unsigned long long* p, uint32_t tag, const unsigned int* status,
                                       unsigned long long& w) {
   unsigned int spins = 0;
-  while (!has_tag(w, tag)) {
-    if (++spins > kSpinLimit ||
-        ((spins & 63u) == 0u && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-      return false;
-    }
+  while ((uint32_t)(w >> 32) != tag) {
+    if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) return false;
     __builtin_amdgcn_s_sleep(1);
     w = ld_word(p);
   }
   return true;
 }
 
-// Argmax key with the position tag in the low word: score (32) | tag (8) | 0xFFFFFF - v (24).
+// Argmax key carrying the position tag: score (32) | tag (8) | 0xFFFFFF - v (24).
 __device__ __forceinline__ unsigned long long b1_key(float s, uint32_t v, uint32_t tag) {
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0u;
@@ -99,12 +104,13 @@ __device__ __forceinline__ unsigned long long b1_key(float s, uint32_t v, uint32
 __device__ __forceinline__ bool key_tagged(unsigned long long k, uint32_t tag) {
   return k != 0ull && ((uint32_t)(k >> 24) & 0xFFu) == (tag & 0xFFu);
 }
+__device__ __forceinline__ int key_index(unsigned long long k) { return (int)(0xFFFFFFu - (uint32_t)(k & 0xFFFFFFull)); }
 
-// Max over the G argmax keys published for one position (tag), on one wave.
-// The loads of a lane are all in flight before any is checked.
+// Max over the G keys published for one position, on one wave; every load of a
+// lane is in flight before the first is checked.
 __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int G, uint32_t tag,
                                             const unsigned int* status, unsigned long long& best) {
-  constexpr int kMaxPer = 4;  // G <= 4 * 64
+  constexpr int kMaxPer = 4;  // G <= 256
   const int lane = threadIdx.x & 63;
   unsigned long long k[kMaxPer];
 #pragma unroll
@@ -116,8 +122,7 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
     if (lane + q * 64 < G) {
       unsigned int spins = 0;
       while (!key_tagged(k[q], tag)) {
-        if (++spins > kSpinLimit ||
-            ((spins & 63u) == 0u && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+        if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
           ok = false;
           break;
         }
@@ -135,44 +140,24 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
   return ok;
 }
 
-// Workgroups whose k-step range covers gate-row tile t (contiguous ranges of
-// U k-steps over tiles of KT k-steps), and the segment (0: the workgroup's
-// first tile, 1: its second) that holds tile t.
-__device__ __forceinline__ void tile_owners(int t, int KT, int U, int& w_lo, int& w_hi) {
-  w_lo = (t * KT) / U;
-  w_hi = (t * KT + KT - 1) / U;
-}
-__device__ __forceinline__ int tile_segment(int w, int t, int KT, int U) { return ((w * U) / KT == t) ? 0 : 1; }
-
-// Address of the o-th partial (kind 0: W_ih e, 1: W_hh g) of gate row `row`,
-// or nullptr when the tile has fewer owners (or no W_hh term at step 0).
-__device__ __forceinline__ const unsigned long long* partial_ptr(const Params& p, int kind, int row, int o, int par,
-                                                                 int G, int step) {
+// The o-th W_hh partial of gate row `row` (workgroups whose k-step range covers
+// the row's tile, each holding it in segment 0 (its first tile) or 1), or
+// nullptr when the tile has fewer owners.
+__device__ __forceinline__ const unsigned long long* hh_partial(const Params& p, int row, int o, int par, int G) {
   const int t = row >> 4, c = row & 15;
-  const int KT = kind ? p.KH : p.KI, U = kind ? p.U_hh : p.U_ih;
-  if (kind && step == 0) return nullptr;
-  int lo, hi;
-  tile_owners(t, KT, U, lo, hi);
+  const int lo = (t * p.KH) / p.U_hh, hi = (t * p.KH + p.KH - 1) / p.U_hh;
   const int ow = lo + o;
   if (ow > hi) return nullptr;
-  const unsigned long long* base = kind ? p.x_hh : p.x_ih;
-  return base + (((size_t)par * G + ow) * 2 + tile_segment(ow, t, KT, U)) * 16 + c;
+  const int seg = ((ow * p.U_hh) / p.KH == t) ? 0 : 1;
+  return p.x_hh + (((size_t)par * G + ow) * 2 + seg) * 16 + c;
 }
 
-// bf16 hi/lo operand fragment of 8 floats (lanes whose batch row is empty pass zeros).
-__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-  ActFrag<Bf16> a;
-  a.from_f32(x);
-  hi = a.hi;
-  lo = a.lo;
-}
-
-// L_i[v] = base + (W2 u)[v] + b2[v] for the lane's vocabulary entry v (row 0
-// of the accumulator); returns the running argmax key.
-__device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, f32x4 acc, int v, int step, uint32_t tag,
+// L_i[v] = base + (W2 u)[v] + b2[v] for the lane's vocabulary entry (row 0 of
+// the accumulator); returns the running argmax key.
+__device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, float dl, int v, int step, uint32_t tag,
                                                             float lbv, float bbv, unsigned long long best) {
   if (v < p.V) {
-    const float Lv = lbv + (acc[0] + bbv);
+    const float Lv = lbv + (dl + bbv);
     if (p.logits) p.logits[(size_t)step * p.V + v] = Lv;
     float sc = Lv;
     if (p.sampled) sc = Lv * p.inv_temp + gumbel_from_word(philox_word(p.seed, p.offset, 0u, step, v));
@@ -183,72 +168,61 @@ __device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, f32
 }
 
 struct Lds {
-  // byte offsets into dynamic LDS
-  int ihw, w2l, erow, gst, utile, red, gs_new, gs_prev, kred, total;
+  int w2l, w1u, gst, utile, pu, gs_new, gs_prev, red, total;
 };
 
-__host__ __device__ inline Lds lds_layout(int U_ih, int nl, int RK, int d, int H, int r) {
+// The W2 pool is shared: ordinary workgroups keep nl tiles there; unit
+// workgroups keep nl_unit tiles followed by their W1 columns (r x units bf16).
+__host__ __device__ inline Lds lds_layout(int nl, int nl_unit, int RK, int H, int r) {
   Lds L{};
   int off = 0;
-  L.ihw = off;
-  off += U_ih * 1024;
   L.w2l = off;
-  off += nl * RK * 1024;
-  L.erow = off;
-  off += d * 2;
+  L.w1u = nl_unit * RK * 1024;
+  const int unit_pool = L.w1u + r * (H / kUnitWGs) * 2;
+  const int pool = nl * RK * 1024;
+  off += pool > unit_pool ? pool : unit_pool;
   L.gst = off;
   off += H * 4;
   L.utile = off;
   off += r * 4;  // hi then lo, r bf16 each
+  L.pu = off;
+  off += 2 * r * 4;
+  L.gs_new = off;
+  off += kUnitMax * 4;
+  L.gs_prev = off;
+  off += kUnitMax * 4;
   L.red = off;
   off += kWaves * 2 * 16 * 4;
-  L.gs_new = off;
-  off += (H / kUnitWGs) * 4;
-  L.gs_prev = off;
-  off += (H / kUnitWGs) * 4;
-  L.kred = off;
-  off += 64;
   L.total = off;
   return L;
 }
 
-template <int UIW, int UHW, int NR, int RK>
+template <int UHW, int NR, int RK>
 __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ unsigned long long s_key[kWaves];
   __shared__ int s_tok;
-  __shared__ int s_fail;
   const int w = blockIdx.x, G = gridDim.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
-  const int H = p.H, d = p.d, V = p.V, r = p.r;
-  const int rows3 = 3 * H;
-  const int T3 = rows3 >> 4;
-  const Lds L = lds_layout(p.U_ih, p.nl, RK, d, H, r);
-  unsigned char* ihw = smem + L.ihw;
+  const int H = p.H, V = p.V, r = p.r;
+  const int T3 = (3 * H) >> 4;
+  const Lds L = lds_layout(p.nl, p.nl_unit, RK, H, r);
   unsigned char* w2l = smem + L.w2l;
-  const uint16_t* erow = reinterpret_cast<const uint16_t*>(smem + L.erow);
+  const uint16_t* w1u = reinterpret_cast<const uint16_t*>(smem + L.w1u);
   float* gst = reinterpret_cast<float*>(smem + L.gst);
   uint16_t* utile = reinterpret_cast<uint16_t*>(smem + L.utile);
-  float* red = reinterpret_cast<float*>(smem + L.red);
+  float* pu = reinterpret_cast<float*>(smem + L.pu);
   float* gs_new = reinterpret_cast<float*>(smem + L.gs_new);
   float* gs_prev = reinterpret_cast<float*>(smem + L.gs_prev);
-  unsigned long long* kred = reinterpret_cast<unsigned long long*>(smem + L.kred);
-  const int units = H / kUnitWGs;  // GRU units per unit workgroup
+  float* red = reinterpret_cast<float*>(smem + L.red);
+  const int units = H / kUnitWGs;
   const bool unit_wg = w < kUnitWGs;
+  constexpr int kLdsSlots = 2;  // LDS W2 tiles a wave can own: nl <= kLdsSlots * kWaves
+  const int my_nl = unit_wg ? p.nl_unit : p.nl;
 
-  // ---------------- load the resident weights ----------------
-  const long total_ih = (long)T3 * p.KI, total_hh = (long)T3 * p.KH;
-  const long ih0 = (long)w * p.U_ih, hh0 = (long)w * p.U_hh;
-  for (int j = tid; j < p.U_ih * 64; j += kThreads) {
-    const int lu = j >> 6, ln = j & 63;
-    const long gu = ih0 + lu;
-    u32x4 v = {0, 0, 0, 0};
-    if (gu < total_ih) {
-      const int t = (int)(gu / p.KI), s = (int)(gu % p.KI);
-      v = ld16(p.w_ih + (size_t)(t * 16 + (ln & 15)) * d + s * 32 + (ln >> 4) * 8);
-    }
-    st16(ihw + (size_t)lu * 1024 + ln * 16, v);
-  }
+  // ---------------- resident weights ----------------
+  const long total_hh = (long)T3 * p.KH, hh0 = (long)w * p.U_hh;
   u32x4 whh[UHW];
 #pragma unroll
   for (int q = 0; q < UHW; ++q) {
@@ -259,8 +233,18 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       whh[q] = ld16(p.w_hh + (size_t)(t * 16 + col) * H + s * 32 + grp * 8);
     }
   }
-  // W2 tiles [t_lo, t_hi): local j < 4*NR in registers (wave j%4, slot j/4), the rest in LDS
-  const int t_lo = (int)((long)w * p.ntiles / G), t_hi = (int)((long)(w + 1) * p.ntiles / G);
+  int t_lo, t_hi;
+  {
+    const int rest = p.ntiles - kUnitWGs * p.ut, others = G - kUnitWGs;
+    if (unit_wg) {
+      t_lo = w * p.ut;
+      t_hi = t_lo + p.ut;
+    } else {
+      const int o = w - kUnitWGs;
+      t_lo = kUnitWGs * p.ut + (int)((long)o * rest / others);
+      t_hi = kUnitWGs * p.ut + (int)((long)(o + 1) * rest / others);
+    }
+  }
   const int nt = t_hi - t_lo;
   u32x4 w2r[NR][RK];
 #pragma unroll
@@ -271,7 +255,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     for (int k = 0; k < RK; ++k)
       w2r[s][k] = j < nt ? ld16(p.w2 + (size_t)v * r + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
   }
-  for (int j = tid; j < p.nl * RK * 64; j += kThreads) {
+  for (int j = tid; j < my_nl * RK * 64; j += kThreads) {
     const int l = j / (RK * 64), k = (j / 64) % RK, ln = j & 63;
     const int lt = kWaves * NR + l;
     u32x4 v = {0, 0, 0, 0};
@@ -281,47 +265,48 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     }
     st16(w2l + ((size_t)l * RK + k) * 1024 + ln * 16, v);
   }
-  // unit workgroups: their columns of W1[:, d:] for bottleneck row `tid`
-  constexpr int UW = 16;  // 16-byte chunks of the unit slice (128 units / 8)
-  u32x4 w1g[UW];
-  if (unit_wg && tid < r) {
-#pragma unroll
-    for (int c = 0; c < UW; ++c)
-      w1g[c] = (c * 8 < units) ? ld16(p.w1 + (size_t)tid * (d + H) + d + w * units + c * 8) : u32x4{0, 0, 0, 0};
+  // unit workgroups: W1[:, d + w*units : d + (w+1)*units] as [r][units] bf16 in LDS
+  const int urow = tid % r, uhalf = tid / r;
+  const int half_units = units / 2;
+  if (unit_wg) {
+    const int chunks = units / 8;
+    for (int j = tid; j < r * chunks; j += kThreads) {
+      const int row = j / chunks, c = j - row * chunks;
+      st16(smem + L.w1u + ((size_t)row * units + c * 8) * 2, ld16(p.w1 + (size_t)row * (p.d + H) + p.d + w * units + c * 8));
+    }
   }
-  if (tid < units) gs_prev[tid] = 0.f;
+  if (tid < kUnitMax) gs_prev[tid] = 0.f;
   __syncthreads();
 
-  const int t_first_ih = (int)(ih0 / p.KI), t_first_hh = (int)(hh0 / p.KH);
+  const int t_first_hh = (int)(hh0 / p.KH);
+  const long hh_last = min(hh0 + p.U_hh, total_hh) - 1;
+  const int t_last_hh = hh_last >= hh0 ? (int)(hh_last / p.KH) : -1;
   bool ok = true;
   for (int step = 0; step < p.K; ++step) {
     const uint32_t tag = step + 1;
     const int par = step & 1;
-    // prefetch the base logits (and b2) this workgroup's tiles need at this position
-    float lb[NR + 4], bb[NR + 4];
+    // base logits and b2 of this wave's tiles at this position (lanes of row 0 only)
+    float lb[NR + kLdsSlots], bb[NR + kLdsSlots];
 #pragma unroll
-    for (int s = 0; s < NR + 4; ++s) {
-      const int l = (s - NR) * kWaves + wave;  // LDS slot (s >= NR)
+    for (int s = 0; s < NR + kLdsSlots; ++s) {
+      const int l = (s - NR) * kWaves + wave;
       const int j = s < NR ? s * kWaves + wave : kWaves * NR + l;
       const int v = (t_lo + j) * 16 + col;
-      const bool live = j < nt && (s < NR || l < p.nl) && v < V && grp == 0;
+      const bool live = grp == 0 && j < nt && (s < NR || l < my_nl) && v < V;
       lb[s] = live ? p.base[(size_t)step * V + v] : 0.f;
       bb[s] = live && p.b2 ? bf16_to_f32(p.b2[v]) : 0.f;
     }
 
-    // ---------- A1: W_hh g_{i-1} ----------
+    // ---------- A: W_hh g_{i-1} ----------
     if (step > 0) {
       {
-        constexpr int kMaxPer = 4;  // H <= 4 * kThreads
+        constexpr int kPer = 2;  // H <= kPer * kThreads
         const unsigned long long* src = p.x_g + (size_t)(par ^ 1) * H;
-        unsigned long long x[kMaxPer];
+        unsigned long long x[kPer];
 #pragma unroll
-        for (int q = 0; q < kMaxPer; ++q) {
-          const int j = tid + q * kThreads;
-          x[q] = j < H ? ld_word(src + j) : 0ull;
-        }
+        for (int q = 0; q < kPer; ++q) x[q] = tid + q * kThreads < H ? ld_word(src + tid + q * kThreads) : 0ull;
 #pragma unroll
-        for (int q = 0; q < kMaxPer; ++q) {
+        for (int q = 0; q < kPer; ++q) {
           const int j = tid + q * kThreads;
           if (j < H) {
             ok &= settle(src + j, step, p.status, x[q]);
@@ -333,7 +318,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         ok = false;
         break;
       }
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < UHW; ++q) {
         const long gu = hh0 + wave * UHW + q;
@@ -342,140 +327,83 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
           float x[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = col == 0 ? gst[s * 32 + grp * 8 + e] : 0.f;
-          u32x4 hi, lo;
-          split8(x, hi, lo);
-          const int seg = t == t_first_hh ? 0 : 1;
-          if (seg == 0) {
-            acc[0] = mma16<Bf16>(acc[0], hi, whh[q]);
-            acc[0] = mma16<Bf16>(acc[0], lo, whh[q]);
-          } else {
-            acc[1] = mma16<Bf16>(acc[1], hi, whh[q]);
-            acc[1] = mma16<Bf16>(acc[1], lo, whh[q]);
-          }
+          ActFrag<Bf16> a;
+          a.from_f32(x);
+          if (t == t_first_hh)
+            acc0 = a.mma(acc0, whh[q]);
+          else
+            acc1 = a.mma(acc1, whh[q]);
         }
       }
       if (grp == 0) {
-        red[(wave * 2 + 0) * 16 + col] = acc[0][0];
-        red[(wave * 2 + 1) * 16 + col] = acc[1][0];
+        red[(wave * 2 + 0) * 16 + col] = acc0[0];
+        red[(wave * 2 + 1) * 16 + col] = acc1[0];
       }
       __syncthreads();
       if (tid < 32) {
         const int seg = tid >> 4, c = tid & 15;
-        const long last = min(hh0 + p.U_hh, total_hh) - 1;
-        const int t_last = last >= hh0 ? (int)(last / p.KH) : -1;
-        if (t_first_hh + seg <= t_last) {
+        if (t_first_hh + seg <= t_last_hh) {
           float sum = 0.f;
 #pragma unroll
           for (int wv = 0; wv < kWaves; ++wv) sum += red[(wv * 2 + seg) * 16 + c];
           put_f32(p.x_hh + (((size_t)par * G + w) * 2 + seg) * 16 + c, sum, tag);
         }
       }
-      __syncthreads();
     }
 
-    // ---------- A2: the previous token, its embedding row, W_ih e ----------
-    if (wave == 0) {
-      int tok;
-      if (step == 0) {
-        tok = p.x_t[0];
-      } else {
-        unsigned long long best;
-        ok &= gather_keys(p.x_key + (size_t)(par ^ 1) * G, G, step, p.status, best);
-        const int picked = (int)(0xFFFFFFu - (uint32_t)(best & 0xFFFFFFull));
-        if (w == 0 && lane == 0) p.tokens[step - 1] = picked;
-        tok = p.teacher ? p.teacher[step - 1] : picked;
-      }
-      if (lane == 0) s_tok = min(max(tok, 0), V - 1);
-    }
-    if (__syncthreads_or(!ok)) {
-      ok = false;
-      break;
-    }
-    {
-      const uint16_t* e = p.embed + (size_t)s_tok * d;
-      for (int j = tid; j < d / 8; j += kThreads)
-        st16(smem + L.erow + j * 16, ld16(e + j * 8));
-    }
-    __syncthreads();
-    {
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int q = 0; q < UIW; ++q) {
-        const int lu = wave * UIW + q;
-        const long gu = ih0 + lu;
-        if (gu < total_ih) {
-          const int t = (int)(gu / p.KI), s = (int)(gu % p.KI);
-          const u32x4 wv = ld16(ihw + (size_t)lu * 1024 + lane * 16);
-          const u32x4 a = col == 0 ? ld16(erow + s * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-          if (t == t_first_ih)
-            acc[0] = mma16<Bf16>(acc[0], a, wv);
-          else
-            acc[1] = mma16<Bf16>(acc[1], a, wv);
-        }
-      }
-      if (grp == 0) {
-        red[(wave * 2 + 0) * 16 + col] = acc[0][0];
-        red[(wave * 2 + 1) * 16 + col] = acc[1][0];
-      }
-      __syncthreads();
-      if (tid < 32) {
-        const int seg = tid >> 4, c = tid & 15;
-        const long last = min(ih0 + p.U_ih, total_ih) - 1;
-        const int t_last = last >= ih0 ? (int)(last / p.KI) : -1;
-        if (t_first_ih + seg <= t_last) {
-          float sum = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < kWaves; ++wv) sum += red[(wv * 2 + seg) * 16 + c];
-          put_f32(p.x_ih + (((size_t)par * G + w) * 2 + seg) * 16 + c, sum, tag);
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---------- B: unit workgroups -> new state of their units, share of W1[:, d:] g ----------
+    // ---------- B: unit workgroups ----------
     if (unit_wg) {
+      if (wave == 0) {
+        int tok;
+        if (step == 0) {
+          tok = p.x_t[0];
+        } else {
+          unsigned long long best;
+          ok &= gather_keys(p.x_key + (size_t)(par ^ 1) * G, G, step, p.status, best);
+          const int picked = key_index(best);
+          if (w == 0 && lane == 0) p.tokens[step - 1] = picked;
+          tok = p.teacher ? p.teacher[step - 1] : picked;
+        }
+        if (lane == 0) s_tok = min(max(tok, 0), V - 1);
+      }
+      if (__syncthreads_or(!ok)) {
+        ok = false;
+        break;
+      }
       if (tid < units) {
         const int j = w * units + tid;
-        // every partial this unit needs: 3 gate rows x (<= 3 W_ih owners + <= 3 W_hh owners);
-        // all loads are issued before any is checked
-        constexpr int kOwn = 3;
-        unsigned long long x[3][2][kOwn];
+        const float* trow = p.table + (size_t)s_tok * 3 * H;
+        float a3[3];
+        unsigned long long x[3][3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          const int row = q * H + j;
+          a3[q] = trow[q * H + j];
 #pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const unsigned long long* ptr = nullptr;
-#pragma unroll
-            for (int o = 0; o < kOwn; ++o) {
-              ptr = partial_ptr(p, k, row, o, par, G, step);
-              x[q][k][o] = ptr ? ld_word(ptr) : 0ull;
-            }
+          for (int o = 0; o < 3; ++o) {
+            const unsigned long long* src = step > 0 ? hh_partial(p, q * H + j, o, par, G) : nullptr;
+            x[q][o] = src ? ld_word(src) : 0ull;
           }
         }
-        float pre[3], hpre[3];
+        float c3[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          const int row = q * H + j;
-          float acc2[2] = {0.f, 0.f};
+          float h = 0.f;
 #pragma unroll
-          for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int o = 0; o < kOwn; ++o) {
-              const unsigned long long* ptr = partial_ptr(p, k, row, o, par, G, step);
-              if (ptr) {
-                ok &= settle(ptr, tag, p.status, x[q][k][o]);
-                acc2[k] += __uint_as_float((uint32_t)x[q][k][o]);
-              }
+          for (int o = 0; o < 3; ++o) {
+            const unsigned long long* src = step > 0 ? hh_partial(p, q * H + j, o, par, G) : nullptr;
+            if (src) {
+              ok &= settle(src, tag, p.status, x[q][o]);
+              h += __uint_as_float((uint32_t)x[q][o]);
             }
-          pre[q] = acc2[0] + (p.b_ih ? bf16_to_f32(p.b_ih[row]) : 0.f);
-          hpre[q] = acc2[1] + (p.b_hh ? bf16_to_f32(p.b_hh[row]) : 0.f);
+          }
+          c3[q] = h + (p.b_hh ? bf16_to_f32(p.b_hh[q * H + j]) : 0.f);
         }
-        const float rg = sigmoidf_(pre[0] + hpre[0]);
-        const float zg = sigmoidf_(pre[1] + hpre[1]);
-        const float ng = tanhf(pre[2] + rg * hpre[2]);
+        const float rg = sigmoidf_(a3[0] + c3[0]);
+        const float zg = sigmoidf_(a3[1] + c3[1]);
+        const float ng = tanhf(a3[2] + rg * c3[2]);
         const float g = (1.f - zg) * ng + zg * gs_prev[tid];
         gs_new[tid] = g;
+        gs_prev[tid] = g;
         p.states[(size_t)step * H + j] = g;
         put_f32(p.x_g + (size_t)par * H + j, g, tag);
       }
@@ -483,23 +411,22 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         ok = false;
         break;
       }
-      if (tid < r) {
+      if (uhalf < 2) {
+        // bottleneck row urow, units [uhalf * half_units, (uhalf + 1) * half_units)
         float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < UW; ++c) {
+        const uint16_t* wr = w1u + (size_t)urow * units + uhalf * half_units;
+        for (int k = 0; k < half_units; k += 8) {
+          const u32x4 wb = ld16(wr + k);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t wbits = w1g[c][e];
-            const int k = c * 8 + e * 2;
-            if (k < units) {
-              s += bf16_to_f32((uint16_t)(wbits & 0xFFFFu)) * gs_new[k];
-              s += bf16_to_f32((uint16_t)(wbits >> 16)) * gs_new[k + 1];
-            }
+            s += bf16_to_f32((uint16_t)(wb[e] & 0xFFFFu)) * gs_new[uhalf * half_units + k + 2 * e];
+            s += bf16_to_f32((uint16_t)(wb[e] >> 16)) * gs_new[uhalf * half_units + k + 2 * e + 1];
           }
         }
-        put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + tid, s, tag);
+        pu[uhalf * r + urow] = s;
       }
-      if (tid < units) gs_prev[tid] = gs_new[tid];
+      __syncthreads();
+      if (tid < r) put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + tid, pu[tid] + pu[r + tid], tag);
     }
 
     // ---------- C: u, W2 tiles, argmax ----------
@@ -536,14 +463,14 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
           acc = mma16<Bf16>(acc, ahi, w2r[s][k]);
           acc = mma16<Bf16>(acc, alo, w2r[s][k]);
         }
-        best = tile_epilogue(p, acc, grp == 0 ? (t_lo + j) * 16 + col : V, step, tag, lb[s], bb[s], best);
+        if (grp == 0) best = tile_epilogue(p, acc[0], (t_lo + j) * 16 + col, step, tag, lb[s], bb[s], best);
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < kLdsSlots; ++s) {
       const int l = s * kWaves + wave;
       const int j = kWaves * NR + l;
-      if (l < p.nl && j < nt) {
+      if (l < my_nl && j < nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < RK; ++k) {
@@ -553,7 +480,8 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
           acc = mma16<Bf16>(acc, ahi, wv);
           acc = mma16<Bf16>(acc, alo, wv);
         }
-        best = tile_epilogue(p, acc, grp == 0 ? (t_lo + j) * 16 + col : V, step, tag, lb[NR + s], bb[NR + s], best);
+        if (grp == 0)
+          best = tile_epilogue(p, acc[0], (t_lo + j) * 16 + col, step, tag, lb[NR + s], bb[NR + s], best);
       }
     }
 #pragma unroll
@@ -561,23 +489,21 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       const unsigned long long o = __shfl_xor(best, sh, 64);
       best = o > best ? o : best;
     }
-    if (lane == 0) kred[wave] = best;
+    if (lane == 0) s_key[wave] = best;
     __syncthreads();
     if (tid == 0) {
-      unsigned long long k = kred[0];
+      unsigned long long k = s_key[0];
 #pragma unroll
-      for (int wv = 1; wv < kWaves; ++wv) k = kred[wv] > k ? kred[wv] : k;
-      if (k == 0ull) k = (unsigned long long)(tag & 0xFFu) << 24;  // no tiles: a valid lowest key
+      for (int wv = 1; wv < kWaves; ++wv) k = s_key[wv] > k ? s_key[wv] : k;
+      if (k == 0ull) k = (unsigned long long)(tag & 0xFFu) << 24;  // no tiles: a tagged lowest key
       put_word(p.x_key + (size_t)par * G + w, k);
     }
   }
 
-  if (ok && w == 0 && wave == 0) {
-    // the token of the last position
-    const int step = p.K;
+  if (ok && w == 0 && wave == 0) {  // the token of the last position
     unsigned long long best;
-    ok &= gather_keys(p.x_key + (size_t)((step - 1) & 1) * G, G, step, p.status, best);
-    if (lane == 0 && ok) p.tokens[step - 1] = (int)(0xFFFFFFu - (uint32_t)(best & 0xFFFFFFull));
+    ok &= gather_keys(p.x_key + (size_t)((p.K - 1) & 1) * G, G, p.K, p.status, best);
+    if (lane == 0 && ok) p.tokens[p.K - 1] = key_index(best);
   }
   if (!ok) {
     if (tid == 0) atomicOr(p.status, 1u);
@@ -586,9 +512,9 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   }
 }
 
-template <int UIW, int UHW, int NR, int RK>
+template <int UHW, int NR, int RK>
 static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
-  auto kern = draft_b1_kernel<UIW, UHW, NR, RK>;
+  auto kern = draft_b1_kernel<UHW, NR, RK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -605,49 +531,53 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
 }  // namespace b1
 
 size_t b1_exchange_words(int H, int r, int max_wg) {
-  return 2 * ((size_t)max_wg * 2 * 16 * 2 + (size_t)H + (size_t)b1::kUnitWGs * r + (size_t)max_wg);
+  return 2 * ((size_t)max_wg * 2 * 16 + (size_t)H + (size_t)b1::kUnitWGs * r + (size_t)max_wg);
 }
 
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   using namespace b1;
-  constexpr int NR = 8;
-  if (a.dtype != 1 || a.B != 1) return hipErrorNotSupported;
-  if (a.d % 32 || a.H % 32 || a.r != 256 || a.H % kUnitWGs || a.H / kUnitWGs > 128 || a.r > kThreads)
+  constexpr int NR = 3, RK = 8;
+  if (a.dtype != 1 || a.B != 1 || !a.table) return hipErrorNotSupported;
+  if (a.r != RK * 32 || a.H % (2 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 2 * kThreads)
     return hipErrorNotSupported;
-  const int G = std::min(a.num_cu, a.max_wg);
-  const int KI = a.d / 32, KH = a.H / 32, T3 = 3 * a.H / 16;
-  auto round4 = [](long x) { return (int)((x + kWaves - 1) / kWaves * kWaves); };
-  const int U_ih = round4(((long)T3 * KI + G - 1) / G);
-  const int U_hh = round4(((long)T3 * KH + G - 1) / G);
-  if (U_ih > KI || U_hh > KH) return hipErrorNotSupported;  // a range must span at most two tiles
-  const int ntiles = (a.V + 15) / 16;
-  const int per_wg = (ntiles + G - 1) / G;
-  const int nl = std::max(0, per_wg - kWaves * NR);
-  if (nl > 4 * kWaves) return hipErrorNotSupported;
-  constexpr int RK = 8;
-  const Lds L = lds_layout(U_ih, nl, RK, a.d, a.H, a.r);
-  if (L.total > 160 * 1024) return hipErrorNotSupported;
+  const int G = std::min(a.num_cu, std::min(a.max_wg, 256));
   if (G < kUnitWGs) return hipErrorNotSupported;
+  const int KH = a.H / 32, T3 = 3 * a.H / 16;
+  const long need = ((long)T3 * KH + G - 1) / G;
+  const int U_hh = (int)((need + kWaves - 1) / kWaves * kWaves);
+  if (U_hh > KH) return hipErrorNotSupported;  // a range spans at most two tiles
+  const int ntiles = (a.V + 15) / 16;
+  const int units = a.H / kUnitWGs;
+  const int w1_bytes = a.r * units * 2;
+  constexpr int kSlots = 2;  // LDS W2 tiles per wave
+  // unit workgroups give up LDS tiles for their W1 columns; the others take the rest
+  const int nl_max = kSlots * kWaves;
+  const int nl_unit = std::max(0, (nl_max * RK * 1024 - w1_bytes) / (RK * 1024));
+  const int ut = std::min(kWaves * NR + nl_unit, ntiles / G);
+  const int rest = ntiles - kUnitWGs * ut;
+  const int per_other = (rest + (G - kUnitWGs) - 1) / (G - kUnitWGs);
+  const int nl = std::max(0, per_other - kWaves * NR);
+  if (nl > nl_max || G <= kUnitWGs) return hipErrorNotSupported;
+  const Lds L = lds_layout(nl, nl_unit, RK, a.H, a.r);
+  if (L.total > 160 * 1024 - 256) return hipErrorNotSupported;
   Params p{};
   p.d = a.d;
   p.V = a.V;
   p.H = a.H;
   p.r = a.r;
   p.K = a.K;
-  p.KI = KI;
   p.KH = KH;
-  p.U_ih = U_ih;
   p.U_hh = U_hh;
   p.ntiles = ntiles;
   p.nl = nl;
-  p.embed = static_cast<const uint16_t*>(a.embed);
-  p.w_ih = static_cast<const uint16_t*>(a.w_ih);
+  p.nl_unit = nl_unit;
+  p.ut = ut;
   p.w_hh = static_cast<const uint16_t*>(a.w_hh);
-  p.b_ih = static_cast<const uint16_t*>(a.b_ih);
   p.b_hh = static_cast<const uint16_t*>(a.b_hh);
   p.w1 = static_cast<const uint16_t*>(a.w1);
   p.w2 = static_cast<const uint16_t*>(a.w2);
   p.b2 = static_cast<const uint16_t*>(a.b2);
+  p.table = a.table;
   p.base = a.base;
   p.P = a.P;
   p.x_t = a.x_t;
@@ -661,8 +591,6 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.tokens = a.tokens;
   p.status = reinterpret_cast<unsigned int*>(a.keys + (size_t)a.K * a.B);
   unsigned long long* x = a.xpart;
-  p.x_ih = x;
-  x += 2 * (size_t)a.max_wg * 2 * 16;
   p.x_hh = x;
   x += 2 * (size_t)a.max_wg * 2 * 16;
   p.x_g = x;
@@ -670,10 +598,14 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.x_pu = x;
   x += 2 * (size_t)kUnitWGs * a.r;
   p.x_key = x;
-  const int UIW = U_ih / kWaves, UHW = U_hh / kWaves;
-  if (UIW == 24 && UHW == 6) return launch_t<24, 6, NR, RK>(p, G, L.total, s);  // d = 4096, H = 1024, 256 CUs
-  if (UIW == 15 && UHW == 6) return launch_t<15, 6, NR, RK>(p, G, L.total, s);  // d = 2560, H = 1024, 256 CUs
-  return hipErrorNotSupported;
+  const int UHW = U_hh / kWaves;
+  switch (UHW) {
+    case 1: return launch_t<1, NR, RK>(p, G, L.total, s);
+    case 2: return launch_t<2, NR, RK>(p, G, L.total, s);
+    case 3: return launch_t<3, NR, RK>(p, G, L.total, s);
+    case 4: return launch_t<4, NR, RK>(p, G, L.total, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace domino

@@ -20,6 +20,7 @@ int check_head(const domino_head* h) {
   const void* mats[] = {h->lm_head, h->embed, h->w_ih, h->w_hh, h->w1, h->w2};
   for (const void* p : mats)
     if (!aligned16(p)) return DOMINO_ERR_ALIGN;
+  if (h->gru_input_table && !aligned16(h->gru_input_table)) return DOMINO_ERR_ALIGN;
   const long es = elem_size(h->dtype);
   if ((long)h->d * es > kMaxRowBytes) return DOMINO_ERR_UNSUPPORTED;
   if (h->gru_hidden > kMaxGruHidden || h->rank > kMaxRank) return DOMINO_ERR_UNSUPPORTED;
@@ -56,7 +57,9 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   off += up256(B * K * H * sizeof(float));
   // tagged exchange words of the persistent loop: partials, GRU state, u, keys,
   // each double-buffered by position parity
-  w.xwords = 2 * ((ks + 1) * B * 3 * H + B * H + B * r + (size_t)kMaxLoopWorkgroups * B);
+  const size_t multi = 2 * ((ks + 1) * B * 3 * H + B * H + B * r + (size_t)kMaxLoopWorkgroups * B);
+  const size_t single = 2 * ((size_t)kMaxLoopWorkgroups * 2 * 16 + H + 8 * r + (size_t)kMaxLoopWorkgroups);
+  w.xwords = multi > single ? multi : single;
   w.xchg = off;
   off += up256(w.xwords * sizeof(unsigned long long));
   w.total = off;
@@ -122,6 +125,14 @@ extern "C" const char* domino_status_string(int status) {
 extern "C" int domino_version(void) { return 100; }
 
 extern "C" int domino_check_head(const domino_head* head) { return domino::check_head(head); }
+
+extern "C" int domino_gru_table_size(const domino_head* head, size_t* bytes) {
+  if (!bytes) return DOMINO_ERR_NULL;
+  int st = domino::check_head(head);
+  if (st != DOMINO_OK) return st;
+  *bytes = (size_t)head->vocab * 3 * (size_t)head->gru_hidden * sizeof(float);
+  return DOMINO_OK;
+}
 
 extern "C" int domino_workspace_size(const domino_head* head, int32_t batch, size_t* bytes) {
   if (!bytes) return DOMINO_ERR_NULL;

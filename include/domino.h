@@ -73,6 +73,12 @@ typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
  *   b1      [r]         (NULL = zero)
  *   w2      [V, r]      second correction projection to the vocabulary
  *   b2      [V]         (NULL = zero)
+ *   gru_input_table [V, 3H] float32, or NULL: T[v] = W_ih embed[v] + b_ih,
+ *                       the GRU's input pre-activation for every token, filled
+ *                       by domino_prepare_gru_table.  Both factors are frozen,
+ *                       so the table is a per-head constant; when it is given,
+ *                       domino_draft_block reads T[token] instead of
+ *                       multiplying by W_ih at every position.
  *
  * Limits of this build: d * sizeof(element) <= 8192 bytes (bf16: d <= 4096,
  * f32: d <= 2048); H <= 4096; r <= 1024; batch <= 128.
@@ -94,6 +100,7 @@ typedef struct {
   const void *b1;
   const void *w2;
   const void *b2;
+  const float *gru_input_table;
 } domino_head;
 
 /* Library version, as major * 10000 + minor * 100 + patch. */
@@ -105,6 +112,18 @@ const char *domino_status_string(int status);
 /* Host-only check of a head descriptor (sizes, dtype, pointers, alignment).
  * Touches no device memory and makes no HIP call. */
 int domino_check_head(const domino_head *head);
+
+/* Bytes of the head's GRU input table: vocab * 3 * gru_hidden * 4. */
+int domino_gru_table_size(const domino_head *head, size_t *bytes);
+
+/*
+ * Fills table[v, :] = W_ih embed[v] + b_ih for every v (the GRU input
+ * pre-activation of each token, [notes] §二.1(2) item 1), as float32 with the
+ * products accumulated in float32.  table: caller-owned device buffer of
+ * domino_gru_table_size() bytes, 16-byte aligned.  Run once per head; the
+ * result is then passed as head->gru_input_table.
+ */
+int domino_prepare_gru_table(const domino_head *head, float *table, void *stream);
 
 /* Bytes of device workspace that domino_draft_block needs for `batch` blocks. */
 int domino_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);

@@ -52,7 +52,7 @@ def fake_head(**kw):
     ptrs.update({k: v for k, v in kw.items() if k in ptrs})
     return DominoHeadStruct(f["d"], f["vocab"], f["gru_hidden"], f["rank"], f["block"], f["dtype"],
                             *[ptrs[k] for k in ["lm_head", "embed", "w_ih", "w_hh", "b_ih", "b_hh", "w1", "b1",
-                                                "w2", "b2"]])
+                                                "w2", "b2"]], kw.get("gru_input_table"))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -74,11 +74,26 @@ def fake_head(**kw):
     ({"d": 4128}, E_UNSUP),
     ({"d": 4096, "dtype": 0}, E_UNSUP),
     ({"d": 2048, "dtype": 0}, OK),
+    ({"gru_input_table": 0x900000}, OK),
+    ({"gru_input_table": 0x900004}, E_ALIGN),
+    ({"vocab": 1 << 24}, E_UNSUP),
 ])
 def test_check_head(lib, kw, code):
     h = fake_head(**kw)
     assert lib.domino_check_head(ctypes.byref(h)) == code
     assert lib.domino_check_head(None) == E_NULL
+
+
+def test_gru_table_size_and_prepare_validation(lib):
+    h = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=256)
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_gru_table_size(ctypes.byref(h), ctypes.byref(sz)) == OK
+    assert sz.value == 151936 * 3 * 1024 * 4
+    assert lib.domino_gru_table_size(ctypes.byref(h), None) == E_NULL
+    assert lib.domino_prepare_gru_table(ctypes.byref(h), None, None) == E_NULL
+    assert lib.domino_prepare_gru_table(ctypes.byref(h), 0x900004, None) == E_ALIGN
+    bad = fake_head(d=100)
+    assert lib.domino_prepare_gru_table(ctypes.byref(bad), 0x900000, None) == E_SHAPE
 
 
 def test_workspace_size(lib):

@@ -72,13 +72,22 @@ def _sampled_checks(w, f, inp, teacher, base_gpu, logits_tf, states_tf, n=4096, 
     return err, serr, lerr
 
 
-def _parity(w, dev, check_blocks=None, sampled=False):
+def _parity(w, dev, check_blocks=None, sampled=False, table=False):
     import draft_block_causal_amd as D
 
     log(f"{w.name}: generating inputs")
     head_np, inp = workload_arrays(w)
     f = head_f64(w)
     head = device_head(w, dev)
+    if table:
+        D.domino_prepare_gru_table(head)
+    try:
+        return _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled)
+    finally:
+        head.set_gru_input_table(None)
+
+
+def _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled):
     B, K, V = inp["hidden"].shape[0], w.block, w.vocab
     hidden_t = _t(inp["hidden"], dev)
     x_t = _t(inp["x_t"], dev)
@@ -152,6 +161,35 @@ def test_qwen3_8b_b1_greedy(dev, mode, monkeypatch):
 def test_qwen3_8b_b32_t1(dev, mode, monkeypatch):
     monkeypatch.setenv("DOMINO_LOOP", mode)
     _parity(S.get_workload("qwen3_8b_b32_t1"), dev, check_blocks=[0, 31], sampled=True)
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_qwen3_8b_b1_gru_table(dev, temperature):
+    # single block: the on-chip-weight loop, fed by the GRU input table
+    _parity(S.get_workload("qwen3_8b_b1_greedy").with_(temperature=temperature, philox_seed=5), dev, table=True)
+
+
+def test_qwen3_4b_b1_tied_gru_table(dev):
+    _parity(S.get_workload("qwen3_4b_b8_tied").with_(batch=1), dev, table=True)
+
+
+def test_gru_table_matches_oracle(dev):
+    import draft_block_causal_amd as D
+
+    for name in ("tiny_stress_b4", "qwen3_8b_b1_greedy"):
+        w = S.get_workload(name)
+        workload_arrays(w)
+        f = head_f64(w)
+        head = device_head(w, dev)
+        try:
+            table = D.domino_prepare_gru_table(head).cpu().numpy()
+        finally:
+            head.set_gru_input_table(None)
+        rows = np.random.default_rng(3).integers(0, w.vocab, 256)
+        want = f["embed"][rows] @ f["w_ih"].T + f["b_ih"]
+        err = np.abs(table[rows] - want).max()
+        log(f"{name}: GRU input table max err {err:.2e}")
+        assert err <= 1e-4
 
 
 def test_qwen3_4b_b8_tied(dev):
