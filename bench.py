@@ -82,7 +82,7 @@ def cpu_baseline(w, head_np, inp, target, min_seconds: float = 10.0):
         O.accept_len(out["tokens"], target[:1])
         n += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or n >= 50:
+        if el >= min_seconds or n >= 1000:
             break
     return {"value": n / el, "unit": "draft blocks/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} x one {w.name} block (B=1): float64 numpy base logits + 16-position loop + "
@@ -96,6 +96,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_b1_greedy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the benchmark, run a plain device-to-device copy of 1 GiB five times; its "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-traffic counters of the LM head")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -110,6 +113,14 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}), flush=True)
+        return 0
     import domino_synth as S
     import draft_block_causal_amd as D
 
@@ -143,6 +154,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev_draft = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def step(i=None):
         if i is not None:
@@ -152,6 +164,8 @@ def main() -> int:
             ev[i][1].record()
         D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature, seed=w.philox_seed,
                              tokens=tokens, workspace=ws)
+        if i is not None:
+            ev_draft[i].record()
         D.domino_accept_len(tokens, target, accept)
 
     for _ in range(args.warmup):
@@ -164,6 +178,7 @@ def main() -> int:
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     lm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    draft_ms = float(np.mean([b.elapsed_time(c) for (_, b), c in zip(ev, ev_draft)]))
     elem = 2 if w.dtype == "bf16" else 4
     alg = lmhead_algorithmic_bytes(B, K, d, V, elem)
     flops = lmhead_flops(B, K, d, V)
@@ -200,6 +215,8 @@ def main() -> int:
                    "rank": w.rank, "temperature": w.temperature, "tied": w.tied, "parallelism": "none (1 GPU)",
                    "gru_input_table": not args.no_table},
         "gru_table_prepare_ms": prepare_ms,
+        "lm_head_ms": lm_ms,
+        "draft_block_ms": draft_ms,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
