@@ -11,7 +11,8 @@
 //   * W2:   a contiguous range of 16-row vocabulary tiles, NR per wave in
 //           registers and the rest in LDS;
 //   * W_hh: a contiguous range of U_hh "k-steps" (16 gate rows x 32 inputs)
-//           of the stacked [3H, H] matrix, in registers;
+//           of the stacked [3H, H] matrix, in registers (all workgroups but
+//           the unit ones);
 //   * W1[:, d:] (the GRU half of the first correction projection): the
 //           kUnitWGs "unit" workgroups hold the columns of their H / kUnitWGs
 //           GRU units in LDS, in place of some of their W2 tiles.
@@ -21,12 +22,19 @@
 //
 // Per position i (every exchanged word is {tag = i + 1, payload}, written and
 // polled with relaxed agent-scope atomics, double-buffered by the parity of i):
-//   A. every workgroup: W_hh g_{i-1} partials of its k-range         -> x_hh
-//   B. unit workgroups: y_{i-1} from the G argmax keys, T[y_{i-1}] for their
-//      units, gates, new state (-> states, x_g), their share of
-//      W1[:, d:] g                                                    -> x_pu
-//   C. every workgroup: u = SiLU(P_i + sum of the shares), its W2 tiles on the
-//      matrix cores, + b2 + base logits (+ Gumbel), argmax            -> x_key
+//   B(i)   the kUnitWGs unit workgroups: y_{i-1} from the G argmax keys,
+//          T[y_{i-1}] for their units, W_hh g_{i-1} from the partials, gates,
+//          new state g_i (-> states, x_g), their share of W1[:, d:] g_i on
+//          the matrix cores                                        -> x_pu
+//   C(i)   every workgroup: u = SiLU(P_i + sum of the shares), its W2 tiles
+//          on the matrix cores, + b2 + base logits (+ Gumbel), argmax -> x_key
+//   A(i+1) the other workgroups (the W_hh owners), after publishing their
+//          key: W_hh g_i partials of their k-range, from g_i staged in C(i)
+//                                                                  -> x_hh
+// The only exchanges on the token-to-token path are the key gather and the
+// u shares; A(i+1) overlaps the key gather and the T row read of B(i+1).
+// A wave's loads wait for the completion of its earlier stores (one counter
+// covers both), so each role polls before it publishes wherever it can.
 // Every wait is bounded: a workgroup that gives up records it in `status`
 // and all others leave at their next poll; the tokens are then -1.
 #include <algorithm>
@@ -37,19 +45,21 @@
 namespace domino {
 namespace b1 {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
+// One wave per SIMD: each wave may use 512 registers (256 VGPRs + 256 AGPRs),
+// which is where the workgroup's whole share of W2 lives.
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kNR = 10;  // W2 tiles per wave, held in registers
 constexpr int kUnitWGs = 8;
 constexpr int kUnitMax = 128;  // GRU units per unit workgroup (H <= 1024)
 constexpr unsigned int kSpinLimit = 1u << 20;
+constexpr int kMaxWgTiles = kNR * kWaves;  // W2 tiles per workgroup
 
 struct Params {
   int d, V, H, r, K;
   int KH;      // 32-element k-steps per W_hh row: H / 32
-  int U_hh;    // W_hh k-steps per workgroup (multiple of kWaves)
+  int U_hh;    // W_hh k-steps per W_hh owner (multiple of 2 * kWaves)
   int ntiles;  // ceil(V / 16)
-  int nl;      // W2 tiles kept in LDS by an ordinary workgroup
-  int nl_unit; // ... by a unit workgroup (the rest of its LDS pool holds its W1 columns)
   int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
   const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
   const float* table;     // [V][3H]: W_ih E[v] + b_ih
@@ -81,16 +91,38 @@ __device__ __forceinline__ bool gave_up(const unsigned int* status) {
   return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
-// Polls *p until it carries `tag` in its high word (bounded); w is the last value read.
-__device__ __forceinline__ bool settle(const unsigned long long* p, uint32_t tag, const unsigned int* status,
-                                      unsigned long long& w) {
+// Polls the words src[q] (skipping null entries) until each carries `tag` in
+// its high word; x[q] holds the last value read (preloaded by the caller, so
+// all first loads are in flight together).  Bounded: false if the spin limit
+// is reached or another workgroup gave up.
+template <int N>
+__device__ __forceinline__ bool settle_all(const unsigned long long* const (&src)[N], uint32_t tag,
+                                          const unsigned int* status, unsigned long long (&x)[N]) {
   unsigned int spins = 0;
-  while ((uint32_t)(w >> 32) != tag) {
+  while (true) {
+    bool done = true;
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (src[q] && (uint32_t)(x[q] >> 32) != tag) {
+        done = false;
+        x[q] = ld_word(src[q]);
+      }
+    if (done) return true;
     if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) return false;
     __builtin_amdgcn_s_sleep(1);
-    w = ld_word(p);
   }
-  return true;
+}
+
+// Lanes 0..n-1 of one wave poll one word each, src0 + lane * stride, until it
+// carries `tag`: a cheap "probably all there" signal before every thread
+// loads (and tag-checks) its words of a published block, so that the whole
+// grid does not re-poll thousands of words per round.
+__device__ __forceinline__ bool wait_sentinels(const unsigned long long* src0, int n, size_t stride, uint32_t tag,
+                                               const unsigned int* status) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long* src[1] = {lane < n ? src0 + (size_t)lane * stride : nullptr};
+  unsigned long long x[1] = {src[0] ? ld_word(src[0]) : 0ull};
+  return settle_all(src, tag, status, x);
 }
 
 // Argmax key carrying the position tag: score (32) | tag (8) | 0xFFFFFF - v (24).
@@ -113,25 +145,32 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
   constexpr int kMaxPer = 4;  // G <= 256
   const int lane = threadIdx.x & 63;
   unsigned long long k[kMaxPer];
-#pragma unroll
-  for (int q = 0; q < kMaxPer; ++q) k[q] = lane + q * 64 < G ? ld_word(keys + lane + q * 64) : 0ull;
-  bool ok = true;
-  best = 0ull;
+  const unsigned long long* src[kMaxPer];
 #pragma unroll
   for (int q = 0; q < kMaxPer; ++q) {
-    if (lane + q * 64 < G) {
-      unsigned int spins = 0;
-      while (!key_tagged(k[q], tag)) {
-        if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        k[q] = ld_word(keys + lane + q * 64);
-      }
-      best = k[q] > best ? k[q] : best;
-    }
+    src[q] = lane + q * 64 < G ? keys + lane + q * 64 : nullptr;
+    k[q] = src[q] ? ld_word(src[q]) : 0ull;
   }
+  bool ok = true;
+  unsigned int spins = 0;
+  while (true) {
+    bool done = true;
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q)
+      if (src[q] && !key_tagged(k[q], tag)) {
+        done = false;
+        k[q] = ld_word(src[q]);
+      }
+    if (done) break;
+    if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  best = 0ull;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) best = k[q] > best ? k[q] : best;
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) {
     const unsigned long long o = __shfl_xor(best, sh, 64);
@@ -140,27 +179,28 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
   return ok;
 }
 
-// The o-th W_hh partial of gate row `row` (workgroups whose k-step range covers
-// the row's tile, each holding it in segment 0 (its first tile) or 1), or
-// nullptr when the tile has fewer owners.
-__device__ __forceinline__ const unsigned long long* hh_partial(const Params& p, int row, int o, int par, int G) {
+// Word offset, within the parity-0 half of x_hh, of the o-th W_hh partial of
+// gate row `row` (the W_hh owners, i.e. the workgroups after the unit ones,
+// numbered from 0, whose k-step range covers the row's tile, each holding it
+// in segment 0 (its first tile) or 1), or -1 when the tile has fewer owners.
+__device__ __forceinline__ int hh_partial_offset(const Params& p, int row, int o, int G) {
   const int t = row >> 4, c = row & 15;
   const int lo = (t * p.KH) / p.U_hh, hi = (t * p.KH + p.KH - 1) / p.U_hh;
   const int ow = lo + o;
-  if (ow > hi) return nullptr;
+  if (ow > hi) return -1;
   const int seg = ((ow * p.U_hh) / p.KH == t) ? 0 : 1;
-  return p.x_hh + (((size_t)par * G + ow) * 2 + seg) * 16 + c;
+  return (ow * 2 + seg) * 16 + c;
 }
 
-// L_i[v] = base + (W2 u)[v] + b2[v] for the lane's vocabulary entry (row 0 of
-// the accumulator); returns the running argmax key.
+// L_i[v] = (W2 u)[v] + (base + b2)[v] for the lane's vocabulary entry; the
+// score is L_i[v] (greedy) or L_i[v] / T + Gumbel noise; returns the running
+// argmax key.
 __device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, float dl, int v, int step, uint32_t tag,
-                                                            float lbv, float bbv, unsigned long long best) {
+                                                            float bias, float noise, unsigned long long best) {
   if (v < p.V) {
-    const float Lv = lbv + (dl + bbv);
+    const float Lv = dl + bias;
     if (p.logits) p.logits[(size_t)step * p.V + v] = Lv;
-    float sc = Lv;
-    if (p.sampled) sc = Lv * p.inv_temp + gumbel_from_word(philox_word(p.seed, p.offset, 0u, step, v));
+    const float sc = p.sampled ? Lv * p.inv_temp + noise : Lv;
     const unsigned long long k = b1_key(sc, v, tag);
     best = k > best ? k : best;
   }
@@ -168,33 +208,52 @@ __device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, flo
 }
 
 struct Lds {
-  int w2l, w1u, gst, utile, pu, gs_new, gs_prev, red, total;
+  int pool, ghl, utile, lbs, b2s, gum, uhl, gs_prev, zero, red, total;
 };
 
-// The W2 pool is shared: ordinary workgroups keep nl tiles there; unit
-// workgroups keep nl_unit tiles followed by their W1 columns (r x units bf16).
-__host__ __device__ inline Lds lds_layout(int nl, int nl_unit, int RK, int H, int r) {
+// The pool holds a unit workgroup's W1 columns, or a W_hh owner's k-steps,
+// both as matrix-core fragments [.. 16-row tiles][.. k-steps][64 lanes][16 B].
+__host__ __device__ inline Lds lds_layout(int U_hh, int H, int r) {
   Lds L{};
   int off = 0;
-  L.w2l = off;
-  L.w1u = nl_unit * RK * 1024;
-  const int unit_pool = L.w1u + r * (H / kUnitWGs) * 2;
-  const int pool = nl * RK * 1024;
-  off += pool > unit_pool ? pool : unit_pool;
-  L.gst = off;
-  off += H * 4;
+  L.pool = off;
+  const int unit_pool = r * (H / kUnitWGs) * 2, owner_pool = U_hh * 1024;
+  off += unit_pool > owner_pool ? unit_pool : owner_pool;
+  L.ghl = off;
+  off += 2 * H * 2;  // g split into bf16 hi and lo rows (W_hh owners)
   L.utile = off;
-  off += r * 4;  // hi then lo, r bf16 each
-  L.pu = off;
-  off += 2 * r * 4;
-  L.gs_new = off;
-  off += kUnitMax * 4;
+  off += 2 * r * 2;  // u split into bf16 hi and lo rows
+  L.lbs = off;
+  off += kMaxWgTiles * 16 * 4;  // base logits + b2 of this workgroup's vocabulary range
+  L.b2s = off;
+  off += kMaxWgTiles * 16 * 4;  // b2 of the same range
+  L.gum = off;
+  off += kMaxWgTiles * 16 * 4;  // Gumbel noise of the same range at this position (sampling)
+  L.uhl = off;
+  off += 2 * kUnitMax * 2;  // a unit workgroup's g split into bf16 hi and lo rows
   L.gs_prev = off;
   off += kUnitMax * 4;
+  L.zero = off;
+  off += 16;  // 16 zero bytes: the A operand of the lanes of rows 2-15
   L.red = off;
   off += kWaves * 2 * 16 * 4;
   L.total = off;
   return L;
+}
+
+// Vectors enter the matrix cores as the A operand of a 16x16x32 product with
+// only two live rows: x is split into bf16 halves x = hi + lo, stored as two
+// LDS rows (hl[j] = hi, hl[n + j] = lo); row 0 of the operand (col == 0
+// lanes) carries hi and row 1 (col == 1 lanes) carries lo, so one instruction
+// forms both products and the result is D[0][c] + D[1][c] = acc[0] + acc[1]
+// on the grp == 0 lanes.  The lanes of rows 2-15 read 16 zero bytes.
+__device__ __forceinline__ void split_store(uint16_t* hl, int n, int j, float x) {
+  const uint32_t u = __float_as_uint(x) & 0xFFFF0000u;
+  hl[j] = (uint16_t)(u >> 16);
+  hl[n + j] = (uint16_t)f32_to_bf16_rne(x - __uint_as_float(u));
+}
+__device__ __forceinline__ u32x4 row_frag(const uint16_t* hl, int n, int k0, int col, int grp, const void* zero) {
+  return ld16(col < 2 ? static_cast<const void*>(hl + col * n + k0 + grp * 8) : zero);
 }
 
 template <int UHW, int NR, int RK>
@@ -207,32 +266,22 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   const int grp = lane >> 4, col = lane & 15;
   const int H = p.H, V = p.V, r = p.r;
   const int T3 = (3 * H) >> 4;
-  const Lds L = lds_layout(p.nl, p.nl_unit, RK, H, r);
-  unsigned char* w2l = smem + L.w2l;
-  const uint16_t* w1u = reinterpret_cast<const uint16_t*>(smem + L.w1u);
-  float* gst = reinterpret_cast<float*>(smem + L.gst);
+  const Lds L = lds_layout(p.U_hh, H, r);
+  unsigned char* pool = smem + L.pool;
+  uint16_t* ghl = reinterpret_cast<uint16_t*>(smem + L.ghl);
   uint16_t* utile = reinterpret_cast<uint16_t*>(smem + L.utile);
-  float* pu = reinterpret_cast<float*>(smem + L.pu);
-  float* gs_new = reinterpret_cast<float*>(smem + L.gs_new);
+  uint16_t* uhl = reinterpret_cast<uint16_t*>(smem + L.uhl);
   float* gs_prev = reinterpret_cast<float*>(smem + L.gs_prev);
+  const void* zero = smem + L.zero;
   float* red = reinterpret_cast<float*>(smem + L.red);
+  float* lbs = reinterpret_cast<float*>(smem + L.lbs);
+  float* b2s = reinterpret_cast<float*>(smem + L.b2s);
+  float* gum = reinterpret_cast<float*>(smem + L.gum);
   const int units = H / kUnitWGs;
+  const int ksu = units / 32;  // k-steps of a unit workgroup's W1 columns
   const bool unit_wg = w < kUnitWGs;
-  constexpr int kLdsSlots = 2;  // LDS W2 tiles a wave can own: nl <= kLdsSlots * kWaves
-  const int my_nl = unit_wg ? p.nl_unit : p.nl;
 
   // ---------------- resident weights ----------------
-  const long total_hh = (long)T3 * p.KH, hh0 = (long)w * p.U_hh;
-  u32x4 whh[UHW];
-#pragma unroll
-  for (int q = 0; q < UHW; ++q) {
-    const long gu = hh0 + wave * UHW + q;
-    whh[q] = u32x4{0, 0, 0, 0};
-    if (gu < total_hh) {
-      const int t = (int)(gu / p.KH), s = (int)(gu % p.KH);
-      whh[q] = ld16(p.w_hh + (size_t)(t * 16 + col) * H + s * 32 + grp * 8);
-    }
-  }
   int t_lo, t_hi;
   {
     const int rest = p.ntiles - kUnitWGs * p.ut, others = G - kUnitWGs;
@@ -246,6 +295,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     }
   }
   const int nt = t_hi - t_lo;
+  // W2: tile s * kWaves + wave of this workgroup's range, 8 k-step fragments each
   u32x4 w2r[NR][RK];
 #pragma unroll
   for (int s = 0; s < NR; ++s) {
@@ -255,105 +305,105 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     for (int k = 0; k < RK; ++k)
       w2r[s][k] = j < nt ? ld16(p.w2 + (size_t)v * r + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
   }
-  for (int j = tid; j < my_nl * RK * 64; j += kThreads) {
-    const int l = j / (RK * 64), k = (j / 64) % RK, ln = j & 63;
-    const int lt = kWaves * NR + l;
-    u32x4 v = {0, 0, 0, 0};
-    if (lt < nt) {
-      const int vv = min((t_lo + lt) * 16 + (ln & 15), V - 1);
-      v = ld16(p.w2 + (size_t)vv * r + k * 32 + (ln >> 4) * 8);
-    }
-    st16(w2l + ((size_t)l * RK + k) * 1024 + ln * 16, v);
-  }
-  // unit workgroups: W1[:, d + w*units : d + (w+1)*units] as [r][units] bf16 in LDS
-  const int urow = tid % r, uhalf = tid / r;
-  const int half_units = units / 2;
+  // W_hh owners: k-steps [hw * U_hh, (hw + 1) * U_hh) of the stacked W_hh (hw = w - kUnitWGs)
+  const long total_hh = (long)T3 * p.KH, hh0 = unit_wg ? total_hh : (long)(w - kUnitWGs) * p.U_hh;
+  float bhh[3] = {0.f, 0.f, 0.f};
+  int hoff[3][3];  // unit workgroups: offsets of the W_hh partials of this thread's gate rows
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int o = 0; o < 3; ++o) hoff[q][o] = -1;
   if (unit_wg) {
-    const int chunks = units / 8;
-    for (int j = tid; j < r * chunks; j += kThreads) {
-      const int row = j / chunks, c = j - row * chunks;
-      st16(smem + L.w1u + ((size_t)row * units + c * 8) * 2, ld16(p.w1 + (size_t)row * (p.d + H) + p.d + w * units + c * 8));
+    // W1[:, d + w*units : d + (w+1)*units] as fragments of 16 rows x 32 columns
+    for (int j = tid; j < (r / 16) * ksu * 64; j += kThreads) {
+      const int f = j >> 6, ln = j & 63;
+      const int rt = f / ksu, ks = f - rt * ksu;
+      const int row = rt * 16 + (ln & 15), c0 = ks * 32 + (ln >> 4) * 8;
+      st16(pool + (size_t)j * 16, ld16(p.w1 + (size_t)row * (p.d + H) + p.d + w * units + c0));
+    }
+    if (tid < units && p.b_hh)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) bhh[q] = bf16_to_f32(p.b_hh[q * H + w * units + tid]);
+    if (tid < units)
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int o = 0; o < 3; ++o) hoff[q][o] = hh_partial_offset(p, q * H + w * units + tid, o, G);
+  } else {
+    for (int j = tid; j < p.U_hh * 64; j += kThreads) {
+      const long gu = hh0 + (j >> 6);
+      const int ln = j & 63;
+      u32x4 v = {0, 0, 0, 0};
+      if (gu < total_hh) {
+        const int t = (int)(gu / p.KH), s = (int)(gu % p.KH);
+        v = ld16(p.w_hh + (size_t)(t * 16 + (ln & 15)) * H + s * 32 + (ln >> 4) * 8);
+      }
+      st16(pool + (size_t)j * 16, v);
     }
   }
+  const int nv = nt * 16;  // vocabulary entries of this workgroup: [t_lo * 16, t_lo * 16 + nv)
+  for (int i = tid; i < nv; i += kThreads) {
+    const int v = t_lo * 16 + i;
+    b2s[i] = v < V && p.b2 ? bf16_to_f32(p.b2[v]) : 0.f;
+  }
+  if (tid < 4) reinterpret_cast<uint32_t*>(smem + L.zero)[tid] = 0u;
   if (tid < kUnitMax) gs_prev[tid] = 0.f;
   __syncthreads();
 
   const int t_first_hh = (int)(hh0 / p.KH);
   const long hh_last = min(hh0 + p.U_hh, total_hh) - 1;
   const int t_last_hh = hh_last >= hh0 ? (int)(hh_last / p.KH) : -1;
+  const int hw = w - kUnitWGs;
+  // this wave's W_hh k-steps: hcount of them from global k-step hh0 + wave * UHW
+  int hseg0 = 0, hs0 = 0, hcount = 0;
+  if (!unit_wg) {
+    const long g0 = hh0 + (long)wave * UHW;
+    hcount = (int)max(0L, min((long)UHW, total_hh - g0));
+    if (hcount > 0) {
+      hseg0 = (int)(g0 / p.KH) - t_first_hh;
+      hs0 = (int)(g0 % p.KH);
+    }
+  }
   bool ok = true;
+  // Position i: unit workgroups run B(i) then C(i); the others run C(i) then
+  // A(i+1).
   for (int step = 0; step < p.K; ++step) {
     const uint32_t tag = step + 1;
     const int par = step & 1;
-    // base logits and b2 of this wave's tiles at this position (lanes of row 0 only)
-    float lb[NR + kLdsSlots], bb[NR + kLdsSlots];
+    // base logits of this workgroup's vocabulary range at this position:
+    // loaded now, stored to LDS (with b2 added) just before C needs them
+    // (unit workgroups issue them after the key gather: a wave's loads
+    // complete in order, so the gather's polls would wait for them)
+    constexpr int kLbPer = (kMaxWgTiles * 16 + kThreads - 1) / kThreads;
+    float lbr[kLbPer];
+    auto load_base = [&]() {
 #pragma unroll
-    for (int s = 0; s < NR + kLdsSlots; ++s) {
-      const int l = (s - NR) * kWaves + wave;
-      const int j = s < NR ? s * kWaves + wave : kWaves * NR + l;
-      const int v = (t_lo + j) * 16 + col;
-      const bool live = grp == 0 && j < nt && (s < NR || l < my_nl) && v < V;
-      lb[s] = live ? p.base[(size_t)step * V + v] : 0.f;
-      bb[s] = live && p.b2 ? bf16_to_f32(p.b2[v]) : 0.f;
-    }
+      for (int q = 0; q < kLbPer; ++q) {
+        const int i = tid + q * kThreads, v = t_lo * 16 + i;
+        lbr[q] = i < nv && v < V ? p.base[(size_t)step * V + v] : 0.f;
+      }
+    };
+    if (!unit_wg) load_base();
+    // the hidden-state part of the bottleneck pre-activation (one entry per thread)
+    const float p_pre = tid < r ? p.P[(size_t)step * r + tid] : 0.f;
+    // Gumbel noise for this position (read in C, after two barriers)
+    if (p.sampled)
+      for (int i = tid; i < nv; i += kThreads)
+        gum[i] = gumbel_from_word(philox_word(p.seed, p.offset, 0u, step, t_lo * 16 + i));
 
-    // ---------- A: W_hh g_{i-1} ----------
-    if (step > 0) {
-      {
-        constexpr int kPer = 2;  // H <= kPer * kThreads
-        const unsigned long long* src = p.x_g + (size_t)(par ^ 1) * H;
-        unsigned long long x[kPer];
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) x[q] = tid + q * kThreads < H ? ld_word(src + tid + q * kThreads) : 0ull;
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int j = tid + q * kThreads;
-          if (j < H) {
-            ok &= settle(src + j, step, p.status, x[q]);
-            gst[j] = __uint_as_float((uint32_t)x[q]);
-          }
-        }
-      }
-      if (__syncthreads_or(!ok)) {
-        ok = false;
-        break;
-      }
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < UHW; ++q) {
-        const long gu = hh0 + wave * UHW + q;
-        if (gu < total_hh) {
-          const int t = (int)(gu / p.KH), s = (int)(gu % p.KH);
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = col == 0 ? gst[s * 32 + grp * 8 + e] : 0.f;
-          ActFrag<Bf16> a;
-          a.from_f32(x);
-          if (t == t_first_hh)
-            acc0 = a.mma(acc0, whh[q]);
-          else
-            acc1 = a.mma(acc1, whh[q]);
-        }
-      }
-      if (grp == 0) {
-        red[(wave * 2 + 0) * 16 + col] = acc0[0];
-        red[(wave * 2 + 1) * 16 + col] = acc1[0];
-      }
-      __syncthreads();
-      if (tid < 32) {
-        const int seg = tid >> 4, c = tid & 15;
-        if (t_first_hh + seg <= t_last_hh) {
-          float sum = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < kWaves; ++wv) sum += red[(wv * 2 + seg) * 16 + c];
-          put_f32(p.x_hh + (((size_t)par * G + w) * 2 + seg) * 16 + c, sum, tag);
-        }
-      }
-    }
-
-    // ---------- B: unit workgroups ----------
     if (unit_wg) {
-      if (wave == 0) {
+      // ---------- B(i): unit workgroups ----------
+      // W_hh g_{i-1} partials (published during the previous position): in
+      // flight while the keys are gathered
+      const unsigned long long* hsrc[9];
+      unsigned long long hx[9];
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        const int off = hoff[q / 3][q % 3];
+        hsrc[q] = tid < units && step > 0 && off >= 0 ? p.x_hh + (size_t)par * G * 32 + off : nullptr;
+        hx[q] = hsrc[q] ? ld_word(hsrc[q]) : 0ull;
+      }
+      if (wave == kWaves - 1) {
         int tok;
         if (step == 0) {
           tok = p.x_t[0];
@@ -370,39 +420,28 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         ok = false;
         break;
       }
+      load_base();
       if (tid < units) {
         const int j = w * units + tid;
         const float* trow = p.table + (size_t)s_tok * 3 * H;
         float a3[3];
-        unsigned long long x[3][3];
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          a3[q] = trow[q * H + j];
-#pragma unroll
-          for (int o = 0; o < 3; ++o) {
-            const unsigned long long* src = step > 0 ? hh_partial(p, q * H + j, o, par, G) : nullptr;
-            x[q][o] = src ? ld_word(src) : 0ull;
-          }
-        }
+        for (int q = 0; q < 3; ++q) a3[q] = trow[q * H + j];
+        ok &= settle_all(hsrc, tag, p.status, hx);
         float c3[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
           float h = 0.f;
 #pragma unroll
-          for (int o = 0; o < 3; ++o) {
-            const unsigned long long* src = step > 0 ? hh_partial(p, q * H + j, o, par, G) : nullptr;
-            if (src) {
-              ok &= settle(src, tag, p.status, x[q][o]);
-              h += __uint_as_float((uint32_t)x[q][o]);
-            }
-          }
-          c3[q] = h + (p.b_hh ? bf16_to_f32(p.b_hh[q * H + j]) : 0.f);
+          for (int o = 0; o < 3; ++o)
+            if (hsrc[q * 3 + o]) h += __uint_as_float((uint32_t)hx[q * 3 + o]);
+          c3[q] = h + bhh[q];
         }
         const float rg = sigmoidf_(a3[0] + c3[0]);
         const float zg = sigmoidf_(a3[1] + c3[1]);
         const float ng = tanhf(a3[2] + rg * c3[2]);
         const float g = (1.f - zg) * ng + zg * gs_prev[tid];
-        gs_new[tid] = g;
+        split_store(uhl, units, tid, g);
         gs_prev[tid] = g;
         p.states[(size_t)step * H + j] = g;
         put_f32(p.x_g + (size_t)par * H + j, g, tag);
@@ -411,79 +450,91 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         ok = false;
         break;
       }
-      if (uhalf < 2) {
-        // bottleneck row urow, units [uhalf * half_units, (uhalf + 1) * half_units)
-        float s = 0.f;
-        const uint16_t* wr = w1u + (size_t)urow * units + uhalf * half_units;
-        for (int k = 0; k < half_units; k += 8) {
-          const u32x4 wb = ld16(wr + k);
+      // this workgroup's share of W1[:, d:] g on the matrix cores: wave wv
+      // owns bottleneck rows [wv * r / kWaves, (wv + 1) * r / kWaves)
+      constexpr int kRtPerWave = 256 / 16 / kWaves;  // r / 16 / kWaves with r = 256
+      f32x4 acc[kRtPerWave];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s += bf16_to_f32((uint16_t)(wb[e] & 0xFFFFu)) * gs_new[uhalf * half_units + k + 2 * e];
-            s += bf16_to_f32((uint16_t)(wb[e] >> 16)) * gs_new[uhalf * half_units + k + 2 * e + 1];
-          }
-        }
-        pu[uhalf * r + urow] = s;
+      for (int i = 0; i < kRtPerWave; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < ksu; ++ks) {
+        const u32x4 a = row_frag(uhl, units, ks * 32, col, grp, zero);
+#pragma unroll
+        for (int i = 0; i < kRtPerWave; ++i)
+          acc[i] = mma16<Bf16>(acc[i], a, ld16(pool + ((size_t)((wave * kRtPerWave + i) * ksu + ks) * 64 + lane) * 16));
       }
-      __syncthreads();
-      if (tid < r) put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + tid, pu[tid] + pu[r + tid], tag);
+      if (grp == 0)
+#pragma unroll
+        for (int i = 0; i < kRtPerWave; ++i)
+          put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + (wave * kRtPerWave + i) * 16 + col, acc[i][0] + acc[i][1],
+                  tag);
     }
 
-    // ---------- C: u, W2 tiles, argmax ----------
-    if (tid < r) {
-      const unsigned long long* src = p.x_pu + (size_t)par * kUnitWGs * r + tid;
-      unsigned long long x[kUnitWGs];
+    // ---------- C(i): u, W2 tiles, argmax ----------
+    const bool do_hh = !unit_wg && step + 1 < p.K && hh0 < total_hh;
 #pragma unroll
-      for (int q = 0; q < kUnitWGs; ++q) x[q] = ld_word(src + (size_t)q * r);
-      float s = p.P[(size_t)step * r + tid];
+    for (int q = 0; q < kLbPer; ++q)
+      if (tid + q * kThreads < nv) lbs[tid + q * kThreads] = lbr[q] + b2s[tid + q * kThreads];
+    if (wave == 0) ok &= wait_sentinels(p.x_pu + (size_t)par * kUnitWGs * r, kUnitWGs, r, tag, p.status);
+    if (do_hh && wave == 1) ok &= wait_sentinels(p.x_g + (size_t)par * H, kUnitWGs, units, tag, p.status);
+    if (__syncthreads_or(!ok)) {
+      ok = false;
+      break;
+    }
+    {
+      // this thread's u entry (tid < r = kThreads) from the kUnitWGs shares and,
+      // for a W_hh owner, its g_i entries for A(i+1) (published before the u
+      // shares); all loads are issued before any is checked
+      constexpr int kPer = 1024 / kThreads;  // H <= kPer * kThreads
+      const unsigned long long* src[kUnitWGs + kPer];
+      unsigned long long x[kUnitWGs + kPer];
 #pragma unroll
-      for (int q = 0; q < kUnitWGs; ++q) {
-        ok &= settle(src + (size_t)q * r, tag, p.status, x[q]);
-        s += __uint_as_float((uint32_t)x[q]);
+      for (int q = 0; q < kUnitWGs; ++q) src[q] = tid < r ? p.x_pu + ((size_t)par * kUnitWGs + q) * r + tid : nullptr;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        src[kUnitWGs + q] = do_hh && tid + q * kThreads < H ? p.x_g + (size_t)par * H + tid + q * kThreads : nullptr;
+#pragma unroll
+      for (int q = 0; q < kUnitWGs + kPer; ++q) x[q] = src[q] ? ld_word(src[q]) : 0ull;
+      ok &= settle_all(src, tag, p.status, x);
+      if (tid < r) {
+        float s = p_pre;
+#pragma unroll
+        for (int q = 0; q < kUnitWGs; ++q) s += __uint_as_float((uint32_t)x[q]);
+        split_store(utile, r, tid, s * sigmoidf_(s));
       }
-      const float uv = s * sigmoidf_(s);
-      const uint32_t hb = __float_as_uint(uv) & 0xFFFF0000u;
-      utile[tid] = (uint16_t)(hb >> 16);
-      utile[r + tid] = (uint16_t)f32_to_bf16_rne(uv - __uint_as_float(hb));
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (src[kUnitWGs + q]) split_store(ghl, H, tid + q * kThreads, __uint_as_float((uint32_t)x[kUnitWGs + q]));
     }
     if (__syncthreads_or(!ok)) {
       ok = false;
       break;
     }
+    // u's hi / lo halves ride in rows 0 / 1 of the A operand (rows 2-15 read
+    // zeros); its 8 k-step fragments are loaded once for all tiles.  Every
+    // register slot is multiplied (a slot without a tile holds zeros) so the
+    // tile loop is straight-line code; only live tiles reach the epilogue.
+    u32x4 ua[RK];
+#pragma unroll
+    for (int k = 0; k < RK; ++k) ua[k] = row_frag(utile, r, k * 32, col, grp, zero);
+    f32x4 acc[NR];
+#pragma unroll
+    for (int s = 0; s < NR; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < RK; ++k)
+#pragma unroll
+      for (int s = 0; s < NR; ++s) acc[s] = mma16<Bf16>(acc[s], ua[k], w2r[s][k]);
     unsigned long long best = 0ull;
+    if (grp == 0)
 #pragma unroll
-    for (int s = 0; s < NR; ++s) {
-      const int j = s * kWaves + wave;
-      if (j < nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < RK; ++k) {
-          const u32x4 ahi = col == 0 ? ld16(utile + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-          const u32x4 alo = col == 0 ? ld16(utile + r + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-          acc = mma16<Bf16>(acc, ahi, w2r[s][k]);
-          acc = mma16<Bf16>(acc, alo, w2r[s][k]);
-        }
-        if (grp == 0) best = tile_epilogue(p, acc[0], (t_lo + j) * 16 + col, step, tag, lb[s], bb[s], best);
+      for (int s = 0; s < NR; ++s) {
+        int i = (s * kWaves + wave) * 16 + col;
+        // opaque here, so per-tile constants derived from i are not hoisted
+        // out of the position loop (where they would be spilled)
+        asm volatile("" : "+v"(i));
+        if (i < nv)
+          best = tile_epilogue(p, acc[s][0] + acc[s][1], t_lo * 16 + i, step, tag, lbs[i], p.sampled ? gum[i] : 0.f,
+                               best);
       }
-    }
-#pragma unroll
-    for (int s = 0; s < kLdsSlots; ++s) {
-      const int l = s * kWaves + wave;
-      const int j = kWaves * NR + l;
-      if (l < my_nl && j < nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < RK; ++k) {
-          const u32x4 wv = ld16(w2l + ((size_t)l * RK + k) * 1024 + lane * 16);
-          const u32x4 ahi = col == 0 ? ld16(utile + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-          const u32x4 alo = col == 0 ? ld16(utile + r + k * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-          acc = mma16<Bf16>(acc, ahi, wv);
-          acc = mma16<Bf16>(acc, alo, wv);
-        }
-        if (grp == 0)
-          best = tile_epilogue(p, acc[0], (t_lo + j) * 16 + col, step, tag, lb[NR + s], bb[NR + s], best);
-      }
-    }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) {
       const unsigned long long o = __shfl_xor(best, sh, 64);
@@ -498,9 +549,44 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       if (k == 0ull) k = (unsigned long long)(tag & 0xFFu) << 24;  // no tiles: a tagged lowest key
       put_word(p.x_key + (size_t)par * G + w, k);
     }
+
+    // ---------- A(i+1): W_hh g_i (W_hh owners), from LDS only ----------
+    if (do_hh) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      int seg = hseg0, s = hs0;  // this wave's first k-step: segment (tile - t_first_hh) and column step
+#pragma unroll
+      for (int q = 0; q < UHW; ++q) {
+        if (q < hcount) {
+          const u32x4 a = row_frag(ghl, H, s * 32, col, grp, zero);
+          const u32x4 b = ld16(pool + ((size_t)(wave * UHW + q) * 64 + lane) * 16);
+          if (seg == 0)
+            acc0 = mma16<Bf16>(acc0, a, b);
+          else
+            acc1 = mma16<Bf16>(acc1, a, b);
+        }
+        if (++s == p.KH) {
+          s = 0;
+          ++seg;
+        }
+      }
+      if (grp == 0) {
+        red[(wave * 2 + 0) * 16 + col] = acc0[0] + acc0[1];
+        red[(wave * 2 + 1) * 16 + col] = acc1[0] + acc1[1];
+      }
+      __syncthreads();
+      if (tid < 32) {
+        const int sg = tid >> 4, c = tid & 15;
+        if (t_first_hh + sg <= t_last_hh) {
+          float sum = 0.f;
+#pragma unroll
+          for (int wv = 0; wv < kWaves; ++wv) sum += red[(wv * 2 + sg) * 16 + c];
+          put_f32(p.x_hh + (((size_t)(par ^ 1) * G + hw) * 2 + sg) * 16 + c, sum, tag + 1);
+        }
+      }
+    }
   }
 
-  if (ok && w == 0 && wave == 0) {  // the token of the last position
+  if (ok && w == 0 && wave == kWaves - 1) {  // the token of the last position
     unsigned long long best;
     ok &= gather_keys(p.x_key + (size_t)((p.K - 1) & 1) * G, G, p.K, p.status, best);
     if (lane == 0 && ok) p.tokens[p.K - 1] = key_index(best);
@@ -536,29 +622,24 @@ size_t b1_exchange_words(int H, int r, int max_wg) {
 
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   using namespace b1;
-  constexpr int NR = 3, RK = 8;
+  constexpr int NR = kNR, RK = 8;
   if (a.dtype != 1 || a.B != 1 || !a.table) return hipErrorNotSupported;
-  if (a.r != RK * 32 || a.H % (2 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 2 * kThreads)
+  if (a.r != RK * 32 || a.H % (32 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 1024)
     return hipErrorNotSupported;
   const int G = std::min(a.num_cu, std::min(a.max_wg, 256));
-  if (G < kUnitWGs) return hipErrorNotSupported;
+  if (G <= kUnitWGs) return hipErrorNotSupported;
   const int KH = a.H / 32, T3 = 3 * a.H / 16;
-  const long need = ((long)T3 * KH + G - 1) / G;
-  const int U_hh = (int)((need + kWaves - 1) / kWaves * kWaves);
+  const long need = ((long)T3 * KH + (G - kUnitWGs) - 1) / (G - kUnitWGs);  // over the W_hh owners
+  const int U_hh = (int)((need + 2 * kWaves - 1) / (2 * kWaves) * (2 * kWaves));  // UHW even
   if (U_hh > KH) return hipErrorNotSupported;  // a range spans at most two tiles
   const int ntiles = (a.V + 15) / 16;
-  const int units = a.H / kUnitWGs;
-  const int w1_bytes = a.r * units * 2;
-  constexpr int kSlots = 2;  // LDS W2 tiles per wave
-  // unit workgroups give up LDS tiles for their W1 columns; the others take the rest
-  const int nl_max = kSlots * kWaves;
-  const int nl_unit = std::max(0, (nl_max * RK * 1024 - w1_bytes) / (RK * 1024));
-  const int ut = std::min(kWaves * NR + nl_unit, ntiles / G);
+  // the unit workgroups take ut tiles each, the others share the rest; every
+  // workgroup's tiles must fit its waves' registers
+  const int ut = std::min(kWaves * NR, ntiles / G);
   const int rest = ntiles - kUnitWGs * ut;
   const int per_other = (rest + (G - kUnitWGs) - 1) / (G - kUnitWGs);
-  const int nl = std::max(0, per_other - kWaves * NR);
-  if (nl > nl_max || G <= kUnitWGs) return hipErrorNotSupported;
-  const Lds L = lds_layout(nl, nl_unit, RK, a.H, a.r);
+  if (per_other > kWaves * NR) return hipErrorNotSupported;
+  const Lds L = lds_layout(U_hh, a.H, a.r);
   if (L.total > 160 * 1024 - 256) return hipErrorNotSupported;
   Params p{};
   p.d = a.d;
@@ -569,8 +650,6 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.KH = KH;
   p.U_hh = U_hh;
   p.ntiles = ntiles;
-  p.nl = nl;
-  p.nl_unit = nl_unit;
   p.ut = ut;
   p.w_hh = static_cast<const uint16_t*>(a.w_hh);
   p.b_hh = static_cast<const uint16_t*>(a.b_hh);
@@ -600,10 +679,10 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.x_key = x;
   const int UHW = U_hh / kWaves;
   switch (UHW) {
-    case 1: return launch_t<1, NR, RK>(p, G, L.total, s);
     case 2: return launch_t<2, NR, RK>(p, G, L.total, s);
-    case 3: return launch_t<3, NR, RK>(p, G, L.total, s);
     case 4: return launch_t<4, NR, RK>(p, G, L.total, s);
+    case 6: return launch_t<6, NR, RK>(p, G, L.total, s);
+    case 8: return launch_t<8, NR, RK>(p, G, L.total, s);
     default: return hipErrorNotSupported;
   }
 }
