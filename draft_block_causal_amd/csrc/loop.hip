@@ -6,10 +6,13 @@
 // Pages: [notes] "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn);
 //        [explainer] the yhxrc.cn article on the Domino paper.
 //
-// Each position has three phases, written once as device functions:
-//   1. gru_partial_job  - GRU pre-activations W_ih e(prev) (split over K) and
-//                         W_hh g on the matrix cores, one 16-row tile per wave;
-//   2. gates_u_tile     - GRU gates -> new state; u = SiLU(P + W1[:, d:] g);
+// Each position has three phases:
+//   1. gru_partial_job  - GRU pre-activations W_ih e(prev) (split over K; not
+//                         needed with the GRU input table) and W_hh g on the
+//                         matrix cores, one 16-row tile per wave;
+//   2. GRU gates -> new state g; u = SiLU(P + W1[:, d:] g)  (gates_kernel +
+//                         u_kernel when kernel boundaries order the phases,
+//                         gates_u_tile in the persistent kernel);
 //   3. w2_sample_block  - L = L_base + W2 u + b2 (+ Gumbel noise), vocabulary
 //                         argmax as a 64-bit key max.
 // Two schedules run them:
@@ -45,6 +48,7 @@ struct DevLoop {
   int B, K, d, V, H, r, KS;
   const E *embed, *w_ih, *w_hh, *b_ih, *b_hh, *w1, *w2, *b2;
   const float* base;
+  const float* table;  // optional GRU input table [V][3H] = W_ih E^T + b_ih (three-kernel schedule)
   const int32_t *x_t, *teacher;
   float inv_temp;
   int sampled;
@@ -479,6 +483,101 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
 }
 
 // ---------------------------------------------------------------------------
+// Plain-schedule phase 2, split in two launches:
+//   gates_kernel - one thread per (batch row, GRU unit): the gates from the
+//                  phase-1 partials (or the GRU input table row of the token)
+//                  and the previous state -> states[b][step];
+//   u_kernel     - u rows 16t..16t+15 for batch rows 16m..16m+15:
+//                  SiLU(P + W1[:, d:] g) on the matrix cores.
+// ---------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ int step_token(const DevLoop<T>& p, int step, int b) {
+  int tk;
+  if (step == 0)
+    tk = p.x_t[b];
+  else if (p.teacher)
+    tk = p.teacher[(size_t)b * p.K + step - 1];
+  else
+    tk = key_token(p.keys[(size_t)(step - 1) * p.B + b]);
+  return min(max(tk, 0), p.V - 1);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) gates_kernel(DevLoop<T> p, int step) {
+  const int H = p.H, G3 = 3 * H, KS = p.KS;
+  const int b = blockIdx.y, j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= H) return;
+  float a3[3], c3[3] = {0.f, 0.f, 0.f};
+  if (p.table) {
+    const float* trow = p.table + (size_t)step_token(p, step, b) * G3;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) a3[q] = trow[q * H + j];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      float x = 0.f;
+      for (int ks = 0; ks < KS; ++ks) x += p.part_ih[((size_t)ks * p.B + b) * G3 + q * H + j];
+      a3[q] = x + (p.b_ih ? T::to_f32(p.b_ih[q * H + j]) : 0.f);
+    }
+  }
+  float gp = 0.f;
+  if (step > 0) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) c3[q] = p.part_hh[(size_t)b * G3 + q * H + j];
+    gp = p.states[((size_t)b * p.K + step - 1) * H + j];
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) c3[q] += p.b_hh ? T::to_f32(p.b_hh[q * H + j]) : 0.f;
+  const float rg = sigmoidf_(a3[0] + c3[0]);
+  const float zg = sigmoidf_(a3[1] + c3[1]);
+  const float ng = tanhf(a3[2] + rg * c3[2]);
+  p.states[((size_t)b * p.K + step) * H + j] = (1.f - zg) * ng + zg * gp;
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  using E = typename T::elem;
+  const int H = p.H, B = p.B;
+  const int t = blockIdx.x, m0 = blockIdx.y * 16;
+  float* gt = reinterpret_cast<float*>(smem);  // [16][H + 4]
+  const int gstride = H + 4;
+  float* red = gt + 16 * gstride;  // [4][16][16]
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int ldw1 = p.d + H;
+  constexpr int EPF = T::kPer16B;
+  for (int idx = threadIdx.x; idx < 16 * H; idx += blockDim.x) {
+    const int rr = idx / H, j = idx - rr * H;
+    const int b = m0 + rr;
+    gt[rr * gstride + j] = b < B ? p.states[((size_t)b * p.K + step) * H + j] : 0.f;
+  }
+  __syncthreads();
+  // u rows t*16 + col; the four waves take interleaved 64-byte K chunks
+  const int row = t * 16 + col;
+  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(p.w1 + (size_t)row * ldw1 + p.d) + grp * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = wave * 4 * EPF; k0 < H; k0 += 16 * EPF) {
+    const u32x4 w = ld16(wrow + (size_t)k0 * sizeof(E));
+    ActFrag<T> a;
+    a.from_f32(gt + col * gstride + k0 + grp * EPF);
+    acc = a.mma(acc, w);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[(wave * 16 + grp * 4 + j) * 16 + col] = acc[j];
+  __syncthreads();
+  const int rr = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int b = m0 + rr;
+  if (b < B) {
+    const float sum = red[(0 * 16 + rr) * 16 + c] + red[(1 * 16 + rr) * 16 + c] + red[(2 * 16 + rr) * 16 + c] +
+                      red[(3 * 16 + rr) * 16 + c];
+    const int q = t * 16 + c;
+    const float pre = p.P[((size_t)b * p.K + step) * p.r + q] + sum;
+    p.u[(size_t)b * p.r + q] = pre * sigmoidf_(pre);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // three-kernels-per-position schedule
 // ---------------------------------------------------------------------------
 template <class T, int MT>
@@ -495,15 +594,11 @@ __global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step
     tok[b] = min(max(tk, 0), p.V - 1);
   }
   __syncthreads();
-  const int job = blockIdx.x * 4 + wave_id();
+  // with a GRU input table only the W_hh tiles remain (job numbers after the W_ih ones)
+  const int job = blockIdx.x * 4 + wave_id() + (p.table ? ((3 * p.H) >> 4) * p.KS : 0);
   if (job < gru_jobs(p.H, p.KS, step)) gru_partial_job<T, MT, Plain>(p, step, job, tok);
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) gates_u_kernel(DevLoop<T> p, int step) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  gates_u_tile<T, Plain>(p, step, blockIdx.x, smem);
-}
 
 template <class T, int MT>
 __global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step) {
@@ -623,6 +718,7 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
   p.w2 = static_cast<const E*>(a.w2);
   p.b2 = static_cast<const E*>(a.b2);
   p.base = a.base;
+  p.table = a.table;
   p.x_t = a.x_t;
   p.teacher = a.teacher;
   p.inv_temp = a.inv_temp;
@@ -648,17 +744,21 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
 template <class T, int MT>
 static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t s) {
   hipError_t e;
-  const size_t lds_g = gates_lds_bytes(p.H);
-  if ((e = allow_lds(gates_u_kernel<T>, lds_g)) != hipSuccess) return e;
+  const size_t lds_u = gates_lds_bytes(p.H);
+  if ((e = allow_lds(u_kernel<T>, lds_u)) != hipSuccess) return e;
   constexpr int MW = MT > 2 ? 2 : MT;  // w2 rows per workgroup: 16 * MW
   const size_t lds_w = w2_lds_bytes<T>(p.r, 16 * MW);
   if ((e = allow_lds(w2_sample_kernel<T, MW>, lds_w)) != hipSuccess) return e;
   const int ntiles = (p.V + 15) / 16;
   const dim3 wgrid(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW));
+  const dim3 ggrid((p.H + 255) / 256, p.B);
+  const dim3 ugrid(p.r / 16, (p.B + 15) / 16);
+  const int t3 = 3 * p.H / 16;
   for (int step = 0; step < p.K; ++step) {
-    const int jobs = (3 * p.H / 16) * p.KS + (step > 0 ? 3 * p.H / 16 : 0);
-    hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((jobs + 3) / 4), dim3(256), 0, s, p, step);
-    hipLaunchKernelGGL(gates_u_kernel<T>, dim3(p.r / 16), dim3(256), lds_g, s, p, step);
+    const int jobs = (p.table ? 0 : t3 * p.KS) + (step > 0 ? t3 : 0);
+    if (jobs > 0) hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((jobs + 3) / 4), dim3(256), 0, s, p, step);
+    hipLaunchKernelGGL(gates_kernel<T>, ggrid, dim3(256), 0, s, p, step);
+    hipLaunchKernelGGL(u_kernel<T>, ugrid, dim3(256), lds_u, s, p, step);
     hipLaunchKernelGGL((w2_sample_kernel<T, MW>), wgrid, dim3(256), lds_w, s, p, step);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

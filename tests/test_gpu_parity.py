@@ -173,6 +173,21 @@ def test_qwen3_4b_b1_tied_gru_table(dev):
     _parity(S.get_workload("qwen3_4b_b8_tied").with_(batch=1), dev, table=True)
 
 
+@pytest.mark.parametrize("case", ["qwen3_8b_b32_t1", "qwen3_4b_b8_tied", "tiny_stress_b4", "small_b17", "small_b65"])
+def test_batched_gru_table(dev, case, monkeypatch):
+    # several blocks with the GRU input table: the three-kernel schedule reads
+    # T[token] instead of forming W_ih e
+    monkeypatch.delenv("DOMINO_LOOP", raising=False)
+    if case.startswith("small"):
+        w = _small("bf16", batch=int(case[7:]), vocab=777, block=3, d=96, gru_hidden=64)
+        _parity(w, dev, table=True)
+    elif case == "tiny_stress_b4":
+        _parity(S.get_workload(case).with_(temperature=1.0, philox_seed=7), dev, table=True)
+    else:
+        w = S.get_workload(case)
+        _parity(w, dev, check_blocks=[0, w.batch - 1], sampled=True, table=True)
+
+
 def test_gru_table_matches_oracle(dev):
     import draft_block_causal_amd as D
 
