@@ -53,10 +53,16 @@ hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s);
 
 // The B = 1 persistent loop with on-chip weights; hipErrorNotSupported when the
 // shape, dtype or device does not fit it (the caller then uses another schedule).
+// The single-block on-chip loop: b1_supported() tells whether it takes these
+// arguments (host-side checks only); launch_draft_b1 reads a.P, the hidden
+// half of the first correction projection, computed beforehand.
+bool b1_supported(const LoopArgs& a);
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s);
 size_t b1_exchange_words(int H, int r, int max_wg);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
+// clears n words at p and m words at q in one launch
+hipError_t launch_fill2_u64(unsigned long long* p, int n, unsigned long long* q, int m, hipStream_t s);
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,

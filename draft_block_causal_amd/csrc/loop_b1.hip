@@ -55,6 +55,7 @@ constexpr int kUnitMax = 128;  // GRU units per unit workgroup (H <= 1024)
 constexpr unsigned int kSpinLimit = 1u << 20;
 constexpr int kMaxWgTiles = kNR * kWaves;  // W2 tiles per workgroup
 
+
 struct Params {
   int d, V, H, r, K;
   int KH;      // 32-element k-steps per W_hh row: H / 32
@@ -63,7 +64,7 @@ struct Params {
   int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
   const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
   const float* table;     // [V][3H]: W_ih E[v] + b_ih
-  const float *base, *P;  // base [K][V], P [K][r] (includes b1)
+  const float *base, *P;  // base [K][V], P [K][r] = W1[:, :d] h + b1
   const int32_t *x_t, *teacher;
   float inv_temp;
   int sampled;
@@ -620,27 +621,48 @@ size_t b1_exchange_words(int H, int r, int max_wg) {
   return 2 * ((size_t)max_wg * 2 * 16 + (size_t)H + (size_t)b1::kUnitWGs * r + (size_t)max_wg);
 }
 
+namespace b1 {
+struct Plan {
+  int G, KH, U_hh, ntiles, ut;
+  size_t lds;
+};
+
+// Host-side checks of the single-block loop; fills the launch plan.
+static bool make_plan(const LoopArgs& a, Plan& pl) {
+  constexpr int RK = 8;
+  if (a.dtype != 1 || a.B != 1 || !a.table) return false;
+  if (a.r != RK * 32 || a.H % (32 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 1024) return false;
+  pl.G = std::min(a.num_cu, std::min(a.max_wg, 256));
+  if (pl.G <= kUnitWGs) return false;
+  pl.KH = a.H / 32;
+  const int T3 = 3 * a.H / 16;
+  const long need = ((long)T3 * pl.KH + (pl.G - kUnitWGs) - 1) / (pl.G - kUnitWGs);  // over the W_hh owners
+  pl.U_hh = (int)((need + 2 * kWaves - 1) / (2 * kWaves) * (2 * kWaves));           // UHW even
+  if (pl.U_hh > pl.KH || pl.U_hh / kWaves > 8) return false;  // a range spans at most two tiles
+  pl.ntiles = (a.V + 15) / 16;
+  // the unit workgroups take ut tiles each, the others share the rest; every
+  // workgroup's tiles must fit its waves' registers
+  pl.ut = std::min(kWaves * kNR, pl.ntiles / pl.G);
+  const int rest = pl.ntiles - kUnitWGs * pl.ut;
+  const int per_other = (rest + (pl.G - kUnitWGs) - 1) / (pl.G - kUnitWGs);
+  if (per_other > kWaves * kNR) return false;
+  pl.lds = (size_t)lds_layout(pl.U_hh, a.H, a.r).total;
+  return pl.lds <= 160 * 1024 - 256;
+}
+}  // namespace b1
+
+bool b1_supported(const LoopArgs& a) {
+  b1::Plan pl;
+  return b1::make_plan(a, pl);
+}
+
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   using namespace b1;
   constexpr int NR = kNR, RK = 8;
-  if (a.dtype != 1 || a.B != 1 || !a.table) return hipErrorNotSupported;
-  if (a.r != RK * 32 || a.H % (32 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 1024)
-    return hipErrorNotSupported;
-  const int G = std::min(a.num_cu, std::min(a.max_wg, 256));
-  if (G <= kUnitWGs) return hipErrorNotSupported;
-  const int KH = a.H / 32, T3 = 3 * a.H / 16;
-  const long need = ((long)T3 * KH + (G - kUnitWGs) - 1) / (G - kUnitWGs);  // over the W_hh owners
-  const int U_hh = (int)((need + 2 * kWaves - 1) / (2 * kWaves) * (2 * kWaves));  // UHW even
-  if (U_hh > KH) return hipErrorNotSupported;  // a range spans at most two tiles
-  const int ntiles = (a.V + 15) / 16;
-  // the unit workgroups take ut tiles each, the others share the rest; every
-  // workgroup's tiles must fit its waves' registers
-  const int ut = std::min(kWaves * NR, ntiles / G);
-  const int rest = ntiles - kUnitWGs * ut;
-  const int per_other = (rest + (G - kUnitWGs) - 1) / (G - kUnitWGs);
-  if (per_other > kWaves * NR) return hipErrorNotSupported;
+  Plan pl;
+  if (!make_plan(a, pl)) return hipErrorNotSupported;
+  const int G = pl.G, KH = pl.KH, U_hh = pl.U_hh, ntiles = pl.ntiles, ut = pl.ut;
   const Lds L = lds_layout(U_hh, a.H, a.r);
-  if (L.total > 160 * 1024 - 256) return hipErrorNotSupported;
   Params p{};
   p.d = a.d;
   p.V = a.V;
