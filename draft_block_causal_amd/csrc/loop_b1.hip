@@ -99,18 +99,19 @@ __device__ __forceinline__ bool gave_up(const unsigned int* status) {
 template <int N>
 __device__ __forceinline__ bool settle_all(const unsigned long long* const (&src)[N], uint32_t tag,
                                           const unsigned int* status, unsigned long long (&x)[N]) {
+  // every exit follows a check of every load, so no load is left in flight
+  // (a later wait would otherwise cover this wave's pending stores too)
   unsigned int spins = 0;
   while (true) {
     bool done = true;
 #pragma unroll
-    for (int q = 0; q < N; ++q)
-      if (src[q] && (uint32_t)(x[q] >> 32) != tag) {
-        done = false;
-        x[q] = ld_word(src[q]);
-      }
+    for (int q = 0; q < N; ++q) done &= !src[q] || (uint32_t)(x[q] >> 32) == tag;
     if (done) return true;
     if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) return false;
     __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (src[q] && (uint32_t)(x[q] >> 32) != tag) x[q] = ld_word(src[q]);
   }
 }
 
@@ -157,17 +158,16 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
   while (true) {
     bool done = true;
 #pragma unroll
-    for (int q = 0; q < kMaxPer; ++q)
-      if (src[q] && !key_tagged(k[q], tag)) {
-        done = false;
-        k[q] = ld_word(src[q]);
-      }
+    for (int q = 0; q < kMaxPer; ++q) done &= !src[q] || key_tagged(k[q], tag);
     if (done) break;
     if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
       ok = false;
       break;
     }
     __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q)
+      if (src[q] && !key_tagged(k[q], tag)) k[q] = ld_word(src[q]);
   }
   best = 0ull;
 #pragma unroll
@@ -193,19 +193,12 @@ __device__ __forceinline__ int hh_partial_offset(const Params& p, int row, int o
   return (ow * 2 + seg) * 16 + c;
 }
 
-// L_i[v] = (W2 u)[v] + (base + b2)[v] for the lane's vocabulary entry; the
-// score is L_i[v] (greedy) or L_i[v] / T + Gumbel noise; returns the running
-// argmax key.
-__device__ __forceinline__ unsigned long long tile_epilogue(const Params& p, float dl, int v, int step, uint32_t tag,
-                                                            float bias, float noise, unsigned long long best) {
-  if (v < p.V) {
-    const float Lv = dl + bias;
-    if (p.logits) p.logits[(size_t)step * p.V + v] = Lv;
-    const float sc = p.sampled ? Lv * p.inv_temp + noise : Lv;
-    const unsigned long long k = b1_key(sc, v, tag);
-    best = k > best ? k : best;
-  }
-  return best;
+// The argmax key of one entry: L_i[v] = (W2 u)[v] + (base + b2)[v], scored
+// as L_i[v] (greedy) or L_i[v] / T + Gumbel noise.  Entries past the
+// workgroup's range or the vocabulary carry a bias of -inf and never win.
+template <bool SAMPLED>
+__device__ __forceinline__ unsigned long long entry_key(float L, float inv_temp, float noise, uint32_t v, uint32_t tag) {
+  return b1_key(SAMPLED ? L * inv_temp + noise : L, v, tag);
 }
 
 struct Lds {
@@ -257,7 +250,7 @@ __device__ __forceinline__ u32x4 row_frag(const uint16_t* hl, int n, int k0, int
   return ld16(col < 2 ? static_cast<const void*>(hl + col * n + k0 + grp * 8) : zero);
 }
 
-template <int UHW, int NR, int RK>
+template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
 __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ unsigned long long s_key[kWaves];
@@ -347,6 +340,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     const int v = t_lo * 16 + i;
     b2s[i] = v < V && p.b2 ? bf16_to_f32(p.b2[v]) : 0.f;
   }
+  for (int i = nv + tid; i < kMaxWgTiles * 16; i += kThreads) lbs[i] = -INFINITY;  // slots without a tile
   if (tid < 4) reinterpret_cast<uint32_t*>(smem + L.zero)[tid] = 0u;
   if (tid < kUnitMax) gs_prev[tid] = 0.f;
   __syncthreads();
@@ -388,7 +382,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     // the hidden-state part of the bottleneck pre-activation (one entry per thread)
     const float p_pre = tid < r ? p.P[(size_t)step * r + tid] : 0.f;
     // Gumbel noise for this position (read in C, after two barriers)
-    if (p.sampled)
+    if (SAMPLED)
       for (int i = tid; i < nv; i += kThreads)
         gum[i] = gumbel_from_word(philox_word(p.seed, p.offset, 0u, step, t_lo * 16 + i));
 
@@ -474,7 +468,8 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     const bool do_hh = !unit_wg && step + 1 < p.K && hh0 < total_hh;
 #pragma unroll
     for (int q = 0; q < kLbPer; ++q)
-      if (tid + q * kThreads < nv) lbs[tid + q * kThreads] = lbr[q] + b2s[tid + q * kThreads];
+      if (tid + q * kThreads < nv)
+        lbs[tid + q * kThreads] = t_lo * 16 + tid + q * kThreads < V ? lbr[q] + b2s[tid + q * kThreads] : -INFINITY;
     if (wave == 0) ok &= wait_sentinels(p.x_pu + (size_t)par * kUnitWGs * r, kUnitWGs, r, tag, p.status);
     if (do_hh && wave == 1) ok &= wait_sentinels(p.x_g + (size_t)par * H, kUnitWGs, units, tag, p.status);
     if (__syncthreads_or(!ok)) {
@@ -517,6 +512,9 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     u32x4 ua[RK];
 #pragma unroll
     for (int k = 0; k < RK; ++k) ua[k] = row_frag(utile, r, k * 32, col, grp, zero);
+    float bias[NR];  // Lb + b2 of the row-0 lanes' entries, read while the products run
+#pragma unroll
+    for (int s = 0; s < NR; ++s) bias[s] = lbs[min((s * kWaves + wave) * 16 + col, kMaxWgTiles * 16 - 1)];
     f32x4 acc[NR];
 #pragma unroll
     for (int s = 0; s < NR; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -524,18 +522,24 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     for (int k = 0; k < RK; ++k)
 #pragma unroll
       for (int s = 0; s < NR; ++s) acc[s] = mma16<Bf16>(acc[s], ua[k], w2r[s][k]);
+    __builtin_amdgcn_sched_group_barrier(0x100, RK + NR, 0);  // every LDS read first,
+    __builtin_amdgcn_sched_group_barrier(0x008, NR * RK, 0);  // then the products
+    // branch-free over every slot and lane: only row-0 lanes (grp == 0) hold
+    // results, the others and the slots without an entry (bias -inf) lose
     unsigned long long best = 0ull;
-    if (grp == 0)
 #pragma unroll
-      for (int s = 0; s < NR; ++s) {
-        int i = (s * kWaves + wave) * 16 + col;
-        // opaque here, so per-tile constants derived from i are not hoisted
-        // out of the position loop (where they would be spilled)
-        asm volatile("" : "+v"(i));
-        if (i < nv)
-          best = tile_epilogue(p, acc[s][0] + acc[s][1], t_lo * 16 + i, step, tag, lbs[i], p.sampled ? gum[i] : 0.f,
-                               best);
-      }
+    for (int s = 0; s < NR; ++s) {
+      int i = (s * kWaves + wave) * 16 + col;
+      // opaque here, so per-tile constants derived from i are not hoisted
+      // out of the position loop (where they would be spilled)
+      asm volatile("" : "+v"(i));
+      const float L = acc[s][0] + acc[s][1] + bias[s];
+      if constexpr (LOGITS)
+        if (grp == 0 && i < nv && t_lo * 16 + i < V) p.logits[(size_t)step * V + t_lo * 16 + i] = L;
+      const unsigned long long k = entry_key<SAMPLED>(L, p.inv_temp, SAMPLED ? gum[min(i, kMaxWgTiles * 16 - 1)] : 0.f,
+                                                      (uint32_t)(t_lo * 16 + i), tag);
+      best = grp == 0 && k > best ? k : best;
+    }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) {
       const unsigned long long o = __shfl_xor(best, sh, 64);
@@ -599,9 +603,9 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   }
 }
 
-template <int UHW, int NR, int RK>
+template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
 static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
-  auto kern = draft_b1_kernel<UHW, NR, RK>;
+  auto kern = draft_b1_kernel<UHW, NR, RK, SAMPLED, LOGITS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -613,6 +617,23 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
   void* args[] = {&pp};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(G), dim3(kThreads), args,
                                     (unsigned)lds, s);
+}
+
+template <int UHW, int NR, int RK>
+static hipError_t launch_flags(const Params& p, int G, size_t lds, hipStream_t s) {
+  if (p.sampled) return p.logits ? launch_t<UHW, NR, RK, true, true>(p, G, lds, s) : launch_t<UHW, NR, RK, true, false>(p, G, lds, s);
+  return p.logits ? launch_t<UHW, NR, RK, false, true>(p, G, lds, s) : launch_t<UHW, NR, RK, false, false>(p, G, lds, s);
+}
+
+template <int NR, int RK>
+static hipError_t launch_uhw(const Params& p, int uhw, int G, size_t lds, hipStream_t s) {
+  switch (uhw) {
+    case 2: return launch_flags<2, NR, RK>(p, G, lds, s);
+    case 4: return launch_flags<4, NR, RK>(p, G, lds, s);
+    case 6: return launch_flags<6, NR, RK>(p, G, lds, s);
+    case 8: return launch_flags<8, NR, RK>(p, G, lds, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace b1
@@ -699,14 +720,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.x_pu = x;
   x += 2 * (size_t)kUnitWGs * a.r;
   p.x_key = x;
-  const int UHW = U_hh / kWaves;
-  switch (UHW) {
-    case 2: return launch_t<2, NR, RK>(p, G, L.total, s);
-    case 4: return launch_t<4, NR, RK>(p, G, L.total, s);
-    case 6: return launch_t<6, NR, RK>(p, G, L.total, s);
-    case 8: return launch_t<8, NR, RK>(p, G, L.total, s);
-    default: return hipErrorNotSupported;
-  }
+  return launch_uhw<NR, RK>(p, U_hh / kWaves, G, L.total, s);
 }
 
 }  // namespace domino
