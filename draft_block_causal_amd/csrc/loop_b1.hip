@@ -140,6 +140,34 @@ __device__ __forceinline__ bool key_tagged(unsigned long long k, uint32_t tag) {
 }
 __device__ __forceinline__ int key_index(unsigned long long k) { return (int)(0xFFFFFFu - (uint32_t)(k & 0xFFFFFFull)); }
 
+// 64-bit max across lanes with DPP moves (no LDS round trips): within each
+// 16-lane row by rotations of 8 and 4 and two quad swaps, then across the
+// four rows with lane reads (the result is wave-uniform).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long x) {
+  const unsigned lo = __builtin_amdgcn_update_dpp(0u, (unsigned)x, CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0u, (unsigned)(x >> 32), CTRL, 0xF, 0xF, false);
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o > x ? o : x;
+}
+__device__ __forceinline__ unsigned long long row_max16(unsigned long long x) {
+  x = dpp_max_step<0x128>(x);  // row_ror:8
+  x = dpp_max_step<0x124>(x);  // row_ror:4
+  x = dpp_max_step<0x4E>(x);   // quad_perm [2,3,0,1]
+  return dpp_max_step<0xB1>(x);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ unsigned long long wave_max(unsigned long long x) {
+  x = row_max16(x);
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const unsigned long long y = ((unsigned long long)__builtin_amdgcn_readlane((unsigned)(x >> 32), row * 16) << 32) |
+                                 __builtin_amdgcn_readlane((unsigned)x, row * 16);
+    m = y > m ? y : m;
+  }
+  return m;
+}
+
 // Max over the G keys published for one position, on one wave; every load of a
 // lane is in flight before the first is checked.
 __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int G, uint32_t tag,
@@ -172,11 +200,7 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
   best = 0ull;
 #pragma unroll
   for (int q = 0; q < kMaxPer; ++q) best = k[q] > best ? k[q] : best;
-#pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    const unsigned long long o = __shfl_xor(best, sh, 64);
-    best = o > best ? o : best;
-  }
+  best = wave_max(best);
   return ok;
 }
 
@@ -540,11 +564,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
                                                       (uint32_t)(t_lo * 16 + i), tag);
       best = grp == 0 && k > best ? k : best;
     }
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const unsigned long long o = __shfl_xor(best, sh, 64);
-      best = o > best ? o : best;
-    }
+    best = row_max16(best);  // the candidates are in row 0 (lanes 0-15)
     if (lane == 0) s_key[wave] = best;
     __syncthreads();
     if (tid == 0) {
@@ -652,7 +672,7 @@ struct Plan {
 static bool make_plan(const LoopArgs& a, Plan& pl) {
   constexpr int RK = 8;
   if (a.dtype != 1 || a.B != 1 || !a.table) return false;
-  if (a.r != RK * 32 || a.H % (32 * kUnitWGs) || a.H / kUnitWGs > kUnitMax || a.H > 1024) return false;
+  if (a.r != RK * 32 || a.H != kUnitWGs * kUnitMax) return false;  // 128 GRU units per unit workgroup
   pl.G = std::min(a.num_cu, std::min(a.max_wg, 256));
   if (pl.G <= kUnitWGs) return false;
   pl.KH = a.H / 32;
