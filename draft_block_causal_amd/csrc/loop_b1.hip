@@ -4,12 +4,12 @@
 // Pages: [notes] "完全开源的语言模型学习记录--推理加速Domino" (gsyq.cn);
 //        [explainer] the yhxrc.cn article on the Domino paper.
 //
-// One cooperative launch of G = #CU workgroups (512 threads, 8 waves each)
-// runs the whole K-position loop.  Re-reading W2 and W_hh from HBM at every
-// position would cost ~85 MB per position; each workgroup instead loads its
-// share once and keeps it resident:
-//   * W2:   a contiguous range of 16-row vocabulary tiles, NR per wave in
-//           registers and the rest in LDS;
+// One launch of G = #CU workgroups (256 threads, 4 waves each, one workgroup
+// per compute unit) runs the whole K-position loop.  Re-reading W2 and W_hh
+// from HBM at every position would cost ~85 MB per position; each workgroup
+// instead loads its share once and keeps it resident:
+//   * W2:   a contiguous range of 16-row vocabulary tiles, up to NR per wave,
+//           in registers;
 //   * W_hh: a contiguous range of U_hh "k-steps" (16 gate rows x 32 inputs)
 //           of the stacked [3H, H] matrix, in registers (all workgroups but
 //           the unit ones);
@@ -37,6 +37,14 @@
 // covers both), so each role polls before it publishes wherever it can.
 // Every wait is bounded: a workgroup that gives up records it in `status`
 // and all others leave at their next poll; the tokens are then -1.
+//
+// The workgroups wait on one another, so all G must be resident at once.  The
+// kernel is an ordinary launch (a cooperative launch costs ~20 us more per
+// call in the runtime): the host checks that one workgroup fits per compute
+// unit, and as G is the compute-unit count every workgroup starts as soon as
+// earlier work on the device has left the compute units.  Work on other
+// streams that keeps compute units busy only delays the loop; a wait gives up
+// after about a second, so even a loop that cannot complete ends.
 #include <algorithm>
 
 #include "common.h"
@@ -633,10 +641,8 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
-  Params pp = p;
-  void* args[] = {&pp};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(G), dim3(kThreads), args,
-                                    (unsigned)lds, s);
+  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
 }
 
 template <int UHW, int NR, int RK>
