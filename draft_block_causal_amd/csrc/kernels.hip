@@ -138,6 +138,153 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
   }
 }
 
+// ---------------------------------------------------------------------------
+// rowstream_gemm: the split-K product above with W read the way HBM streams
+// best.  A load instruction of the split-K kernel covers 64 B of each of 16
+// rows; here each covers whole 16-B chunks of one contiguous run of a row
+// (1 KB of one row when KW = 16), read non-temporally since W is used once.
+// Each wave writes its 16 row slices into a private LDS tile and reads them
+// back in the matrix-core operand layout (row = lane column).  The 16-B
+// chunks of row r are stored XOR-swizzled by r & 15, so both the row-wise
+// writes and the column-wise reads touch 16 distinct bank groups per 16 lanes.
+// W and the bias are read through buffer descriptors sized to the valid rows
+// of the tile: rows past N, and the prefetch past the last tile, read as zero
+// without touching memory, so every load is unconditional and the next tile
+// is always in flight while the current one is multiplied (two register
+// buffers used in turn, so no copies).  The partial tiles of the 8 waves are
+// summed in LDS in a fixed order; the two halves of the loop use separate
+// reduction buffers, so one barrier per tile suffices.  KW in {4, 8, 16}.
+// ---------------------------------------------------------------------------
+template <int KW>
+struct RowStream {
+  static constexpr int kSlice = KW * 64;             // bytes of a row per wave
+  static constexpr int kChunks = kSlice / 16;        // 16-B chunks per row slice
+  static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one load instruction covers
+  static constexpr size_t kTileLds = 16 * kSlice;    // one wave's transposition tile
+  static constexpr int kRed = kSplitWaves * 16 * 17; // floats per reduction buffer
+  static constexpr size_t kLds = kSplitWaves * kTileLds + 2 * kRed * sizeof(float);
+  static_assert(kChunks >= 16 && kRowsPerLoad >= 1, "swizzle needs >= 16 chunks per row slice");
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+constexpr int kLoadNonTemporal = 2;
+
+template <class T>
+__device__ __forceinline__ unsigned load_elem_bits(__amdgpu_buffer_rsrc_t r, int off);
+template <>
+__device__ __forceinline__ unsigned load_elem_bits<Bf16>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ unsigned load_elem_bits<F32>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <class T>
+__device__ __forceinline__ float elem_bits_to_f32(unsigned u);
+template <>
+__device__ __forceinline__ float elem_bits_to_f32<Bf16>(unsigned u) { return __uint_as_float(u << 16); }
+template <>
+__device__ __forceinline__ float elem_bits_to_f32<F32>(unsigned u) { return __uint_as_float(u); }
+
+template <class T, int KW, bool BIAS>
+__global__ void __launch_bounds__(kSplitWaves * 64)
+    rowstream_gemm_kernel(const typename T::elem* __restrict__ A, int lda, int M,
+                          const typename T::elem* __restrict__ W, int ldw, int N,
+                          const typename T::elem* __restrict__ bias, float* __restrict__ C, int ldc) {
+  using RS = RowStream<KW>;
+  using E = typename T::elem;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int m0 = blockIdx.y * 16;
+  unsigned char* tile = smem + (size_t)wave * RS::kTileLds;
+  float* red = reinterpret_cast<float*>(smem + kSplitWaves * RS::kTileLds);
+
+  u32x4 af[KW];
+  {
+    const bool live = m0 + col < M;
+    const unsigned char* arow = reinterpret_cast<const unsigned char*>(A + (size_t)(live ? m0 + col : 0) * lda) +
+                                (size_t)wave * RS::kSlice + grp * 16;
+#pragma unroll
+    for (int s = 0; s < KW; ++s) af[s] = live ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
+  }
+  const int ntiles = (N + 15) >> 4;
+  const int row_bytes = ldw * (int)sizeof(E);
+  // load j of a tile: row j * kRowsPerLoad + lrow, chunk lchunk of this wave's slice
+  const int lrow = lane / RS::kChunks, lchunk = lane % RS::kChunks;
+  const int voff = lrow * row_bytes + wave * RS::kSlice + lchunk * 16;
+  const __amdgpu_buffer_rsrc_t brs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(BIAS ? bias : W), (short)0, BIAS ? N * (int)sizeof(E) : 0,
+                                        kRsrcWord3);
+  const int rcol = threadIdx.x & 15;  // output column of a reducing thread
+
+  // Load j reads rows j * kRowsPerLoad ... of the tile through a descriptor
+  // based at its first row and sized to those of its rows below N (none past
+  // the last tile), so one lane offset serves every load and the range check
+  // covers every row.
+  auto stage = [&](int t, u32x4 (&dst)[KW], unsigned& bv) {
+    const int rows = t < ntiles ? min(16, N - t * 16) : 0;
+    const E* base = W + (t < ntiles ? (size_t)t * 16 * ldw : 0);
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int rj = min(max(rows - j * RS::kRowsPerLoad, 0), RS::kRowsPerLoad);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<E*>(base + (rj > 0 ? (size_t)j * RS::kRowsPerLoad * ldw : 0)), (short)0, rj * row_bytes,
+          kRsrcWord3);
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadNonTemporal);
+    }
+    bv = BIAS ? load_elem_bits<T>(brs, (t * 16 + rcol) * (int)sizeof(E)) : 0u;
+  };
+  auto process = [&](int t, const u32x4 (&w)[KW], unsigned bv, float* rb) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int r = j * RS::kRowsPerLoad + lrow;
+      st16(tile + r * RS::kSlice + ((lchunk ^ (r & 15)) << 4), w[j]);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KW; ++s) {
+      const u32x4 b = ld16(tile + col * RS::kSlice + (((s * 4 + grp) ^ col) << 4));
+      acc = mma16<T>(acc, af[s], b);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rb[(wave * 16 + grp * 4 + j) * 17 + col] = acc[j];
+    // converted by every wave, outside the branch below: a load that only one
+    // side of a branch consumes makes the compiler drain the prefetch later
+    float bias_n = elem_bits_to_f32<T>(bv);
+    if (BIAS) asm volatile("" : "+v"(bias_n));  // keeps the compiler from sinking it into the branch
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      const int m = threadIdx.x >> 4;
+      const int n = t * 16 + rcol;
+      float sum = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < kSplitWaves; ++w8) sum += rb[(w8 * 16 + m) * 17 + rcol];
+      if (m0 + m < M && n < N) C[(size_t)(m0 + m) * ldc + n] = sum + bias_n;
+    }
+  };
+
+  const int G = gridDim.x;
+  u32x4 w0[KW], w1[KW];
+  unsigned b0, b1;
+  int t = blockIdx.x;
+  stage(t, w0, b0);
+  // The scheduling barriers keep each prefetch ahead of the LDS traffic of
+  // the tile in hand; left alone, the compiler sinks the loads below it and
+  // the wait for the current tile then drains the prefetch as well.
+  while (t < ntiles) {
+    stage(t + G, w1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, w0, b0, red);
+    t += G;
+    if (t >= ntiles) break;
+    stage(t + G, w0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, w1, b1, red + RS::kRed);
+    t += G;
+  }
+}
+
 __global__ void fill_u64_kernel(unsigned long long* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0ull;
@@ -216,13 +363,37 @@ static hipError_t splitk_t(const void* A, int lda, int M, const void* W, int ldw
   return hipGetLastError();
 }
 
+template <class T, int KW>
+static hipError_t rowstream_t(const void* A, int lda, int M, const void* W, int ldw, int N, const void* bias,
+                              float* C, int ldc, int num_cu, hipStream_t s) {
+  using E = typename T::elem;
+  auto kern = bias ? rowstream_gemm_kernel<T, KW, true> : rowstream_gemm_kernel<T, KW, false>;
+  const size_t lds = RowStream<KW>::kLds;
+  hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  const int ntiles = (N + 15) / 16;
+  dim3 grid(std::min(ntiles, num_cu), (M + 15) / 16);
+  hipLaunchKernelGGL(kern, grid, dim3(kSplitWaves * 64), lds, s, static_cast<const E*>(A), lda, M,
+                     static_cast<const E*>(W), ldw, N, static_cast<const E*>(bias), C, ldc);
+  return hipGetLastError();
+}
+
 // K split over 8 waves in 64-byte steps; returns hipErrorNotSupported for K
-// that does not divide evenly into one of the compiled step counts.
+// that does not divide evenly into one of the compiled step counts.  Every W
+// row must start 16-byte aligned (the row stride is checked here).
 template <class T>
 static hipError_t splitk_dispatch(const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                                   const void* bias, float* C, int ldc, int num_cu, hipStream_t s) {
   const size_t row_bytes = (size_t)K * sizeof(typename T::elem);
   if (row_bytes % (64 * kSplitWaves)) return hipErrorNotSupported;
+  if (((size_t)ldw * sizeof(typename T::elem)) % 16 == 0) {
+    switch (row_bytes / (64 * kSplitWaves)) {
+      case 4: return rowstream_t<T, 4>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
+      case 8: return rowstream_t<T, 8>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
+      case 16: return rowstream_t<T, 16>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
+      default: break;
+    }
+  }
   switch (row_bytes / (64 * kSplitWaves)) {
     case 1: return splitk_t<T, 1>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
     case 2: return splitk_t<T, 2>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
