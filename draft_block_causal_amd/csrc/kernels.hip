@@ -141,10 +141,11 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
 // ---------------------------------------------------------------------------
 // rowstream_gemm: the split-K product above with W read the way HBM streams
 // best.  A load instruction of the split-K kernel covers 64 B of each of 16
-// rows; here each covers whole 16-B chunks of one contiguous run of a row
-// (1 KB of one row when KW = 16), read non-temporally since W is used once.
-// Each wave writes its 16 row slices into a private LDS tile and reads them
-// back in the matrix-core operand layout (row = lane column).  The 16-B
+// rows; here each covers whole 16-B chunks of contiguous runs of one or a
+// few rows (two runs of 512 B when d = 4096 bf16), read non-temporally since
+// W is used once.  Each wave writes its row slices into a private LDS tile and
+// reads them back in the matrix-core operand layout (row = lane column), in
+// passes of at most 512 B per row so that the tile stays 8 KB.  The 16-B
 // chunks of row r are stored XOR-swizzled by r & 15, so both the row-wise
 // writes and the column-wise reads touch 16 distinct bank groups per 16 lanes.
 // W and the bias are read through buffer descriptors sized to the valid rows
@@ -153,18 +154,27 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
 // is always in flight while the current one is multiplied (two register
 // buffers used in turn, so no copies).  The partial tiles of the 8 waves are
 // summed in LDS in a fixed order; the two halves of the loop use separate
-// reduction buffers, so one barrier per tile suffices.  KW in {4, 8, 16}.
+// reduction buffers, so one barrier per tile suffices.  Finished output tiles
+// stay in LDS and are written after the workgroup's last tile: C stores mixed
+// into the W stream cost ~8 % of HBM read throughput, as scattered writes.
+// KW in {4, 8, 16}.
 // ---------------------------------------------------------------------------
 template <int KW>
 struct RowStream {
-  static constexpr int kSlice = KW * 64;             // bytes of a row per wave
-  static constexpr int kChunks = kSlice / 16;        // 16-B chunks per row slice
-  static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one load instruction covers
-  static constexpr size_t kTileLds = 16 * kSlice;    // one wave's transposition tile
-  static constexpr int kRed = kSplitWaves * 16 * 17; // floats per reduction buffer
-  static constexpr size_t kLds = kSplitWaves * kTileLds + 2 * kRed * sizeof(float);
-  static_assert(kChunks >= 16 && kRowsPerLoad >= 1, "swizzle needs >= 16 chunks per row slice");
+  static constexpr int kSlice = KW * 64;                         // bytes of a row per wave
+  static constexpr int kPass = kSlice < 512 ? kSlice : 512;      // bytes of a row per LDS pass
+  static constexpr int kPasses = kSlice / kPass;
+  static constexpr int kChunks = kPass / 16;                     // 16-B chunks per row and pass
+  static constexpr int kRowsPerLoad = 64 / kChunks;              // rows one load instruction covers
+  static constexpr int kLoadsPerPass = 16 / kRowsPerLoad;
+  static constexpr int kStepsPerPass = kPass / 64;               // matrix-core K steps per pass
+  static constexpr size_t kTileLds = 16 * kPass;                 // one wave's transposition tile
+  static constexpr int kRed = kSplitWaves * 16 * 17;             // floats per reduction buffer
+  static constexpr size_t kFixedLds = kSplitWaves * kTileLds + 2 * kRed * sizeof(float);
+  static constexpr int kOutTileFloats = 256;                     // one 16 x 16 output tile
+  static_assert(kChunks >= 16 && kRowsPerLoad >= 1 && kPasses * kLoadsPerPass == KW, "row-stream shape");
 };
+constexpr size_t kMaxLds = 160 * 1024;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
 constexpr int kLoadNonTemporal = 2;
@@ -190,7 +200,8 @@ template <class T, int KW, bool BIAS>
 __global__ void __launch_bounds__(kSplitWaves * 64)
     rowstream_gemm_kernel(const typename T::elem* __restrict__ A, int lda, int M,
                           const typename T::elem* __restrict__ W, int ldw, int N,
-                          const typename T::elem* __restrict__ bias, float* __restrict__ C, int ldc) {
+                          const typename T::elem* __restrict__ bias, float* __restrict__ C, int ldc,
+                          int out_tiles) {
   using RS = RowStream<KW>;
   using E = typename T::elem;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -199,6 +210,7 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
   const int m0 = blockIdx.y * 16;
   unsigned char* tile = smem + (size_t)wave * RS::kTileLds;
   float* red = reinterpret_cast<float*>(smem + kSplitWaves * RS::kTileLds);
+  float* obuf = reinterpret_cast<float*>(smem + RS::kFixedLds);  // out_tiles finished 16 x 16 tiles
 
   u32x4 af[KW];
   {
@@ -209,8 +221,9 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
     for (int s = 0; s < KW; ++s) af[s] = live ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
   }
   const int ntiles = (N + 15) >> 4;
+  const int G = gridDim.x;
   const int row_bytes = ldw * (int)sizeof(E);
-  // load j of a tile: row j * kRowsPerLoad + lrow, chunk lchunk of this wave's slice
+  // load jj of pass p: row jj * kRowsPerLoad + lrow, chunk lchunk of the pass
   const int lrow = lane / RS::kChunks, lchunk = lane % RS::kChunks;
   const int voff = lrow * row_bytes + wave * RS::kSlice + lchunk * 16;
   const __amdgpu_buffer_rsrc_t brs =
@@ -218,34 +231,42 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
                                         kRsrcWord3);
   const int rcol = threadIdx.x & 15;  // output column of a reducing thread
 
-  // Load j reads rows j * kRowsPerLoad ... of the tile through a descriptor
-  // based at its first row and sized to those of its rows below N (none past
-  // the last tile), so one lane offset serves every load and the range check
-  // covers every row.
+  // Load jj of a pass reads rows jj * kRowsPerLoad ... of the tile through a
+  // descriptor based at its first row and sized to those of its rows below N
+  // (none past the last tile), so one lane offset serves every load and the
+  // range check covers every row.
   auto stage = [&](int t, u32x4 (&dst)[KW], unsigned& bv) {
     const int rows = t < ntiles ? min(16, N - t * 16) : 0;
     const E* base = W + (t < ntiles ? (size_t)t * 16 * ldw : 0);
 #pragma unroll
-    for (int j = 0; j < KW; ++j) {
-      const int rj = min(max(rows - j * RS::kRowsPerLoad, 0), RS::kRowsPerLoad);
+    for (int jj = 0; jj < RS::kLoadsPerPass; ++jj) {
+      // (rows >= 0; a clamp on both sides for jj = 0 becomes a vector med3 and
+      // the descriptor a per-lane value)
+      const int rj = jj == 0 ? min(rows, RS::kRowsPerLoad) : min(max(rows - jj * RS::kRowsPerLoad, 0), RS::kRowsPerLoad);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<E*>(base + (rj > 0 ? (size_t)j * RS::kRowsPerLoad * ldw : 0)), (short)0, rj * row_bytes,
+          const_cast<E*>(base + (rj > 0 ? (size_t)jj * RS::kRowsPerLoad * ldw : 0)), (short)0, rj * row_bytes,
           kRsrcWord3);
-      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadNonTemporal);
+#pragma unroll
+      for (int p = 0; p < RS::kPasses; ++p)
+        dst[p * RS::kLoadsPerPass + jj] =
+            __builtin_amdgcn_raw_buffer_load_b128(r, voff + p * RS::kPass, 0, kLoadNonTemporal);
     }
     bv = BIAS ? load_elem_bits<T>(brs, (t * 16 + rcol) * (int)sizeof(E)) : 0u;
   };
-  auto process = [&](int t, const u32x4 (&w)[KW], unsigned bv, float* rb) {
-#pragma unroll
-    for (int j = 0; j < KW; ++j) {
-      const int r = j * RS::kRowsPerLoad + lrow;
-      st16(tile + r * RS::kSlice + ((lchunk ^ (r & 15)) << 4), w[j]);
-    }
+  auto process = [&](int i, int t, const u32x4 (&w)[KW], unsigned bv, float* rb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KW; ++s) {
-      const u32x4 b = ld16(tile + col * RS::kSlice + (((s * 4 + grp) ^ col) << 4));
-      acc = mma16<T>(acc, af[s], b);
+    for (int p = 0; p < RS::kPasses; ++p) {
+#pragma unroll
+      for (int jj = 0; jj < RS::kLoadsPerPass; ++jj) {
+        const int r = jj * RS::kRowsPerLoad + lrow;
+        st16(tile + r * RS::kPass + ((lchunk ^ (r & 15)) << 4), w[p * RS::kLoadsPerPass + jj]);
+      }
+#pragma unroll
+      for (int ss = 0; ss < RS::kStepsPerPass; ++ss) {
+        const u32x4 b = ld16(tile + col * RS::kPass + (((ss * 4 + grp) ^ col) << 4));
+        acc = mma16<T>(acc, af[p * RS::kStepsPerPass + ss], b);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) rb[(wave * 16 + grp * 4 + j) * 17 + col] = acc[j];
@@ -256,18 +277,22 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
     __syncthreads();
     if (threadIdx.x < 256) {
       const int m = threadIdx.x >> 4;
-      const int n = t * 16 + rcol;
       float sum = 0.f;
 #pragma unroll
       for (int w8 = 0; w8 < kSplitWaves; ++w8) sum += rb[(w8 * 16 + m) * 17 + rcol];
-      if (m0 + m < M && n < N) C[(size_t)(m0 + m) * ldc + n] = sum + bias_n;
+      sum += bias_n;
+      if (i < out_tiles) {
+        obuf[i * RS::kOutTileFloats + threadIdx.x] = sum;
+      } else {  // more tiles than the LDS holds: store directly
+        const int n = t * 16 + rcol;
+        if (m0 + m < M && n < N) C[(size_t)(m0 + m) * ldc + n] = sum;
+      }
     }
   };
 
-  const int G = gridDim.x;
   u32x4 w0[KW], w1[KW];
   unsigned b0, b1;
-  int t = blockIdx.x;
+  int t = blockIdx.x, i = 0;
   stage(t, w0, b0);
   // The scheduling barriers keep each prefetch ahead of the LDS traffic of
   // the tile in hand; left alone, the compiler sinks the loads below it and
@@ -275,13 +300,23 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
   while (t < ntiles) {
     stage(t + G, w1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    process(t, w0, b0, red);
+    process(i, t, w0, b0, red);
     t += G;
+    ++i;
     if (t >= ntiles) break;
     stage(t + G, w0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    process(t, w1, b1, red + RS::kRed);
+    process(i, t, w1, b1, red + RS::kRed);
     t += G;
+    ++i;
+  }
+  // the held output tiles, local tile k = global tile blockIdx.x + k * G
+  __syncthreads();
+  const int held = min(i, out_tiles);
+  for (int e = threadIdx.x; e < held * RS::kOutTileFloats; e += kSplitWaves * 64) {
+    const int k = e >> 8, m = (e >> 4) & 15;
+    const int n = (blockIdx.x + k * G) * 16 + (e & 15);
+    if (m0 + m < M && n < N) C[(size_t)(m0 + m) * ldc + n] = obuf[e];
   }
 }
 
@@ -367,14 +402,20 @@ template <class T, int KW>
 static hipError_t rowstream_t(const void* A, int lda, int M, const void* W, int ldw, int N, const void* bias,
                               float* C, int ldc, int num_cu, hipStream_t s) {
   using E = typename T::elem;
+  using RS = RowStream<KW>;
   auto kern = bias ? rowstream_gemm_kernel<T, KW, true> : rowstream_gemm_kernel<T, KW, false>;
-  const size_t lds = RowStream<KW>::kLds;
+  const int ntiles = (N + 15) / 16;
+  const int gx = std::min(ntiles, num_cu);
+  // hold every output tile of a workgroup in LDS when it fits
+  const int per_wg = (ntiles + gx - 1) / gx;
+  const int fit = (int)((kMaxLds - RS::kFixedLds) / (RS::kOutTileFloats * sizeof(float)));
+  const int out_tiles = std::min(per_wg, fit);
+  const size_t lds = RS::kFixedLds + (size_t)out_tiles * RS::kOutTileFloats * sizeof(float);
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
-  const int ntiles = (N + 15) / 16;
-  dim3 grid(std::min(ntiles, num_cu), (M + 15) / 16);
+  dim3 grid(gx, (M + 15) / 16);
   hipLaunchKernelGGL(kern, grid, dim3(kSplitWaves * 64), lds, s, static_cast<const E*>(A), lda, M,
-                     static_cast<const E*>(W), ldw, N, static_cast<const E*>(bias), C, ldc);
+                     static_cast<const E*>(W), ldw, N, static_cast<const E*>(bias), C, ldc, out_tiles);
   return hipGetLastError();
 }
 
