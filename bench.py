@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f) for f in ("kernels.hip", "common.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f) for f in ("rowstream.hip", "common.h")]
 
 
 def kernel_source_hash() -> str:
@@ -193,8 +193,12 @@ def main() -> int:
         achieved = alg / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": alg}
-    kname = ("splitk_gemm_kernel<Bf16,16> (LM head, K split over 8 waves)" if M <= 32
-             else "gemm_bf16_tn_kernel (LM head, 128x128 tiles)")
+    if M <= 32:
+        kname = "rowstream_gemm_kernel (LM head, K split over 8 waves, row-contiguous non-temporal loads)"
+    elif M >= 256 and w.dtype == "bf16":
+        kname = "gemm_bf16_tn_256_kernel (LM head, 256x256 tiles, LDS-DMA operand loads)"
+    else:
+        kname = "gemm_bf16_tn_kernel (LM head, 128x128 tiles)"
     roof.update({"kernel": kname, "avg_launch_ms": lm_ms})
 
     result = {

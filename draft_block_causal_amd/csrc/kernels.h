@@ -13,6 +13,12 @@ namespace domino {
 hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                              const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
 
+// The same product for M <= 32 by the row-streaming kernel (rowstream.hip);
+// hipErrorNotSupported unless K * elem_size is 2, 4 or 8 KB and W rows are
+// 16-byte aligned.
+hipError_t launch_rowstream_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
+                                 const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
+
 // Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 64 == 0 (else hipErrorNotSupported).
 hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
                                float* C, int ldc, hipStream_t s);

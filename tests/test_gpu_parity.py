@@ -243,6 +243,35 @@ def test_batch_tile_boundaries(dev, batch, mode, monkeypatch):
     _parity(_small("bf16", batch=batch, vocab=777, block=3, d=96, gru_hidden=64), dev)
 
 
+def test_lm_head_more_tiles_than_lds(dev):
+    """Base logits when a workgroup finishes more 16-row tiles than it can hold.
+
+    The LM-head kernel keeps each workgroup's output tiles in LDS until its
+    last tile; at d = 1024 (bf16) there is room for 111 of them.  With
+    V = 460000 (28750 tiles over 256 workgroups, 113 each) the last tiles of
+    every workgroup are stored directly.  Every column of those tiles and
+    10000 random others are checked against the oracle.
+    """
+    import draft_block_causal_amd as D
+
+    w = S.Workload("lm_head_460k_d1024", 1, 16, 1024, 460000, 32, 32, "bf16", True, 0.0)
+    log(f"{w.name}: generating inputs")
+    head_np, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    base = D.domino_base_logits(head, _t(inp["hidden"], dev))
+    torch.cuda.synchronize()
+    got = base.cpu().numpy()[0]
+    ntiles = (w.vocab + 15) // 16
+    tail = np.arange(ntiles - 2 * 256, ntiles)  # the last tiles of every workgroup
+    cols = np.concatenate([(tail[:, None] * 16 + np.arange(16)).ravel(),
+                           np.random.default_rng(5).integers(0, w.vocab, 10000)])
+    cols = np.unique(cols[cols < w.vocab])
+    ref = O.base_logits(O.as_f64(inp["hidden"][0]), O.as_f64(head_np["lm_head"][cols]))
+    err = np.abs(got[:, cols] - ref).max()
+    log(f"{w.name}: {cols.size} columns, max err {err:.2e}")
+    assert err <= LOGIT_TOL, f"base logits err {err}"
+
+
 def test_sampled_small_temperature_and_ties(dev):
     _parity(_small("bf16", temperature=0.37, philox_seed=99), dev)
 
