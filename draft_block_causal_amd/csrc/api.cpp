@@ -95,6 +95,7 @@ extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const voi
   a.states = gru_states ? gru_states : reinterpret_cast<float*>(ws + w.states);
   a.keys = reinterpret_cast<unsigned long long*>(ws + w.keys);
   a.P = reinterpret_cast<float*>(ws + w.P);
+  a.ppart = reinterpret_cast<float*>(ws + w.ppart);
   a.part_ih = reinterpret_cast<float*>(ws + w.part_ih);
   a.part_hh = reinterpret_cast<float*>(ws + w.part_hh);
   a.u = reinterpret_cast<float*>(ws + w.u);

@@ -41,6 +41,7 @@ struct LoopArgs {
   // workspace pieces
   unsigned long long* keys;  // [K, B], followed by 2 u64 of loop control (barrier counter, status)
   float* P;                  // [B, K, r]
+  float* ppart;              // B = 1: [S <= 16][K][r] K-slice partials of P
   float* part_ih;            // [KS, B, 3H]
   float* part_hh;            // [B, 3H]
   float* u;                  // [B, r]
@@ -57,18 +58,17 @@ struct LoopArgs {
 // 1 = one persistent cooperative kernel (B <= 32), 2 = three kernels per position.
 hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s);
 
-// The B = 1 persistent loop with on-chip weights; hipErrorNotSupported when the
-// shape, dtype or device does not fit it (the caller then uses another schedule).
-// The single-block on-chip loop: b1_supported() tells whether it takes these
-// arguments (host-side checks only); launch_draft_b1 reads a.P, the hidden
-// half of the first correction projection, computed beforehand.
+// The single-block (B = 1) loop with on-chip weights: b1_supported() tells
+// whether it takes these arguments (host-side checks only); launch_draft_b1
+// returns hipErrorNotSupported when the device does not fit it (the caller
+// then uses another schedule).  It enqueues its own pre-loop kernel, which
+// clears a.keys and the exchange words and writes the hidden half of the
+// first correction projection to a.ppart.
 bool b1_supported(const LoopArgs& a);
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s);
 size_t b1_exchange_words(int H, int r, int max_wg);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
-// clears n words at p and m words at q in one launch
-hipError_t launch_fill2_u64(unsigned long long* p, int n, unsigned long long* q, int m, hipStream_t s);
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,

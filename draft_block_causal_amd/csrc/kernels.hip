@@ -145,14 +145,6 @@ __global__ void fill_u64_kernel(unsigned long long* p, int n) {
   if (i < n) p[i] = 0ull;
 }
 
-__global__ void fill2_u64_kernel(unsigned long long* p, int n, unsigned long long* q, int m) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n)
-    p[i] = 0ull;
-  else if (i - n < m)
-    q[i - n] = 0ull;
-}
-
 __global__ void finalize_tokens_kernel(int B, int K, const unsigned long long* __restrict__ keys,
                                        int32_t* __restrict__ tokens) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -258,12 +250,6 @@ hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const voi
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_u64_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill2_u64(unsigned long long* p, int n, unsigned long long* q, int m, hipStream_t s) {
-  if (n + m <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill2_u64_kernel, dim3((n + m + 255) / 256), dim3(256), 0, s, p, n, q, m);
   return hipGetLastError();
 }
 

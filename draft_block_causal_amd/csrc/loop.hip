@@ -787,13 +787,9 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
   const DevLoop<T> p = make_dev<T>(a);
   if constexpr (MT == 1) {
     if (mode != 2 && b1_supported(a)) {
-      // on-chip-weight loop for a single block (needs the GRU input table):
-      // keys, control words and the tagged exchange words start at zero
-      hipError_t e = launch_fill2_u64(a.keys, a.K * a.B + 1, a.xpart, (int)a.xwords, s);
-      if (e != hipSuccess) return e;
-      e = launch_panel_gemm(a.dtype, a.hidden, a.d, a.K, a.w1, a.d + a.H, a.r, a.d, a.b1, a.P, a.r, a.num_cu, s);
-      if (e != hipSuccess) return e;
-      e = launch_draft_b1(a, s);
+      // on-chip-weight loop for a single block (needs the GRU input table); it
+      // clears its own keys and exchange words and forms P in its pre-launch
+      hipError_t e = launch_draft_b1(a, s);
       if (e != hipErrorNotSupported) return e;
       (void)hipGetLastError();  // the grid cannot be co-resident here: use another schedule
     }

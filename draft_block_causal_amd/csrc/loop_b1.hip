@@ -25,8 +25,9 @@
 //   B(i)   the kUnitWGs unit workgroups: y_{i-1} from the G argmax keys,
 //          T[y_{i-1}] for their units, W_hh g_{i-1} from the partials, gates,
 //          new state g_i (-> states, x_g), their share of W1[:, d:] g_i on
-//          the matrix cores                                        -> x_pu
-//   C(i)   every workgroup: u = SiLU(P_i + sum of the shares), its W2 tiles
+//          the matrix cores, unit workgroup s < S adding slice s of
+//          P_i = W1[:, :d] h_i + b1                                -> x_pu
+//   C(i)   every workgroup: u = SiLU(sum of the shares), its W2 tiles
 //          on the matrix cores, + b2 + base logits (+ Gumbel), argmax -> x_key
 //   A(i+1) the other workgroups (the W_hh owners), after publishing their
 //          key: W_hh g_i partials of their k-range, from g_i staged in C(i)
@@ -72,7 +73,9 @@ struct Params {
   int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
   const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
   const float* table;     // [V][3H]: W_ih E[v] + b_ih
-  const float *base, *P;  // base [K][V], P [K][r] = W1[:, :d] h + b1
+  const float* base;   // [K][V]
+  const float* ppart;  // [S][K][r]: P = W1[:, :d] h + b1 = sum over s of ppart[s] (b1 in s = 0)
+  int S;
   const int32_t *x_t, *teacher;
   float inv_temp;
   int sampled;
@@ -411,8 +414,6 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       }
     };
     if (!unit_wg) load_base();
-    // the hidden-state part of the bottleneck pre-activation (one entry per thread)
-    const float p_pre = tid < r ? p.P[(size_t)step * r + tid] : 0.f;
     // Gumbel noise for this position (read in C, after two barriers)
     if (SAMPLED)
       for (int i = tid; i < nv; i += kThreads)
@@ -448,6 +449,15 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         break;
       }
       load_base();
+      // unit workgroup w < S adds slice w of P = W1[:, :d] h_i + b1 to the
+      // entries it publishes (lanes of row group 0 hold them); it arrives
+      // while the gates are formed
+      constexpr int kRtPerWave = 256 / 16 / kWaves;  // r / 16 / kWaves with r = 256
+      float pslice[kRtPerWave];
+#pragma unroll
+      for (int i = 0; i < kRtPerWave; ++i)
+        pslice[i] = w < p.S && grp == 0 ? p.ppart[((size_t)w * p.K + step) * r + (wave * kRtPerWave + i) * 16 + col]
+                                        : 0.f;
       if (tid < units) {
         const int j = w * units + tid;
         const float* trow = p.table + (size_t)s_tok * 3 * H;
@@ -479,7 +489,6 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       }
       // this workgroup's share of W1[:, d:] g on the matrix cores: wave wv
       // owns bottleneck rows [wv * r / kWaves, (wv + 1) * r / kWaves)
-      constexpr int kRtPerWave = 256 / 16 / kWaves;  // r / 16 / kWaves with r = 256
       f32x4 acc[kRtPerWave];
 #pragma unroll
       for (int i = 0; i < kRtPerWave; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -492,8 +501,8 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       if (grp == 0)
 #pragma unroll
         for (int i = 0; i < kRtPerWave; ++i)
-          put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + (wave * kRtPerWave + i) * 16 + col, acc[i][0] + acc[i][1],
-                  tag);
+          put_f32(p.x_pu + ((size_t)par * kUnitWGs + w) * r + (wave * kRtPerWave + i) * 16 + col,
+                  acc[i][0] + acc[i][1] + pslice[i], tag);
     }
 
     // ---------- C(i): u, W2 tiles, argmax ----------
@@ -524,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       for (int q = 0; q < kUnitWGs + kPer; ++q) x[q] = src[q] ? ld_word(src[q]) : 0ull;
       ok &= settle_all(src, tag, p.status, x);
       if (tid < r) {
-        float s = p_pre;
+        float s = 0.f;  // the shares carry P as well
 #pragma unroll
         for (int q = 0; q < kUnitWGs; ++q) s += __uint_as_float((uint32_t)x[q]);
         split_store(utile, r, tid, s * sigmoidf_(s));
@@ -631,8 +640,104 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Before the loop, one launch clears the argmax keys, the control words and
+// the exchange words (no stale tag may survive from an earlier call), and
+// forms the loop-invariant hidden half of the first correction projection,
+// P_i = W1[:, :d] h_i + b1 for every position i ([notes] §二.1(2) item 2), as
+// S partial sums over K slices.  Each wave takes 512 B of K (8 matrix-core
+// steps) of one 16-row tile of W1 for all positions; the waves of a workgroup
+// add their products in LDS and the workgroup writes slice s; the loop adds
+// the S slices in a fixed order (unit workgroup s adds slice s to its share
+// of W1[:, d:] g).  This spreads the 2 MB of W1 over S x r / 16 workgroups
+// instead of r / 16.
+// ---------------------------------------------------------------------------
+constexpr int kPreWaves = 4;   // waves per workgroup, at most
+constexpr int kPreSteps = 8;   // 64-B K steps per wave
+constexpr int kPreMaxMt = 4;   // 16-row position tiles (K <= 64)
+
+__global__ void __launch_bounds__(kPreWaves * 64)
+    pre_kernel(const uint16_t* __restrict__ hidden, int M, int d, const uint16_t* __restrict__ w1, int ldw, int r,
+               const uint16_t* __restrict__ b1, float* __restrict__ ppart, int waves,
+               unsigned long long* __restrict__ z0, int n0, unsigned long long* __restrict__ z1, int n1) {
+  __shared__ float red[kPreWaves][kPreMaxMt][16][17];
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n0 + n1; i += gridDim.x * blockDim.x) {
+    if (i < n0)
+      z0[i] = 0ull;
+    else
+      z1[i - n0] = 0ull;
+  }
+  const int ntn = r >> 4;
+  const int nt = blockIdx.x % ntn, ks = blockIdx.x / ntn;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int mtiles = (M + 15) >> 4;
+  if (wave < waves) {
+    const size_t kb = (size_t)(ks * waves + wave) * (kPreSteps * 64) + grp * 16;
+    const unsigned char* wrow = reinterpret_cast<const unsigned char*>(w1 + (size_t)(nt * 16 + col) * ldw) + kb;
+    u32x4 wf[kPreSteps];
+#pragma unroll
+    for (int s = 0; s < kPreSteps; ++s) wf[s] = ld16(wrow + s * 64);
+    for (int mt = 0; mt < mtiles; ++mt) {
+      const int m = mt * 16 + col;
+      const unsigned char* arow = reinterpret_cast<const unsigned char*>(hidden + (size_t)min(m, M - 1) * d) + kb;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kPreSteps; ++s) {
+        const u32x4 a = m < M ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
+        acc = mma16<Bf16>(acc, a, wf[s]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][mt][grp * 4 + j][col] = acc[j];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < mtiles * 256; e += blockDim.x) {
+    const int mt = e >> 8, mm = (e >> 4) & 15, c = e & 15;
+    const int m = mt * 16 + mm, n = nt * 16 + c;
+    if (m < M) {
+      float sum = 0.f;
+      for (int w = 0; w < waves; ++w) sum += red[w][mt][mm][c];
+      if (ks == 0 && b1) sum += bf16_to_f32(b1[n]);
+      ppart[((size_t)ks * M + m) * r + n] = sum;
+    }
+  }
+}
+
+// Launch shape of the pre-loop kernel, or false when d does not split into
+// 512-B slices.  Unit workgroup s < S adds slice s of P into the share of
+// W1[:, d:] g it publishes, so every workgroup's u = SiLU(sum of the shares).
+struct Pre {
+  int waves, S, grid;
+};
+static bool pre_shape(int d, int r, Pre& pr) {
+  const int row = d * 2;
+  if (row % 512 || r % 16) return false;
+  const int chunks = row / 512;
+  pr.waves = chunks % 4 == 0 ? 4 : chunks % 2 == 0 ? 2 : 1;
+  pr.S = chunks / pr.waves;
+  pr.grid = pr.S * (r / 16);
+  return pr.S <= 16;
+}
+
+struct PreArgs {
+  const LoopArgs* a;
+  Pre shape;
+};
+
+static hipError_t launch_pre(const PreArgs& q, hipStream_t s) {
+  const LoopArgs& a = *q.a;
+  hipLaunchKernelGGL(pre_kernel, dim3(q.shape.grid), dim3(kPreWaves * 64), 0, s,
+                     static_cast<const uint16_t*>(a.hidden), a.K, a.d, static_cast<const uint16_t*>(a.w1), a.d + a.H,
+                     a.r, static_cast<const uint16_t*>(a.b1), a.ppart, q.shape.waves, a.keys, a.K * a.B + 1, a.xpart,
+                     (int)a.xwords);
+  return hipGetLastError();
+}
+
+// Checks that the loop kernel fits one workgroup per CU, then launches the
+// pre-loop kernel and the loop.
 template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
-static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
+static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q, hipStream_t s) {
   auto kern = draft_b1_kernel<UHW, NR, RK, SAMPLED, LOGITS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
@@ -641,23 +746,28 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, hipStream_t s) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
+  e = launch_pre(q, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
 template <int UHW, int NR, int RK>
-static hipError_t launch_flags(const Params& p, int G, size_t lds, hipStream_t s) {
-  if (p.sampled) return p.logits ? launch_t<UHW, NR, RK, true, true>(p, G, lds, s) : launch_t<UHW, NR, RK, true, false>(p, G, lds, s);
-  return p.logits ? launch_t<UHW, NR, RK, false, true>(p, G, lds, s) : launch_t<UHW, NR, RK, false, false>(p, G, lds, s);
+static hipError_t launch_flags(const Params& p, int G, size_t lds, const PreArgs& q, hipStream_t s) {
+  if (p.sampled)
+    return p.logits ? launch_t<UHW, NR, RK, true, true>(p, G, lds, q, s)
+                    : launch_t<UHW, NR, RK, true, false>(p, G, lds, q, s);
+  return p.logits ? launch_t<UHW, NR, RK, false, true>(p, G, lds, q, s)
+                  : launch_t<UHW, NR, RK, false, false>(p, G, lds, q, s);
 }
 
 template <int NR, int RK>
-static hipError_t launch_uhw(const Params& p, int uhw, int G, size_t lds, hipStream_t s) {
+static hipError_t launch_uhw(const Params& p, int uhw, int G, size_t lds, const PreArgs& q, hipStream_t s) {
   switch (uhw) {
-    case 2: return launch_flags<2, NR, RK>(p, G, lds, s);
-    case 4: return launch_flags<4, NR, RK>(p, G, lds, s);
-    case 6: return launch_flags<6, NR, RK>(p, G, lds, s);
-    case 8: return launch_flags<8, NR, RK>(p, G, lds, s);
+    case 2: return launch_flags<2, NR, RK>(p, G, lds, q, s);
+    case 4: return launch_flags<4, NR, RK>(p, G, lds, q, s);
+    case 6: return launch_flags<6, NR, RK>(p, G, lds, q, s);
+    case 8: return launch_flags<8, NR, RK>(p, G, lds, q, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -679,6 +789,8 @@ static bool make_plan(const LoopArgs& a, Plan& pl) {
   constexpr int RK = 8;
   if (a.dtype != 1 || a.B != 1 || !a.table) return false;
   if (a.r != RK * 32 || a.H != kUnitWGs * kUnitMax) return false;  // 128 GRU units per unit workgroup
+  Pre pre;  // P arrives as S slices, one per unit workgroup at most
+  if (!pre_shape(a.d, a.r, pre) || pre.S > kUnitWGs) return false;
   pl.G = std::min(a.num_cu, std::min(a.max_wg, 256));
   if (pl.G <= kUnitWGs) return false;
   pl.KH = a.H / 32;
@@ -727,7 +839,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.b2 = static_cast<const uint16_t*>(a.b2);
   p.table = a.table;
   p.base = a.base;
-  p.P = a.P;
+  p.ppart = a.ppart;
   p.x_t = a.x_t;
   p.teacher = a.teacher;
   p.inv_temp = a.inv_temp;
@@ -746,7 +858,10 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.x_pu = x;
   x += 2 * (size_t)kUnitWGs * a.r;
   p.x_key = x;
-  return launch_uhw<NR, RK>(p, U_hh / kWaves, G, L.total, s);
+  PreArgs q{&a, {}};
+  if (!pre_shape(a.d, a.r, q.shape)) return hipErrorNotSupported;
+  p.S = q.shape.S;
+  return launch_uhw<NR, RK>(p, U_hh / kWaves, G, L.total, q, s);
 }
 
 }  // namespace domino

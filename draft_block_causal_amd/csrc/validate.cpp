@@ -47,6 +47,9 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   off += up256((K * B + 2) * sizeof(unsigned long long));  // keys + loop control words
   w.P = off;
   off += up256(B * K * r * sizeof(float));
+  // single-block loop: up to 16 K-slice partials of the hidden half of W1 h
+  w.ppart = off;
+  off += batch == 1 ? up256(16 * K * r * sizeof(float)) : 0;
   w.part_ih = off;
   off += up256(ks * B * 3 * H * sizeof(float));
   w.part_hh = off;

@@ -17,7 +17,7 @@ constexpr int kMaxVocab = (1 << 24) - 1;  // the persistent loop's argmax keys h
 constexpr int kMaxLoopWorkgroups = 1024;  // persistent loop grid cap (sizes the key exchange buffer)
 
 struct WorkspaceLayout {
-  size_t keys, P, part_ih, part_hh, u, states, xchg, total;
+  size_t keys, P, ppart, part_ih, part_hh, u, states, xchg, total;
   size_t xwords;  // 64-bit words in the exchange region
   int ks;
 };
