@@ -114,14 +114,22 @@ struct ActFrag<F32> {
   __device__ __forceinline__ f32x4 mma(f32x4 acc, u32x4 w) const { return mma16<F32>(acc, v, w); }
 };
 
+// Buffer descriptors for raw (untyped) loads: word 3 of the descriptor, and
+// the cache-policy bit of a non-temporal load.  A raw buffer load whose offset
+// (lane offset + immediate) is at or past the descriptor's byte count returns
+// zero without touching memory.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNonTemporal = 2;
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 counter-based generator (Salmon et al., SC'11): ten rounds of
 // two 32x32->64 multiplies, with the key advanced by two Weyl constants
 // between rounds.  Counter (v >> 2, pos, b, offset), key (seed lo, seed hi).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint32_t offset, uint32_t b, uint32_t pos,
-                                                uint32_t v) {
-  uint32_t x0 = v >> 2, x1 = pos, x2 = b, x3 = offset;
+// All four output words of the counter (ctr, pos, b, offset): the words of
+// vocabulary entries 4 ctr .. 4 ctr + 3.
+__device__ __forceinline__ u32x4 philox4(uint64_t seed, uint32_t offset, uint32_t b, uint32_t pos, uint32_t ctr) {
+  uint32_t x0 = ctr, x1 = pos, x2 = b, x3 = offset;
   uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
@@ -134,8 +142,14 @@ __device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint32_t offset, 
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
+  return u32x4{x0, x1, x2, x3};
+}
+
+__device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint32_t offset, uint32_t b, uint32_t pos,
+                                                uint32_t v) {
+  const u32x4 x = philox4(seed, offset, b, pos, v >> 2);
   const uint32_t s = v & 3u;
-  return s == 0 ? x0 : s == 1 ? x1 : s == 2 ? x2 : x3;
+  return s == 0 ? x[0] : s == 1 ? x[1] : s == 2 ? x[2] : x[3];
 }
 
 // Gumbel(0,1) sample from a Philox word: U = ((w >> 9) + 1/2) 2^-23 in (0,1).

@@ -13,9 +13,9 @@ namespace domino {
 hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                              const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
 
-// The same product for M <= 32 by the row-streaming kernel (rowstream.hip);
-// hipErrorNotSupported unless K * elem_size is 2, 4 or 8 KB and W rows are
-// 16-byte aligned.
+// The same product by the row-streaming kernel (rowstream.hip) for M <= 32,
+// or M, N <= 4096; hipErrorNotSupported otherwise, or unless
+// K * elem_size is 2, 4 or 8 KB and W rows are 16-byte aligned.
 hipError_t launch_rowstream_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                                  const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
 

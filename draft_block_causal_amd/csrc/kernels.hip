@@ -232,11 +232,13 @@ static hipError_t splitk_dispatch(const void* A, int lda, int M, const void* W, 
 hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                              const void* bias, float* C, int ldc, int num_cu, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (M <= 32) {  // one or two 16-row slices: stream W at full bandwidth
+  if (M <= 32 || (N <= 4096 && M <= 4096)) {  // few rows, or a small W: stream W at full bandwidth
     hipError_t e = launch_rowstream_gemm(dtype, A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
     if (e != hipErrorNotSupported) return e;
-    e = dtype == 1 ? splitk_dispatch<Bf16>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s)
-                   : splitk_dispatch<F32>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
+  }
+  if (M <= 32) {
+    const hipError_t e = dtype == 1 ? splitk_dispatch<Bf16>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s)
+                                    : splitk_dispatch<F32>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
     if (e != hipErrorNotSupported) return e;
   }
   if (dtype == 1) {  // many rows: tiled matrix-core GEMM (W read once per XCD, re-used from L2)

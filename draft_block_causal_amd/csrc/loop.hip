@@ -483,6 +483,177 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
 }
 
 // ---------------------------------------------------------------------------
+// Plain-schedule phase 3 for B > 1: batch rows m0 .. m0 + 16 MT - 1 (grid.y)
+// against vocabulary tiles t = 4 blockIdx.x + wave, stepping by 4 gridDim.x.
+// u is staged in LDS as matrix-core operands.  Each wave reads the NS 64-B
+// K steps of its next tile of W2 (and that tile's base logits and b2) while
+// it multiplies the current one: buffer descriptors sized to the valid rows
+// make the loads past the last tile read zero, so every load is
+// unconditional, and two register sets alternate.  Each 16 x 16 product tile
+// is turned through a wave-private LDS patch so that a lane holds one batch
+// row and four consecutive vocabulary entries: one Philox counter gives the
+// four words it needs.  Argmax keys are reduced over lanes and waves and
+// merged into keys[step][b] with a 64-bit atomic max.
+// ---------------------------------------------------------------------------
+template <class T, int MT, int NS>
+__global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) {
+  using E = typename T::elem;
+  constexpr int EPF = T::kPer16B;
+  constexpr int NPARTS = act_parts<T>();
+  constexpr int rows = 16 * MT;
+  constexpr int row_bytes = NS * 64;  // r * sizeof(E)
+  constexpr int lds_stride = row_bytes + 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* tr = reinterpret_cast<float*>(smem + NPARTS * rows * lds_stride);          // [4][16][17]
+  unsigned long long* kred = reinterpret_cast<unsigned long long*>(tr + 4 * 16 * 17);  // [4][rows]
+  const int B = p.B, V = p.V, r = p.r, K = p.K;
+  const int m0 = blockIdx.y * rows;
+
+  for (int idx = threadIdx.x; idx < rows * (r / EPF); idx += blockDim.x) {
+    const int rr = idx / (r / EPF), c = idx - rr * (r / EPF);
+    const int b = m0 + rr;
+    ActFrag<T> a;
+    if (b < B)
+      a.from_f32(p.u + (size_t)b * r + c * EPF);
+    else
+      a.zero();
+    const u32x4* parts = reinterpret_cast<const u32x4*>(&a);
+#pragma unroll
+    for (int q = 0; q < NPARTS; ++q) st16(smem + (q * rows + rr) * lds_stride + c * 16, parts[q]);
+  }
+  __syncthreads();
+
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int eb = lane >> 2, eq = lane & 3;  // epilogue: batch row eb of a tile, entries 4 eq .. 4 eq + 3
+  float* trw = tr + wave * 16 * 17;
+  const int ntiles = (V + 15) >> 4;
+  const int stride = __builtin_amdgcn_readfirstlane(gridDim.x * 4);  // (computed in a vector register otherwise)
+  const int woff = col * row_bytes + grp * 16;
+  // base logits of this position for the 16 batch rows of slice mt: one
+  // descriptor per slice, based at its first row and ending after the last
+  // batch row's V entries; lane offsets (eb K V + v) * 4 (checked on the host
+  // to fit 31 bits)
+  __amdgpu_buffer_rsrc_t brs[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int live = min(max(B - (m0 + mt * 16), 0), 16);
+    brs[mt] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.base + (live > 0 ? ((size_t)(m0 + mt * 16) * K + step) * V : 0)), (short)0,
+        live > 0 ? ((live - 1) * K * V + V) * 4 : 0, kRsrcWord3);
+  }
+  const int boff = eb * K * V * 4;
+  const __amdgpu_buffer_rsrc_t b2rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(p.b2 ? p.b2 : p.w2), (short)0, p.b2 ? V * (int)sizeof(E) : 0, kRsrcWord3);
+
+  struct Stage {
+    u32x4 w[NS];
+    float base[MT][4];
+    float b2[4];
+  };
+  auto load = [&](int t, Stage& st) {
+    const int nrows = t < ntiles ? min(16, V - t * 16) : 0;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(p.w2 + (t < ntiles ? (size_t)t * 16 * r : 0)), (short)0, nrows * row_bytes, kRsrcWord3);
+#pragma unroll
+    for (int kb = 0; kb < NS; ++kb) st.w[kb] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + kb * 64, 0, 0);
+    const int v0 = t * 16 + 4 * eq;  // past V (or a dead tile): reads zero
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.base[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs[mt], boff + (v0 + i) * 4, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned bits = sizeof(E) == 2 ? (unsigned)__builtin_amdgcn_raw_buffer_load_b16(b2rs, (v0 + i) * 2, 0, 0)
+                                           : __builtin_amdgcn_raw_buffer_load_b32(b2rs, (v0 + i) * 4, 0, 0);
+      st.b2[i] = sizeof(E) == 2 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
+    }
+  };
+  unsigned long long best[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) best[mt] = 0ull;
+  auto process = [&](int t, const Stage& st) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < NPARTS; ++q) {
+          const u32x4 a = ld16(smem + (q * rows + mt * 16 + col) * lds_stride + grp * 16 + kb * 64);
+          acc[mt] = mma16<T>(acc[mt], a, st.w[kb]);
+        }
+    const int v0 = t * 16 + 4 * eq;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) trw[(grp * 4 + j) * 17 + col] = acc[mt][j];
+      const f32x4 d = f32x4{trw[eb * 17 + 4 * eq], trw[eb * 17 + 4 * eq + 1], trw[eb * 17 + 4 * eq + 2],
+                            trw[eb * 17 + 4 * eq + 3]};
+      // branch-free over the lanes (rows past the batch and entries past V
+      // give no key): loads that only one side of a branch consumed would make
+      // the compiler wait for them before the next prefetch reuses the registers
+      const int b = m0 + mt * 16 + eb;
+      u32x4 words = {0u, 0u, 0u, 0u};
+      if (p.sampled) words = philox4(p.seed, p.offset, (uint32_t)b, (uint32_t)step, (uint32_t)(v0 >> 2));
+      const size_t o = ((size_t)b * K + step) * V;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = v0 + i;
+        const bool ok = b < B && v < V;
+        const float L = st.base[mt][i] + (d[i] + st.b2[i]);
+        if (p.logits && ok) p.logits[o + v] = L;
+        const float s = p.sampled ? L * p.inv_temp + gumbel_from_word(words[i]) : L;
+        const unsigned long long k = ok ? argmax_key(s, (uint32_t)v) : 0ull;
+        best[mt] = k > best[mt] ? k : best[mt];
+      }
+    }
+  };
+
+  // (t is kept in a scalar register: the descriptors built from it must be)
+  Stage s0, s1;
+  int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  load(t, s0);
+  while (t < ntiles) {
+    load(t + stride, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, s0);
+    t = __builtin_amdgcn_readfirstlane(t + stride);
+    if (t >= ntiles) break;
+    load(t + stride, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, s1);
+    t = __builtin_amdgcn_readfirstlane(t + stride);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    unsigned long long k = best[mt];
+#pragma unroll
+    for (int sh = 1; sh < 4; sh <<= 1) {
+      const unsigned long long o = __shfl_xor(k, sh, 64);
+      k = o > k ? o : k;
+    }
+    if (eq == 0) kred[wave * rows + mt * 16 + eb] = k;
+  }
+  __syncthreads();
+  for (int rr = threadIdx.x; rr < rows; rr += blockDim.x) {
+    unsigned long long k = kred[rr];
+    for (int w = 1; w < 4; ++w) k = kred[w * rows + rr] > k ? kred[w * rows + rr] : k;
+    const int b = m0 + rr;
+    if (b < B && k != 0ull) atomicMax(p.keys + (size_t)step * B + b, k);
+  }
+}
+
+template <class T, int MT>
+__host__ __device__ inline size_t w2_stream_lds_bytes(int r) {
+  return (size_t)act_parts<T>() * 16 * MT * (r * sizeof(typename T::elem) + 16) + 4 * 16 * 17 * sizeof(float) +
+         4 * 16 * MT * sizeof(unsigned long long);
+}
+
+// ---------------------------------------------------------------------------
 // Plain-schedule phase 2, split in two launches:
 //   gates_kernel - one thread per (batch row, GRU unit): the gates from the
 //                  phase-1 partials (or the GRU input table row of the token)
@@ -534,47 +705,91 @@ __global__ void __launch_bounds__(256) gates_kernel(DevLoop<T> p, int step) {
   p.states[((size_t)b * p.K + step) * H + j] = (1.f - zg) * ng + zg * gp;
 }
 
-template <class T>
-__global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// One wave's share of a 16 x 16 tile of W X^T: W rows wrow (lane column =
+// output row, 16 B of K per lane), X rows xrow (fp32, lane column = batch
+// row; null for a row past the batch), over matrix-core K steps s0 .. s0 + U - 1
+// (steps past nsteps add zero).  Every load of the U steps is issued before
+// the first product.
+template <class T, int U>
+__device__ __forceinline__ f32x4 wave_rows_dot(f32x4 acc, const unsigned char* wrow, const float* xrow, int s0,
+                                               int nsteps) {
   using E = typename T::elem;
-  const int H = p.H, B = p.B;
-  const int t = blockIdx.x, m0 = blockIdx.y * 16;
-  float* gt = reinterpret_cast<float*>(smem);  // [16][H + 4]
-  const int gstride = H + 4;
-  float* red = gt + 16 * gstride;  // [4][16][16]
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int grp = lane >> 4, col = lane & 15;
-  const int ldw1 = p.d + H;
   constexpr int EPF = T::kPer16B;
-  for (int idx = threadIdx.x; idx < 16 * H; idx += blockDim.x) {
-    const int rr = idx / H, j = idx - rr * H;
-    const int b = m0 + rr;
-    gt[rr * gstride + j] = b < B ? p.states[((size_t)b * p.K + step) * H + j] : 0.f;
-  }
-  __syncthreads();
-  // u rows t*16 + col; the four waves take interleaved 64-byte K chunks
-  const int row = t * 16 + col;
-  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(p.w1 + (size_t)row * ldw1 + p.d) + grp * 16;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = wave * 4 * EPF; k0 < H; k0 += 16 * EPF) {
-    const u32x4 w = ld16(wrow + (size_t)k0 * sizeof(E));
-    ActFrag<T> a;
-    a.from_f32(gt + col * gstride + k0 + grp * EPF);
-    acc = a.mma(acc, w);
+  constexpr int KSTEP = 4 * EPF;
+  u32x4 w[U];
+  float x[U][EPF];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = s0 + u;
+    const bool in = s < nsteps;
+    w[u] = in ? ld16(wrow + (size_t)s * KSTEP * sizeof(E)) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < EPF; e += 4) {
+      const f32x4 v = in && xrow ? *reinterpret_cast<const f32x4*>(xrow + s * KSTEP + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[u][e] = v[0];
+      x[u][e + 1] = v[1];
+      x[u][e + 2] = v[2];
+      x[u][e + 3] = v[3];
+    }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[(wave * 16 + grp * 4 + j) * 16 + col] = acc[j];
+  for (int u = 0; u < U; ++u) {
+    ActFrag<T> a;
+    a.from_f32(x[u]);
+    acc = a.mma(acc, w[u]);
+  }
+  return acc;
+}
+
+// 16 output rows (W rows n0 .. n0 + 15) for batch rows m0 .. m0 + 15 of
+// W[:, :ncols] X^T, with the 4 waves of a workgroup taking consecutive ranges
+// of K steps; returns, for thread tid < 256, the sum for batch row m0 + tid / 16
+// and output row n0 + tid % 16 (the four wave partials added in a fixed order).
+template <class T>
+__device__ __forceinline__ float block_rows_dot(const typename T::elem* W, int ldw, int n0, const float* X, int ldx,
+                                                int m0, int B, int ncols) {
+  using E = typename T::elem;
+  constexpr int U = 8;
+  constexpr int KSTEP = 4 * T::kPer16B;
+  __shared__ float red[4][16][17];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int nsteps = ncols / KSTEP;
+  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(W + (size_t)(n0 + col) * ldw) + grp * 16;
+  const float* xrow = m0 + col < B ? X + (size_t)(m0 + col) * ldx + grp * T::kPer16B : nullptr;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int per_wave = (nsteps + 3) / 4;
+  for (int s0 = wave * per_wave; s0 < min(nsteps, (wave + 1) * per_wave); s0 += U)
+    acc = wave_rows_dot<T, U>(acc, wrow, xrow, s0, min(nsteps, (wave + 1) * per_wave));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wave][grp * 4 + j][col] = acc[j];
   __syncthreads();
-  const int rr = threadIdx.x >> 4, c = threadIdx.x & 15;
-  const int b = m0 + rr;
-  if (b < B) {
-    const float sum = red[(0 * 16 + rr) * 16 + c] + red[(1 * 16 + rr) * 16 + c] + red[(2 * 16 + rr) * 16 + c] +
-                      red[(3 * 16 + rr) * 16 + c];
-    const int q = t * 16 + c;
+  const int mm = (threadIdx.x >> 4) & 15, nn = threadIdx.x & 15;
+  return red[0][mm][nn] + red[1][mm][nn] + red[2][mm][nn] + red[3][mm][nn];
+}
+
+// u rows 16t .. 16t+15 for batch rows 16m .. 16m+15: SiLU(P + W1[:, d:] g).
+template <class T>
+__global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
+  const int t = blockIdx.x, m0 = blockIdx.y * 16;
+  // batch row b's state at this position: states[b][step][:], row stride K * H
+  const float sum = block_rows_dot<T>(p.w1 + p.d, p.d + p.H, t * 16, p.states + (size_t)step * p.H, p.K * p.H, m0,
+                                      p.B, p.H);
+  const int b = m0 + (threadIdx.x >> 4), q = t * 16 + (threadIdx.x & 15);
+  if (b < p.B) {
     const float pre = p.P[((size_t)b * p.K + step) * p.r + q] + sum;
     p.u[(size_t)b * p.r + q] = pre * sigmoidf_(pre);
   }
+}
+
+// W_hh g_{step-1}: gate rows 16t .. 16t+15 for batch rows 16m .. 16m+15.
+template <class T>
+__global__ void __launch_bounds__(256) hh_kernel(DevLoop<T> p, int step) {
+  const int t = blockIdx.x, m0 = blockIdx.y * 16;
+  const float sum = block_rows_dot<T>(p.w_hh, p.H, t * 16, p.states + (size_t)(step - 1) * p.H, p.K * p.H, m0, p.B,
+                                      p.H);
+  const int b = m0 + (threadIdx.x >> 4), n = t * 16 + (threadIdx.x & 15);
+  if (b < p.B) p.part_hh[(size_t)b * 3 * p.H + n] = sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -594,9 +809,9 @@ __global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step
     tok[b] = min(max(tk, 0), p.V - 1);
   }
   __syncthreads();
-  // with a GRU input table only the W_hh tiles remain (job numbers after the W_ih ones)
-  const int job = blockIdx.x * 4 + wave_id() + (p.table ? ((3 * p.H) >> 4) * p.KS : 0);
-  if (job < gru_jobs(p.H, p.KS, step)) gru_partial_job<T, MT, Plain>(p, step, job, tok);
+  // the W_ih jobs only (without a GRU input table); hh_kernel forms W_hh g
+  const int job = blockIdx.x * 4 + wave_id();
+  if (job < ((3 * p.H) >> 4) * p.KS) gru_partial_job<T, MT, Plain>(p, step, job, tok);
 }
 
 
@@ -741,25 +956,61 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
   return p;
 }
 
+// The W2 phase: the streaming kernel when a W2 row is 2 to 16 64-B steps,
+// else the generic one.
+template <class T, int MW>
+struct W2Launch {
+  void (*kern)(DevLoop<T>, int);
+  size_t lds;
+  dim3 grid;
+};
+
+template <class T, int MW, int NS>
+static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
+  const int ntiles = (p.V + 15) / 16;
+  const size_t lds = w2_stream_lds_bytes<T, MW>(p.r);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(w2_stream_kernel<T, MW, NS>),
+                                                   256, lds) != hipSuccess)
+    per_cu = 1;
+  // the resident waves take about the same number of tiles each
+  const int slots = std::max(1, per_cu) * num_cu * 4;
+  const int iters = (ntiles + slots - 1) / slots;
+  const int gx = std::max(1, (ntiles + 4 * iters - 1) / (4 * iters));
+  return {w2_stream_kernel<T, MW, NS>, lds, dim3(gx, (p.B + 16 * MW - 1) / (16 * MW))};
+}
+
+template <class T, int MW>
+static W2Launch<T, MW> w2_plan(const DevLoop<T>& p, int num_cu) {
+  const bool offsets_fit = (16LL * p.K * p.V + 16) * 4 < (1LL << 31);
+  switch (offsets_fit ? p.r * (int)sizeof(typename T::elem) / 64 : 0) {
+    case 2: return w2_stream_plan<T, MW, 2>(p, num_cu);
+    case 4: return w2_stream_plan<T, MW, 4>(p, num_cu);
+    case 8: return w2_stream_plan<T, MW, 8>(p, num_cu);
+    case 16: return w2_stream_plan<T, MW, 16>(p, num_cu);
+    default: break;
+  }
+  const int ntiles = (p.V + 15) / 16;
+  return {w2_sample_kernel<T, MW>, w2_lds_bytes<T>(p.r, 16 * MW),
+          dim3(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW))};
+}
+
 template <class T, int MT>
 static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t s) {
   hipError_t e;
-  const size_t lds_u = gates_lds_bytes(p.H);
-  if ((e = allow_lds(u_kernel<T>, lds_u)) != hipSuccess) return e;
   constexpr int MW = MT > 2 ? 2 : MT;  // w2 rows per workgroup: 16 * MW
-  const size_t lds_w = w2_lds_bytes<T>(p.r, 16 * MW);
-  if ((e = allow_lds(w2_sample_kernel<T, MW>, lds_w)) != hipSuccess) return e;
-  const int ntiles = (p.V + 15) / 16;
-  const dim3 wgrid(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW));
+  const W2Launch<T, MW> w2 = w2_plan<T, MW>(p, num_cu);
+  if ((e = allow_lds(w2.kern, w2.lds)) != hipSuccess) return e;
   const dim3 ggrid((p.H + 255) / 256, p.B);
   const dim3 ugrid(p.r / 16, (p.B + 15) / 16);
   const int t3 = 3 * p.H / 16;
+  const dim3 hgrid(t3, (p.B + 15) / 16);
   for (int step = 0; step < p.K; ++step) {
-    const int jobs = (p.table ? 0 : t3 * p.KS) + (step > 0 ? t3 : 0);
-    if (jobs > 0) hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((jobs + 3) / 4), dim3(256), 0, s, p, step);
+    if (!p.table) hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((t3 * p.KS + 3) / 4), dim3(256), 0, s, p, step);
+    if (step > 0) hipLaunchKernelGGL(hh_kernel<T>, hgrid, dim3(256), 0, s, p, step);
     hipLaunchKernelGGL(gates_kernel<T>, ggrid, dim3(256), 0, s, p, step);
-    hipLaunchKernelGGL(u_kernel<T>, ugrid, dim3(256), lds_u, s, p, step);
-    hipLaunchKernelGGL((w2_sample_kernel<T, MW>), wgrid, dim3(256), lds_w, s, p, step);
+    hipLaunchKernelGGL(u_kernel<T>, ugrid, dim3(256), 0, s, p, step);
+    hipLaunchKernelGGL(w2.kern, w2.grid, dim3(256), w2.lds, s, p, step);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_finalize_tokens(p.B, p.K, p.keys, p.tokens, s);

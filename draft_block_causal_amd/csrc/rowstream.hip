@@ -51,8 +51,6 @@ struct RowStream {
 };
 constexpr size_t kMaxLds = 160 * 1024;
 
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
-constexpr int kLoadNonTemporal = 2;
 
 template <class T>
 __device__ __forceinline__ unsigned load_elem_bits(__amdgpu_buffer_rsrc_t r, int off);
@@ -219,12 +217,16 @@ static hipError_t rowstream_t(const void* A, int lda, int M, const void* W, int 
 
 
 // Returns hipErrorNotSupported unless K * elem_size is 8 * 64 * KW bytes with
-// KW in {4, 8, 16} and every W row starts 16-byte aligned.
+// KW in {4, 8, 16} and every W row starts 16-byte aligned.  Each 16-row slice
+// of A (grid.y) streams all of W, so more than 32 rows are taken only for a
+// small W and a moderate M (N, M <= 4096: the hidden half of the first
+// correction projection at B > 2), whose re-reads come from the caches.
 hipError_t launch_rowstream_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                                  const void* bias, float* C, int ldc, int num_cu, hipStream_t s) {
   const size_t elem = dtype == 1 ? 2 : 4;
   const size_t row_bytes = (size_t)K * elem;
-  if (M > 32 || row_bytes % (64 * kRowStreamWaves) || ((size_t)ldw * elem) % 16) return hipErrorNotSupported;
+  if ((M > 32 && (N > 4096 || M > 4096)) || row_bytes % (64 * kRowStreamWaves) || ((size_t)ldw * elem) % 16)
+    return hipErrorNotSupported;
   switch (row_bytes / (64 * kRowStreamWaves)) {
     case 4: return dtype == 1 ? rowstream_t<Bf16, 4>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s)
                               : rowstream_t<F32, 4>(A, lda, M, W, ldw, N, bias, C, ldc, num_cu, s);
