@@ -152,10 +152,14 @@ __device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint32_t offset, 
   return s == 0 ? x[0] : s == 1 ? x[1] : s == 2 ? x[2] : x[3];
 }
 
-// Gumbel(0,1) sample from a Philox word: U = ((w >> 9) + 1/2) 2^-23 in (0,1).
+// Gumbel(0,1) sample from a Philox word: U = ((w >> 9) + 1/2) 2^-23 in (0,1),
+// G = -ln(-ln U).  The logarithms use the hardware base-2 logarithm (about one
+// ulp) times ln 2: U is exact, G is within a few ulps of a libm evaluation,
+// and this transform runs once per vocabulary entry of every sampled position.
+__device__ __forceinline__ float ln_hw(float x) { return __builtin_amdgcn_logf(x) * 0.69314718055994531f; }
 __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   const float u = ((float)(w >> 9) + 0.5f) * 1.1920928955078125e-07f;
-  return -logf(-logf(u));
+  return -ln_hw(-ln_hw(u));
 }
 
 // 64-bit argmax key: larger score wins, then the lower index.  The score's

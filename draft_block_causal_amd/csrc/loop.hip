@@ -495,7 +495,9 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
 // four words it needs.  Argmax keys are reduced over lanes and waves and
 // merged into keys[step][b] with a 64-bit atomic max.
 // ---------------------------------------------------------------------------
-template <class T, int MT, int NS>
+// VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
+// logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
+template <class T, int MT, int NS, bool VEC>
 __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) {
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
@@ -509,17 +511,39 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) 
   const int B = p.B, V = p.V, r = p.r, K = p.K;
   const int m0 = blockIdx.y * rows;
 
-  for (int idx = threadIdx.x; idx < rows * (r / EPF); idx += blockDim.x) {
-    const int rr = idx / (r / EPF), c = idx - rr * (r / EPF);
-    const int b = m0 + rr;
-    ActFrag<T> a;
-    if (b < B)
-      a.from_f32(p.u + (size_t)b * r + c * EPF);
-    else
-      a.zero();
-    const u32x4* parts = reinterpret_cast<const u32x4*>(&a);
+  // u rows -> LDS operands; each thread's fragments (rows * NS * 4 / 256 of
+  // them, r = NS * 64 / sizeof(E) entries per row) are all loaded first
+  {
+    constexpr int kFrags = rows * NS * 4;  // EPF-entry fragments of the staged rows
+    constexpr int kPer = (kFrags + 255) / 256;
+    float x[kPer][EPF];
 #pragma unroll
-    for (int q = 0; q < NPARTS; ++q) st16(smem + (q * rows + rr) * lds_stride + c * 16, parts[q]);
+    for (int q = 0; q < kPer; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      const int rr = idx / (NS * 4), c = idx - rr * (NS * 4);
+      const bool live = idx < kFrags && m0 + rr < B;
+#pragma unroll
+      for (int e = 0; e < EPF; e += 4) {
+        const f32x4 v = live ? *reinterpret_cast<const f32x4*>(p.u + (size_t)(m0 + rr) * r + c * EPF + e)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[q][e] = v[0];
+        x[q][e + 1] = v[1];
+        x[q][e + 2] = v[2];
+        x[q][e + 3] = v[3];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      if (idx < kFrags) {
+        const int rr = idx / (NS * 4), c = idx - rr * (NS * 4);
+        ActFrag<T> a;
+        a.from_f32(x[q]);
+        const u32x4* parts = reinterpret_cast<const u32x4*>(&a);
+#pragma unroll
+        for (int pq = 0; pq < NPARTS; ++pq) st16(smem + (pq * rows + rr) * lds_stride + c * 16, parts[pq]);
+      }
+    }
   }
   __syncthreads();
 
@@ -558,16 +582,34 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) 
 #pragma unroll
     for (int kb = 0; kb < NS; ++kb) st.w[kb] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff + kb * 64, 0, 0);
     const int v0 = t * 16 + 4 * eq;  // past V (or a dead tile): reads zero
+    if constexpr (VEC) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(brs[mt], boff + v0 * 4, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.base[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs[mt], boff + (v0 + i) * 4, 0, 0));
+        for (int i = 0; i < 4; ++i) st.base[mt][i] = __uint_as_float(q[i]);
+      }
+      if constexpr (sizeof(E) == 2) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b64(b2rs, v0 * 2, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned bits = sizeof(E) == 2 ? (unsigned)__builtin_amdgcn_raw_buffer_load_b16(b2rs, (v0 + i) * 2, 0, 0)
-                                           : __builtin_amdgcn_raw_buffer_load_b32(b2rs, (v0 + i) * 4, 0, 0);
-      st.b2[i] = sizeof(E) == 2 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
+        for (int i = 0; i < 4; ++i) st.b2[i] = __uint_as_float(((q[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+      } else {
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(b2rs, v0 * 4, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.b2[i] = __uint_as_float(q[i]);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st.base[mt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs[mt], boff + (v0 + i) * 4, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned bits = sizeof(E) == 2 ? (unsigned)__builtin_amdgcn_raw_buffer_load_b16(b2rs, (v0 + i) * 2, 0, 0)
+                                             : __builtin_amdgcn_raw_buffer_load_b32(b2rs, (v0 + i) * 4, 0, 0);
+        st.b2[i] = sizeof(E) == 2 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
+      }
     }
   };
   unsigned long long best[MT];
@@ -969,15 +1011,16 @@ template <class T, int MW, int NS>
 static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int ntiles = (p.V + 15) / 16;
   const size_t lds = w2_stream_lds_bytes<T, MW>(p.r);
+  auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true> : w2_stream_kernel<T, MW, NS, false>;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(w2_stream_kernel<T, MW, NS>),
-                                                   256, lds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 256, lds) !=
+      hipSuccess)
     per_cu = 1;
   // the resident waves take about the same number of tiles each
   const int slots = std::max(1, per_cu) * num_cu * 4;
   const int iters = (ntiles + slots - 1) / slots;
   const int gx = std::max(1, (ntiles + 4 * iters - 1) / (4 * iters));
-  return {w2_stream_kernel<T, MW, NS>, lds, dim3(gx, (p.B + 16 * MW - 1) / (16 * MW))};
+  return {kern, lds, dim3(gx, (p.B + 16 * MW - 1) / (16 * MW))};
 }
 
 template <class T, int MW>
