@@ -195,10 +195,11 @@ def main() -> int:
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": alg}
     if M <= 32:
         kname = "rowstream_gemm_kernel (LM head, K split over 8 waves, row-contiguous non-temporal loads)"
-    elif M >= 256 and w.dtype == "bf16":
-        kname = "gemm_bf16_tn_256_kernel (LM head, 256x256 tiles, LDS-DMA operand loads)"
+    elif w.dtype == "bf16":
+        kname = ("gemm_bf16_tn_big_kernel<%d> (LM head, %dx256 tiles, LDS-DMA operand loads)"
+                 % ((256, 256) if M >= 256 else (128, 128)))
     else:
-        kname = "gemm_bf16_tn_kernel (LM head, 128x128 tiles)"
+        kname = "panel_gemm_kernel (LM head, f32)"
     roof.update({"kernel": kname, "avg_launch_ms": lm_ms})
 
     result = {

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "psplit.h"
+
 namespace domino {
 
 // C[m, n] = sum_k A[m, k] W[n, k] (+ bias[n]) for m < M, n < N, in float32.
@@ -19,7 +21,15 @@ hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const voi
 hipError_t launch_rowstream_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                                  const void* bias, float* C, int ldc, int num_cu, hipStream_t s);
 
-// Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 64 == 0 (else hipErrorNotSupported).
+// P = A W1[:, :d]^T + b1 (bf16 A rows of lda elements, W1 rows of ldw) as S
+// partial sums over K slices, ppart[S][M][r] float32 (b1 in slice 0), plus
+// zeroing z0[0..n0) and z1[0..n1) (z1 may be null).  p_split_shape gives the
+// slicing for hidden size d (psplit.h).
+hipError_t launch_p_partials(const void* A, int M, int lda, const void* w1, int ldw, int r, const void* b1,
+                             float* ppart, const PSplit& ps, unsigned long long* z0, int n0, unsigned long long* z1,
+                             int n1, hipStream_t s);
+
+// Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 32 == 0 (else hipErrorNotSupported).
 hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
                                float* C, int ldc, hipStream_t s);
 

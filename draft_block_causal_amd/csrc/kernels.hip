@@ -140,6 +140,71 @@ __global__ void __launch_bounds__(kSplitWaves * 64)
   }
 }
 
+// ---------------------------------------------------------------------------
+// p_partials: the loop-invariant hidden half of the first correction
+// projection, P = A W1[:, :d]^T + b1 for every block position
+// ([notes] §二.1(2) item 2), as S partial sums over K slices, together with
+// the clears the loop needs before it starts.  Each wave takes 512 B of K
+// (8 matrix-core steps) of one 16-row tile of W1 for up to 64 rows of A
+// (grid.y walks the 64-row groups); the waves of a workgroup add their
+// products in LDS and the workgroup writes slice s: ppart[s][m][n], with b1
+// in slice 0.  The consumer adds the S slices in a fixed order.  This spreads
+// the W1 read over S x r / 16 workgroups instead of r / 16.
+// ---------------------------------------------------------------------------
+constexpr int kPreWaves = 4;  // waves per workgroup, at most
+constexpr int kPreSteps = 8;  // 64-B K steps per wave
+constexpr int kPreMt = 4;     // 16-row tiles of A per workgroup
+
+__global__ void __launch_bounds__(kPreWaves * 64)
+    p_partials_kernel(const uint16_t* __restrict__ A, int M, int lda, const uint16_t* __restrict__ w1, int ldw, int r,
+                      const uint16_t* __restrict__ b1, float* __restrict__ ppart, int waves,
+                      unsigned long long* __restrict__ z0, int n0, unsigned long long* __restrict__ z1, int n1) {
+  __shared__ float red[kPreWaves][kPreMt][16][17];
+  const int nthreads = gridDim.x * gridDim.y * blockDim.x;
+  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < n0 + n1; i += nthreads) {
+    if (i < n0)
+      z0[i] = 0ull;
+    else
+      z1[i - n0] = 0ull;
+  }
+  const int ntn = r >> 4;
+  const int nt = blockIdx.x % ntn, ks = blockIdx.x / ntn;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int mt0 = blockIdx.y * kPreMt;
+  const int mtiles = min(kPreMt, ((M + 15) >> 4) - mt0);
+  if (wave < waves) {
+    const size_t kb = (size_t)(ks * waves + wave) * (kPreSteps * 64) + grp * 16;
+    const unsigned char* wrow = reinterpret_cast<const unsigned char*>(w1 + (size_t)(nt * 16 + col) * ldw) + kb;
+    u32x4 wf[kPreSteps];
+#pragma unroll
+    for (int s = 0; s < kPreSteps; ++s) wf[s] = ld16(wrow + s * 64);
+    for (int mt = 0; mt < mtiles; ++mt) {
+      const int m = (mt0 + mt) * 16 + col;
+      const unsigned char* arow = reinterpret_cast<const unsigned char*>(A + (size_t)min(m, M - 1) * lda) + kb;
+      u32x4 a[kPreSteps];
+#pragma unroll
+      for (int s = 0; s < kPreSteps; ++s) a[s] = m < M ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kPreSteps; ++s) acc = mma16<Bf16>(acc, a[s], wf[s]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][mt][grp * 4 + j][col] = acc[j];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < mtiles * 256; e += blockDim.x) {
+    const int mt = e >> 8, mm = (e >> 4) & 15, c = e & 15;
+    const int m = (mt0 + mt) * 16 + mm, n = nt * 16 + c;
+    if (m < M) {
+      float sum = 0.f;
+      for (int w = 0; w < waves; ++w) sum += red[w][mt][mm][c];
+      if (ks == 0 && b1) sum += bf16_to_f32(b1[n]);
+      ppart[((size_t)ks * M + m) * r + n] = sum;
+    }
+  }
+}
+
 __global__ void fill_u64_kernel(unsigned long long* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0ull;
@@ -247,6 +312,18 @@ hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const voi
   }
   if (dtype == 1) return panel_gemm_t<Bf16>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
   return panel_gemm_t<F32>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
+}
+
+hipError_t launch_p_partials(const void* A, int M, int lda, const void* w1, int ldw, int r, const void* b1,
+                             float* ppart, const PSplit& ps, unsigned long long* z0, int n0, unsigned long long* z1,
+                             int n1, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const int gy = (M + 16 * kPreMt - 1) / (16 * kPreMt);
+  if (gy > 65535) return hipErrorNotSupported;
+  hipLaunchKernelGGL(p_partials_kernel, dim3(ps.S * (r / 16), gy), dim3(kPreWaves * 64), 0, s,
+                     static_cast<const uint16_t*>(A), M, lda, static_cast<const uint16_t*>(w1), ldw, r,
+                     static_cast<const uint16_t*>(b1), ppart, ps.waves, z0, n0, z1, n1);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s) {

@@ -55,6 +55,8 @@ struct DevLoop {
   uint64_t seed;
   uint32_t offset;
   float *logits, *states, *P, *part_ih, *part_hh, *u;
+  const float* ppart;  // [S][B K][r] K-slice partials of P (S > 0), else P is whole
+  int S;
   unsigned long long* keys;  // [K, B]  (three-kernel schedule)
   unsigned int* ctrl;        // [1]: non-zero once a persistent-kernel wait gave up
   int32_t* tokens;
@@ -819,7 +821,13 @@ __global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
                                       p.B, p.H);
   const int b = m0 + (threadIdx.x >> 4), q = t * 16 + (threadIdx.x & 15);
   if (b < p.B) {
-    const float pre = p.P[((size_t)b * p.K + step) * p.r + q] + sum;
+    const size_t row = ((size_t)b * p.K + step) * p.r + q;
+    float ph = 0.f;  // P: whole, or its S slices added in order
+    if (p.S > 0)
+      for (int sl = 0; sl < p.S; ++sl) ph += p.ppart[(size_t)sl * p.B * p.K * p.r + row];
+    else
+      ph = p.P[row];
+    const float pre = ph + sum;
     p.u[(size_t)b * p.r + q] = pre * sigmoidf_(pre);
   }
 }
@@ -985,6 +993,8 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
   p.logits = a.logits;
   p.states = a.states;
   p.P = a.P;
+  p.ppart = a.ppart;
+  p.S = 0;
   p.part_ih = a.part_ih;
   p.part_hh = a.part_hh;
   p.u = a.u;
@@ -1088,8 +1098,21 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
       (void)hipGetLastError();  // the grid cannot be co-resident here: use another schedule
     }
   }
+  hipError_t e;
+  PSplit ps;
+  if (mode != 1 && a.dtype == 1 && p_split_shape(a.d, a.r, ps)) {
+    // one launch: the keys [K, B] and control words cleared, and the
+    // loop-invariant hidden half of the first correction projection (+ b1)
+    // as K-slice partials that u_kernel adds up
+    e = launch_p_partials(a.hidden, a.B * a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, ps, a.keys,
+                          a.K * a.B + 1, nullptr, 0, s);
+    if (e != hipSuccess) return e;
+    DevLoop<T> q = p;
+    q.S = ps.S;
+    return multi_kernel_loop<T, MT>(q, a.num_cu, s);
+  }
   // keys [K, B] and the control words start at zero on every call
-  hipError_t e = launch_fill_u64(a.keys, a.K * a.B + 1, s);
+  e = launch_fill_u64(a.keys, a.K * a.B + 1, s);
   if (e != hipSuccess) return e;
   // loop-invariant hidden half of the first correction projection (+ b1)
   e = launch_panel_gemm(a.dtype, a.hidden, a.d, a.B * a.K, a.w1, a.d + a.H, a.r, a.d, a.b1, a.P, a.r, a.num_cu, s);

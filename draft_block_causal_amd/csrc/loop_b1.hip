@@ -640,98 +640,20 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   }
 }
 
-// ---------------------------------------------------------------------------
 // Before the loop, one launch clears the argmax keys, the control words and
-// the exchange words (no stale tag may survive from an earlier call), and
-// forms the loop-invariant hidden half of the first correction projection,
-// P_i = W1[:, :d] h_i + b1 for every position i ([notes] §二.1(2) item 2), as
-// S partial sums over K slices.  Each wave takes 512 B of K (8 matrix-core
-// steps) of one 16-row tile of W1 for all positions; the waves of a workgroup
-// add their products in LDS and the workgroup writes slice s; the loop adds
-// the S slices in a fixed order (unit workgroup s adds slice s to its share
-// of W1[:, d:] g).  This spreads the 2 MB of W1 over S x r / 16 workgroups
-// instead of r / 16.
-// ---------------------------------------------------------------------------
-constexpr int kPreWaves = 4;   // waves per workgroup, at most
-constexpr int kPreSteps = 8;   // 64-B K steps per wave
-constexpr int kPreMaxMt = 4;   // 16-row position tiles (K <= 64)
-
-__global__ void __launch_bounds__(kPreWaves * 64)
-    pre_kernel(const uint16_t* __restrict__ hidden, int M, int d, const uint16_t* __restrict__ w1, int ldw, int r,
-               const uint16_t* __restrict__ b1, float* __restrict__ ppart, int waves,
-               unsigned long long* __restrict__ z0, int n0, unsigned long long* __restrict__ z1, int n1) {
-  __shared__ float red[kPreWaves][kPreMaxMt][16][17];
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n0 + n1; i += gridDim.x * blockDim.x) {
-    if (i < n0)
-      z0[i] = 0ull;
-    else
-      z1[i - n0] = 0ull;
-  }
-  const int ntn = r >> 4;
-  const int nt = blockIdx.x % ntn, ks = blockIdx.x / ntn;
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int grp = lane >> 4, col = lane & 15;
-  const int mtiles = (M + 15) >> 4;
-  if (wave < waves) {
-    const size_t kb = (size_t)(ks * waves + wave) * (kPreSteps * 64) + grp * 16;
-    const unsigned char* wrow = reinterpret_cast<const unsigned char*>(w1 + (size_t)(nt * 16 + col) * ldw) + kb;
-    u32x4 wf[kPreSteps];
-#pragma unroll
-    for (int s = 0; s < kPreSteps; ++s) wf[s] = ld16(wrow + s * 64);
-    for (int mt = 0; mt < mtiles; ++mt) {
-      const int m = mt * 16 + col;
-      const unsigned char* arow = reinterpret_cast<const unsigned char*>(hidden + (size_t)min(m, M - 1) * d) + kb;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kPreSteps; ++s) {
-        const u32x4 a = m < M ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
-        acc = mma16<Bf16>(acc, a, wf[s]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][mt][grp * 4 + j][col] = acc[j];
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < mtiles * 256; e += blockDim.x) {
-    const int mt = e >> 8, mm = (e >> 4) & 15, c = e & 15;
-    const int m = mt * 16 + mm, n = nt * 16 + c;
-    if (m < M) {
-      float sum = 0.f;
-      for (int w = 0; w < waves; ++w) sum += red[w][mt][mm][c];
-      if (ks == 0 && b1) sum += bf16_to_f32(b1[n]);
-      ppart[((size_t)ks * M + m) * r + n] = sum;
-    }
-  }
-}
-
-// Launch shape of the pre-loop kernel, or false when d does not split into
-// 512-B slices.  Unit workgroup s < S adds slice s of P into the share of
-// W1[:, d:] g it publishes, so every workgroup's u = SiLU(sum of the shares).
-struct Pre {
-  int waves, S, grid;
-};
-static bool pre_shape(int d, int r, Pre& pr) {
-  const int row = d * 2;
-  if (row % 512 || r % 16) return false;
-  const int chunks = row / 512;
-  pr.waves = chunks % 4 == 0 ? 4 : chunks % 2 == 0 ? 2 : 1;
-  pr.S = chunks / pr.waves;
-  pr.grid = pr.S * (r / 16);
-  return pr.S <= 16;
-}
-
+// the exchange words (no stale tag may survive from an earlier call) and
+// writes P = W1[:, :d] h + b1 as S K-slice partials (launch_p_partials);
+// unit workgroup s < S adds slice s of P into the share of W1[:, d:] g it
+// publishes, so every workgroup's u = SiLU(sum of the shares).
 struct PreArgs {
   const LoopArgs* a;
-  Pre shape;
+  PSplit shape;
 };
 
 static hipError_t launch_pre(const PreArgs& q, hipStream_t s) {
   const LoopArgs& a = *q.a;
-  hipLaunchKernelGGL(pre_kernel, dim3(q.shape.grid), dim3(kPreWaves * 64), 0, s,
-                     static_cast<const uint16_t*>(a.hidden), a.K, a.d, static_cast<const uint16_t*>(a.w1), a.d + a.H,
-                     a.r, static_cast<const uint16_t*>(a.b1), a.ppart, q.shape.waves, a.keys, a.K * a.B + 1, a.xpart,
-                     (int)a.xwords);
-  return hipGetLastError();
+  return launch_p_partials(a.hidden, a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, q.shape, a.keys, a.K * a.B + 1,
+                           a.xpart, (int)a.xwords, s);
 }
 
 // Checks that the loop kernel fits one workgroup per CU, then launches the
@@ -789,8 +711,8 @@ static bool make_plan(const LoopArgs& a, Plan& pl) {
   constexpr int RK = 8;
   if (a.dtype != 1 || a.B != 1 || !a.table) return false;
   if (a.r != RK * 32 || a.H != kUnitWGs * kUnitMax) return false;  // 128 GRU units per unit workgroup
-  Pre pre;  // P arrives as S slices, one per unit workgroup at most
-  if (!pre_shape(a.d, a.r, pre) || pre.S > kUnitWGs) return false;
+  PSplit pre;  // P arrives as S slices, one per unit workgroup at most
+  if (!p_split_shape(a.d, a.r, pre) || pre.S > kUnitWGs) return false;
   pl.G = std::min(a.num_cu, std::min(a.max_wg, 256));
   if (pl.G <= kUnitWGs) return false;
   pl.KH = a.H / 32;
@@ -859,7 +781,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   x += 2 * (size_t)kUnitWGs * a.r;
   p.x_key = x;
   PreArgs q{&a, {}};
-  if (!pre_shape(a.d, a.r, q.shape)) return hipErrorNotSupported;
+  if (!p_split_shape(a.d, a.r, q.shape)) return hipErrorNotSupported;
   p.S = q.shape.S;
   return launch_uhw<NR, RK>(p, U_hh / kWaves, G, L.total, q, s);
 }

@@ -2,7 +2,10 @@
 // Pure C++ (no HIP calls), so it can also be built and sanitised on a CPU.
 #include "validate.h"
 
+#include "psplit.h"
+
 #include <cmath>
+#include <initializer_list>
 
 namespace domino {
 
@@ -47,9 +50,12 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   off += up256((K * B + 2) * sizeof(unsigned long long));  // keys + loop control words
   w.P = off;
   off += up256(B * K * r * sizeof(float));
-  // single-block loop: up to 16 K-slice partials of the hidden half of W1 h
+  // K-slice partials of the hidden half of W1 h (bf16 heads): the single-block
+  // loop and the per-position kernels add them up
   w.ppart = off;
-  off += batch == 1 ? up256(16 * K * r * sizeof(float)) : 0;
+  PSplit ps;
+  if (h->dtype == DOMINO_BF16 && p_split_shape(h->d, h->rank, ps))
+    off += up256((size_t)ps.S * B * K * r * sizeof(float));
   w.part_ih = off;
   off += up256(ks * B * 3 * H * sizeof(float));
   w.part_hh = off;
