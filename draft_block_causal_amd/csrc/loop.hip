@@ -497,10 +497,16 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
 // four words it needs.  Argmax keys are reduced over lanes and waves and
 // merged into keys[step][b] with a 64-bit atomic max.
 // ---------------------------------------------------------------------------
+template <class T>
+__device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0);
+
 // VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
 // logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
+// hh_step > 0: the first 3H/16 x ceil(B/16) workgroups first form one 16 x 16
+// unit of W_hh g for position hh_step (g of this position is final), which
+// takes that product off the token-to-token path.
 template <class T, int MT, int NS, bool VEC>
-__global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) {
+__global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step) {
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
   constexpr int NPARTS = act_parts<T>();
@@ -512,6 +518,11 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step) 
   unsigned long long* kred = reinterpret_cast<unsigned long long*>(tr + 4 * 16 * 17);  // [4][rows]
   const int B = p.B, V = p.V, r = p.r, K = p.K;
   const int m0 = blockIdx.y * rows;
+  if (hh_step > 0) {
+    const int t3 = (3 * p.H) >> 4;
+    const int unit = blockIdx.y * gridDim.x + blockIdx.x;
+    if (unit < t3 * ((B + 15) >> 4)) hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+  }
 
   // u rows -> LDS operands; each thread's fragments (rows * NS * 4 / 256 of
   // them, r = NS * 64 / sizeof(E) entries per row) are all loaded first
@@ -832,14 +843,20 @@ __global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
   }
 }
 
-// W_hh g_{step-1}: gate rows 16t .. 16t+15 for batch rows 16m .. 16m+15.
+// W_hh g_{step-1}: gate rows 16t .. 16t+15 for batch rows m0 .. m0+15 (one
+// workgroup; every thread must call it).
 template <class T>
-__global__ void __launch_bounds__(256) hh_kernel(DevLoop<T> p, int step) {
-  const int t = blockIdx.x, m0 = blockIdx.y * 16;
+__device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0) {
   const float sum = block_rows_dot<T>(p.w_hh, p.H, t * 16, p.states + (size_t)(step - 1) * p.H, p.K * p.H, m0, p.B,
                                       p.H);
   const int b = m0 + (threadIdx.x >> 4), n = t * 16 + (threadIdx.x & 15);
   if (b < p.B) p.part_hh[(size_t)b * 3 * p.H + n] = sum;
+  __syncthreads();  // the reduction buffer is reused by the caller
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) hh_kernel(DevLoop<T> p, int step) {
+  hh_unit(p, step, blockIdx.x, blockIdx.y * 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -866,7 +883,7 @@ __global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step
 
 
 template <class T, int MT>
-__global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step) {
+__global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step, int /*hh_step: not fused here*/) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   w2_sample_block<T, MT, Plain>(p, step, blockIdx.x, gridDim.x, blockIdx.y * 16 * MT, smem);
 }
@@ -1012,9 +1029,10 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
 // else the generic one.
 template <class T, int MW>
 struct W2Launch {
-  void (*kern)(DevLoop<T>, int);
+  void (*kern)(DevLoop<T>, int, int);
   size_t lds;
   dim3 grid;
+  bool fused_hh;  // the kernel forms W_hh g for the next position
 };
 
 template <class T, int MW, int NS>
@@ -1030,7 +1048,9 @@ static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int slots = std::max(1, per_cu) * num_cu * 4;
   const int iters = (ntiles + slots - 1) / slots;
   const int gx = std::max(1, (ntiles + 4 * iters - 1) / (4 * iters));
-  return {kern, lds, dim3(gx, (p.B + 16 * MW - 1) / (16 * MW))};
+  const dim3 grid(gx, (p.B + 16 * MW - 1) / (16 * MW));
+  const long hh_units = (long)(3 * p.H / 16) * ((p.B + 15) / 16);
+  return {kern, lds, grid, hh_units <= (long)grid.x * grid.y};
 }
 
 template <class T, int MW>
@@ -1045,7 +1065,7 @@ static W2Launch<T, MW> w2_plan(const DevLoop<T>& p, int num_cu) {
   }
   const int ntiles = (p.V + 15) / 16;
   return {w2_sample_kernel<T, MW>, w2_lds_bytes<T>(p.r, 16 * MW),
-          dim3(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW))};
+          dim3(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW)), false};
 }
 
 template <class T, int MT>
@@ -1060,10 +1080,13 @@ static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t
   const dim3 hgrid(t3, (p.B + 15) / 16);
   for (int step = 0; step < p.K; ++step) {
     if (!p.table) hipLaunchKernelGGL((gru_partial_kernel<T, MT>), dim3((t3 * p.KS + 3) / 4), dim3(256), 0, s, p, step);
-    if (step > 0) hipLaunchKernelGGL(hh_kernel<T>, hgrid, dim3(256), 0, s, p, step);
+    // W_hh g for this position: formed by the previous position's W2 launch
+    // when it carries it, else a launch of its own
+    if (step > 0 && !w2.fused_hh) hipLaunchKernelGGL(hh_kernel<T>, hgrid, dim3(256), 0, s, p, step);
     hipLaunchKernelGGL(gates_kernel<T>, ggrid, dim3(256), 0, s, p, step);
     hipLaunchKernelGGL(u_kernel<T>, ugrid, dim3(256), 0, s, p, step);
-    hipLaunchKernelGGL(w2.kern, w2.grid, dim3(256), w2.lds, s, p, step);
+    const int hh_next = w2.fused_hh && step + 1 < p.K ? step + 1 : 0;
+    hipLaunchKernelGGL(w2.kern, w2.grid, dim3(256), w2.lds, s, p, step, hh_next);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_finalize_tokens(p.B, p.K, p.keys, p.tokens, s);
