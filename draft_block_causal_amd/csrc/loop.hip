@@ -1071,7 +1071,7 @@ static W2Launch<T, MW> w2_plan(const DevLoop<T>& p, int num_cu) {
 template <class T, int MT>
 static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t s) {
   hipError_t e;
-  constexpr int MW = MT > 2 ? 2 : MT;  // w2 rows per workgroup: 16 * MW
+  constexpr int MW = MT > 4 ? 4 : MT;  // w2 rows per workgroup: 16 * MW (W2 read once per 64 rows)
   const W2Launch<T, MW> w2 = w2_plan<T, MW>(p, num_cu);
   if ((e = allow_lds(w2.kern, w2.lds)) != hipSuccess) return e;
   const dim3 ggrid((p.H + 255) / 256, p.B);
