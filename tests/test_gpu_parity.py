@@ -272,6 +272,33 @@ def test_lm_head_more_tiles_than_lds(dev):
     assert err <= LOGIT_TOL, f"base logits err {err}"
 
 
+@pytest.mark.parametrize("batch,vocab", [(3, 20001), (13, 65531), (19, 5003)])
+def test_lm_head_tile_shapes(dev, batch, vocab):
+    """Base logits through both shapes of the many-row matrix-core kernel.
+
+    48 rows (one partial M tile) and 208 rows (two) take 128 x 256 tiles, 304
+    rows take 256 x 256 tiles; every vocabulary is larger than the row-streaming
+    kernel takes and ends in a partial tile.  All rows of the last 600 columns
+    and 3000 random columns are checked against the oracle.
+    """
+    import draft_block_causal_amd as D
+
+    w = S.Workload(f"lm_head_b{batch}_v{vocab}", batch, 16, 256, vocab, 32, 32, "bf16", False, 0.0)
+    log(f"{w.name}: generating inputs")
+    head_np, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    base = D.domino_base_logits(head, _t(inp["hidden"], dev))
+    torch.cuda.synchronize()
+    got = base.cpu().numpy().reshape(batch * 16, vocab)
+    cols = np.unique(np.concatenate([np.arange(vocab - 600, vocab),
+                                     np.random.default_rng(batch).integers(0, vocab, 3000)]))
+    hid = O.as_f64(inp["hidden"]).reshape(batch * 16, -1)
+    ref = O.base_logits(hid, O.as_f64(head_np["lm_head"][cols]))
+    err = np.abs(got[:, cols] - ref).max()
+    log(f"{w.name}: {cols.size} columns x {batch * 16} rows, max err {err:.2e}")
+    assert err <= LOGIT_TOL, f"base logits err {err}"
+
+
 def test_sampled_small_temperature_and_ties(dev):
     _parity(_small("bf16", temperature=0.37, philox_seed=99), dev)
 
