@@ -36,6 +36,14 @@ in the design notes):
   * The token decision is taken on the score rounded to float32 (the
     kernel's precision); ties go to the lowest vocabulary index.
   * Acceptance length: the bare length of the longest matching prefix.
+  * Verification of a sampled draft (the pages report T = 1 decoding, verified
+    in parallel by the target model, without the rule): standard speculative
+    sampling (Leviathan, Kalman, Matias, ICML 2023; Chen et al. 2023).
+    Position i is accepted when U_i * p_d(y_i) < p_t(y_i); at the first
+    rejection the next token is drawn from max(0, p_t - p_d) (renormalised),
+    after a fully accepted block from the target's distribution one past it.
+    U_i is the Philox word of entry 0 at counter (0, i, b, offset) mapped as
+    for the Gumbel noise; the resampling noise uses offset + 1.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py``
 against something other than itself (closed forms, brute force, invariants,
@@ -61,6 +69,9 @@ __all__ = [
     "draft_block",
     "accept_len",
     "top2_margin",
+    "uniform01",
+    "softmax",
+    "verify_sampled",
 ]
 
 _MASK32 = np.uint64(0xFFFFFFFF)
@@ -287,3 +298,75 @@ def top2_margin(scores) -> np.ndarray:
     if s.shape[-1] < 2:
         return np.full(s.shape[:-1], np.inf)
     return s[..., -1] - s[..., -2]
+
+
+# ---------------------------------------------------------------------------
+# Verification of a sampled draft (speculative sampling).  The pages report
+# sampled decoding at T = 1 ([notes] §三.2(1): "采样解码（T=1）") and say that
+# the target model verifies the drafted block in parallel ([abstract],
+# English original, first sentence) without giving the acceptance rule; the
+# rule below is the published one (Leviathan, Kalman, Matias, "Fast Inference
+# from Transformers via Speculative Decoding", ICML 2023, Algorithm 1; Chen et
+# al., "Accelerating Large Language Model Decoding with Speculative
+# Sampling", 2023), which leaves the target's distribution unchanged.
+# ---------------------------------------------------------------------------
+def uniform01(seed: int, offset: int, b, i) -> np.ndarray:
+    """U in (0, 1) for position i of block b: the Philox word of entry 0 at
+    counter (0, i, b, offset), mapped as U = ((word >> 9) + 1/2) * 2^-23."""
+    w = philox_words(seed, offset, b, i, 0).astype(np.float64)
+    return (np.floor(w / 512.0) + 0.5) * 2.0 ** -23
+
+
+def softmax(logits, temperature: float) -> np.ndarray:
+    """softmax(L / T) along the last axis, in float64."""
+    x = as_f64(logits) / temperature
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def verify_sampled(target_logits, draft_logits, draft, temperature: float, seed: int, offset: int):
+    """Accepted prefix length and the next token of each drafted block.
+
+    target_logits [B, K + 1, V]: the target model's logits at the K drafted
+    positions and one past them; draft_logits [B, K, V]: the logits the draft
+    tokens draft [B, K] were sampled from; both distributions are
+    softmax(logits / T).  For i = 0 … K-1, position i is accepted when
+    U_i p_d(y_i) < p_t(y_i), i.e. with probability min(1, p_t(y_i) / p_d(y_i));
+    the first rejected position n ends the block and the next token is drawn
+    from max(0, p_t - p_d) at n; if all K are accepted, n = K and the next
+    token is drawn from p_t at position K.  Draws use Gumbel-max with noise
+    G(b, n, v) at offset + 1: scores log max(0, p_t - p_d) + G (log 0 = -inf)
+    or L_t / T + G.  Returns (accept [B] int32, next_token [B] int32, scores),
+    scores [B, V] being the scores of each block's draw.
+    """
+    if not temperature > 0:
+        raise ValueError("verification of a sampled draft needs T > 0")
+    tl = as_f64(target_logits)
+    dl = as_f64(draft_logits)
+    draft = np.asarray(draft)
+    B, K = draft.shape
+    V = tl.shape[-1]
+    accept = np.zeros(B, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    scores = np.zeros((B, V))
+    for b in range(B):
+        n = K
+        for i in range(K):
+            pt = softmax(tl[b, i], temperature)
+            pd = softmax(dl[b, i], temperature)
+            y = int(draft[b, i])
+            if not (uniform01(seed, offset, b, i) * pd[y] < pt[y]):
+                n = i
+                break
+        accept[b] = n
+        g = gumbel_noise(seed, offset + 1, b, n, np.arange(V))
+        if n < K:
+            q = softmax(tl[b, n], temperature) - softmax(dl[b, n], temperature)
+            with np.errstate(divide="ignore"):
+                s = np.where(q > 0, np.log(np.where(q > 0, q, 1.0)), -np.inf) + g
+        else:
+            s = tl[b, K] / temperature + g
+        scores[b] = s
+        nxt[b] = pick_token(s)
+    return accept, nxt, scores

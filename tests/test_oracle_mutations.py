@@ -28,6 +28,13 @@ MUTATIONS = {
     "philox_lane": ("lane = np.broadcast_to(v & np.uint64(3), shape)",
                     "lane = np.broadcast_to((v >> np.uint64(1)) & np.uint64(3), shape)"),
     "temperature_ignored": ("return logits / temperature + gumbel_noise", "return logits + gumbel_noise"),
+    "verify_ratio_inverted": ("if not (uniform01(seed, offset, b, i) * pd[y] < pt[y]):",
+                              "if not (uniform01(seed, offset, b, i) * pt[y] < pd[y]):"),
+    "verify_residual_reversed": ("q = softmax(tl[b, n], temperature) - softmax(dl[b, n], temperature)",
+                                 "q = softmax(dl[b, n], temperature) - softmax(tl[b, n], temperature)"),
+    "verify_bonus_position": ("s = tl[b, K] / temperature + g", "s = tl[b, K - 1] / temperature + g"),
+    "verify_shared_noise_stream": ("g = gumbel_noise(seed, offset + 1, b, n, np.arange(V))",
+                                   "g = gumbel_noise(seed, offset, b, n, np.arange(V))"),
     "base_logits_transposed_operand": ("return as_f64(hidden) @ as_f64(lm_head).T",
                                        "return (as_f64(lm_head) @ as_f64(hidden).swapaxes(-1, -2)).swapaxes(-1, -2)[..., ::-1]"),
 }

@@ -414,3 +414,91 @@ def test_head_parameter_count_matches_pages():
     # a GRU whose input were the GRU width instead of d would miss the pages' figure
     alt = 3 * 1024 * 1024 * 2 + 256 * (4096 + 1024) + 151936 * 256
     assert round(alt / 1e6) != g["head_params_millions"]
+
+
+# ---------------------------------------------------------------------------
+# Verification of a sampled draft (speculative sampling).  The defining
+# property of the rule (Leviathan et al. 2023, Theorem 1; Chen et al. 2023):
+# the token emitted at the first drafted position is distributed exactly as
+# the target's p_t, whatever p_d is, and the draft token survives with
+# probability sum_x min(p_t(x), p_d(x)).  Both are checked by sampling the
+# draft token from p_d with an independent generator and running the oracle
+# once per trial (its own Philox stream decides acceptance and resampling).
+# ---------------------------------------------------------------------------
+def _verify_trials(t_logits, d_logits, T, n, seed0=1000):
+    rng = np.random.default_rng(7)
+    pd = O.softmax(d_logits, T)
+    V = pd.size
+    emitted = np.zeros(V)
+    accepted = 0
+    residual = np.zeros(V)
+    tl = np.stack([t_logits, np.zeros(V)])[None]  # position 1 (the bonus) is never the first emission
+    for k in range(n):
+        y = int(rng.choice(V, p=pd))
+        acc, nxt, _ = O.verify_sampled(tl, d_logits[None, None], np.array([[y]]), T, seed0 + k, 3)
+        if acc[0] == 1:
+            accepted += 1
+            emitted[y] += 1
+        else:
+            emitted[nxt[0]] += 1
+            residual[nxt[0]] += 1
+    return emitted / n, accepted / n, residual
+
+
+def test_verify_first_emission_follows_target_and_acceptance_rate():
+    t = np.array([1.2, -0.3, 0.4, 0.0, -1.1])
+    d = np.array([-0.2, 0.9, 0.4, -0.7, 0.5])
+    T, n = 0.8, 6000
+    emp, acc, _ = _verify_trials(t, d, T, n)
+    pt, pd = O.softmax(t, T), O.softmax(d, T)
+    sd = np.sqrt(pt * (1 - pt) / n)
+    assert np.all(np.abs(emp - pt) < 5 * sd + 1e-9), (emp, pt)
+    p_acc = np.minimum(pt, pd).sum()
+    assert abs(acc - p_acc) < 5 * np.sqrt(p_acc * (1 - p_acc) / n), (acc, p_acc)
+
+
+def test_verify_residual_draw_is_positive_part():
+    t = np.array([2.0, 0.0, 0.0, -1.0])
+    d = np.array([0.0, 1.5, 0.0, 0.5])
+    T, n = 1.0, 4000
+    _, _, res = _verify_trials(t, d, T, n)
+    q = np.maximum(O.softmax(t, T) - O.softmax(d, T), 0.0)
+    q /= q.sum()
+    m = res.sum()
+    assert m > 500
+    sd = np.sqrt(q * (1 - q) / m)
+    assert np.all(np.abs(res / m - q) < 5 * sd + 1e-9), (res / m, q)
+    assert res[q == 0].sum() == 0  # entries where p_t <= p_d are never drawn
+
+
+def test_verify_equal_distributions_accept_every_position():
+    rng = np.random.default_rng(3)
+    B, K, V = 3, 6, 11
+    d = rng.normal(0, 1, (B, K, V))
+    t = np.concatenate([d, rng.normal(0, 1, (B, 1, V))], axis=1)
+    y = rng.integers(0, V, (B, K))
+    for seed in range(40):
+        acc, nxt, scores = O.verify_sampled(t, d, y, 1.3, seed, 9)
+        assert np.all(acc == K)
+        # the bonus draw is Gumbel-max over the target's last distribution
+        g = O.gumbel_noise(seed, 10, np.arange(B)[:, None], K, np.arange(V)[None, :])
+        assert np.array_equal(nxt, np.argmax(t[:, K] / 1.3 + g, axis=-1))
+
+
+def test_verify_zero_target_mass_always_rejects():
+    rng = np.random.default_rng(4)
+    B, K, V = 2, 5, 9
+    d = rng.normal(0, 1, (B, K, V))
+    t = np.concatenate([d + rng.normal(0, 0.1, (B, K, V)), rng.normal(0, 1, (B, 1, V))], axis=1)
+    y = rng.integers(0, V, (B, K))
+    j = 2
+    t[np.arange(B), j, y[:, j]] = -1e4  # p_t(y_j) underflows to 0
+    for seed in range(30):
+        acc, nxt, _ = O.verify_sampled(t, d, y, 1.0, seed, 0)
+        assert np.all(acc <= j)
+        assert np.all((acc < j) | (nxt != y[:, j]))
+
+
+def test_verify_needs_positive_temperature():
+    with pytest.raises(ValueError):
+        O.verify_sampled(np.zeros((1, 2, 3)), np.zeros((1, 1, 3)), np.zeros((1, 1), dtype=int), 0.0, 0, 0)
