@@ -25,6 +25,11 @@ Generation recipe (fixed so that every caller sees the same values):
   * accept-length targets (``make_targets``): a separate generator seeded 1;
     each position copies the draft token with probability p (0.9), otherwise
     takes a uniform token on [0, V).
+  * sampled-draft verification inputs (``make_verify_inputs``): one
+    ``default_rng(seed)``; draft logits N(0, 2^2) [B, K, V]; target logits =
+    draft logits + N(0, spread^2) at the K drafted positions and N(0, 2^2)
+    one past them; each draft token is the draft row's largest logit with
+    probability 0.8, otherwise a uniform token.
 """
 from __future__ import annotations
 
@@ -189,6 +194,19 @@ def make_targets(draft: np.ndarray, vocab: int, p: float = 0.9, seed: int = 1) -
     keep = rng.random(size=draft.shape) < p
     other = rng.integers(0, vocab, size=draft.shape, dtype=np.int64).astype(np.int32)
     return np.where(keep, draft, other).astype(np.int32)
+
+
+def make_verify_inputs(batch: int, block: int, vocab: int, spread: float, seed: int = 2):
+    """(target_logits [B, K+1, V], draft_logits [B, K, V], draft [B, K]) for sampled-draft verification."""
+    rng = np.random.default_rng(seed)
+    d = (rng.standard_normal((batch, block, vocab), dtype=np.float32) * 2.0).astype(np.float32)
+    t = np.empty((batch, block + 1, vocab), dtype=np.float32)
+    t[:, :block] = d + rng.standard_normal((batch, block, vocab), dtype=np.float32) * np.float32(spread)
+    t[:, block] = rng.standard_normal((batch, vocab), dtype=np.float32) * 2.0
+    top = np.argmax(d, axis=-1)
+    uni = rng.integers(0, vocab, size=(batch, block))
+    y = np.where(rng.random((batch, block)) < 0.8, top, uni).astype(np.int32)
+    return t, d, y
 
 
 def to_torch(a: np.ndarray, device=None):

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     domino_draft_block,
     domino_gru_table_size,
     domino_prepare_gru_table,
+    domino_verify_sampled,
+    domino_verify_workspace_size,
     domino_version,
     domino_workspace_size,
     load_library,

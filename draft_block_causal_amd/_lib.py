@@ -42,6 +42,8 @@ EXPORTED = [
     "domino_base_logits",
     "domino_draft_block",
     "domino_accept_len",
+    "domino_verify_sampled",
+    "domino_verify_workspace_size",
     "domino_debug_philox",
 ]
 
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_base_logits": (ctypes.c_int, [HP, I32, P, P, P]),
         "domino_draft_block": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P, SZ, P]),
         "domino_accept_len": (ctypes.c_int, [I32, I32, P, P, P, P]),
+        "domino_verify_sampled": (ctypes.c_int, [I32, I32, I32, P, P, P, F, U64, U32, P, P, P, SZ, P]),
+        "domino_verify_workspace_size": (SZ, [I32, I32, I32]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -269,6 +273,39 @@ def domino_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: Optiona
     _check("domino_accept_len", load_library().domino_accept_len(
         B, K, _ptr(draft), _ptr(target), _ptr(accept), _stream_ptr(stream)))
     return accept
+
+
+def domino_verify_workspace_size(batch: int, block: int, vocab: int) -> int:
+    return int(load_library().domino_verify_workspace_size(int(batch), int(block), int(vocab)))
+
+
+def domino_verify_sampled(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft: torch.Tensor,
+                          temperature: float, seed: int = 0, offset: int = 0,
+                          accept: Optional[torch.Tensor] = None, next_token: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Speculative-sampling verification; returns (accept [B], next_token [B]) int32."""
+    B, K = draft.shape
+    V = draft_logits.shape[-1]
+    dev = draft.device
+    _need(target_logits, "target_logits", torch.float32, (B, K + 1, V), dev)
+    _need(draft_logits, "draft_logits", torch.float32, (B, K, V), dev)
+    _need(draft, "draft", torch.int32, (B, K), dev)
+    if accept is None:
+        accept = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(accept, "accept", torch.int32, (B,), dev)
+    _need(next_token, "next_token", torch.int32, (B,), dev)
+    need = domino_verify_workspace_size(B, K, V) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    _check("domino_verify_sampled", load_library().domino_verify_sampled(
+        B, K, V, _ptr(target_logits), _ptr(draft_logits), _ptr(draft), float(temperature),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(accept), _ptr(next_token),
+        _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return accept, next_token
 
 
 def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,

@@ -128,6 +128,26 @@ extern "C" int domino_accept_len(int32_t batch, int32_t block, const int32_t* dr
   return hip_status(domino::launch_accept_len(batch, block, draft, target, accept, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" size_t domino_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
+  if (batch < 1 || batch > domino::kMaxVerifyBatch || block < 1 || block > domino::kMaxVerifyBlock || vocab < 1 ||
+      vocab > domino::kMaxVocab)
+    return 0;
+  return domino::verify_plan(batch, block, vocab).total;
+}
+
+extern "C" int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
+                                     const float* draft_logits, const int32_t* draft, float temperature,
+                                     uint64_t seed, uint32_t offset, int32_t* accept, int32_t* next_token,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = domino::check_verify_args(batch, block, vocab, target_logits, draft_logits, draft, temperature, accept,
+                                     next_token, workspace, workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  return hip_status(domino::launch_verify_sampled(batch, block, vocab, target_logits, draft_logits, draft,
+                                                  temperature, seed, offset, accept, next_token,
+                                                  domino::verify_plan(batch, block, vocab), workspace,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int domino_debug_philox(uint64_t seed, uint32_t offset, int32_t b, int32_t pos, int32_t v0, int32_t n,
                                    uint32_t* out, void* stream) {
   if (n < 0 || n > (1 << 26) || b < 0 || pos < 0 || v0 < 0) return DOMINO_ERR_SHAPE;

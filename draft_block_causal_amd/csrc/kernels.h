@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "psplit.h"
+#include "verify_plan.h"
 
 namespace domino {
 
@@ -80,6 +81,13 @@ size_t b1_exchange_words(int H, int r, int max_wg);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
+
+// Sampled-draft verification (verify.hip): accept[b] and next[b] from the
+// target's [B][K + 1][V] and the draft's [B][K][V] float32 logits; the
+// workspace follows verify_plan(B, K, V).
+hipError_t launch_verify_sampled(int B, int K, int V, const float* target, const float* draft, const int32_t* tokens,
+                                 float temperature, uint64_t seed, uint32_t offset, int32_t* accept, int32_t* next,
+                                 const VerifyPlan& plan, void* workspace, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s);

@@ -114,6 +114,23 @@ int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const 
   return DOMINO_OK;
 }
 
+int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
+                      const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
+                      const int32_t* next_token, const void* workspace, size_t workspace_bytes) {
+  if (batch < 0 || batch > kMaxVerifyBatch || block < 1 || block > kMaxVerifyBlock || vocab < 1 ||
+      vocab > kMaxVocab)
+    return DOMINO_ERR_SHAPE;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return DOMINO_ERR_ARG;
+  if (batch == 0) return DOMINO_OK;
+  if (!target_logits || !draft_logits || !draft || !accept || !next_token) return DOMINO_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(target_logits) & 3u) || (reinterpret_cast<uintptr_t>(draft_logits) & 3u))
+    return DOMINO_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < verify_plan(batch, block, vocab).total)
+    return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
 }  // namespace domino
 
 extern "C" const char* domino_status_string(int status) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/domino.h"
+#include "verify_plan.h"
 
 namespace domino {
 
@@ -32,5 +33,8 @@ int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, co
 int check_base_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits);
 int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
                       const int32_t* accept);
+int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
+                      const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
+                      const int32_t* next_token, const void* workspace, size_t workspace_bytes);
 
 }  // namespace domino

@@ -180,6 +180,43 @@ int domino_accept_len(int32_t batch, int32_t block, const int32_t *draft, const 
                       int32_t *accept, void *stream);
 
 /*
+ * Verification of a sampled draft.  The pages report sampled decoding at T = 1
+ * ([notes] §三.2(1)) and have the target model verify the drafted block in
+ * parallel without giving the acceptance rule; this call applies the published
+ * speculative-sampling rule (Leviathan, Kalman, Matias, ICML 2023, Algorithm 1;
+ * Chen et al. 2023), which keeps the output distributed as the target's.  With
+ * p_t = softmax(target_logits[b, i] / T) and p_d = softmax(draft_logits[b, i] / T):
+ *   position i = 0, 1, ... is accepted while U_i * p_d(y_i) < p_t(y_i),
+ *   U_i = ((word >> 9) + 0.5) * 2^-23 with word = the Philox4x32-10 output lane 0
+ *   at counter (0, i, b, offset), key (seed lo, seed hi);
+ *   accept[b] = n, the first rejected position (block if none);
+ *   next_token[b] = argmax_v log max(0, p_t(v) - p_d(v)) + G(v) at position n
+ *   (log 0 = -inf), or argmax_v target_logits[b, block, v] / T + G(v) when
+ *   n == block; G is the Gumbel noise of domino_draft_block at counter offset
+ *   offset + 1, block b, position n.  Ties go to the lowest index.
+ * The caller passes an offset whose streams (offset, offset + 1) the drafter
+ * does not use for the same blocks.
+ *
+ * target_logits [batch, block + 1, vocab] float32 (4-byte aligned)
+ * draft_logits  [batch, block, vocab] float32 (4-byte aligned): the logits the
+ *               draft tokens were sampled from
+ * draft         [batch, block] int32; ids outside [0, vocab) are clamped
+ * temperature   T > 0 and finite (else DOMINO_ERR_ARG)
+ * accept, next_token  [batch] int32 (outputs)
+ * workspace     device scratch of at least domino_verify_workspace_size()
+ *               bytes, 256-byte aligned; its contents are overwritten.
+ * batch in 0 … 2^20 (0 is a no-op), block in 1 … 255, vocab in 1 … 2^24 - 1.
+ * Arithmetic: float32 (log-sum-exp normalisers merged over vocabulary slices).
+ */
+int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab, const float *target_logits,
+                          const float *draft_logits, const int32_t *draft, float temperature, uint64_t seed,
+                          uint32_t offset, int32_t *accept, int32_t *next_token, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Workspace bytes domino_verify_sampled needs (0 for sizes out of range). */
+size_t domino_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

@@ -169,3 +169,35 @@ def test_binding_rejects_bad_tensors():
         D.Head(bad)
     with pytest.raises(TypeError):
         D.Head(dict(t, w1=t["w1"].double()))
+
+
+def test_verify_validation_and_workspace(lib):
+    ws = lib.domino_verify_workspace_size(2, 16, 151936)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.domino_verify_workspace_size(0, 16, 100) == 0
+    assert lib.domino_verify_workspace_size(1, 256, 100) == 0
+    assert lib.domino_verify_workspace_size(1, 16, 1 << 24) == 0
+    args = dict(B=2, K=16, V=151936, t=0x10000, d=0x20000, y=0x30000, T=1.0, a=0x40000, n=0x50000,
+                w=0x100000, wb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.domino_verify_sampled(a["B"], a["K"], a["V"], a["t"], a["d"], a["y"], a["T"], 7, 3,
+                                         a["a"], a["n"], a["w"], a["wb"], None)
+
+    assert call() == E_HIP  # valid arguments, no GPU here
+    assert call(B=-1) == E_SHAPE
+    assert call(K=0) == E_SHAPE
+    assert call(K=256) == E_SHAPE
+    assert call(V=0) == E_SHAPE
+    assert call(T=0.0) == E_ARG
+    assert call(T=-1.0) == E_ARG
+    assert call(T=float("inf")) == E_ARG
+    assert call(T=float("nan")) == E_ARG
+    assert call(t=None) == E_NULL
+    assert call(n=None) == E_NULL
+    assert call(d=0x20002) == E_ALIGN
+    assert call(w=None) == E_WS
+    assert call(w=0x100010) == E_WS
+    assert call(wb=ws - 1) == E_WS
+    assert call(B=0, t=None, d=None, y=None, a=None, n=None, w=None, wb=0) == OK
