@@ -502,9 +502,10 @@ __device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0);
 
 // VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
 // logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
-// hh_step > 0: the first 3H/16 x ceil(B/16) workgroups first form one 16 x 16
-// unit of W_hh g for position hh_step (g of this position is final), which
-// takes that product off the token-to-token path.
+// hh_step > 0: the workgroups first form the 3H/16 x ceil(B/16) 16 x 16 units
+// of W_hh g for position hh_step (g of this position is final), unit q in
+// workgroup q mod (grid size), which takes that product off the
+// token-to-token path.
 template <class T, int MT, int NS, bool VEC>
 __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step) {
   using E = typename T::elem;
@@ -520,8 +521,10 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
   const int m0 = blockIdx.y * rows;
   if (hh_step > 0) {
     const int t3 = (3 * p.H) >> 4;
-    const int unit = blockIdx.y * gridDim.x + blockIdx.x;
-    if (unit < t3 * ((B + 15) >> 4)) hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+    const int units = t3 * ((B + 15) >> 4), nwg = gridDim.x * gridDim.y;
+    // (the trip count is uniform over the workgroup: hh_unit synchronises it)
+    for (int unit = blockIdx.y * gridDim.x + blockIdx.x; unit < units; unit += nwg)
+      hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
   }
 
   // u rows -> LDS operands; each thread's fragments (rows * NS * 4 / 256 of
@@ -827,17 +830,21 @@ __device__ __forceinline__ float block_rows_dot(const typename T::elem* W, int l
 template <class T>
 __global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
   const int t = blockIdx.x, m0 = blockIdx.y * 16;
-  // batch row b's state at this position: states[b][step][:], row stride K * H
-  const float sum = block_rows_dot<T>(p.w1 + p.d, p.d + p.H, t * 16, p.states + (size_t)step * p.H, p.K * p.H, m0,
-                                      p.B, p.H);
   const int b = m0 + (threadIdx.x >> 4), q = t * 16 + (threadIdx.x & 15);
+  const size_t row = ((size_t)b * p.K + step) * p.r + q;
+  // P (whole, or its S slices added in order) is read before the product, so
+  // that its loads are in flight with the product's
+  float ph = 0.f;
   if (b < p.B) {
-    const size_t row = ((size_t)b * p.K + step) * p.r + q;
-    float ph = 0.f;  // P: whole, or its S slices added in order
     if (p.S > 0)
       for (int sl = 0; sl < p.S; ++sl) ph += p.ppart[(size_t)sl * p.B * p.K * p.r + row];
     else
       ph = p.P[row];
+  }
+  // batch row b's state at this position: states[b][step][:], row stride K * H
+  const float sum = block_rows_dot<T>(p.w1 + p.d, p.d + p.H, t * 16, p.states + (size_t)step * p.H, p.K * p.H, m0,
+                                      p.B, p.H);
+  if (b < p.B) {
     const float pre = ph + sum;
     p.u[(size_t)b * p.r + q] = pre * sigmoidf_(pre);
   }
@@ -1040,17 +1047,14 @@ static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int ntiles = (p.V + 15) / 16;
   const size_t lds = w2_stream_lds_bytes<T, MW>(p.r);
   auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true> : w2_stream_kernel<T, MW, NS, false>;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 256, lds) !=
-      hipSuccess)
-    per_cu = 1;
-  // the resident waves take about the same number of tiles each
-  const int slots = std::max(1, per_cu) * num_cu * 4;
-  const int iters = (ntiles + slots - 1) / slots;
-  const int gx = std::max(1, (ntiles + 4 * iters - 1) / (4 * iters));
+  // one workgroup per compute unit for each slice of 16 MW batch rows: each
+  // wave then streams ~ntiles / (4 #CU) tiles, which amortises staging u and
+  // the key reduction (measured at Qwen3 shapes, B = 8 / 32 / 128: 19 / 26 /
+  // 51 us per position against 23 / 33 / 60 us with one wave per resident
+  // slot and 3-4 tiles per wave)
+  const int gx = std::max(1, std::min(num_cu, (ntiles + 3) / 4));
   const dim3 grid(gx, (p.B + 16 * MW - 1) / (16 * MW));
-  const long hh_units = (long)(3 * p.H / 16) * ((p.B + 15) / 16);
-  return {kern, lds, grid, hh_units <= (long)grid.x * grid.y};
+  return {kern, lds, grid, true};
 }
 
 template <class T, int MW>
