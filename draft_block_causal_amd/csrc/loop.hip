@@ -502,12 +502,14 @@ __device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0);
 
 // VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
 // logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
-// hh_step > 0: the workgroups first form the 3H/16 x ceil(B/16) 16 x 16 units
-// of W_hh g for position hh_step (g of this position is final), unit q in
-// workgroup q mod (grid size), which takes that product off the
-// token-to-token path.
+// Workgroups x < gx_w2 of each batch slice stream W2.  hh_step > 0: the
+// 3H/16 x ceil(B/16) 16 x 16 units of W_hh g for position hh_step (g of this
+// position is final) are formed here too, which takes that product off the
+// token-to-token path: by the workgroups x >= gx_w2, which do nothing else,
+// when the grid has them, else by the W2 workgroups before their tiles
+// (unit q in workgroup q mod the grid size).
 template <class T, int MT, int NS, bool VEC>
-__global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step) {
+__global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step, int gx_w2) {
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
   constexpr int NPARTS = act_parts<T>();
@@ -519,13 +521,20 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
   unsigned long long* kred = reinterpret_cast<unsigned long long*>(tr + 4 * 16 * 17);  // [4][rows]
   const int B = p.B, V = p.V, r = p.r, K = p.K;
   const int m0 = blockIdx.y * rows;
+  // (trip counts are uniform over the workgroup: hh_unit synchronises it)
+  const int hx = gridDim.x - gx_w2;  // W_hh-only workgroups per batch slice
   if (hh_step > 0) {
     const int t3 = (3 * p.H) >> 4;
-    const int units = t3 * ((B + 15) >> 4), nwg = gridDim.x * gridDim.y;
-    // (the trip count is uniform over the workgroup: hh_unit synchronises it)
-    for (int unit = blockIdx.y * gridDim.x + blockIdx.x; unit < units; unit += nwg)
-      hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+    const int units = t3 * ((B + 15) >> 4);
+    if (hx == 0) {
+      for (int unit = blockIdx.y * gridDim.x + blockIdx.x; unit < units; unit += gridDim.x * gridDim.y)
+        hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+    } else if ((int)blockIdx.x >= gx_w2) {
+      for (int unit = blockIdx.y * hx + (blockIdx.x - gx_w2); unit < units; unit += hx * gridDim.y)
+        hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+    }
   }
+  if ((int)blockIdx.x >= gx_w2) return;
 
   // u rows -> LDS operands; each thread's fragments (rows * NS * 4 / 256 of
   // them, r = NS * 64 / sizeof(E) entries per row) are all loaded first
@@ -568,7 +577,7 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
   const int eb = lane >> 2, eq = lane & 3;  // epilogue: batch row eb of a tile, entries 4 eq .. 4 eq + 3
   float* trw = tr + wave * 16 * 17;
   const int ntiles = (V + 15) >> 4;
-  const int stride = __builtin_amdgcn_readfirstlane(gridDim.x * 4);  // (computed in a vector register otherwise)
+  const int stride = __builtin_amdgcn_readfirstlane(gx_w2 * 4);  // (computed in a vector register otherwise)
   const int woff = col * row_bytes + grp * 16;
   // base logits of this position for the 16 batch rows of slice mt: one
   // descriptor per slice, based at its first row and ending after the last
@@ -890,7 +899,8 @@ __global__ void __launch_bounds__(256) gru_partial_kernel(DevLoop<T> p, int step
 
 
 template <class T, int MT>
-__global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step, int /*hh_step: not fused here*/) {
+__global__ void __launch_bounds__(256) w2_sample_kernel(DevLoop<T> p, int step, int /*hh_step: not fused here*/,
+                                                        int /*gx_w2: the whole grid*/) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   w2_sample_block<T, MT, Plain>(p, step, blockIdx.x, gridDim.x, blockIdx.y * 16 * MT, smem);
 }
@@ -1036,9 +1046,10 @@ static DevLoop<T> make_dev(const LoopArgs& a) {
 // else the generic one.
 template <class T, int MW>
 struct W2Launch {
-  void (*kern)(DevLoop<T>, int, int);
+  void (*kern)(DevLoop<T>, int, int, int);
   size_t lds;
   dim3 grid;
+  int gx_w2;      // workgroups per batch slice that stream W2 (the rest form W_hh g)
   bool fused_hh;  // the kernel forms W_hh g for the next position
 };
 
@@ -1053,8 +1064,18 @@ static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   // 51 us per position against 23 / 33 / 60 us with one wave per resident
   // slot and 3-4 tiles per wave)
   const int gx = std::max(1, std::min(num_cu, (ntiles + 3) / 4));
-  const dim3 grid(gx, (p.B + 16 * MW - 1) / (16 * MW));
-  return {kern, lds, grid, true};
+  const int gy = (p.B + 16 * MW - 1) / (16 * MW);
+  // W_hh g in workgroups of its own when they fit beside the W2 ones (B = 8 /
+  // 32 at Qwen3 shapes: the launch takes 17.0 / 28.2 us against 18.7 / 31.5
+  // with the units inside the W2 workgroups), else inside the W2 workgroups
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 256, lds) !=
+      hipSuccess)
+    per_cu = 1;
+  const long units = (long)(3 * p.H / 16) * ((p.B + 15) / 16);
+  const long hx = (units + gy - 1) / gy;
+  const bool own = (long)(gx + hx) * gy <= (long)per_cu * num_cu;
+  return {kern, lds, dim3(gx + (own ? (int)hx : 0), gy), gx, true};
 }
 
 template <class T, int MW>
@@ -1068,8 +1089,9 @@ static W2Launch<T, MW> w2_plan(const DevLoop<T>& p, int num_cu) {
     default: break;
   }
   const int ntiles = (p.V + 15) / 16;
-  return {w2_sample_kernel<T, MW>, w2_lds_bytes<T>(p.r, 16 * MW),
-          dim3(std::min((ntiles + 3) / 4, num_cu * 4), (p.B + 16 * MW - 1) / (16 * MW)), false};
+  const int gx = std::min((ntiles + 3) / 4, num_cu * 4);
+  return {w2_sample_kernel<T, MW>, w2_lds_bytes<T>(p.r, 16 * MW), dim3(gx, (p.B + 16 * MW - 1) / (16 * MW)), gx,
+          false};
 }
 
 template <class T, int MT>
@@ -1090,7 +1112,7 @@ static hipError_t multi_kernel_loop(const DevLoop<T>& p, int num_cu, hipStream_t
     hipLaunchKernelGGL(gates_kernel<T>, ggrid, dim3(256), 0, s, p, step);
     hipLaunchKernelGGL(u_kernel<T>, ugrid, dim3(256), 0, s, p, step);
     const int hh_next = w2.fused_hh && step + 1 < p.K ? step + 1 : 0;
-    hipLaunchKernelGGL(w2.kern, w2.grid, dim3(256), w2.lds, s, p, step, hh_next);
+    hipLaunchKernelGGL(w2.kern, w2.grid, dim3(256), w2.lds, s, p, step, hh_next, w2.gx_w2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_finalize_tokens(p.B, p.K, p.keys, p.tokens, s);
