@@ -67,6 +67,7 @@ __all__ = [
     "sampling_scores",
     "pick_token",
     "draft_block",
+    "base_draft",
     "accept_len",
     "top2_margin",
     "uniform01",
@@ -273,6 +274,24 @@ def draft_block(head: dict, hidden, x_t, teacher=None, temperature: float = 0.0,
             prev = int(teacher[b, i]) if teacher is not None else int(tokens[b, i])
     return {"tokens": tokens, "logits": logits, "states": states, "scores": scores,
             "base": base}
+
+
+def base_draft(base, temperature: float = 0.0, seed: int = 0, offset: int = 0) -> np.ndarray:
+    """Head-off drafting: every position's token from its base logits alone.
+
+    The configuration the pages measure the head against: the parallel
+    backbone drafts the block from L^base by itself ([notes] §二.1(1); the head
+    ablation of [notes] §三 and [explainer] §六).  Without the correction
+    L_i = L_i^base, so each position is picked on its own, with the same
+    sampler as the draft loop.  base [B, K, V]; returns tokens [B, K] int32.
+    """
+    base = np.asarray(base, dtype=np.float64)
+    B, K, _ = base.shape
+    tokens = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        for i in range(K):
+            tokens[b, i] = pick_token(sampling_scores(base[b, i], temperature, seed, offset, b, i))
+    return tokens
 
 
 def accept_len(draft, target) -> np.ndarray:

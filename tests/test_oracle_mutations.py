@@ -35,6 +35,8 @@ MUTATIONS = {
     "verify_bonus_position": ("s = tl[b, K] / temperature + g", "s = tl[b, K - 1] / temperature + g"),
     "verify_shared_noise_stream": ("g = gumbel_noise(seed, offset + 1, b, n, np.arange(V))",
                                    "g = gumbel_noise(seed, offset, b, n, np.arange(V))"),
+    "base_draft_position_keys_swapped": ("sampling_scores(base[b, i], temperature, seed, offset, b, i)",
+                                         "sampling_scores(base[b, i], temperature, seed, offset, i, b)"),
     "base_logits_transposed_operand": ("return as_f64(hidden) @ as_f64(lm_head).T",
                                        "return (as_f64(lm_head) @ as_f64(hidden).swapaxes(-1, -2)).swapaxes(-1, -2)[..., ::-1]"),
 }

@@ -183,6 +183,28 @@ def test_residual_invariants_in_draft_block():
     np.testing.assert_allclose(o2["logits"] - o2["base"], 2 * (o1["logits"] - o1["base"]), atol=1e-12)
 
 
+def test_base_draft_hand_case():
+    # greedy: each position's largest base logit; a tie goes to the lower index
+    base = np.array([[[0.1, 2.0, -1.0, 2.0, 0.3],
+                      [5.0, -5.0, 4.9, 0.0, 1.0],
+                      [-3.0, -2.0, -1.0, -0.5, -0.75]]])
+    np.testing.assert_array_equal(O.base_draft(base), [[1, 0, 3]])
+
+
+def test_base_draft_is_draft_block_without_correction():
+    # head off (W2 = 0, b2 = 0) the draft loop drafts from the base logits alone,
+    # greedy and sampled (the same noise stream keyed by block and position)
+    rng = np.random.default_rng(17)
+    d, H, r, V, K, B = 6, 4, 3, 29, 4, 3
+    head = dict(_head(rng, d, H, r, V, scale=1.0), w2=np.zeros((V, r)), b2=np.zeros(V))
+    hidden = rng.normal(size=(B, K, d))
+    x_t = rng.integers(0, V, size=B)
+    base = O.base_logits(hidden, head["lm_head"])
+    for T, seed, offset in ((0.0, 0, 0), (0.7, 5, 3), (1.0, 2**40 + 7, 11)):
+        want = O.draft_block(head, hidden, x_t, temperature=T, seed=seed, offset=offset)["tokens"]
+        np.testing.assert_array_equal(O.base_draft(base, T, seed, offset), want)
+
+
 # ------------------------------------------------------------- loop wiring
 def _torch_chain_logits(head, hidden_b, x_t, seq):
     """Independent re-derivation with torch modules: logits of every position when
