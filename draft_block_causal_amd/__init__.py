@@ -20,6 +20,8 @@ from ._lib import (  # noqa: F401
     domino_prepare_gru_table,
     domino_verify_sampled,
     domino_verify_workspace_size,
+    domino_base_draft,
+    domino_base_draft_workspace_size,
     domino_version,
     domino_workspace_size,
     load_library,

@@ -44,6 +44,8 @@ EXPORTED = [
     "domino_accept_len",
     "domino_verify_sampled",
     "domino_verify_workspace_size",
+    "domino_base_draft",
+    "domino_base_draft_workspace_size",
     "domino_debug_philox",
 ]
 
@@ -103,6 +105,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_accept_len": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "domino_verify_sampled": (ctypes.c_int, [I32, I32, I32, P, P, P, F, U64, U32, P, P, P, SZ, P]),
         "domino_verify_workspace_size": (SZ, [I32, I32, I32]),
+        "domino_base_draft": (ctypes.c_int, [I32, I32, I32, P, F, U64, U32, P, P, SZ, P]),
+        "domino_base_draft_workspace_size": (SZ, [I32, I32]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -306,6 +310,31 @@ def domino_verify_sampled(target_logits: torch.Tensor, draft_logits: torch.Tenso
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(accept), _ptr(next_token),
         _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return accept, next_token
+
+
+def domino_base_draft_workspace_size(batch: int, block: int) -> int:
+    return int(load_library().domino_base_draft_workspace_size(batch, block))
+
+
+def domino_base_draft(base_logits: torch.Tensor, temperature: float = 0.0, seed: int = 0, offset: int = 0,
+                      tokens: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Base-only (head-off) drafting: each position's token from its base logits alone."""
+    if base_logits.dim() != 3:
+        raise ValueError("base_logits must be [batch, block, vocab]")
+    B, K, V = base_logits.shape
+    dev = base_logits.device
+    _need(base_logits, "base_logits", torch.float32, (B, K, V), dev)
+    if tokens is None:
+        tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _need(tokens, "tokens", torch.int32, (B, K), dev)
+    need = domino_base_draft_workspace_size(B, K) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("domino_base_draft", load_library().domino_base_draft(
+        B, K, V, _ptr(base_logits), float(temperature), int(seed), int(offset), _ptr(tokens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return tokens
 
 
 def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,

@@ -12,8 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdomino.so")
-SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "verify.hip", "api.cpp",
-           "validate.cpp"]
+SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "verify.hip", "base_draft.hip",
+           "api.cpp", "validate.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

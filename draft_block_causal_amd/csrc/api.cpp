@@ -148,6 +148,20 @@ extern "C" int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab
                                                   static_cast<hipStream_t>(stream)));
 }
 
+extern "C" size_t domino_base_draft_workspace_size(int32_t batch, int32_t block) {
+  return domino::base_draft_workspace_bytes(batch, block);
+}
+
+extern "C" int domino_base_draft(int32_t batch, int32_t block, int32_t vocab, const float* base_logits,
+                                 float temperature, uint64_t seed, uint32_t offset, int32_t* tokens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int st = domino::check_base_draft_args(batch, block, vocab, base_logits, temperature, tokens, workspace,
+                                         workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  return hip_status(domino::launch_base_draft(batch, block, vocab, base_logits, temperature, seed, offset, tokens,
+                                              workspace, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int domino_debug_philox(uint64_t seed, uint32_t offset, int32_t b, int32_t pos, int32_t v0, int32_t n,
                                    uint32_t* out, void* stream) {
   if (n < 0 || n > (1 << 26) || b < 0 || pos < 0 || v0 < 0) return DOMINO_ERR_SHAPE;

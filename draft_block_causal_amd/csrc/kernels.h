@@ -49,6 +49,7 @@ struct LoopArgs {
   int32_t* tokens;
   float* logits;
   float* states;  // [B, K, H]
+  uint32_t rng_block;  // block index of row 0 in the sampler's counter (rows are rng_block + b)
   // workspace pieces
   unsigned long long* keys;  // [K, B], followed by 2 u64 of loop control (barrier counter, status)
   float* P;                  // [B, K, r]
@@ -88,6 +89,12 @@ hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, 
 hipError_t launch_verify_sampled(int B, int K, int V, const float* target, const float* draft, const int32_t* tokens,
                                  float temperature, uint64_t seed, uint32_t offset, int32_t* accept, int32_t* next,
                                  const VerifyPlan& plan, void* workspace, hipStream_t s);
+
+// Base-only drafting (base_draft.hip): tokens[b][i] picked from base[b][i][:]
+// alone (greedy, or Gumbel-max when temperature > 0); workspace holds B K
+// 64-bit keys.
+hipError_t launch_base_draft(int B, int K, int V, const float* base, float temperature, uint64_t seed,
+                             uint32_t offset, int32_t* tokens, void* workspace, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s);

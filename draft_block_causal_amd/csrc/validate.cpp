@@ -114,6 +114,25 @@ int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const 
   return DOMINO_OK;
 }
 
+size_t base_draft_workspace_bytes(int32_t batch, int32_t block) {
+  if (batch < 1 || batch > kMaxVerifyBatch || block < 1 || block > 1024) return 0;
+  return ((size_t)batch * block * 8 + 255) & ~(size_t)255;
+}
+
+int check_base_draft_args(int32_t batch, int32_t block, int32_t vocab, const float* base_logits, float temperature,
+                          const int32_t* tokens, const void* workspace, size_t workspace_bytes) {
+  if (batch < 0 || batch > kMaxVerifyBatch || block < 1 || block > 1024 || vocab < 1 || vocab > kMaxVocab)
+    return DOMINO_ERR_SHAPE;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return DOMINO_ERR_ARG;
+  if (batch == 0) return DOMINO_OK;
+  if (!base_logits || !tokens) return DOMINO_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(base_logits) & 3u) return DOMINO_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < base_draft_workspace_bytes(batch, block))
+    return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes) {

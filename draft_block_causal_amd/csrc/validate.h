@@ -33,6 +33,9 @@ int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, co
 int check_base_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits);
 int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const int32_t* target,
                       const int32_t* accept);
+int check_base_draft_args(int32_t batch, int32_t block, int32_t vocab, const float* base_logits, float temperature,
+                          const int32_t* tokens, const void* workspace, size_t workspace_bytes);
+size_t base_draft_workspace_bytes(int32_t batch, int32_t block);
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes);

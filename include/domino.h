@@ -217,6 +217,32 @@ int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab, const flo
 size_t domino_verify_workspace_size(int32_t batch, int32_t block, int32_t vocab);
 
 /*
+ * Base-only drafting, the head-off configuration the pages measure Domino
+ * against: the parallel backbone's block drafted from its base logits alone
+ * ([notes] §二.1(1); the head ablation of [notes] §三 and [explainer] §六).
+ * With no causal correction L_i = L_i^base, so every position is picked
+ * independently, with the sampler of domino_draft_block:
+ *   tokens[b, i] = argmax_v base_logits[b, i, v]                 (temperature == 0)
+ *                = argmax_v base_logits[b, i, v] / T + G[b, i, v] (temperature T > 0)
+ * G is the Gumbel noise of domino_draft_block (same counter layout), so a head
+ * whose correction is identically zero drafts the same tokens through either
+ * call.  Ties go to the lowest index.
+ *
+ * base_logits [batch, block, vocab] float32 (4-byte aligned)
+ * tokens      [batch, block] int32 (output)
+ * temperature >= 0 and finite (else DOMINO_ERR_ARG)
+ * workspace   device scratch of at least domino_base_draft_workspace_size()
+ *             bytes, 256-byte aligned; its contents are overwritten.
+ * batch in 0 … 2^20 (0 is a no-op), block in 1 … 1024, vocab in 1 … 2^24 - 1.
+ */
+int domino_base_draft(int32_t batch, int32_t block, int32_t vocab, const float *base_logits, float temperature,
+                      uint64_t seed, uint32_t offset, int32_t *tokens, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Workspace bytes domino_base_draft needs (0 for sizes out of range). */
+size_t domino_base_draft_workspace_size(int32_t batch, int32_t block);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

@@ -201,3 +201,32 @@ def test_verify_validation_and_workspace(lib):
     assert call(w=0x100010) == E_WS
     assert call(wb=ws - 1) == E_WS
     assert call(B=0, t=None, d=None, y=None, a=None, n=None, w=None, wb=0) == OK
+
+
+def test_base_draft_validation_and_workspace(lib):
+    ws = lib.domino_base_draft_workspace_size(3, 16)
+    assert ws >= 3 * 16 * 8 and ws % 256 == 0
+    assert lib.domino_base_draft_workspace_size(0, 16) == 0
+    assert lib.domino_base_draft_workspace_size(1, 1025) == 0
+    args = dict(B=3, K=16, V=151936, L=0x10000, T=0.0, y=0x30000, w=0x100000, wb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.domino_base_draft(a["B"], a["K"], a["V"], a["L"], a["T"], 7, 3, a["y"], a["w"], a["wb"], None)
+
+    assert call() == E_HIP  # valid arguments, no GPU here
+    assert call(T=1.0) == E_HIP
+    assert call(B=-1) == E_SHAPE
+    assert call(K=0) == E_SHAPE
+    assert call(V=0) == E_SHAPE
+    assert call(V=1 << 24) == E_SHAPE
+    assert call(T=-0.5) == E_ARG
+    assert call(T=float("nan")) == E_ARG
+    assert call(T=float("inf")) == E_ARG
+    assert call(L=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(L=0x10002) == E_ALIGN
+    assert call(w=None) == E_WS
+    assert call(w=0x100010) == E_WS
+    assert call(wb=ws - 1) == E_WS
+    assert call(B=0, L=None, y=None, w=None, wb=0) == OK
