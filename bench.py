@@ -8,6 +8,7 @@ domino_accept_len (against synthetic targets).  Inputs are resident in HBM
 before the timed region.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--workload qwen3_8b_b1_greedy]
+    python bench.py --sweep 1,2,4,8,16,32,64,128 [--steps 30]   # concurrency sweep of one head
 """
 from __future__ import annotations
 
@@ -89,6 +90,72 @@ def cpu_baseline(w, head_np, inp, target, min_seconds: float = 10.0):
                       f"accept_len, {el:.1f} s wall"}
 
 
+def sweep(args, w, batches) -> int:
+    """Draft blocks/s of one head at several batch sizes (blocks per call): the
+    concurrency axis of the pages' serving measurements. Each row times
+    base logits + draft block + accept_len on the first B blocks of one input set."""
+    import torch
+
+    import domino_synth as S
+    import draft_block_causal_amd as D
+
+    dev = torch.device("cuda:0")
+    Bmax = max(batches)
+    head_np, inp = S.make_workload(w, batch=Bmax)
+    tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}
+    if w.tied:
+        tensors["embed"] = tensors["lm_head"]
+    head = D.Head(tensors, block=w.block)
+    if not args.no_table:
+        D.domino_prepare_gru_table(head)
+    hidden_all = S.to_torch(inp["hidden"], dev)
+    x_all = S.to_torch(inp["x_t"], dev)
+    target_all = S.to_torch(S.make_targets(S.make_tokens((Bmax, w.block), w.vocab, seed=11), w.vocab, p=0.9,
+                                           seed=1), dev)
+    rows = []
+    for B in batches:
+        hidden, x_t, target = hidden_all[:B], x_all[:B], target_all[:B]
+        base = torch.empty((B, w.block, w.vocab), dtype=torch.float32, device=dev)
+        tokens = torch.empty((B, w.block), dtype=torch.int32, device=dev)
+        accept = torch.empty((B,), dtype=torch.int32, device=dev)
+        ws = torch.empty(D.domino_workspace_size(head, B), dtype=torch.uint8, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+        def step(e=None):
+            if e:
+                e[0].record()
+            D.domino_base_logits(head, hidden, base)
+            if e:
+                e[1].record()
+            D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature, seed=w.philox_seed,
+                                 tokens=tokens, workspace=ws)
+            if e:
+                e[2].record()
+            D.domino_accept_len(tokens, target, accept)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        rows.append({"batch": B, "blocks_per_s": B / (ms * 1e-3), "ms_per_call": ms, "ms_per_block": ms / B,
+                     "lm_head_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                     "draft_block_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))})
+        print(f"sweep B={B}: {rows[-1]['blocks_per_s']:.1f} blocks/s, {ms:.4f} ms/call", file=sys.stderr, flush=True)
+        del base, tokens, accept, ws
+    print(json.dumps({"metric": "draft blocks/s vs blocks per call (concurrency sweep)", "unit": "draft blocks/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
+                      "data": "synthetic (seeded Gaussian weights and hidden states)",
+                      "config": {"workload": w.name, "block": w.block, "d": w.d, "vocab": w.vocab,
+                                 "gru_hidden": w.gru_hidden, "rank": w.rank, "temperature": w.temperature,
+                                 "tied": w.tied, "gru_input_table": not args.no_table},
+                      "sweep": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +166,10 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run a plain device-to-device copy of 1 GiB five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-traffic counters of the LM head")
+    ap.add_argument("--sweep", default=None, metavar="B1,B2,...",
+                    help="concurrency sweep: the workload's head at each batch size in the list (e.g. "
+                         "1,2,4,8,16,32,64,128); prints one JSON line with a row per batch size instead of the "
+                         "benchmark line")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -127,6 +198,8 @@ def main() -> int:
     D.load_library()
     dev = torch.device("cuda:0")
     w = S.get_workload(args.workload)
+    if args.sweep:
+        return sweep(args, w, [int(x) for x in args.sweep.split(",") if x.strip()])
     head_np, inp = S.make_workload(w)
     B, K, V, d, H = w.batch, w.block, w.vocab, w.d, w.gru_hidden
     tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}

@@ -1135,6 +1135,32 @@ static hipError_t persistent_loop(const DevLoop<T>& p, int num_cu, int max_wg, h
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(G), dim3(256), args, (unsigned)lds, s);
 }
 
+// Blocks per call up to which the single-block loop runs once per block.
+constexpr int kB1PerBlockMax = 2;
+
+// Block b of a bf16 call as a call of its own (row pointers offset, the
+// sampler keyed by b); hipErrorNotSupported before any launch if the
+// single-block loop does not take these shapes.
+static hipError_t b1_per_block(const LoopArgs& a, hipStream_t s) {
+  LoopArgs a1 = a;
+  a1.B = 1;
+  if (a.dtype != 1 || !b1_supported(a1)) return hipErrorNotSupported;
+  const size_t K = (size_t)a.K;
+  for (int b = 0; b < a.B; ++b) {
+    a1.hidden = static_cast<const uint16_t*>(a.hidden) + b * K * a.d;
+    a1.base = a.base + b * K * a.V;
+    a1.x_t = a.x_t + b;
+    a1.teacher = a.teacher ? a.teacher + b * K : nullptr;
+    a1.tokens = a.tokens + b * K;
+    a1.logits = a.logits ? a.logits + b * K * a.V : nullptr;
+    a1.states = a.states + b * K * a.H;
+    a1.rng_block = a.rng_block + (uint32_t)b;
+    const hipError_t e = launch_draft_b1(a1, s);
+    if (e != hipSuccess) return e == hipErrorNotSupported && b > 0 ? hipErrorUnknown : e;
+  }
+  return hipSuccess;
+}
+
 template <class T, int MT>
 static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
   const DevLoop<T> p = make_dev<T>(a);
@@ -1145,6 +1171,13 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
       hipError_t e = launch_draft_b1(a, s);
       if (e != hipErrorNotSupported) return e;
       (void)hipGetLastError();  // the grid cannot be co-resident here: use another schedule
+    } else if (mode != 2 && a.B <= kB1PerBlockMax) {
+      // a few blocks: the single-block loop once per block, back to back on
+      // the stream (at Qwen3-8B shapes ~157 us a block, against ~590 us for the
+      // per-position kernels at B = 2 or 3); the workspace is reused in order
+      hipError_t e = b1_per_block(a, s);
+      if (e != hipErrorNotSupported) return e;
+      (void)hipGetLastError();
     }
   }
   hipError_t e;

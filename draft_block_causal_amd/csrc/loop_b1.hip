@@ -81,6 +81,7 @@ struct Params {
   int sampled;
   uint64_t seed;
   uint32_t offset;
+  uint32_t rng_b;  // the block's index in the sampler's counter
   float *logits, *states;
   int32_t* tokens;
   unsigned int* status;
@@ -417,7 +418,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     // Gumbel noise for this position (read in C, after two barriers)
     if (SAMPLED)
       for (int i = tid; i < nv; i += kThreads)
-        gum[i] = gumbel_from_word(philox_word(p.seed, p.offset, 0u, step, t_lo * 16 + i));
+        gum[i] = gumbel_from_word(philox_word(p.seed, p.offset, p.rng_b, step, t_lo * 16 + i));
 
     if (unit_wg) {
       // ---------- B(i): unit workgroups ----------
@@ -768,6 +769,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.sampled = a.sampled;
   p.seed = a.seed;
   p.offset = a.offset;
+  p.rng_b = a.rng_block;
   p.logits = a.logits;
   p.states = a.states;
   p.tokens = a.tokens;

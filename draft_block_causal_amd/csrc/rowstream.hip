@@ -74,13 +74,27 @@ __global__ void __launch_bounds__(kRowStreamWaves * 64)
     rowstream_gemm_kernel(const typename T::elem* __restrict__ A, int lda, int M,
                           const typename T::elem* __restrict__ W, int ldw, int N,
                           const typename T::elem* __restrict__ bias, float* __restrict__ C, int ldc,
-                          int out_tiles) {
+                          int out_tiles, int G, int groups) {
   using RS = RowStream<KW>;
   using E = typename T::elem;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
-  const int m0 = blockIdx.y * 16;
+  // x: the workgroup's W range (tiles x, x + G, ...); y: its 16-row slice of A.
+  // groups > 1 (a 1-D grid of G * groups): the `groups` slices of one W range
+  // get consecutive numbers on one XCD (workgroups go round-robin over the 8
+  // XCDs), so they stream the same W tiles at about the same time and all but
+  // the first read hit that XCD's L2.
+  int x, y;
+  if (groups > 1) {
+    const int b = blockIdx.x, local = b >> 3;
+    y = local % groups;
+    x = (b & 7) + 8 * (local / groups);
+  } else {
+    x = blockIdx.x;
+    y = blockIdx.y;
+  }
+  const int m0 = y * 16;
   unsigned char* tile = smem + (size_t)wave * RS::kTileLds;
   float* red = reinterpret_cast<float*>(smem + kRowStreamWaves * RS::kTileLds);
   float* obuf = reinterpret_cast<float*>(smem + RS::kFixedLds);  // out_tiles finished 16 x 16 tiles
@@ -94,7 +108,6 @@ __global__ void __launch_bounds__(kRowStreamWaves * 64)
     for (int s = 0; s < KW; ++s) af[s] = live ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
   }
   const int ntiles = (N + 15) >> 4;
-  const int G = gridDim.x;
   const int row_bytes = ldw * (int)sizeof(E);
   // load jj of pass p: row jj * kRowsPerLoad + lrow, chunk lchunk of the pass
   const int lrow = lane / RS::kChunks, lchunk = lane % RS::kChunks;
@@ -165,7 +178,7 @@ __global__ void __launch_bounds__(kRowStreamWaves * 64)
 
   u32x4 w0[KW], w1[KW];
   unsigned b0, b1;
-  int t = blockIdx.x, i = 0;
+  int t = x, i = 0;
   stage(t, w0, b0);
   // The scheduling barriers keep each prefetch ahead of the LDS traffic of
   // the tile in hand; left alone, the compiler sinks the loads below it and
@@ -183,12 +196,12 @@ __global__ void __launch_bounds__(kRowStreamWaves * 64)
     t += G;
     ++i;
   }
-  // the held output tiles, local tile k = global tile blockIdx.x + k * G
+  // the held output tiles, local tile k = global tile x + k * G
   __syncthreads();
   const int held = min(i, out_tiles);
   for (int e = threadIdx.x; e < held * RS::kOutTileFloats; e += kRowStreamWaves * 64) {
     const int k = e >> 8, m = (e >> 4) & 15;
-    const int n = (blockIdx.x + k * G) * 16 + (e & 15);
+    const int n = (x + k * G) * 16 + (e & 15);
     if (m0 + m < M && n < N) C[(size_t)(m0 + m) * ldc + n] = obuf[e];
   }
 }
@@ -200,7 +213,14 @@ static hipError_t rowstream_t(const void* A, int lda, int M, const void* W, int 
   using RS = RowStream<KW>;
   auto kern = bias ? rowstream_gemm_kernel<T, KW, true> : rowstream_gemm_kernel<T, KW, false>;
   const int ntiles = (N + 15) / 16;
-  const int gx = std::min(ntiles, num_cu);
+  // 17 .. 32 rows with a large W: the two 16-row slices share W ranges
+  // through L2 (Qwen3-8B LM head, 32 rows: 226 us against 383 us with one W
+  // read from HBM per slice; four slices sharing a range took 396 us at 64
+  // rows, slower than the tiled kernel); else one W range per compute unit
+  // and slice
+  const int slices = (M + 15) / 16;
+  const bool grouped = slices == 2 && num_cu % (8 * slices) == 0 && ntiles >= num_cu;
+  const int gx = grouped ? num_cu / slices : std::min(ntiles, num_cu);
   // hold every output tile of a workgroup in LDS when it fits
   const int per_wg = (ntiles + gx - 1) / gx;
   const int fit = (int)((kMaxLds - RS::kFixedLds) / (RS::kOutTileFloats * sizeof(float)));
@@ -209,18 +229,20 @@ static hipError_t rowstream_t(const void* A, int lda, int M, const void* W, int 
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  dim3 grid(gx, (M + 15) / 16);
+  const dim3 grid = grouped ? dim3(gx * slices) : dim3(gx, slices);
   hipLaunchKernelGGL(kern, grid, dim3(kRowStreamWaves * 64), lds, s, static_cast<const E*>(A), lda, M,
-                     static_cast<const E*>(W), ldw, N, static_cast<const E*>(bias), C, ldc, out_tiles);
+                     static_cast<const E*>(W), ldw, N, static_cast<const E*>(bias), C, ldc, out_tiles, gx,
+                     grouped ? slices : 1);
   return hipGetLastError();
 }
 
 
 // Returns hipErrorNotSupported unless K * elem_size is 8 * 64 * KW bytes with
 // KW in {4, 8, 16} and every W row starts 16-byte aligned.  Each 16-row slice
-// of A (grid.y) streams all of W, so more than 32 rows are taken only for a
-// small W and a moderate M (N, M <= 4096: the hidden half of the first
-// correction projection at B > 2), whose re-reads come from the caches.
+// of A streams all of W (two slices share it through L2, above), so more than
+// 32 rows are taken only for a small W and a moderate M (N, M <= 4096: the
+// hidden half of the first correction projection at B > 2), whose re-reads
+// come from the caches.
 hipError_t launch_rowstream_gemm(int dtype, const void* A, int lda, int M, const void* W, int ldw, int N, int K,
                                  const void* bias, float* C, int ldc, int num_cu, hipStream_t s) {
   const size_t elem = dtype == 1 ? 2 : 4;

@@ -188,6 +188,15 @@ def test_batched_gru_table(dev, case, monkeypatch):
         _parity(w, dev, check_blocks=[0, w.batch - 1], sampled=True, table=True)
 
 
+@pytest.mark.parametrize("batch,temperature", [(2, 1.0), (3, 0.0)])
+def test_qwen3_8b_few_blocks_gru_table(dev, batch, temperature, monkeypatch):
+    # two or three blocks with the GRU input table: the single-block loop runs
+    # once per block, its sampler keyed by each block's own index
+    monkeypatch.delenv("DOMINO_LOOP", raising=False)
+    w = S.get_workload("qwen3_8b_b1_greedy").with_(batch=batch, temperature=temperature, philox_seed=9)
+    _parity(w, dev, table=True)
+
+
 def test_gru_table_matches_oracle(dev):
     import draft_block_causal_amd as D
 
@@ -269,6 +278,31 @@ def test_lm_head_more_tiles_than_lds(dev):
     ref = O.base_logits(O.as_f64(inp["hidden"][0]), O.as_f64(head_np["lm_head"][cols]))
     err = np.abs(got[:, cols] - ref).max()
     log(f"{w.name}: {cols.size} columns, max err {err:.2e}")
+    assert err <= LOGIT_TOL, f"base logits err {err}"
+
+
+@pytest.mark.parametrize("batch,vocab,d", [(2, 60001, 1024), (2, 460000, 1024), (2, 20011, 4096)])
+def test_lm_head_row_slices_sharing_w(dev, batch, vocab, d):
+    """Base logits for 2 blocks (32 rows) through the row-streaming kernel,
+    whose two 16-row slices take the same W ranges on one XCD: ragged
+    vocabularies, and at V = 460000 more tiles per workgroup than LDS holds
+    (the rest are stored directly).  Every row of the last 600 columns and
+    3000 random columns are checked against the oracle."""
+    import draft_block_causal_amd as D
+
+    w = S.Workload(f"lm_head_rows_b{batch}_v{vocab}", batch, 16, d, vocab, 32, 32, "bf16", True, 0.0)
+    log(f"{w.name}: generating inputs")
+    head_np, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    base = D.domino_base_logits(head, _t(inp["hidden"], dev))
+    torch.cuda.synchronize()
+    got = base.cpu().numpy().reshape(batch * 16, vocab)
+    cols = np.unique(np.concatenate([np.arange(vocab - 600, vocab),
+                                     np.random.default_rng(batch).integers(0, vocab, 3000)]))
+    hid = O.as_f64(inp["hidden"]).reshape(batch * 16, -1)
+    ref = O.base_logits(hid, O.as_f64(head_np["lm_head"][cols]))
+    err = np.abs(got[:, cols] - ref).max()
+    log(f"{w.name}: {cols.size} columns x {batch * 16} rows, max err {err:.2e}")
     assert err <= LOGIT_TOL, f"base logits err {err}"
 
 
