@@ -156,6 +156,59 @@ def sweep(args, w, batches) -> int:
     return 0
 
 
+def library_gemm(args, w) -> int:
+    """The workload's LM-head product C = h W_lm^T through torch's bf16 matmul
+    (hipBLASLt), with float32 and bf16 outputs, timed with HIP events next to
+    domino_base_logits on the same operands. A reference point only: the
+    Domino path never calls it."""
+    import torch
+
+    import domino_synth as S
+    import draft_block_causal_amd as D
+
+    if w.dtype != "bf16":
+        print("bench.py: --library-gemm needs a bf16 workload", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    head_np, inp = S.make_workload(w)
+    lm = S.to_torch(head_np["lm_head"], dev).view(torch.bfloat16)
+    hidden = S.to_torch(inp["hidden"], dev).view(torch.bfloat16)
+    M, V, d = w.batch * w.block, w.vocab, w.d
+    A = hidden.reshape(M, d)
+    z = lambda *shape: torch.zeros(*shape, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    H, r = w.gru_hidden, w.rank
+    head = D.Head({"lm_head": lm, "embed": lm, "w_ih": z(3 * H, d), "w_hh": z(3 * H, H), "w1": z(r, d + H),
+                   "w2": z(V, r)}, block=w.block)
+    base = torch.empty((w.batch, w.block, V), dtype=torch.float32, device=dev)
+    out32 = torch.empty((M, V), dtype=torch.float32, device=dev)
+    out16 = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+
+    def timeit(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    flops = lmhead_flops(w.batch, w.block, d, V)
+    rows = {"domino_base_logits (float32 out)": timeit(lambda: D.domino_base_logits(head, hidden, base)),
+            "torch.matmul bf16 (bf16 out)": timeit(lambda: torch.matmul(A, lm.t(), out=out16))}
+    try:
+        rows["torch.mm bf16 (float32 out)"] = timeit(
+            lambda: torch.mm(A, lm.t(), out_dtype=torch.float32, out=out32))
+    except (TypeError, RuntimeError) as ex:  # older torch: no out_dtype
+        print(f"bench.py: float32-output matmul unavailable: {ex}", file=sys.stderr)
+    res = {name: {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS} for name, ms in rows.items()}
+    print(json.dumps({"workload": w.name, "M": M, "N": V, "K": d, "steps": args.steps, "results": res}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +223,9 @@ def main() -> int:
                     help="concurrency sweep: the workload's head at each batch size in the list (e.g. "
                          "1,2,4,8,16,32,64,128); prints one JSON line with a row per batch size instead of the "
                          "benchmark line")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="instead of the benchmark, time the LM-head product of the workload through torch's bf16 "
+                         "matmul (hipBLASLt on ROCm) next to domino_base_logits, as a reference for the kernel")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -200,6 +256,8 @@ def main() -> int:
     w = S.get_workload(args.workload)
     if args.sweep:
         return sweep(args, w, [int(x) for x in args.sweep.split(",") if x.strip()])
+    if args.library_gemm:
+        return library_gemm(args, w)
     head_np, inp = S.make_workload(w)
     B, K, V, d, H = w.batch, w.block, w.vocab, w.d, w.gru_hidden
     tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}
