@@ -68,6 +68,10 @@ __all__ = [
     "pick_token",
     "draft_block",
     "base_draft",
+    "curriculum_lambda",
+    "position_weights",
+    "cross_entropy",
+    "curriculum_loss",
     "accept_len",
     "top2_margin",
     "uniform01",
@@ -292,6 +296,69 @@ def base_draft(base, temperature: float = 0.0, seed: int = 0, offset: int = 0) -
         for i in range(K):
             tokens[b, i] = pick_token(sampling_scores(base[b, i], temperature, seed, offset, b, i))
     return tokens
+
+
+def curriculum_lambda(step: int, total_steps: int) -> float:
+    """λ_t of the base-anchored curriculum: 1 at the first training step,
+    falling linearly to 0 at total_steps and staying there ([notes] §二.2(2))."""
+    if total_steps <= 0:
+        return 0.0
+    return max(0.0, 1.0 - step / total_steps)
+
+
+def position_weights(K: int, gamma: float) -> np.ndarray:
+    """w_i = gamma^i: the per-position weights that decay exponentially along
+    the block, so the early positions, whose acceptance gates the whole block,
+    count most ([notes] §二.2(2)).  gamma in (0, 1]; the pages give no value."""
+    return np.power(float(gamma), np.arange(K, dtype=np.float64))
+
+
+def cross_entropy(logits, target: int) -> float:
+    """-log softmax(logits)[target] = logsumexp(logits) - logits[target]."""
+    x = np.asarray(logits, dtype=np.float64)
+    m = x.max()
+    return float(m + np.log(np.exp(x - m).sum()) - x[target])
+
+
+def curriculum_loss(base, final, targets, lam: float, gamma: float):
+    """The base-anchored curriculum loss ([notes] §二.2(2)):
+
+        loss = (1 - λ) L_final + λ L_base,
+
+    with L_x the cross-entropy of logits x against the reference token at
+    each drafted position, weighted by w_i = gamma^i, averaged over positions
+    with those weights (Σ_i w_i CE_i / Σ_i w_i) and then over blocks.  The
+    final logits are the teacher-forced ones (the GRU reads the reference
+    tokens, [notes] §二.2(1)), so targets[b, i] is both the label of position
+    i and the GRU input of position i + 1.
+
+    base, final [B, K, V]; targets [B, K].  Returns dict(loss, ce_base [B, K],
+    ce_final [B, K], grad_base, grad_final): the gradients of loss with
+    respect to base and final, [B, K, V] each.
+    """
+    base = np.asarray(base, dtype=np.float64)
+    final = np.asarray(final, dtype=np.float64)
+    B, K, V = base.shape
+    w = position_weights(K, gamma)
+    wsum = w.sum()
+    ce_b = np.zeros((B, K))
+    ce_f = np.zeros((B, K))
+    g_b = np.zeros((B, K, V))
+    g_f = np.zeros((B, K, V))
+    loss = 0.0
+    for b in range(B):
+        for i in range(K):
+            y = int(targets[b, i])
+            ce_b[b, i] = cross_entropy(base[b, i], y)
+            ce_f[b, i] = cross_entropy(final[b, i], y)
+            loss += w[i] * ((1.0 - lam) * ce_f[b, i] + lam * ce_b[b, i])
+            # d CE / d logits = softmax(logits) - onehot(y)
+            for grad, x, coef in ((g_f, final[b, i], (1.0 - lam)), (g_b, base[b, i], lam)):
+                p = np.exp(x - x.max())
+                p /= p.sum()
+                p[y] -= 1.0
+                grad[b, i] = coef * w[i] / (wsum * B) * p
+    return {"loss": loss / (wsum * B), "ce_base": ce_b, "ce_final": ce_f, "grad_base": g_b, "grad_final": g_f}
 
 
 def accept_len(draft, target) -> np.ndarray:

@@ -37,6 +37,11 @@ MUTATIONS = {
                                    "g = gumbel_noise(seed, offset, b, n, np.arange(V))"),
     "base_draft_position_keys_swapped": ("sampling_scores(base[b, i], temperature, seed, offset, b, i)",
                                          "sampling_scores(base[b, i], temperature, seed, offset, i, b)"),
+    "curriculum_lambda_swapped": ("loss += w[i] * ((1.0 - lam) * ce_f[b, i] + lam * ce_b[b, i])",
+                                  "loss += w[i] * (lam * ce_f[b, i] + (1.0 - lam) * ce_b[b, i])"),
+    "position_weights_growing": ("return np.power(float(gamma), np.arange(K, dtype=np.float64))",
+                                 "return np.power(float(gamma), -np.arange(K, dtype=np.float64))"),
+    "gradient_without_onehot": ("p[y] -= 1.0", "p[y] -= 0.0"),
     "base_logits_transposed_operand": ("return as_f64(hidden) @ as_f64(lm_head).T",
                                        "return (as_f64(lm_head) @ as_f64(hidden).swapaxes(-1, -2)).swapaxes(-1, -2)[..., ::-1]"),
 }

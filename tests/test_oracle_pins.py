@@ -205,6 +205,73 @@ def test_base_draft_is_draft_block_without_correction():
         np.testing.assert_array_equal(O.base_draft(base, T, seed, offset), want)
 
 
+# ------------------------------------------------------- curriculum loss
+def test_curriculum_lambda_anneals_linearly():
+    assert O.curriculum_lambda(0, 1000) == 1.0
+    assert O.curriculum_lambda(250, 1000) == 0.75
+    assert O.curriculum_lambda(1000, 1000) == 0.0
+    assert O.curriculum_lambda(5000, 1000) == 0.0
+
+
+def test_cross_entropy_matches_torch_and_closed_form():
+    rng = np.random.default_rng(21)
+    x = rng.normal(0, 3, size=(6, 37))
+    y = rng.integers(0, 37, 6)
+    want = torch.nn.functional.cross_entropy(torch.from_numpy(x), torch.from_numpy(y), reduction="none").numpy()
+    got = np.array([O.cross_entropy(x[j], y[j]) for j in range(6)])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert abs(O.cross_entropy(np.full(1000, 4.25), 17) - math.log(1000)) < 1e-12  # uniform: log V
+
+
+def test_curriculum_loss_limits_match_torch_mean_cross_entropy():
+    # gamma = 1 (equal weights): lambda = 0 is the mean CE of the final logits
+    # over every (block, position), lambda = 1 that of the base logits
+    rng = np.random.default_rng(22)
+    B, K, V = 3, 5, 41
+    base, final = rng.normal(0, 2, (B, K, V)), rng.normal(0, 2, (B, K, V))
+    y = rng.integers(0, V, (B, K))
+    ce = lambda L: torch.nn.functional.cross_entropy(torch.from_numpy(L.reshape(-1, V)),  # noqa: E731
+                                                     torch.from_numpy(y.reshape(-1))).item()
+    assert abs(O.curriculum_loss(base, final, y, 0.0, 1.0)["loss"] - ce(final)) < 1e-12
+    assert abs(O.curriculum_loss(base, final, y, 1.0, 1.0)["loss"] - ce(base)) < 1e-12
+
+
+def test_curriculum_loss_position_weights_hand_case():
+    # one block of two positions, V = 2, gamma = 1/2, lambda = 1/4:
+    # weights 1, 1/2 (sum 3/2); CE of [0, 0] against 0 is ln 2, CE of [ln 3, 0]
+    # against 1 is ln 4
+    base = np.array([[[0.0, 0.0], [math.log(3.0), 0.0]]])
+    final = np.array([[[math.log(3.0), 0.0], [0.0, 0.0]]])
+    y = np.array([[0, 1]])
+    out = O.curriculum_loss(base, final, y, 0.25, 0.5)
+    ce_base = [math.log(2.0), math.log(4.0)]
+    ce_final = [math.log(4.0 / 3.0), math.log(2.0)]
+    want = (1.0 * (0.75 * ce_final[0] + 0.25 * ce_base[0]) + 0.5 * (0.75 * ce_final[1] + 0.25 * ce_base[1])) / 1.5
+    assert abs(out["loss"] - want) < 1e-12
+    np.testing.assert_allclose(out["ce_base"][0], ce_base, rtol=1e-12)
+    np.testing.assert_allclose(out["ce_final"][0], ce_final, rtol=1e-12)
+
+
+def test_curriculum_loss_gradients_match_autograd():
+    rng = np.random.default_rng(23)
+    B, K, V, lam, gamma = 2, 4, 19, 0.3, 0.7
+    base, final = rng.normal(0, 2, (B, K, V)), rng.normal(0, 2, (B, K, V))
+    y = rng.integers(0, V, (B, K))
+    out = O.curriculum_loss(base, final, y, lam, gamma)
+    tb = torch.tensor(base, requires_grad=True)
+    tf = torch.tensor(final, requires_grad=True)
+    w = torch.tensor([gamma ** i for i in range(K)], dtype=torch.float64)
+    ty = torch.from_numpy(y)
+    ce_b = torch.nn.functional.cross_entropy(tb.permute(0, 2, 1), ty, reduction="none")  # [B, K]
+    ce_f = torch.nn.functional.cross_entropy(tf.permute(0, 2, 1), ty, reduction="none")
+    loss = (((1 - lam) * ce_f + lam * ce_b) * w).sum() / (w.sum() * B)
+    loss.backward()
+    assert abs(out["loss"] - loss.item()) < 1e-12
+    np.testing.assert_allclose(out["grad_base"], tb.grad.numpy(), atol=1e-14)
+    np.testing.assert_allclose(out["grad_final"], tf.grad.numpy(), atol=1e-14)
+    np.testing.assert_allclose(out["grad_final"].sum(-1), 0.0, atol=1e-14)  # softmax - onehot sums to 0
+
+
 # ------------------------------------------------------------- loop wiring
 def _torch_chain_logits(head, hidden_b, x_t, seq):
     """Independent re-derivation with torch modules: logits of every position when
