@@ -46,6 +46,8 @@ EXPORTED = [
     "domino_verify_workspace_size",
     "domino_base_draft",
     "domino_base_draft_workspace_size",
+    "domino_curriculum_loss",
+    "domino_curriculum_loss_workspace_size",
     "domino_debug_philox",
 ]
 
@@ -107,6 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_verify_workspace_size": (SZ, [I32, I32, I32]),
         "domino_base_draft": (ctypes.c_int, [I32, I32, I32, P, F, U64, U32, P, P, SZ, P]),
         "domino_base_draft_workspace_size": (SZ, [I32, I32]),
+        "domino_curriculum_loss": (ctypes.c_int, [I32, I32, I32, P, P, P, F, F, P, P, P, P, P, P, SZ, P]),
+        "domino_curriculum_loss_workspace_size": (SZ, [I32, I32, I32]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -335,6 +339,39 @@ def domino_base_draft(base_logits: torch.Tensor, temperature: float = 0.0, seed:
         B, K, V, _ptr(base_logits), float(temperature), int(seed), int(offset), _ptr(tokens), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return tokens
+
+
+def domino_curriculum_loss(base_logits: torch.Tensor, final_logits: torch.Tensor, targets: torch.Tensor,
+                           lam: float, gamma: float, loss: Optional[torch.Tensor] = None,
+                           ce_base: Optional[torch.Tensor] = None, ce_final: Optional[torch.Tensor] = None,
+                           grad_base: Optional[torch.Tensor] = None, grad_final: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The base-anchored curriculum loss (a one-element device tensor); the optional
+    per-position cross-entropies and logit gradients are written when given."""
+    if base_logits.dim() != 3:
+        raise ValueError("base_logits must be [batch, block, vocab]")
+    B, K, V = base_logits.shape
+    dev = base_logits.device
+    _need(base_logits, "base_logits", torch.float32, (B, K, V), dev)
+    _need(final_logits, "final_logits", torch.float32, (B, K, V), dev)
+    _need(targets, "targets", torch.int32, (B, K), dev)
+    if loss is None:
+        loss = torch.zeros((1,), dtype=torch.float32, device=dev)
+    _need(loss, "loss", torch.float32, (1,), dev)
+    for t, name in ((ce_base, "ce_base"), (ce_final, "ce_final")):
+        if t is not None:
+            _need(t, name, torch.float32, (B, K), dev)
+    for t, name in ((grad_base, "grad_base"), (grad_final, "grad_final")):
+        if t is not None:
+            _need(t, name, torch.float32, (B, K, V), dev)
+    need = int(load_library().domino_curriculum_loss_workspace_size(B, K, V)) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("domino_curriculum_loss", load_library().domino_curriculum_loss(
+        B, K, V, _ptr(base_logits), _ptr(final_logits), _ptr(targets), float(lam), float(gamma), _ptr(loss),
+        _ptr(ce_base), _ptr(ce_final), _ptr(grad_base), _ptr(grad_final), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return loss
 
 
 def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,

@@ -148,6 +148,26 @@ extern "C" int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab
                                                   static_cast<hipStream_t>(stream)));
 }
 
+extern "C" size_t domino_curriculum_loss_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
+  if (batch < 1 || batch > domino::kMaxLossBatch || block < 1 || block > domino::kMaxLossBlock || vocab < 1 ||
+      vocab > domino::kMaxVocab)
+    return 0;
+  return domino::loss_plan(batch, block, vocab).total;
+}
+
+extern "C" int domino_curriculum_loss(int32_t batch, int32_t block, int32_t vocab, const float* base_logits,
+                                      const float* final_logits, const int32_t* targets, float lambda, float gamma,
+                                      float* loss, float* ce_base, float* ce_final, float* grad_base,
+                                      float* grad_final, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = domino::check_loss_args(batch, block, vocab, base_logits, final_logits, targets, lambda, gamma, loss,
+                                   ce_base, ce_final, grad_base, grad_final, workspace, workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  return hip_status(domino::launch_curriculum_loss(batch, block, vocab, base_logits, final_logits, targets, lambda,
+                                                   gamma, loss, ce_base, ce_final, grad_base, grad_final,
+                                                   domino::loss_plan(batch, block, vocab), workspace,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 extern "C" size_t domino_base_draft_workspace_size(int32_t batch, int32_t block) {
   return domino::base_draft_workspace_bytes(batch, block);
 }

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "loss_plan.h"
 #include "psplit.h"
 #include "verify_plan.h"
 
@@ -95,6 +96,14 @@ hipError_t launch_verify_sampled(int B, int K, int V, const float* target, const
 // 64-bit keys.
 hipError_t launch_base_draft(int B, int K, int V, const float* base, float temperature, uint64_t seed,
                              uint32_t offset, int32_t* tokens, void* workspace, hipStream_t s);
+
+// Base-anchored curriculum loss (loss.hip) over [B][K][V] float32 base and
+// final logits with targets [B][K]; ce_*, grad_* may be null; the workspace
+// follows loss_plan(B, K, V).
+hipError_t launch_curriculum_loss(int B, int K, int V, const float* base, const float* final_,
+                                  const int32_t* targets, float lam, float gamma, float* loss, float* ce_base,
+                                  float* ce_final, float* grad_base, float* grad_final, const LossPlan& plan,
+                                  void* workspace, hipStream_t s);
 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s);

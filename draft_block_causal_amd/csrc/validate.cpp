@@ -133,6 +133,25 @@ int check_base_draft_args(int32_t batch, int32_t block, int32_t vocab, const flo
   return DOMINO_OK;
 }
 
+int check_loss_args(int32_t batch, int32_t block, int32_t vocab, const float* base_logits, const float* final_logits,
+                    const int32_t* targets, float lambda, float gamma, const float* loss, const float* ce_base,
+                    const float* ce_final, const float* grad_base, const float* grad_final, const void* workspace,
+                    size_t workspace_bytes) {
+  if (batch < 0 || batch > kMaxLossBatch || block < 1 || block > kMaxLossBlock || vocab < 1 || vocab > kMaxVocab)
+    return DOMINO_ERR_SHAPE;
+  if (!std::isfinite(lambda) || lambda < 0.f || lambda > 1.f) return DOMINO_ERR_ARG;
+  if (!std::isfinite(gamma) || !(gamma > 0.f) || gamma > 1.f) return DOMINO_ERR_ARG;
+  if (batch == 0) return DOMINO_OK;
+  if (!base_logits || !final_logits || !targets || !loss) return DOMINO_ERR_NULL;
+  for (const void* q : {(const void*)base_logits, (const void*)final_logits, (const void*)loss, (const void*)ce_base,
+                        (const void*)ce_final, (const void*)grad_base, (const void*)grad_final})
+    if (reinterpret_cast<uintptr_t>(q) & 3u) return DOMINO_ERR_ALIGN;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < loss_plan(batch, block, vocab).total)
+    return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/domino.h"
+#include "loss_plan.h"
 #include "verify_plan.h"
 
 namespace domino {
@@ -36,6 +37,10 @@ int check_accept_args(int32_t batch, int32_t block, const int32_t* draft, const 
 int check_base_draft_args(int32_t batch, int32_t block, int32_t vocab, const float* base_logits, float temperature,
                           const int32_t* tokens, const void* workspace, size_t workspace_bytes);
 size_t base_draft_workspace_bytes(int32_t batch, int32_t block);
+int check_loss_args(int32_t batch, int32_t block, int32_t vocab, const float* base_logits, const float* final_logits,
+                    const int32_t* targets, float lambda, float gamma, const float* loss, const float* ce_base,
+                    const float* ce_final, const float* grad_base, const float* grad_final, const void* workspace,
+                    size_t workspace_bytes);
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes);

@@ -243,6 +243,41 @@ int domino_base_draft(int32_t batch, int32_t block, int32_t vocab, const float *
 size_t domino_base_draft_workspace_size(int32_t batch, int32_t block);
 
 /*
+ * Base-anchored curriculum loss of the head's teacher-forced training
+ * ([notes] §二.2): with CE_x[b, i] = logsumexp(x[b, i, :]) - x[b, i, targets[b, i]]
+ * for x = base_logits and final_logits (the final logits of a teacher-forced
+ * domino_draft_block call, whose GRU read the same reference tokens),
+ *   loss = Σ_b Σ_i w_i ((1 - lambda) CE_final[b, i] + lambda CE_base[b, i]) / (B Σ_i w_i),
+ *   w_i = gamma^i (weights decaying along the block).
+ * lambda is the curriculum weight λ_t, annealed by the caller from 1 to 0 over
+ * training; the pages fix neither the decay rate nor the normalisation: gamma
+ * is a parameter and the weighted mean above is this library's reading.
+ * Optional outputs: ce_base, ce_final [batch, block] (the per-position
+ * cross-entropies) and grad_base, grad_final [batch, block, vocab], the
+ * gradients of loss with respect to each logit tensor,
+ *   coef (softmax(x[b, i]) - onehot(targets[b, i])),
+ *   coef = lambda w_i / (B Σw) for base, (1 - lambda) w_i / (B Σw) for final.
+ * A gradient may be written over its own logits (grad_final == final_logits).
+ *
+ * base_logits, final_logits [batch, block, vocab] float32 (4-byte aligned)
+ * targets     [batch, block] int32; ids outside [0, vocab) are clamped
+ * loss        one float32 in device memory (output)
+ * lambda in [0, 1], gamma in (0, 1], both finite (else DOMINO_ERR_ARG)
+ * workspace   device scratch of at least domino_curriculum_loss_workspace_size()
+ *             bytes, 256-byte aligned; its contents are overwritten.
+ * batch in 0 … 2^20 (0 is a no-op that leaves loss untouched), block in
+ * 1 … 1024, vocab in 1 … 2^24 - 1.  Arithmetic: float32; the loss is summed
+ * in a fixed order, so repeated calls give the same bits.
+ */
+int domino_curriculum_loss(int32_t batch, int32_t block, int32_t vocab, const float *base_logits,
+                           const float *final_logits, const int32_t *targets, float lambda, float gamma,
+                           float *loss, float *ce_base, float *ce_final, float *grad_base, float *grad_final,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes domino_curriculum_loss needs (0 for sizes out of range). */
+size_t domino_curriculum_loss_workspace_size(int32_t batch, int32_t block, int32_t vocab);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

@@ -230,3 +230,41 @@ def test_base_draft_validation_and_workspace(lib):
     assert call(w=0x100010) == E_WS
     assert call(wb=ws - 1) == E_WS
     assert call(B=0, L=None, y=None, w=None, wb=0) == OK
+
+
+def test_curriculum_loss_validation_and_workspace(lib):
+    ws = lib.domino_curriculum_loss_workspace_size(2, 16, 151936)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.domino_curriculum_loss_workspace_size(0, 16, 100) == 0
+    assert lib.domino_curriculum_loss_workspace_size(1, 1025, 100) == 0
+    assert lib.domino_curriculum_loss_workspace_size(1, 16, 1 << 24) == 0
+    args = dict(B=2, K=16, V=151936, b=0x10000, f=0x20000, y=0x30000, lam=0.5, g=0.8, loss=0x40000, cb=None,
+                cf=None, gb=None, gf=None, w=0x100000, wb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.domino_curriculum_loss(a["B"], a["K"], a["V"], a["b"], a["f"], a["y"], a["lam"], a["g"],
+                                          a["loss"], a["cb"], a["cf"], a["gb"], a["gf"], a["w"], a["wb"], None)
+
+    assert call() == E_HIP  # valid arguments, no GPU here
+    assert call(cb=0x50000, cf=0x60000, gb=0x70000, gf=0x20000) == E_HIP  # gradient over its own logits
+    assert call(B=-1) == E_SHAPE
+    assert call(K=0) == E_SHAPE
+    assert call(K=1025) == E_SHAPE
+    assert call(V=0) == E_SHAPE
+    assert call(lam=-0.1) == E_ARG
+    assert call(lam=1.5) == E_ARG
+    assert call(lam=float("nan")) == E_ARG
+    assert call(g=0.0) == E_ARG
+    assert call(g=1.01) == E_ARG
+    assert call(g=float("inf")) == E_ARG
+    assert call(b=None) == E_NULL
+    assert call(f=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(loss=None) == E_NULL
+    assert call(f=0x20002) == E_ALIGN
+    assert call(gb=0x70001) == E_ALIGN
+    assert call(w=None) == E_WS
+    assert call(w=0x100010) == E_WS
+    assert call(wb=ws - 1) == E_WS
+    assert call(B=0, b=None, f=None, y=None, loss=None, w=None, wb=0) == OK
