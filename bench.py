@@ -209,6 +209,95 @@ def library_gemm(args, w) -> int:
     return 0
 
 
+def next_rows(args, w) -> int:
+    """Timings (HIP events, mean over --steps after --warmup) of the calls beyond
+    the draft path, at the workload's shapes, with the HBM rate of each
+    bandwidth-bound kernel group against the 8 TB/s peak:
+      train_forward: base logits + teacher-forced draft block (final logits out)
+                     + curriculum loss with both logit gradients written in place;
+      verify:        sampled-draft verification on synthetic target / draft logits;
+      head_off:      base logits + base-only drafting, beside base logits + draft block."""
+    import torch
+
+    import domino_synth as S
+    import draft_block_causal_amd as D
+
+    dev = torch.device("cuda:0")
+    head_np, inp = S.make_workload(w)
+    tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}
+    if w.tied:
+        tensors["embed"] = tensors["lm_head"]
+    head = D.Head(tensors, block=w.block)
+    if not args.no_table:
+        D.domino_prepare_gru_table(head)
+    B, K, V = w.batch, w.block, w.vocab
+    hidden = S.to_torch(inp["hidden"], dev)
+    x_t = S.to_torch(inp["x_t"], dev)
+    gold = S.to_torch(S.make_tokens((B, K), V, seed=31), dev)
+    base = torch.empty((B, K, V), dtype=torch.float32, device=dev)
+    final = torch.empty_like(base)
+    tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(D.domino_workspace_size(head, B), dtype=torch.uint8, device=dev)
+    lws = torch.empty(max(1, int(D.load_library().domino_curriculum_loss_workspace_size(B, K, V))),
+                      dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(1, D.domino_base_draft_workspace_size(B, K)), dtype=torch.uint8, device=dev)
+    loss = torch.zeros((1,), dtype=torch.float32, device=dev)
+
+    def timed(stages):
+        """mean ms of each stage (list of callables run in order) over the timed steps"""
+        n = len(stages)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+        for _ in range(args.warmup):
+            for f in stages:
+                f()
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            for j, f in enumerate(stages):
+                f()
+                e[j + 1].record()
+        torch.cuda.synchronize()
+        return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(n)]
+
+    lm = lambda: D.domino_base_logits(head, hidden, base)  # noqa: E731
+    tf = lambda: D.domino_draft_block(head, hidden, base, x_t, teacher=gold, temperature=w.temperature,  # noqa: E731
+                                      seed=w.philox_seed, tokens=tokens, logits=final, workspace=ws)
+    cl = lambda: D.domino_curriculum_loss(base, final, gold, 0.5, 0.9, loss=loss, grad_base=base,  # noqa: E731
+                                          grad_final=final, workspace=lws)
+    t_lm, t_tf, t_cl = timed([lm, tf, cl])
+    loss_bytes = 2 * B * K * V * 4 * 3  # pass 1 reads both tensors; the gradient pass reads and writes both
+    out = {"train_forward": {"base_logits_ms": t_lm, "teacher_forced_draft_ms": t_tf, "curriculum_loss_ms": t_cl,
+                             "blocks_per_s": B / ((t_lm + t_tf + t_cl) * 1e-3),
+                             "loss_kernels_gb_s": loss_bytes / (t_cl * 1e-3) / 1e9,
+                             "loss_kernels_hbm_frac": loss_bytes / (t_cl * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "loss_bytes": loss_bytes}}
+
+    vt, vd, vy = S.make_verify_inputs(B, K, V, 0.2, seed=2)
+    tt, dd, yy = (torch.from_numpy(a).to(dev) for a in (vt, vd, vy))
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    vws = torch.empty(max(1, D.domino_verify_workspace_size(B, K, V)), dtype=torch.uint8, device=dev)
+    (t_v,) = timed([lambda: D.domino_verify_sampled(tt, dd, yy, 1.0, seed=0, offset=40, accept=acc, next_token=nxt,
+                                                    workspace=vws)])
+    v_bytes = B * (2 * K + 1) * V * 4  # the normaliser pass; the draw reads at most 2 B V more
+    out["verify"] = {"ms": t_v, "blocks_per_s": B / (t_v * 1e-3), "gb_s": v_bytes / (t_v * 1e-3) / 1e9,
+                     "hbm_frac": v_bytes / (t_v * 1e-3) / 1e9 / HBM_PEAK_GBS, "bytes": v_bytes}
+    del tt, dd, yy, vws
+
+    fr = lambda: D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature,  # noqa: E731
+                                      seed=w.philox_seed, tokens=tokens, workspace=ws)
+    bd = lambda: D.domino_base_draft(base, w.temperature, seed=w.philox_seed, tokens=tokens, workspace=bws)  # noqa: E731
+    t_lm2, t_fr, t_bd = timed([lm, fr, bd])
+    bd_bytes = B * K * V * 4
+    out["head_off"] = {"base_logits_ms": t_lm2, "head_on_draft_ms": t_fr, "head_off_draft_ms": t_bd,
+                       "head_on_blocks_per_s": B / ((t_lm2 + t_fr) * 1e-3),
+                       "head_off_blocks_per_s": B / ((t_lm2 + t_bd) * 1e-3),
+                       "base_draft_gb_s": bd_bytes / (t_bd * 1e-3) / 1e9}
+    print(json.dumps({"workload": w.name, "batch": B, "block": K, "vocab": V, "steps": args.steps, **out}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +315,10 @@ def main() -> int:
     ap.add_argument("--library-gemm", action="store_true",
                     help="instead of the benchmark, time the LM-head product of the workload through torch's bf16 "
                          "matmul (hipBLASLt on ROCm) next to domino_base_logits, as a reference for the kernel")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="instead of the benchmark, time the rows beyond the draft path at the workload's shapes: "
+                         "the teacher-forced training forward with the curriculum loss and its logit gradients, "
+                         "sampled-draft verification, and head-off drafting beside the full head")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -258,6 +351,8 @@ def main() -> int:
         return sweep(args, w, [int(x) for x in args.sweep.split(",") if x.strip()])
     if args.library_gemm:
         return library_gemm(args, w)
+    if args.next_rows:
+        return next_rows(args, w)
     head_np, inp = S.make_workload(w)
     B, K, V, d, H = w.batch, w.block, w.vocab, w.d, w.gru_hidden
     tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}

@@ -31,7 +31,8 @@ __global__ void __launch_bounds__(kLseThreads) loss_stats_kernel(int V, const fl
                                                                  float4* __restrict__ stats) {
   __shared__ LsePart red[kLseWaves];
   const int row = blockIdx.x, s = blockIdx.y, S = gridDim.y;
-  const long v0 = (long)V * s / S, v1 = (long)V * (s + 1) / S;
+  long v0, v1;
+  slice_bounds(V, s, S, v0, v1);
   const LsePart b = block_lse(base + (size_t)row * V, v0, v1, 1.f, red);
   const LsePart f = block_lse(final_ + (size_t)row * V, v0, v1, 1.f, red);
   if (threadIdx.x == 0) stats[(size_t)row * S + s] = float4{b.m, b.s, f.m, f.s};
@@ -90,13 +91,39 @@ __global__ void __launch_bounds__(kLseThreads) loss_grad_kernel(int K, int V, co
                                                                 const float2* __restrict__ lse, float* grad_base,
                                                                 float* grad_final) {
   const int row = blockIdx.x, s = blockIdx.y, S = gridDim.y;
-  const long v0 = (long)V * s / S, v1 = (long)V * (s + 1) / S;
+  long v0, v1;
+  slice_bounds(V, s, S, v0, v1);
   const int y = clamp_token(targets[row], V);
   const float w = powf(gamma, (float)(row % K)) * scale;
   const float cb = lam * w, cf = (1.f - lam) * w;
   const float2 l = lse[row];
   const size_t o = (size_t)row * V;
-  for (long v = v0 + threadIdx.x; v < v1; v += kLseThreads) {
+  long vs = v0;
+  // 16 B per lane where every tensor's row slice is 16-byte aligned
+  const uintptr_t al = reinterpret_cast<uintptr_t>(base + o + v0) | reinterpret_cast<uintptr_t>(final_ + o + v0) |
+                       reinterpret_cast<uintptr_t>(grad_base ? grad_base + o + v0 : base + o + v0) |
+                       reinterpret_cast<uintptr_t>(grad_final ? grad_final + o + v0 : final_ + o + v0);
+  if ((al & 15u) == 0) {
+    const long n4 = (v1 - v0) / 4;
+    for (long q = threadIdx.x; q < n4; q += kLseThreads) {
+      const long v = v0 + 4 * q;
+      const float h0 = v == y, h1 = v + 1 == y, h2 = v + 2 == y, h3 = v + 3 == y;
+      if (grad_base) {
+        const float4 x = *reinterpret_cast<const float4*>(base + o + v);
+        *reinterpret_cast<float4*>(grad_base + o + v) =
+            float4{cb * (expf(x.x - l.x) - h0), cb * (expf(x.y - l.x) - h1), cb * (expf(x.z - l.x) - h2),
+                   cb * (expf(x.w - l.x) - h3)};
+      }
+      if (grad_final) {
+        const float4 x = *reinterpret_cast<const float4*>(final_ + o + v);
+        *reinterpret_cast<float4*>(grad_final + o + v) =
+            float4{cf * (expf(x.x - l.y) - h0), cf * (expf(x.y - l.y) - h1), cf * (expf(x.z - l.y) - h2),
+                   cf * (expf(x.w - l.y) - h3)};
+      }
+    }
+    vs = v0 + 4 * n4;
+  }
+  for (long v = vs + threadIdx.x; v < v1; v += kLseThreads) {
     const float hot = v == y ? 1.f : 0.f;
     if (grad_base) {
       const float x = base[o + v];

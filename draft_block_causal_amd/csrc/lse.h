@@ -32,12 +32,46 @@ __device__ __forceinline__ LsePart wave_lse(LsePart p) {
   return p;
 }
 
+// Entries [v0, v1) of slice s of S over a row of V: boundaries fall on
+// multiples of 4 (whole 16-byte groups), the last slice ends at V.
+__device__ __forceinline__ void slice_bounds(long V, int s, int S, long& v0, long& v1) {
+  v0 = s == 0 ? 0 : (V * s / S) & ~3L;
+  v1 = s == S - 1 ? V : (V * (s + 1) / S) & ~3L;
+}
+
+// Folds four values into a running pair: one rescale when their maximum
+// exceeds the running one, then four exponentials.
+__device__ __forceinline__ LsePart lse_add4(LsePart p, float x0, float x1, float x2, float x3) {
+  const float m4 = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+  if (m4 > p.m) {
+    p.s *= expf(p.m - m4);  // (exp(-inf) = 0 for the empty pair)
+    p.m = m4;
+  }
+  p.s += expf(x0 - p.m) + expf(x1 - p.m) + expf(x2 - p.m) + expf(x3 - p.m);
+  return p;
+}
+
 // Partial log-sum-exp of row[v0 .. v1) * inv_t over a workgroup of
 // kLseThreads threads; thread 0 holds the result.  red: kLseWaves entries of
-// LDS.  Every thread of the workgroup must call it.
+// LDS.  Every thread of the workgroup must call it.  When the row and v0 are
+// 16-byte aligned the body reads 16 B per lane, two loads in flight per
+// thread; the (up to 3 + 2 * 4 * kLseThreads) entries past the last full
+// pair of loads are taken one by one.
 __device__ inline LsePart block_lse(const float* __restrict__ row, long v0, long v1, float inv_t, LsePart* red) {
   LsePart p{-INFINITY, 0.f};
-  for (long v = v0 + threadIdx.x; v < v1; v += kLseThreads) {
+  long v = v0;
+  if (((reinterpret_cast<uintptr_t>(row + v0)) & 15u) == 0) {
+    constexpr long kStep = 8L * kLseThreads;  // entries per workgroup iteration
+    const long nv = (v1 - v0) / kStep * kStep;
+    const float4* r4 = reinterpret_cast<const float4*>(row + v0);
+    for (long q = threadIdx.x; q < nv / 4; q += 2L * kLseThreads) {
+      const float4 a = r4[q], b = r4[q + kLseThreads];
+      p = lse_add4(p, a.x * inv_t, a.y * inv_t, a.z * inv_t, a.w * inv_t);
+      p = lse_add4(p, b.x * inv_t, b.y * inv_t, b.z * inv_t, b.w * inv_t);
+    }
+    v = v0 + nv;
+  }
+  for (v += threadIdx.x; v < v1; v += kLseThreads) {
     const float x = row[v] * inv_t;
     if (x > p.m) {
       p.s = p.s * expf(p.m - x) + 1.f;

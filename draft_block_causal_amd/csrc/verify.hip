@@ -34,7 +34,8 @@ __global__ void __launch_bounds__(kVThreads) verify_stats_kernel(int K, int V, c
   __shared__ LsePart red[kVWaves];
   const int row = blockIdx.x, s = blockIdx.y, S = gridDim.y;
   const int b = row / (K + 1), i = row - b * (K + 1);
-  const long v0 = (long)V * s / S, v1 = (long)V * (s + 1) / S;
+  long v0, v1;
+  slice_bounds(V, s, S, v0, v1);
   if (s == 0 && i == 0 && threadIdx.x == 0) keys[b] = 0ull;
   const LsePart t = block_lse(target + (size_t)row * V, v0, v1, inv_t, red);
   LsePart d{-INFINITY, 0.f};
