@@ -405,6 +405,33 @@ def test_determinism_qwen3_8b_b1(dev):
         np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("batch,table", [(2, True), (32, True), (32, False)])
+def test_determinism_batched_schedules(dev, batch, table, monkeypatch):
+    # the per-block single-block loop (2 blocks, GRU input table) and the
+    # per-position kernels (32 blocks, sampled): two calls give the same bits
+    import draft_block_causal_amd as D
+
+    monkeypatch.delenv("DOMINO_LOOP", raising=False)
+    w = S.get_workload("qwen3_8b_b32_t1").with_(batch=batch)
+    _, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    if table:
+        D.domino_prepare_gru_table(head)
+    try:
+        hidden, x_t = _t(inp["hidden"], dev), _t(inp["x_t"], dev)
+        runs = []
+        for _ in range(2):
+            base = D.domino_base_logits(head, hidden)
+            lg = torch.empty((batch, w.block, w.vocab), device=dev)
+            st = torch.empty((batch, w.block, w.gru_hidden), device=dev)
+            tok = D.domino_draft_block(head, hidden, base, x_t, temperature=1.0, seed=3, logits=lg, gru_states=st)
+            runs.append([x.cpu().numpy() for x in (base, tok, lg, st)])
+        for a, b in zip(*runs):
+            np.testing.assert_array_equal(a, b)
+    finally:
+        head.set_gru_input_table(None)
+
+
 # --------------------------------------------------------------- bit-exact
 @pytest.mark.parametrize("seed,offset,b,pos,v0,n", [
     (0, 0, 0, 0, 0, 4096),
