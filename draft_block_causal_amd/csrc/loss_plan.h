@@ -17,13 +17,15 @@ struct LossPlan {
   size_t total;  // workspace bytes
 };
 
-// About 2048 workgroups per pass, each slice at least 2048 entries long.
+// About 2048 workgroups per pass, each slice at least 2048 entries long, and
+// at most 32 slices per row (one thread merges a row's partials in order).
 inline LossPlan loss_plan(int B, int K, int V) {
   auto align256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   LossPlan p{};
   const long rows = (long)B * K;
   long S = (2048 + rows - 1) / rows;
-  const long smax = V / 2048 > 1 ? V / 2048 : 1;
+  long smax = V / 2048 > 1 ? V / 2048 : 1;
+  smax = smax > 32 ? 32 : smax;
   S = S < 1 ? 1 : S > smax ? smax : S;
   p.S = (int)S;
   p.stats = 0;
