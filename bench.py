@@ -319,6 +319,10 @@ def main() -> int:
                     help="instead of the benchmark, time the rows beyond the draft path at the workload's shapes: "
                          "the teacher-forced training forward with the curriculum loss and its logit gradients, "
                          "sampled-draft verification, and head-off drafting beside the full head")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MB buffer between steps (outside the timed events) so that every step starts "
+                         "with the weights evicted from the on-die cache; value is then the mean of the per-step "
+                         "HIP-event times")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -381,6 +385,8 @@ def main() -> int:
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     ev_draft = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     def step(i=None):
         if i is not None:
@@ -393,18 +399,26 @@ def main() -> int:
         if i is not None:
             ev_draft[i].record()
         D.domino_accept_len(tokens, target, accept)
+        if i is not None:
+            ev_end[i].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 255)
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    draft_ms = float(np.mean([b.elapsed_time(c) for (_, b), c in zip(ev, ev_draft)]))
+    step_ms = np.array([a.elapsed_time(e) for (a, _), e in zip(ev, ev_end)])
+    ms_per_step = float(step_ms.mean()) if args.cold else (t1 - t0) * 1e3 / args.steps
+    lm_all = np.array([a.elapsed_time(b) for a, b in ev])
+    draft_all = np.array([b.elapsed_time(c) for (_, b), c in zip(ev, ev_draft)])
+    lm_ms, draft_ms = float(lm_all.mean()), float(draft_all.mean())
+    pct = lambda x: {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),  # noqa: E731
+                     "p90": float(np.percentile(x, 90))}
     elem = 2 if w.dtype == "bf16" else 4
     alg = lmhead_algorithmic_bytes(B, K, d, V, elem)
     flops = lmhead_flops(B, K, d, V)
@@ -448,6 +462,10 @@ def main() -> int:
         "gru_table_prepare_ms": prepare_ms,
         "lm_head_ms": lm_ms,
         "draft_block_ms": draft_ms,
+        "step_ms_events": pct(step_ms),
+        "lm_head_ms_events": pct(lm_all),
+        "draft_block_ms_events": pct(draft_all),
+        "cold": bool(args.cold),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
