@@ -328,7 +328,7 @@ def main() -> int:
                          "by W_ih at every position")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: this benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding of the path is a design, not an implementation.", file=sys.stderr)
         return 2
 

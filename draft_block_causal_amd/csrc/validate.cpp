@@ -181,7 +181,7 @@ extern "C" const char* domino_status_string(int status) {
     case DOMINO_ERR_ARG: return "invalid scalar argument";
     case DOMINO_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case DOMINO_ERR_HIP: return "HIP runtime error";
-    case DOMINO_ERR_UNSUPPORTED: return "request outside this build's limits";
+    case DOMINO_ERR_UNSUPPORTED: return "request outside the library's limits";
     default: return "unknown status";
   }
 }

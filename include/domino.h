@@ -46,7 +46,7 @@ typedef enum {
   DOMINO_ERR_ARG = -5,         /* a scalar argument is invalid (e.g. T < 0, NaN)  */
   DOMINO_ERR_WORKSPACE = -6,   /* workspace missing, too small or not 256-aligned */
   DOMINO_ERR_HIP = -7,         /* the HIP runtime reported an error               */
-  DOMINO_ERR_UNSUPPORTED = -8  /* valid request outside this build's limits       */
+  DOMINO_ERR_UNSUPPORTED = -8  /* valid request outside the library's limits     */
 } domino_status;
 
 typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
@@ -80,7 +80,7 @@ typedef enum { DOMINO_F32 = 0, DOMINO_BF16 = 1 } domino_dtype;
  *                       domino_draft_block reads T[token] instead of
  *                       multiplying by W_ih at every position.
  *
- * Limits of this build: d * sizeof(element) <= 8192 bytes (bf16: d <= 4096,
+ * Limits of the library: d * sizeof(element) <= 8192 bytes (bf16: d <= 4096,
  * f32: d <= 2048); H <= 4096; r <= 1024; batch <= 128.
  */
 typedef struct {
