@@ -1,0 +1,37 @@
+"""The benchmark's own arithmetic and contract on the CPU: the compulsory
+bytes and FLOPs of the LM-head launch at the Qwen3 workloads (the counts the
+roofline fractions are computed from), the traffic record's source check, and
+the single-GPU refusal."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_lmhead_bytes_and_flops_at_qwen3_shapes():
+    # Qwen3-8B head, one block of 16 positions: W_lm once (151936 x 4096 bf16),
+    # 16 hidden rows in, 16 x V float32 base logits out
+    assert bench.lmhead_algorithmic_bytes(1, 16, 4096, 151936, 2) == 1_254_514_688
+    assert 151936 * 4096 * 2 == 1_244_659_712
+    # 32 blocks: 2 * 512 * 151936 * 4096 FLOPs = 637.3 GFLOP, above the ridge
+    flops = bench.lmhead_flops(32, 16, 4096, 151936)
+    assert flops == 637_265_772_544
+    assert flops / bench.lmhead_algorithmic_bytes(32, 16, 4096, 151936, 2) > bench.RIDGE_FLOP_PER_BYTE
+    # one block stays far below it (HBM-bound)
+    assert bench.lmhead_flops(1, 16, 4096, 151936) / 1_254_514_688 < bench.RIDGE_FLOP_PER_BYTE
+
+
+def test_traffic_record_matches_current_source_or_is_ignored():
+    got = bench.measured_traffic(bench.kernel_source_hash())
+    assert got is None or abs(got / bench.lmhead_algorithmic_bytes(1, 16, 4096, 151936, 2) - 1.0) < 0.01
+    assert bench.measured_traffic("0" * 64) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
