@@ -136,7 +136,9 @@ def test_tiny_f32_b1(dev):
     _parity(S.get_workload("tiny_f32_b1"), dev)
 
 
-LOOP_MODES = ["persistent", "multi"]
+# "default" lets the library choose (for the tiny heads: one workgroup per
+# block runs the whole loop); the others force a schedule
+LOOP_MODES = ["default", "persistent", "multi"]
 
 
 @pytest.mark.parametrize("mode", LOOP_MODES)
