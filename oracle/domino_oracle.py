@@ -72,6 +72,7 @@ __all__ = [
     "position_weights",
     "cross_entropy",
     "curriculum_loss",
+    "correction_backward",
     "accept_len",
     "top2_margin",
     "uniform01",
@@ -359,6 +360,38 @@ def curriculum_loss(base, final, targets, lam: float, gamma: float):
                 p[y] -= 1.0
                 grad[b, i] = coef * w[i] / (wsum * B) * p
     return {"loss": loss / (wsum * B), "ce_base": ce_b, "ce_final": ce_f, "grad_base": g_b, "grad_final": g_f}
+
+
+def correction_backward(head: dict, hidden, states, grad_final):
+    """Gradients of a loss through the low-rank correction head, given the
+    loss's gradient G with respect to the final logits of every position.
+
+    The head computes z_i = W1 [h_i ; g_i] + b1, u_i = SiLU(z_i) and
+    L_i = L_i^base + W2 u_i + b2 ([notes] §二.1(2) items 2-3); the base logits
+    come from the frozen LM head and carry no parameters of the head.  By the
+    chain rule, summing over every block b and position i:
+        dW2 = Σ G_i u_iᵀ,  db2 = Σ G_i,  du_i = W2ᵀ G_i,
+        dz_i = du_i ⊙ SiLU'(z_i),  SiLU'(z) = σ(z) (1 + z (1 - σ(z))),
+        dW1 = Σ dz_i [h_i ; g_i]ᵀ,  db1 = Σ dz_i,  dg_i = W1[:, d:]ᵀ dz_i
+    (dg_i is what the GRU's own backward through time starts from).
+    hidden [B, K, d]; states [B, K, H] (the teacher-forced GRU states);
+    grad_final [B, K, V].  Returns dict(dw2 [V, r], db2 [V], dw1 [r, d + H],
+    db1 [r], dg [B, K, H]).
+    """
+    f = {k: as_f64(v) for k, v in head.items() if k in ("w1", "b1", "w2", "b2")}
+    h = as_f64(hidden)
+    g = np.asarray(states, dtype=np.float64)
+    G = np.asarray(grad_final, dtype=np.float64)
+    B, K, d = h.shape
+    x = np.concatenate([h, g], axis=-1).reshape(B * K, -1)  # [h_i ; g_i] per row
+    z = x @ f["w1"].T + f["b1"]
+    sz = sigmoid(z)
+    u = z * sz
+    Gr = G.reshape(B * K, -1)
+    du = Gr @ f["w2"]
+    dz = du * sz * (1.0 + z * (1.0 - sz))
+    return {"dw2": Gr.T @ u, "db2": Gr.sum(axis=0), "dw1": dz.T @ x, "db1": dz.sum(axis=0),
+            "dg": (dz @ f["w1"][:, d:]).reshape(B, K, -1)}
 
 
 def accept_len(draft, target) -> np.ndarray:

@@ -42,6 +42,8 @@ MUTATIONS = {
     "position_weights_growing": ("return np.power(float(gamma), np.arange(K, dtype=np.float64))",
                                  "return np.power(float(gamma), -np.arange(K, dtype=np.float64))"),
     "gradient_without_onehot": ("p[y] -= 1.0", "p[y] -= 0.0"),
+    "silu_derivative_wrong": ("dz = du * sz * (1.0 + z * (1.0 - sz))", "dz = du * sz * (1.0 - sz)"),
+    "backward_state_columns": ("\"dg\": (dz @ f[\"w1\"][:, d:])", "\"dg\": (dz @ f[\"w1\"][:, :g.shape[-1]])"),
     "base_logits_transposed_operand": ("return as_f64(hidden) @ as_f64(lm_head).T",
                                        "return (as_f64(lm_head) @ as_f64(hidden).swapaxes(-1, -2)).swapaxes(-1, -2)[..., ::-1]"),
 }

@@ -272,6 +272,25 @@ def test_curriculum_loss_gradients_match_autograd():
     np.testing.assert_allclose(out["grad_final"].sum(-1), 0.0, atol=1e-14)  # softmax - onehot sums to 0
 
 
+def test_correction_backward_matches_autograd():
+    rng = np.random.default_rng(24)
+    B, K, d, H, r, V = 2, 3, 8, 4, 5, 11
+    head = _head(rng, d, H, r, V, scale=0.7)
+    hidden = rng.normal(size=(B, K, d))
+    states = rng.normal(0, 0.5, size=(B, K, H))
+    G = rng.normal(size=(B, K, V))
+    out = O.correction_backward(head, hidden, states, G)
+    t = {k: torch.tensor(head[k], requires_grad=True) for k in ("w1", "b1", "w2", "b2")}
+    tg = torch.tensor(states, requires_grad=True)
+    x = torch.cat([torch.from_numpy(hidden), tg], -1)
+    dl = torch.nn.functional.linear(torch.nn.functional.silu(torch.nn.functional.linear(x, t["w1"], t["b1"])),
+                                    t["w2"], t["b2"])
+    (dl * torch.from_numpy(G)).sum().backward()
+    for name, key in (("dw2", "w2"), ("db2", "b2"), ("dw1", "w1"), ("db1", "b1")):
+        np.testing.assert_allclose(out[name], t[key].grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["dg"], tg.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------- loop wiring
 def _torch_chain_logits(head, hidden_b, x_t, seq):
     """Independent re-derivation with torch modules: logits of every position when
