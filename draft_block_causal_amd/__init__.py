@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     domino_accept_len,
     domino_base_logits,
     domino_check_head,
+    domino_correction_backward,
     domino_curriculum_loss,
     domino_debug_philox,
     domino_draft_block,

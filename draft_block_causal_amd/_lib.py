@@ -48,6 +48,8 @@ EXPORTED = [
     "domino_base_draft_workspace_size",
     "domino_curriculum_loss",
     "domino_curriculum_loss_workspace_size",
+    "domino_correction_backward",
+    "domino_correction_backward_workspace_size",
     "domino_debug_philox",
 ]
 
@@ -111,6 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_base_draft_workspace_size": (SZ, [I32, I32]),
         "domino_curriculum_loss": (ctypes.c_int, [I32, I32, I32, P, P, P, F, F, P, P, P, P, P, P, SZ, P]),
         "domino_curriculum_loss_workspace_size": (SZ, [I32, I32, I32]),
+        "domino_correction_backward": (ctypes.c_int, [HP, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "domino_correction_backward_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -372,6 +376,28 @@ def domino_curriculum_loss(base_logits: torch.Tensor, final_logits: torch.Tensor
         _ptr(ce_base), _ptr(ce_final), _ptr(grad_base), _ptr(grad_final), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return loss
+
+
+def domino_correction_backward(head: Head, hidden: torch.Tensor, gru_states: torch.Tensor,
+                               grad_final: torch.Tensor, d_b: bool = True, d_states: bool = True, stream=None):
+    """Gradients of W2, b2, W1, b1 (and of the GRU states) from the loss's gradient on
+    the final logits; returns dict(d_w2, d_b2, d_w1, d_b1, d_states) of float32 tensors."""
+    B = hidden.shape[0]
+    K, V, d, H, r, dev = head.block, head.vocab, head.d, head.gru_hidden, head.rank, head.device
+    _need(hidden, "hidden", head.dtype, (B, K, d), dev)
+    _need(gru_states, "gru_states", torch.float32, (B, K, H), dev)
+    _need(grad_final, "grad_final", torch.float32, (B, K, V), dev)
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    out = {"d_w2": f(V, r), "d_b2": f(V) if d_b else None, "d_w1": f(r, d + H), "d_b1": f(r) if d_b else None,
+           "d_states": f(B, K, H) if d_states else None}
+    sz = ctypes.c_size_t(0)
+    _check("domino_correction_backward_workspace_size",
+           load_library().domino_correction_backward_workspace_size(head.ref, B, ctypes.byref(sz)))
+    ws = torch.empty(max(int(sz.value), 1), dtype=torch.uint8, device=dev)
+    _check("domino_correction_backward", load_library().domino_correction_backward(
+        head.ref, B, _ptr(hidden), _ptr(gru_states), _ptr(grad_final), _ptr(out["d_w2"]), _ptr(out["d_b2"]),
+        _ptr(out["d_w1"]), _ptr(out["d_b1"]), _ptr(out["d_states"]), _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return out
 
 
 def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,

@@ -148,6 +148,46 @@ extern "C" int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab
                                                   static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int domino_correction_backward_workspace_size(const domino_head* h, int32_t batch, size_t* bytes) {
+  if (!bytes) return DOMINO_ERR_NULL;
+  int st = domino::check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > domino::kMaxBatch || h->rank > 512) return DOMINO_ERR_UNSUPPORTED;
+  *bytes = batch == 0 ? 0 : domino::backward_plan(batch * h->block, h->rank, h->vocab).total;
+  return DOMINO_OK;
+}
+
+extern "C" int domino_correction_backward(const domino_head* h, int32_t batch, const void* hidden,
+                                          const float* gru_states, const float* grad_final, float* d_w2,
+                                          float* d_b2, float* d_w1, float* d_b1, float* d_states, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  int st = domino::check_backward_args(h, batch, hidden, gru_states, grad_final, d_w2, d_b2, d_w1, d_b1, d_states,
+                                       workspace, workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  domino::BackwardArgs a{};
+  a.dtype = h->dtype;
+  a.R = batch * h->block;
+  a.d = h->d;
+  a.H = h->gru_hidden;
+  a.r = h->rank;
+  a.V = h->vocab;
+  a.hidden = hidden;
+  a.w1 = h->w1;
+  a.b1 = h->b1;
+  a.w2 = h->w2;
+  a.states = gru_states;
+  a.grad = grad_final;
+  a.d_w2 = d_w2;
+  a.d_b2 = d_b2;
+  a.d_w1 = d_w1;
+  a.d_b1 = d_b1;
+  a.d_states = d_states;
+  a.workspace = workspace;
+  a.plan = domino::backward_plan(a.R, a.r, a.V);
+  return hip_status(domino::launch_correction_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" size_t domino_curriculum_loss_workspace_size(int32_t batch, int32_t block, int32_t vocab) {
   if (batch < 1 || batch > domino::kMaxLossBatch || block < 1 || block > domino::kMaxLossBlock || vocab < 1 ||
       vocab > domino::kMaxVocab)

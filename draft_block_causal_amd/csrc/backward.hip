@@ -1,0 +1,259 @@
+// Backward through the low-rank correction head ([notes] §二.1(2) items 2-3):
+// from G = d loss / d L_final (every block and position, [R = B K][V]) to the
+// gradients of W2, b2, W1, b1 and of the GRU states.  With x_i = [h_i ; g_i],
+// z_i = W1 x_i + b1, u_i = SiLU(z_i):
+//   dW2 = Σ_i G_i u_iᵀ, db2 = Σ_i G_i, du_i = W2ᵀ G_i,
+//   dz_i = du_i ⊙ SiLU'(z_i), dW1 = Σ_i dz_i x_iᵀ, db1 = Σ_i dz_i,
+//   dg_i = W1[:, d:]ᵀ dz_i.
+// Launches on the caller's stream, all in float32 with every sum in a fixed
+// order (no atomics, so two calls give the same bits):
+//   1. bw_z_kernel     (R workgroups): z and u of each row, rows of W1 split
+//                      over the lanes of a wave;
+//   2. bw_dw2_kernel   (V / 256 x r / 32): dW2 and db2, one vocabulary entry
+//                      per thread, u staged in LDS 64 rows at a time;
+//   3. bw_du_kernel    (S vocabulary slices x R / 64): partial W2ᵀ G over a
+//                      slice for 64 rows (G staged in LDS), W2 read once per
+//                      64 rows;
+//   4. bw_dz_kernel    (R x r threads): the S partials added in slice order,
+//                      times SiLU'(z);
+//   5. bw_dw1_kernel   ((d + H) / 256 x r / 16): dW1 and db1;
+//   6. bw_dg_kernel    (H / 256 x R / 16): the state gradient.
+#include "common.h"
+#include "kernels.h"
+
+namespace domino {
+
+constexpr int kBwThreads = 256;
+constexpr int kBwWaves = kBwThreads / 64;
+constexpr int kBwRowsDu = 64;   // rows per du workgroup
+constexpr int kBwQDw2 = 32;     // outputs of a W2 row per dW2 thread
+constexpr int kBwRowsLds = 64;  // u rows staged per round in the dW2 kernel
+constexpr int kBwQDw1 = 16;     // W1 rows per dW1 thread
+constexpr int kBwRowsDg = 16;   // rows per dg thread
+
+__device__ __forceinline__ float bw_wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// z = W1 [h ; g] + b1 and u = SiLU(z) for row `row`; x staged in LDS.
+template <class T>
+__global__ void __launch_bounds__(kBwThreads) bw_z_kernel(int d, int H, int r, const typename T::elem* __restrict__ hidden,
+                                                          const float* __restrict__ states,
+                                                          const typename T::elem* __restrict__ w1,
+                                                          const typename T::elem* __restrict__ b1,
+                                                          float* __restrict__ z, float* __restrict__ u) {
+  using E = typename T::elem;
+  constexpr int EPF = T::kPer16B;
+  extern __shared__ __attribute__((aligned(16))) float xs[];  // [d + H]
+  const int row = blockIdx.x, n = d + H;
+  for (int k = threadIdx.x; k < d; k += kBwThreads) xs[k] = T::to_f32(hidden[(size_t)row * d + k]);
+  for (int k = threadIdx.x; k < H; k += kBwThreads) xs[d + k] = states[(size_t)row * H + k];
+  __syncthreads();
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  for (int q0 = wave * 4; q0 < r; q0 += kBwWaves * 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = lane * EPF; k < n; k += 64 * EPF) {
+      u32x4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = q0 + j < r ? ld16(w1 + (size_t)(q0 + j) * n + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const E* e = reinterpret_cast<const E*>(&w[j]);
+#pragma unroll
+        for (int c = 0; c < EPF; ++c) acc[j] += T::to_f32(e[c]) * xs[k + c];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = bw_wave_sum(acc[j]);
+      if (lane == 0 && q0 + j < r) {
+        const float zz = s + (b1 ? T::to_f32(b1[q0 + j]) : 0.f);
+        z[(size_t)row * r + q0 + j] = zz;
+        u[(size_t)row * r + q0 + j] = zz * sigmoidf_(zz);
+      }
+    }
+  }
+}
+
+// dW2[v][q0 .. q0 + 31] = Σ_rows G[row][v] u[row][q]; db2[v] = Σ_rows G[row][v] (blockIdx.y == 0).
+__global__ void __launch_bounds__(kBwThreads) bw_dw2_kernel(int R, int V, int r, const float* __restrict__ G,
+                                                            const float* __restrict__ u, float* __restrict__ dw2,
+                                                            float* __restrict__ db2) {
+  __shared__ float us[kBwRowsLds][kBwQDw2];
+  const int v = blockIdx.x * kBwThreads + threadIdx.x, q0 = blockIdx.y * kBwQDw2;
+  const int nq = min(kBwQDw2, r - q0);
+  float acc[kBwQDw2];
+#pragma unroll
+  for (int q = 0; q < kBwQDw2; ++q) acc[q] = 0.f;
+  float gs = 0.f;
+  for (int r0 = 0; r0 < R; r0 += kBwRowsLds) {
+    const int nr = min(kBwRowsLds, R - r0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kBwRowsLds * kBwQDw2; e += kBwThreads) {
+      const int rr = e / kBwQDw2, q = e % kBwQDw2;
+      us[rr][q] = rr < nr && q < nq ? u[(size_t)(r0 + rr) * r + q0 + q] : 0.f;
+    }
+    __syncthreads();
+    if (v < V)
+      for (int rr = 0; rr < nr; ++rr) {
+        const float g = G[(size_t)(r0 + rr) * V + v];
+        gs += g;
+#pragma unroll
+        for (int q = 0; q < kBwQDw2; ++q) acc[q] += g * us[rr][q];
+      }
+  }
+  if (v >= V) return;
+  for (int q = 0; q < nq; ++q) dw2[(size_t)v * r + q0 + q] = acc[q];
+  if (blockIdx.y == 0 && db2) db2[v] = gs;
+}
+
+// part[s][row][q] = Σ_{v in slice s} G[row][v] W2[v][q] for rows m0 .. m0 + 63;
+// G is staged in LDS 128 vocabulary entries at a time (coalesced loads).
+constexpr int kBwVChunk = 128;
+template <class T>
+__global__ void __launch_bounds__(kBwThreads) bw_du_kernel(int R, int V, int r, const float* __restrict__ G,
+                                                           const typename T::elem* __restrict__ w2,
+                                                           float* __restrict__ part) {
+  __shared__ float gs[kBwRowsDu][kBwVChunk];
+  const int s = blockIdx.x, S = gridDim.x, m0 = blockIdx.y * kBwRowsDu;
+  const int nr = min(kBwRowsDu, R - m0);
+  const long v0 = (long)V * s / S, v1 = (long)V * (s + 1) / S;
+  constexpr int kQ = 2;  // W2 columns per thread (r <= kQ * 256)
+  float acc[kQ][kBwRowsDu];
+#pragma unroll
+  for (int c = 0; c < kQ; ++c)
+#pragma unroll
+    for (int i = 0; i < kBwRowsDu; ++i) acc[c][i] = 0.f;
+  for (long vc = v0; vc < v1; vc += kBwVChunk) {
+    const int nv = (int)min((long)kBwVChunk, v1 - vc);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kBwRowsDu * kBwVChunk; e += kBwThreads) {
+      const int i = e / kBwVChunk, vv = e % kBwVChunk;
+      gs[i][vv] = i < nr && vv < nv ? G[(size_t)(m0 + i) * V + vc + vv] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kQ; ++c) {
+      const int q = threadIdx.x + c * kBwThreads;
+      if (q >= r) continue;
+      for (int vv = 0; vv < nv; ++vv) {
+        const float w = T::to_f32(w2[(size_t)(vc + vv) * r + q]);
+#pragma unroll
+        for (int i = 0; i < kBwRowsDu; ++i) acc[c][i] += gs[i][vv] * w;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kQ; ++c) {
+    const int q = threadIdx.x + c * kBwThreads;
+    if (q >= r) continue;
+#pragma unroll
+    for (int i = 0; i < kBwRowsDu; ++i)
+      if (i < nr) part[((size_t)s * R + m0 + i) * r + q] = acc[c][i];
+  }
+}
+
+// dz = (Σ_s part[s]) ⊙ SiLU'(z), the slices added in order.
+__global__ void bw_dz_kernel(int R, int r, int S, const float* __restrict__ part, const float* __restrict__ z,
+                             float* __restrict__ dz) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (long)R * r) return;
+  float du = 0.f;
+  for (int s = 0; s < S; ++s) du += part[(size_t)s * R * r + e];
+  const float zz = z[e], sg = sigmoidf_(zz);
+  dz[e] = du * sg * (1.f + zz * (1.f - sg));
+}
+
+// dW1[q][k] = Σ_rows dz[row][q] x[row][k] for q0 .. q0 + 15; db1 from the
+// workgroups with blockIdx.x == 0.
+template <class T>
+__global__ void __launch_bounds__(kBwThreads) bw_dw1_kernel(int R, int d, int H, int r,
+                                                            const typename T::elem* __restrict__ hidden,
+                                                            const float* __restrict__ states,
+                                                            const float* __restrict__ dz, float* __restrict__ dw1,
+                                                            float* __restrict__ db1) {
+  const int k = blockIdx.x * kBwThreads + threadIdx.x, q0 = blockIdx.y * kBwQDw1, n = d + H;
+  const int nq = min(kBwQDw1, r - q0);
+  float acc[kBwQDw1];
+#pragma unroll
+  for (int q = 0; q < kBwQDw1; ++q) acc[q] = 0.f;
+  if (k < n)
+    for (int row = 0; row < R; ++row) {
+      const float x = k < d ? T::to_f32(hidden[(size_t)row * d + k]) : states[(size_t)row * H + k - d];
+#pragma unroll
+      for (int q = 0; q < kBwQDw1; ++q)
+        if (q < nq) acc[q] += dz[(size_t)row * r + q0 + q] * x;
+    }
+  if (k < n)
+    for (int q = 0; q < nq; ++q) dw1[(size_t)(q0 + q) * n + k] = acc[q];
+  if (blockIdx.x == 0 && db1 && (int)threadIdx.x < nq) {
+    float sum = 0.f;
+    for (int row = 0; row < R; ++row) sum += dz[(size_t)row * r + q0 + threadIdx.x];
+    db1[q0 + threadIdx.x] = sum;
+  }
+}
+
+// dg[row][j] = Σ_q dz[row][q] W1[q][d + j] for rows m0 .. m0 + 15.
+template <class T>
+__global__ void __launch_bounds__(kBwThreads) bw_dg_kernel(int R, int d, int H, int r,
+                                                           const typename T::elem* __restrict__ w1,
+                                                           const float* __restrict__ dz, float* __restrict__ dg) {
+  const int j = blockIdx.x * kBwThreads + threadIdx.x, m0 = blockIdx.y * kBwRowsDg;
+  if (j >= H) return;
+  const int nr = min(kBwRowsDg, R - m0);
+  float acc[kBwRowsDg];
+#pragma unroll
+  for (int i = 0; i < kBwRowsDg; ++i) acc[i] = 0.f;
+  for (int q = 0; q < r; ++q) {
+    const float w = T::to_f32(w1[(size_t)q * (d + H) + d + j]);
+#pragma unroll
+    for (int i = 0; i < kBwRowsDg; ++i)
+      if (i < nr) acc[i] += dz[(size_t)(m0 + i) * r + q] * w;
+  }
+#pragma unroll
+  for (int i = 0; i < kBwRowsDg; ++i)
+    if (i < nr) dg[(size_t)(m0 + i) * H + j] = acc[i];
+}
+
+template <class T>
+static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
+  using E = typename T::elem;
+  const int R = a.R, V = a.V, r = a.r, d = a.d, H = a.H;
+  const BackwardPlan& pl = a.plan;
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  float* z = reinterpret_cast<float*>(ws + pl.z);
+  float* u = reinterpret_cast<float*>(ws + pl.u);
+  float* dz = reinterpret_cast<float*>(ws + pl.dz);
+  float* part = reinterpret_cast<float*>(ws + pl.part);
+  const E* hidden = static_cast<const E*>(a.hidden);
+  const E* w1 = static_cast<const E*>(a.w1);
+  const size_t lds = (size_t)(d + H) * sizeof(float);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_z_kernel<T>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
+                     static_cast<const E*>(a.b1), z, u);
+  hipLaunchKernelGGL(bw_dw2_kernel, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
+                     dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
+  hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu), dim3(kBwThreads), 0, s, R, V, r,
+                     a.grad, static_cast<const E*>(a.w2), part);
+  hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 255) / 256)), dim3(256), 0, s, R, r, pl.S, part, z,
+                     dz);
+  hipLaunchKernelGGL(bw_dw1_kernel<T>, dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1),
+                     dim3(kBwThreads), 0, s, R, d, H, r, hidden, a.states, dz, a.d_w1, a.d_b1);
+  if (a.d_states)
+    hipLaunchKernelGGL(bw_dg_kernel<T>, dim3((H + kBwThreads - 1) / kBwThreads, (R + kBwRowsDg - 1) / kBwRowsDg),
+                       dim3(kBwThreads), 0, s, R, d, H, r, w1, dz, a.d_states);
+  return hipGetLastError();
+}
+
+hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s) {
+  if (a.R <= 0) return hipSuccess;
+  return a.dtype == 1 ? backward_t<Bf16>(a, s) : backward_t<F32>(a, s);
+}
+
+}  // namespace domino

@@ -91,6 +91,36 @@ hipError_t launch_verify_sampled(int B, int K, int V, const float* target, const
                                  float temperature, uint64_t seed, uint32_t offset, int32_t* accept, int32_t* next,
                                  const VerifyPlan& plan, void* workspace, hipStream_t s);
 
+// Backward through the correction head (backward.hip).
+struct BackwardPlan {
+  int S;  // vocabulary slices of the du partials
+  size_t z, u, dz, part, total;  // byte offsets of [R][r], [R][r], [R][r], [S][R][r] float32; workspace bytes
+};
+inline BackwardPlan backward_plan(int R, int r, int V) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BackwardPlan p{};
+  const long groups = (R + 63) / 64;
+  long S = (512 + groups - 1) / groups;
+  const long smax = V / 1024 > 1 ? V / 1024 : 1;
+  p.S = (int)(S < 1 ? 1 : S > smax ? smax : S);
+  const size_t m = up((size_t)R * r * sizeof(float));
+  p.z = 0;
+  p.u = m;
+  p.dz = 2 * m;
+  p.part = 3 * m;
+  p.total = 3 * m + up((size_t)p.S * R * r * sizeof(float));
+  return p;
+}
+struct BackwardArgs {
+  int dtype, R, d, H, r, V;
+  const void *hidden, *w1, *b1, *w2;
+  const float *states, *grad;
+  float *d_w2, *d_b2, *d_w1, *d_b1, *d_states;
+  void* workspace;
+  BackwardPlan plan;
+};
+hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
+
 // Base-only drafting (base_draft.hip): tokens[b][i] picked from base[b][i][:]
 // alone (greedy, or Gumbel-max when temperature > 0); workspace holds B K
 // 64-bit keys.

@@ -1,6 +1,7 @@
 // Host-only argument validation and workspace layout of the Domino C ABI.
 // Pure C++ (no HIP calls), so it can also be built and sanitised on a CPU.
 #include "validate.h"
+#include "kernels.h"
 
 #include "psplit.h"
 
@@ -148,6 +149,25 @@ int check_loss_args(int32_t batch, int32_t block, int32_t vocab, const float* ba
     if (reinterpret_cast<uintptr_t>(q) & 3u) return DOMINO_ERR_ALIGN;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
       workspace_bytes < loss_plan(batch, block, vocab).total)
+    return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
+int check_backward_args(const domino_head* h, int32_t batch, const void* hidden, const float* gru_states,
+                        const float* grad_final, const float* d_w2, const float* d_b2, const float* d_w1,
+                        const float* d_b1, const float* d_states, const void* workspace, size_t workspace_bytes) {
+  int st = check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > kMaxBatch || h->rank > 512) return DOMINO_ERR_UNSUPPORTED;
+  if (batch == 0) return DOMINO_OK;
+  if (!hidden || !gru_states || !grad_final || !d_w2 || !d_w1) return DOMINO_ERR_NULL;
+  if (!aligned16(hidden)) return DOMINO_ERR_ALIGN;
+  for (const void* q : {(const void*)gru_states, (const void*)grad_final, (const void*)d_w2, (const void*)d_b2,
+                        (const void*)d_w1, (const void*)d_b1, (const void*)d_states})
+    if (reinterpret_cast<uintptr_t>(q) & 3u) return DOMINO_ERR_ALIGN;
+  const BackwardPlan pl = backward_plan(batch * h->block, h->rank, h->vocab);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < pl.total)
     return DOMINO_ERR_WORKSPACE;
   return DOMINO_OK;
 }

@@ -278,6 +278,36 @@ int domino_curriculum_loss(int32_t batch, int32_t block, int32_t vocab, const fl
 size_t domino_curriculum_loss_workspace_size(int32_t batch, int32_t block, int32_t vocab);
 
 /*
+ * Backward through the low-rank correction head ([notes] §二.1(2) items 2-3)
+ * for training: given G = grad_final, the gradient of a loss with respect to
+ * the final logits of every block and position (domino_curriculum_loss writes
+ * it), and the teacher-forced GRU states g (domino_draft_block's gru_states),
+ * with x_i = [hidden_i ; g_i], z_i = W1 x_i + b1, u_i = SiLU(z_i):
+ *   d_w2 = Σ_i G_i u_iᵀ  [V, r]        d_b2 = Σ_i G_i      [V]   (NULL: skipped)
+ *   d_w1 = Σ_i dz_i x_iᵀ [r, d + H]    d_b1 = Σ_i dz_i     [r]   (NULL: skipped)
+ *   d_states_i = W1[:, d:]ᵀ dz_i [batch, block, H]                (NULL: skipped)
+ * where dz_i = (W2ᵀ G_i) ⊙ SiLU'(z_i) and the sums run over every block and
+ * position.  The base logits carry no head parameter, so G reaches the head
+ * through the correction only; d_states is where the GRU's own backward
+ * through time would start.  Outputs are overwritten, not accumulated.
+ *
+ * hidden      [batch, block, d] head dtype, 16-byte aligned
+ * gru_states  [batch, block, H] float32;  grad_final [batch, block, V] float32
+ * outputs     float32, 4-byte aligned
+ * workspace   device scratch of domino_correction_backward_workspace_size()
+ *             bytes, 256-byte aligned.
+ * batch in 0 … 128 (0 is a no-op), rank ≤ 512 (else DOMINO_ERR_UNSUPPORTED).
+ * Arithmetic: float32, every sum in a fixed order (repeatable bits).
+ */
+int domino_correction_backward(const domino_head *head, int32_t batch, const void *hidden,
+                               const float *gru_states, const float *grad_final, float *d_w2, float *d_b2,
+                               float *d_w1, float *d_b1, float *d_states, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Workspace bytes domino_correction_backward needs for `batch` blocks. */
+int domino_correction_backward_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

@@ -268,3 +268,37 @@ def test_curriculum_loss_validation_and_workspace(lib):
     assert call(w=0x100010) == E_WS
     assert call(wb=ws - 1) == E_WS
     assert call(B=0, b=None, f=None, y=None, loss=None, w=None, wb=0) == OK
+
+
+def test_correction_backward_validation(lib):
+    h = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=256)
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_correction_backward_workspace_size(ctypes.byref(h), 2, ctypes.byref(sz)) == OK
+    ws = sz.value
+    assert ws > 0 and ws % 256 == 0
+    assert lib.domino_correction_backward_workspace_size(ctypes.byref(h), 129, ctypes.byref(sz)) == E_UNSUP
+    assert lib.domino_correction_backward_workspace_size(ctypes.byref(h), 1, None) == E_NULL
+    big_rank = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=544)
+    assert lib.domino_correction_backward_workspace_size(ctypes.byref(big_rank), 1, ctypes.byref(sz)) == E_UNSUP
+    args = dict(B=2, x=0x20000, g=0x30000, G=0x40000, dw2=0x50000, db2=0x60000, dw1=0x70000, db1=0x80000,
+                ds=0x90000, w=0x100000, wb=ws)
+
+    def call(head=h, **kw):
+        a = {**args, **kw}
+        return lib.domino_correction_backward(ctypes.byref(head), a["B"], a["x"], a["g"], a["G"], a["dw2"], a["db2"],
+                                              a["dw1"], a["db1"], a["ds"], a["w"], a["wb"], None)
+
+    assert call() == E_HIP  # valid arguments, no GPU here
+    assert call(db2=None, db1=None, ds=None) == E_HIP
+    assert call(B=-1) == E_SHAPE
+    assert call(B=129) == E_UNSUP
+    assert call(x=None) == E_NULL
+    assert call(g=None) == E_NULL
+    assert call(G=None) == E_NULL
+    assert call(dw2=None) == E_NULL
+    assert call(dw1=None) == E_NULL
+    assert call(x=0x20008) == E_ALIGN
+    assert call(G=0x40002) == E_ALIGN
+    assert call(w=None) == E_WS
+    assert call(wb=ws - 1) == E_WS
+    assert call(B=0, x=None, g=None, G=None, dw2=None, dw1=None, w=None, wb=0) == OK
