@@ -213,8 +213,9 @@ def next_rows(args, w) -> int:
     """Timings (HIP events, mean over --steps after --warmup) of the calls beyond
     the draft path, at the workload's shapes, with the HBM rate of each
     bandwidth-bound kernel group against the 8 TB/s peak:
-      train_forward: base logits + teacher-forced draft block (final logits out)
-                     + curriculum loss with both logit gradients written in place;
+      train_forward: base logits + teacher-forced draft block (final logits and
+                     GRU states out) + curriculum loss with both logit gradients
+                     written in place, then the backward through the correction head;
       verify:        sampled-draft verification on synthetic target / draft logits;
       head_off:      base logits + base-only drafting, beside base logits + draft block."""
     import torch
@@ -260,14 +261,19 @@ def next_rows(args, w) -> int:
         return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(n)]
 
     lm = lambda: D.domino_base_logits(head, hidden, base)  # noqa: E731
+    states = torch.empty((B, K, w.gru_hidden), dtype=torch.float32, device=dev)
     tf = lambda: D.domino_draft_block(head, hidden, base, x_t, teacher=gold, temperature=w.temperature,  # noqa: E731
-                                      seed=w.philox_seed, tokens=tokens, logits=final, workspace=ws)
+                                      seed=w.philox_seed, tokens=tokens, logits=final, gru_states=states,
+                                      workspace=ws)
     cl = lambda: D.domino_curriculum_loss(base, final, gold, 0.5, 0.9, loss=loss, grad_base=base,  # noqa: E731
                                           grad_final=final, workspace=lws)
-    t_lm, t_tf, t_cl = timed([lm, tf, cl])
+    bw = lambda: D.domino_correction_backward(head, hidden, states, final)  # noqa: E731
+    t_lm, t_tf, t_cl, t_bw = timed([lm, tf, cl, bw])
     loss_bytes = 2 * B * K * V * 4 * 3  # pass 1 reads both tensors; the gradient pass reads and writes both
     out = {"train_forward": {"base_logits_ms": t_lm, "teacher_forced_draft_ms": t_tf, "curriculum_loss_ms": t_cl,
+                             "correction_backward_ms": t_bw,
                              "blocks_per_s": B / ((t_lm + t_tf + t_cl) * 1e-3),
+                             "with_backward_blocks_per_s": B / ((t_lm + t_tf + t_cl + t_bw) * 1e-3),
                              "loss_kernels_gb_s": loss_bytes / (t_cl * 1e-3) / 1e9,
                              "loss_kernels_hbm_frac": loss_bytes / (t_cl * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "loss_bytes": loss_bytes}}
