@@ -11,9 +11,9 @@
 //                      over the lanes of a wave;
 //   2. bw_dw2_kernel   (V / 256 x r / 32): dW2 and db2, one vocabulary entry
 //                      per thread, u staged in LDS 64 rows at a time;
-//   3. bw_du_kernel    (S vocabulary slices x R / 64): partial W2ᵀ G over a
-//                      slice for 64 rows (G staged in LDS), W2 read once per
-//                      64 rows;
+//   3. bw_du_kernel    (S vocabulary slices x R / 64 x r / 256): partial W2ᵀ G
+//                      over a slice for 64 rows (G and W2 staged in LDS,
+//                      16 x 4 register tiles), W2 read once per 64 rows;
 //   4. bw_dz_kernel    (R x r threads): the S partials added in slice order,
 //                      times SiLU'(z);
 //   5. bw_dw1_kernel   ((d + H) / 256 x r / 16): dW1 and db1;
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw2_kernel(int R, int V, int r,
   float acc[kBwQDw2];
 #pragma unroll
   for (int q = 0; q < kBwQDw2; ++q) acc[q] = 0.f;
-  float gs = 0.f;
+  float gsum = 0.f;
   for (int r0 = 0; r0 < R; r0 += kBwRowsLds) {
     const int nr = min(kBwRowsLds, R - r0);
     __syncthreads();
@@ -99,33 +99,40 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw2_kernel(int R, int V, int r,
     if (v < V)
       for (int rr = 0; rr < nr; ++rr) {
         const float g = G[(size_t)(r0 + rr) * V + v];
-        gs += g;
+        gsum += g;
 #pragma unroll
         for (int q = 0; q < kBwQDw2; ++q) acc[q] += g * us[rr][q];
       }
   }
   if (v >= V) return;
   for (int q = 0; q < nq; ++q) dw2[(size_t)v * r + q0 + q] = acc[q];
-  if (blockIdx.y == 0 && db2) db2[v] = gs;
+  if (blockIdx.y == 0 && db2) db2[v] = gsum;
 }
 
-// part[s][row][q] = Σ_{v in slice s} G[row][v] W2[v][q] for rows m0 .. m0 + 63;
-// G is staged in LDS 128 vocabulary entries at a time (coalesced loads).
-constexpr int kBwVChunk = 128;
+// part[s][row][q] = Σ_{v in slice s} G[row][v] W2[v][q] for rows m0 .. m0 + 63
+// and columns q0 .. q0 + 255 (q0 = 256 blockIdx.z).  G and W2 are staged in
+// LDS 64 vocabulary entries at a time with coalesced loads.  Thread (wave w,
+// lane l) holds a 16-row x 4-column tile: rows m0 + 16 w .., columns
+// q0 + 4 l ..; the lanes of a wave share their rows, so each LDS read of G is
+// a broadcast that feeds four multiply-adds.
+constexpr int kBwVChunk = 64;
 template <class T>
 __global__ void __launch_bounds__(kBwThreads) bw_du_kernel(int R, int V, int r, const float* __restrict__ G,
                                                            const typename T::elem* __restrict__ w2,
                                                            float* __restrict__ part) {
   __shared__ float gs[kBwRowsDu][kBwVChunk];
-  const int s = blockIdx.x, S = gridDim.x, m0 = blockIdx.y * kBwRowsDu;
-  const int nr = min(kBwRowsDu, R - m0);
+  __shared__ __attribute__((aligned(16))) float ws[kBwVChunk][256];
+  const int s = blockIdx.x, S = gridDim.x, m0 = blockIdx.y * kBwRowsDu, q0 = blockIdx.z * 256;
+  const int nr = min(kBwRowsDu, R - m0), nq = min(256, r - q0);
   const long v0 = (long)V * s / S, v1 = (long)V * (s + 1) / S;
-  constexpr int kQ = 2;  // W2 columns per thread (r <= kQ * 256)
-  float acc[kQ][kBwRowsDu];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int ql = lane * 4;       // first of this thread's 4 columns within the block
+  const bool live = ql < nq;     // r is a multiple of 32, so all 4 or none
+  float acc[16][4];
 #pragma unroll
-  for (int c = 0; c < kQ; ++c)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int i = 0; i < kBwRowsDu; ++i) acc[c][i] = 0.f;
+    for (int c = 0; c < 4; ++c) acc[i][c] = 0.f;
   for (long vc = v0; vc < v1; vc += kBwVChunk) {
     const int nv = (int)min((long)kBwVChunk, v1 - vc);
     __syncthreads();
@@ -133,25 +140,31 @@ __global__ void __launch_bounds__(kBwThreads) bw_du_kernel(int R, int V, int r, 
       const int i = e / kBwVChunk, vv = e % kBwVChunk;
       gs[i][vv] = i < nr && vv < nv ? G[(size_t)(m0 + i) * V + vc + vv] : 0.f;
     }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < kQ; ++c) {
-      const int q = threadIdx.x + c * kBwThreads;
-      if (q >= r) continue;
-      for (int vv = 0; vv < nv; ++vv) {
-        const float w = T::to_f32(w2[(size_t)(vc + vv) * r + q]);
-#pragma unroll
-        for (int i = 0; i < kBwRowsDu; ++i) acc[c][i] += gs[i][vv] * w;
-      }
+    for (int e = threadIdx.x; e < kBwVChunk * 256; e += kBwThreads) {
+      const int vv = e >> 8, c = e & 255;
+      ws[vv][c] = vv < nv && c < nq ? T::to_f32(w2[(size_t)(vc + vv) * r + q0 + c]) : 0.f;
     }
+    __syncthreads();
+    if (live)
+      for (int vv = 0; vv < nv; ++vv) {
+        const float4 w = *reinterpret_cast<const float4*>(&ws[vv][ql]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float g = gs[wave * 16 + i][vv];
+          acc[i][0] += g * w.x;
+          acc[i][1] += g * w.y;
+          acc[i][2] += g * w.z;
+          acc[i][3] += g * w.w;
+        }
+      }
   }
+  if (!live) return;
 #pragma unroll
-  for (int c = 0; c < kQ; ++c) {
-    const int q = threadIdx.x + c * kBwThreads;
-    if (q >= r) continue;
+  for (int i = 0; i < 16; ++i) {
+    const int row = wave * 16 + i;
+    if (row < nr)
 #pragma unroll
-    for (int i = 0; i < kBwRowsDu; ++i)
-      if (i < nr) part[((size_t)s * R + m0 + i) * r + q] = acc[c][i];
+      for (int c = 0; c < 4; ++c) part[((size_t)s * R + m0 + row) * r + q0 + ql + c] = acc[i][c];
   }
 }
 
@@ -239,8 +252,8 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
                      static_cast<const E*>(a.b1), z, u);
   hipLaunchKernelGGL(bw_dw2_kernel, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
                      dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
-  hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu), dim3(kBwThreads), 0, s, R, V, r,
-                     a.grad, static_cast<const E*>(a.w2), part);
+  hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu, (r + 255) / 256), dim3(kBwThreads),
+                     0, s, R, V, r, a.grad, static_cast<const E*>(a.w2), part);
   hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 255) / 256)), dim3(256), 0, s, R, r, pl.S, part, z,
                      dz);
   hipLaunchKernelGGL(bw_dw1_kernel<T>, dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1),
