@@ -73,6 +73,7 @@ __all__ = [
     "cross_entropy",
     "curriculum_loss",
     "correction_backward",
+    "gru_backward",
     "accept_len",
     "top2_margin",
     "uniform01",
@@ -392,6 +393,53 @@ def correction_backward(head: dict, hidden, states, grad_final):
     dz = du * sz * (1.0 + z * (1.0 - sz))
     return {"dw2": Gr.T @ u, "db2": Gr.sum(axis=0), "dw1": dz.T @ x, "db1": dz.sum(axis=0),
             "dg": (dz @ f["w1"][:, d:]).reshape(B, K, -1)}
+
+
+def gru_backward(head: dict, x_t, teacher, states, dg):
+    """Backward through time of the teacher-forced GRU causal encoder.
+
+    Forward ([notes] §二.1(2) item 1, teacher forcing §二.2(1)): g_{-1} = 0,
+    g_i = GRU(E[tok_i], g_{i-1}) with tok_0 = x_t and tok_i = teacher[i-1].
+    Given dg[b, i], a loss's gradient with respect to g_i from outside the
+    recurrence (the correction head's state gradient), the chain rule through
+    g_i = (1 - z) n + z g_{i-1}, n = tanh(a_n + r (c_n)), r = σ(a_r + c_r),
+    z = σ(a_z + c_z), a = W_ih e + b_ih, c = W_hh g_{i-1} + b_hh, from the last
+    position back to the first, carrying the gradient of g_{i-1}.
+    states [B, K, H] are the forward states g_i.  Returns dict(dw_ih [3H, d],
+    dw_hh [3H, H], db_ih [3H], db_hh [3H]); the embedding table is frozen.
+    """
+    f = {k: as_f64(v) for k, v in head.items() if k in ("embed", "w_ih", "w_hh", "b_ih", "b_hh")}
+    g_all = np.asarray(states, dtype=np.float64)
+    dg = np.asarray(dg, dtype=np.float64)
+    B, K, H = g_all.shape
+    out = {"dw_ih": np.zeros_like(f["w_ih"]), "dw_hh": np.zeros_like(f["w_hh"]),
+           "db_ih": np.zeros(3 * H), "db_hh": np.zeros(3 * H)}
+    for b in range(B):
+        carry = np.zeros(H)  # gradient reaching g_i from position i + 1
+        for i in range(K - 1, -1, -1):
+            tok = int(x_t[b]) if i == 0 else int(teacher[b, i - 1])
+            e = f["embed"][tok]
+            g_prev = g_all[b, i - 1] if i > 0 else np.zeros(H)
+            a = f["w_ih"] @ e + f["b_ih"]
+            c = f["w_hh"] @ g_prev + f["b_hh"]
+            r = sigmoid(a[:H] + c[:H])
+            z = sigmoid(a[H:2 * H] + c[H:2 * H])
+            n = np.tanh(a[2 * H:] + r * c[2 * H:])
+            d_g = dg[b, i] + carry
+            d_n = d_g * (1.0 - z)
+            d_z = d_g * (g_prev - n)
+            d_pn = d_n * (1.0 - n * n)
+            d_r = d_pn * c[2 * H:]
+            d_pr = d_r * r * (1.0 - r)
+            d_pz = d_z * z * (1.0 - z)
+            da = np.concatenate([d_pr, d_pz, d_pn])
+            dc = np.concatenate([d_pr, d_pz, d_pn * r])
+            out["dw_ih"] += np.outer(da, e)
+            out["db_ih"] += da
+            out["dw_hh"] += np.outer(dc, g_prev)
+            out["db_hh"] += dc
+            carry = d_g * z + f["w_hh"].T @ dc
+    return out
 
 
 def accept_len(draft, target) -> np.ndarray:

@@ -44,6 +44,8 @@ MUTATIONS = {
     "gradient_without_onehot": ("p[y] -= 1.0", "p[y] -= 0.0"),
     "silu_derivative_wrong": ("dz = du * sz * (1.0 + z * (1.0 - sz))", "dz = du * sz * (1.0 - sz)"),
     "backward_state_columns": ("\"dg\": (dz @ f[\"w1\"][:, d:])", "\"dg\": (dz @ f[\"w1\"][:, :g.shape[-1]])"),
+    "bptt_carry_without_recurrence": ("carry = d_g * z + f[\"w_hh\"].T @ dc", "carry = d_g * z"),
+    "bptt_reset_gradient_position": ("dc = np.concatenate([d_pr, d_pz, d_pn * r])", "dc = np.concatenate([d_pr, d_pz, d_pn])"),
     "base_logits_transposed_operand": ("return as_f64(hidden) @ as_f64(lm_head).T",
                                        "return (as_f64(lm_head) @ as_f64(hidden).swapaxes(-1, -2)).swapaxes(-1, -2)[..., ::-1]"),
 }

@@ -291,6 +291,35 @@ def test_correction_backward_matches_autograd():
     np.testing.assert_allclose(out["dg"], tg.grad.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def test_gru_backward_matches_autograd():
+    # the teacher-forced GRU chain in torch (GRUCell), loss = Σ <dg_i, g_i>
+    rng = np.random.default_rng(25)
+    B, K, d, H, r, V = 2, 4, 6, 5, 3, 9
+    head = _head(rng, d, H, r, V, scale=0.6)
+    x_t = rng.integers(0, V, size=B)
+    teacher = rng.integers(0, V, size=(B, K))
+    dg = rng.normal(size=(B, K, H))
+    cell = torch.nn.GRUCell(d, H).double()
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(head["w_ih"])); cell.weight_hh.copy_(torch.from_numpy(head["w_hh"]))
+        cell.bias_ih.copy_(torch.from_numpy(head["b_ih"])); cell.bias_hh.copy_(torch.from_numpy(head["b_hh"]))
+    emb = torch.from_numpy(head["embed"])
+    loss = 0.0
+    states = np.zeros((B, K, H))
+    for b in range(B):
+        g = torch.zeros(1, H, dtype=torch.float64)
+        for i in range(K):
+            tok = int(x_t[b]) if i == 0 else int(teacher[b, i - 1])
+            g = cell(emb[tok:tok + 1], g)
+            states[b, i] = g.detach().numpy()[0]
+            loss = loss + (g[0] * torch.from_numpy(dg[b, i])).sum()
+    loss.backward()
+    out = O.gru_backward(head, x_t, teacher, states, dg)
+    for name, t in (("dw_ih", cell.weight_ih), ("dw_hh", cell.weight_hh), ("db_ih", cell.bias_ih),
+                    ("db_hh", cell.bias_hh)):
+        np.testing.assert_allclose(out[name], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 # ------------------------------------------------------------- loop wiring
 def _torch_chain_logits(head, hidden_b, x_t, seq):
     """Independent re-derivation with torch modules: logits of every position when
