@@ -50,6 +50,8 @@ EXPORTED = [
     "domino_curriculum_loss_workspace_size",
     "domino_correction_backward",
     "domino_correction_backward_workspace_size",
+    "domino_gru_backward",
+    "domino_gru_backward_workspace_size",
     "domino_debug_philox",
 ]
 
@@ -115,6 +117,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_curriculum_loss_workspace_size": (SZ, [I32, I32, I32]),
         "domino_correction_backward": (ctypes.c_int, [HP, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "domino_correction_backward_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
+        "domino_gru_backward": (ctypes.c_int, [HP, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "domino_gru_backward_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -397,6 +401,29 @@ def domino_correction_backward(head: Head, hidden: torch.Tensor, gru_states: tor
     _check("domino_correction_backward", load_library().domino_correction_backward(
         head.ref, B, _ptr(hidden), _ptr(gru_states), _ptr(grad_final), _ptr(out["d_w2"]), _ptr(out["d_b2"]),
         _ptr(out["d_w1"]), _ptr(out["d_b1"]), _ptr(out["d_states"]), _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return out
+
+
+def domino_gru_backward(head: Head, x_t: torch.Tensor, teacher: torch.Tensor, gru_states: torch.Tensor,
+                        d_states: torch.Tensor, d_b: bool = True, stream=None):
+    """Gradients of W_ih, W_hh (and b_ih, b_hh) of the teacher-forced GRU from the state
+    gradients; returns dict(d_w_ih, d_w_hh, d_b_ih, d_b_hh) of float32 tensors."""
+    B = x_t.shape[0]
+    K, d, H, dev = head.block, head.d, head.gru_hidden, head.device
+    _need(x_t, "x_t", torch.int32, (B,), dev)
+    _need(teacher, "teacher", torch.int32, (B, K), dev)
+    _need(gru_states, "gru_states", torch.float32, (B, K, H), dev)
+    _need(d_states, "d_states", torch.float32, (B, K, H), dev)
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    out = {"d_w_ih": f(3 * H, d), "d_w_hh": f(3 * H, H), "d_b_ih": f(3 * H) if d_b else None,
+           "d_b_hh": f(3 * H) if d_b else None}
+    sz = ctypes.c_size_t(0)
+    _check("domino_gru_backward_workspace_size",
+           load_library().domino_gru_backward_workspace_size(head.ref, B, ctypes.byref(sz)))
+    ws = torch.empty(max(int(sz.value), 1), dtype=torch.uint8, device=dev)
+    _check("domino_gru_backward", load_library().domino_gru_backward(
+        head.ref, B, _ptr(x_t), _ptr(teacher), _ptr(gru_states), _ptr(d_states), _ptr(out["d_w_ih"]),
+        _ptr(out["d_w_hh"]), _ptr(out["d_b_ih"]), _ptr(out["d_b_hh"]), _ptr(ws), ws.numel(), _stream_ptr(stream)))
     return out
 
 

@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdomino.so")
-SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "verify.hip", "base_draft.hip", "loss.hip", "backward.hip",
+SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "verify.hip", "base_draft.hip", "loss.hip", "backward.hip", "gru_backward.hip",
            "api.cpp", "validate.cpp"]
 
 HIPCC_FLAGS = [

@@ -148,6 +148,51 @@ extern "C" int domino_verify_sampled(int32_t batch, int32_t block, int32_t vocab
                                                   static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int domino_gru_backward_workspace_size(const domino_head* h, int32_t batch, size_t* bytes) {
+  if (!bytes) return DOMINO_ERR_NULL;
+  int st = domino::check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > domino::kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  *bytes = batch == 0 ? 0
+                      : domino::gru_backward_plan(batch, h->block, h->d, h->gru_hidden, domino::elem_size(h->dtype)).total;
+  return DOMINO_OK;
+}
+
+extern "C" int domino_gru_backward(const domino_head* h, int32_t batch, const int32_t* x_t, const int32_t* teacher,
+                                   const float* gru_states, const float* d_states, float* d_w_ih, float* d_w_hh,
+                                   float* d_b_ih, float* d_b_hh, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int st = domino::check_gru_backward_args(h, batch, x_t, teacher, gru_states, d_states, d_w_ih, d_w_hh, d_b_ih,
+                                           d_b_hh, workspace, workspace_bytes);
+  if (st != DOMINO_OK || batch == 0) return st;
+  const int num_cu = device_cu_count();
+  if (num_cu <= 0) return DOMINO_ERR_HIP;
+  domino::GruBackwardArgs g{};
+  g.dtype = h->dtype;
+  g.B = batch;
+  g.K = h->block;
+  g.d = h->d;
+  g.H = h->gru_hidden;
+  g.V = h->vocab;
+  g.embed = h->embed;
+  g.w_ih = h->w_ih;
+  g.w_hh = h->w_hh;
+  g.b_ih = h->b_ih;
+  g.b_hh = h->b_hh;
+  g.x_t = x_t;
+  g.teacher = teacher;
+  g.states = gru_states;
+  g.dg = d_states;
+  g.d_w_ih = d_w_ih;
+  g.d_w_hh = d_w_hh;
+  g.d_b_ih = d_b_ih;
+  g.d_b_hh = d_b_hh;
+  g.workspace = workspace;
+  g.plan = domino::gru_backward_plan(batch, h->block, h->d, h->gru_hidden, domino::elem_size(h->dtype));
+  return hip_status(domino::launch_gru_backward(g, num_cu, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int domino_correction_backward_workspace_size(const domino_head* h, int32_t batch, size_t* bytes) {
   if (!bytes) return DOMINO_ERR_NULL;
   int st = domino::check_head(h);

@@ -1,0 +1,198 @@
+// Backward through time of the teacher-forced GRU causal encoder ([notes]
+// §二.1(2) item 1 and §二.2(1)): from dg[b][i], the gradient of a loss with
+// respect to each state g_i from outside the recurrence, to the gradients of
+// W_ih, W_hh, b_ih and b_hh.  The forward is g_i = GRU(E[tok_i], g_{i-1}),
+// g_{-1} = 0, tok_0 = x_t, tok_i = teacher[i - 1]; PyTorch GRUCell gates
+// r | z | n with the reset applied to W_hn g + b_hn.
+//
+// Launches on the caller's stream, all float32 with sums in a fixed order:
+//   1. gb_gather_kernel: per row (b, i) the token's embedding row and the
+//      previous state (zero at i = 0);
+//   2. the pre-activations of every row, independent of the backward:
+//      a = W_ih e + b_ih (the tiled matrix-core GEMM on the gathered rows) and
+//      c = W_hh g_prev + b_hh (gb_matvec_kernel, float32 states);
+//   3. per position i = K-1 … 0: gb_elem_kernel (the gate derivatives of
+//      every row of position i: da, dc and the direct part z dg of the carry)
+//      and gb_carry_kernel (carry += W_hhᵀ dc, the gradient reaching g_{i-1});
+//   4. gb_outer_kernel twice: dW_ih = Σ da eᵀ, db_ih = Σ da and
+//      dW_hh = Σ dc g_prevᵀ, db_hh = Σ dc over every row.
+#include "common.h"
+#include "kernels.h"
+
+namespace domino {
+
+constexpr int kGbThreads = 256;
+constexpr int kGbWaves = kGbThreads / 64;
+constexpr int kGbQ = 16;  // output rows per thread in the outer-product sums
+
+// x_e[row][:] = E[tok(row)][:] (head dtype) and x_g[row][:] = states[b][i - 1][:] (zero at i = 0).
+template <class T>
+__global__ void gb_gather_kernel(int B, int K, int d, int H, int V, const int32_t* __restrict__ x_t,
+                                 const int32_t* __restrict__ teacher, const typename T::elem* __restrict__ embed,
+                                 const float* __restrict__ states, typename T::elem* __restrict__ x_e,
+                                 float* __restrict__ x_g, int32_t* __restrict__ tok) {
+  const int row = blockIdx.x, b = row / K, i = row - b * K;
+  int t = i == 0 ? x_t[b] : teacher[(size_t)b * K + i - 1];
+  t = min(max(t, 0), V - 1);
+  if (threadIdx.x == 0) tok[row] = t;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) x_e[(size_t)row * d + k] = embed[(size_t)t * d + k];
+  for (int k = threadIdx.x; k < H; k += blockDim.x)
+    x_g[(size_t)row * H + k] = i == 0 ? 0.f : states[((size_t)b * K + i - 1) * H + k];
+}
+
+// out[row][q] = W[q][:] . x[row][:] + bias[q] for q in the workgroup's 64 rows
+// of W (blockIdx.y); x (float32) staged in LDS; rows of W split over the
+// lanes of a wave, four at a time.
+template <class T>
+__global__ void __launch_bounds__(kGbThreads) gb_matvec_kernel(int N, int n, const typename T::elem* __restrict__ W,
+                                                               const typename T::elem* __restrict__ bias,
+                                                               const float* __restrict__ x, float* __restrict__ out) {
+  using E = typename T::elem;
+  constexpr int EPF = T::kPer16B;
+  extern __shared__ __attribute__((aligned(16))) float xs[];
+  const int row = blockIdx.x, n0 = blockIdx.y * 64;
+  for (int k = threadIdx.x; k < n; k += kGbThreads) xs[k] = x[(size_t)row * n + k];
+  __syncthreads();
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  for (int q0 = n0 + wave * 4; q0 < min(N, n0 + 64); q0 += kGbWaves * 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = lane * EPF; k < n; k += 64 * EPF) {
+      u32x4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = q0 + j < N ? ld16(W + (size_t)(q0 + j) * n + k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const E* e = reinterpret_cast<const E*>(&w[j]);
+#pragma unroll
+        for (int c = 0; c < EPF; ++c) acc[j] += T::to_f32(e[c]) * xs[k + c];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = acc[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0 && q0 + j < N) out[(size_t)row * N + q0 + j] = s + (bias ? T::to_f32(bias[q0 + j]) : 0.f);
+    }
+  }
+}
+
+// Gate derivatives of the rows of position i, one thread per (b, unit j).
+__global__ void gb_elem_kernel(int B, int K, int H, int i, const float* __restrict__ a, const float* __restrict__ c,
+                               const float* __restrict__ x_g, const float* __restrict__ dg, float* __restrict__ carry,
+                               float* __restrict__ da, float* __restrict__ dc) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
+  if (j >= H) return;
+  const size_t row = (size_t)b * K + i, G3 = 3 * (size_t)H;
+  const float* ar = a + row * G3;
+  const float* cr = c + row * G3;
+  const float r = sigmoidf_(ar[j] + cr[j]);
+  const float z = sigmoidf_(ar[H + j] + cr[H + j]);
+  const float n = tanhf(ar[2 * H + j] + r * cr[2 * H + j]);
+  const float gp = x_g[row * H + j];
+  const float d_g = dg[row * H + j] + carry[(size_t)b * H + j];
+  const float d_n = d_g * (1.f - z);
+  const float d_z = d_g * (gp - n);
+  const float d_pn = d_n * (1.f - n * n);
+  const float d_pr = d_pn * cr[2 * H + j] * r * (1.f - r);
+  const float d_pz = d_z * z * (1.f - z);
+  da[row * G3 + j] = d_pr;
+  da[row * G3 + H + j] = d_pz;
+  da[row * G3 + 2 * H + j] = d_pn;
+  dc[row * G3 + j] = d_pr;
+  dc[row * G3 + H + j] = d_pz;
+  dc[row * G3 + 2 * H + j] = d_pn * r;
+  carry[(size_t)b * H + j] = d_g * z;  // the direct part; gb_carry_kernel adds W_hhᵀ dc
+}
+
+// carry[b][j] += Σ_q W_hh[q][j] dc[row(b, i)][q], the sum over q in order.
+template <class T>
+__global__ void gb_carry_kernel(int K, int H, int i, const typename T::elem* __restrict__ w_hh,
+                                const float* __restrict__ dc, float* __restrict__ carry) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
+  if (j >= H) return;
+  const float* d = dc + ((size_t)b * K + i) * 3 * H;
+  float acc = 0.f;
+  for (int q = 0; q < 3 * H; ++q) acc += T::to_f32(w_hh[(size_t)q * H + j]) * d[q];
+  carry[(size_t)b * H + j] += acc;
+}
+
+// out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X in type X_T);
+// bias[q] = Σ_rows A[row][q] from the workgroups with blockIdx.x == 0.
+template <class XE>
+__global__ void __launch_bounds__(kGbThreads) gb_outer_kernel(int R, int Q, int N, const float* __restrict__ A,
+                                                              const XE* __restrict__ X, float* __restrict__ out,
+                                                              float* __restrict__ bias) {
+  const int k = blockIdx.x * kGbThreads + threadIdx.x, q0 = blockIdx.y * kGbQ;
+  const int nq = min(kGbQ, Q - q0);
+  float acc[kGbQ];
+#pragma unroll
+  for (int q = 0; q < kGbQ; ++q) acc[q] = 0.f;
+  if (k < N)
+    for (int row = 0; row < R; ++row) {
+      float x;
+      if constexpr (sizeof(XE) == 2)
+        x = bf16_to_f32(X[(size_t)row * N + k]);
+      else
+        x = X[(size_t)row * N + k];
+#pragma unroll
+      for (int q = 0; q < kGbQ; ++q)
+        if (q < nq) acc[q] += A[(size_t)row * Q + q0 + q] * x;
+    }
+  if (k < N)
+    for (int q = 0; q < nq; ++q) out[(size_t)(q0 + q) * N + k] = acc[q];
+  if (blockIdx.x == 0 && bias && (int)threadIdx.x < nq) {
+    float s = 0.f;
+    for (int row = 0; row < R; ++row) s += A[(size_t)row * Q + q0 + threadIdx.x];
+    bias[q0 + threadIdx.x] = s;
+  }
+}
+
+template <class T>
+static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream_t s) {
+  using E = typename T::elem;
+  const int B = g.B, K = g.K, d = g.d, H = g.H, V = g.V, R = B * K, G3 = 3 * H;
+  const GruBackwardPlan& pl = g.plan;
+  unsigned char* ws = static_cast<unsigned char*>(g.workspace);
+  E* x_e = reinterpret_cast<E*>(ws + pl.x_e);
+  float* x_g = reinterpret_cast<float*>(ws + pl.x_g);
+  float* a = reinterpret_cast<float*>(ws + pl.a);
+  float* c = reinterpret_cast<float*>(ws + pl.c);
+  float* da = reinterpret_cast<float*>(ws + pl.da);
+  float* dc = reinterpret_cast<float*>(ws + pl.dc);
+  float* carry = reinterpret_cast<float*>(ws + pl.carry);
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + pl.tok);
+  hipLaunchKernelGGL(gb_gather_kernel<T>, dim3(R), dim3(256), 0, s, B, K, d, H, V, g.x_t, g.teacher,
+                     static_cast<const E*>(g.embed), g.states, x_e, x_g, tok);
+  hipError_t e = launch_panel_gemm(g.dtype, x_e, d, R, g.w_ih, d, G3, d, g.b_ih, a, G3, num_cu, s);
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)H * sizeof(float);
+  if (lds > 65536) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gb_matvec_kernel<T>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(gb_matvec_kernel<T>, dim3(R, (G3 + 63) / 64), dim3(kGbThreads), lds, s, G3, H,
+                     static_cast<const E*>(g.w_hh), static_cast<const E*>(g.b_hh), x_g, c);
+  e = launch_fill_u64(reinterpret_cast<unsigned long long*>(carry), (B * H + 1) / 2, s);
+  if (e != hipSuccess) return e;
+  const dim3 eg((H + 255) / 256, B);
+  for (int i = K - 1; i >= 0; --i) {
+    hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, a, c, x_g, g.dg, carry, da, dc);
+    if (i > 0)
+      hipLaunchKernelGGL(gb_carry_kernel<T>, eg, dim3(256), 0, s, K, H, i, static_cast<const E*>(g.w_hh), dc,
+                         carry);
+  }
+  hipLaunchKernelGGL(gb_outer_kernel<E>, dim3((d + kGbThreads - 1) / kGbThreads, (G3 + kGbQ - 1) / kGbQ),
+                     dim3(kGbThreads), 0, s, R, G3, d, da, x_e, g.d_w_ih, g.d_b_ih);
+  hipLaunchKernelGGL(gb_outer_kernel<float>, dim3((H + kGbThreads - 1) / kGbThreads, (G3 + kGbQ - 1) / kGbQ),
+                     dim3(kGbThreads), 0, s, R, G3, H, dc, x_g, g.d_w_hh, g.d_b_hh);
+  return hipGetLastError();
+}
+
+hipError_t launch_gru_backward(const GruBackwardArgs& g, int num_cu, hipStream_t s) {
+  if (g.B <= 0) return hipSuccess;
+  return g.dtype == 1 ? gru_backward_t<Bf16>(g, num_cu, s) : gru_backward_t<F32>(g, num_cu, s);
+}
+
+}  // namespace domino

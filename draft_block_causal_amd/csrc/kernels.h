@@ -121,6 +121,45 @@ struct BackwardArgs {
 };
 hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
 
+// Backward through time of the teacher-forced GRU (gru_backward.hip).
+struct GruBackwardPlan {
+  size_t x_e, x_g, a, c, da, dc, carry, tok, total;  // byte offsets; workspace bytes
+};
+inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t R = (size_t)B * K, G3 = 3 * (size_t)H;
+  GruBackwardPlan p{};
+  size_t off = 0;
+  p.x_e = off;
+  off += up(R * d * elem);
+  p.x_g = off;
+  off += up(R * H * 4);
+  p.a = off;
+  off += up(R * G3 * 4);
+  p.c = off;
+  off += up(R * G3 * 4);
+  p.da = off;
+  off += up(R * G3 * 4);
+  p.dc = off;
+  off += up(R * G3 * 4);
+  p.carry = off;
+  off += up(((size_t)B * H + 1) / 2 * 8);
+  p.tok = off;
+  off += up(R * 4);
+  p.total = off;
+  return p;
+}
+struct GruBackwardArgs {
+  int dtype, B, K, d, H, V;
+  const void *embed, *w_ih, *w_hh, *b_ih, *b_hh;
+  const int32_t *x_t, *teacher;
+  const float *states, *dg;
+  float *d_w_ih, *d_w_hh, *d_b_ih, *d_b_hh;
+  void* workspace;
+  GruBackwardPlan plan;
+};
+hipError_t launch_gru_backward(const GruBackwardArgs& g, int num_cu, hipStream_t s);
+
 // Base-only drafting (base_draft.hip): tokens[b][i] picked from base[b][i][:]
 // alone (greedy, or Gumbel-max when temperature > 0); workspace holds B K
 // 64-bit keys.

@@ -172,6 +172,25 @@ int check_backward_args(const domino_head* h, int32_t batch, const void* hidden,
   return DOMINO_OK;
 }
 
+int check_gru_backward_args(const domino_head* h, int32_t batch, const int32_t* x_t, const int32_t* teacher,
+                            const float* gru_states, const float* d_states, const float* d_w_ih,
+                            const float* d_w_hh, const float* d_b_ih, const float* d_b_hh, const void* workspace,
+                            size_t workspace_bytes) {
+  int st = check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 0) return DOMINO_ERR_SHAPE;
+  if (batch > kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  if (batch == 0) return DOMINO_OK;
+  if (!x_t || !teacher || !gru_states || !d_states || !d_w_ih || !d_w_hh) return DOMINO_ERR_NULL;
+  for (const void* q : {(const void*)x_t, (const void*)teacher, (const void*)gru_states, (const void*)d_states,
+                        (const void*)d_w_ih, (const void*)d_w_hh, (const void*)d_b_ih, (const void*)d_b_hh})
+    if (reinterpret_cast<uintptr_t>(q) & 3u) return DOMINO_ERR_ALIGN;
+  const GruBackwardPlan pl = gru_backward_plan(batch, h->block, h->d, h->gru_hidden, elem_size(h->dtype));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < pl.total)
+    return DOMINO_ERR_WORKSPACE;
+  return DOMINO_OK;
+}
+
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes) {

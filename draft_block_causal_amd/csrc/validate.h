@@ -44,6 +44,10 @@ int check_loss_args(int32_t batch, int32_t block, int32_t vocab, const float* ba
 int check_backward_args(const domino_head* h, int32_t batch, const void* hidden, const float* gru_states,
                         const float* grad_final, const float* d_w2, const float* d_b2, const float* d_w1,
                         const float* d_b1, const float* d_states, const void* workspace, size_t workspace_bytes);
+int check_gru_backward_args(const domino_head* h, int32_t batch, const int32_t* x_t, const int32_t* teacher,
+                            const float* gru_states, const float* d_states, const float* d_w_ih,
+                            const float* d_w_hh, const float* d_b_ih, const float* d_b_hh, const void* workspace,
+                            size_t workspace_bytes);
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes);

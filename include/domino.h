@@ -308,6 +308,32 @@ int domino_correction_backward(const domino_head *head, int32_t batch, const voi
 int domino_correction_backward_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);
 
 /*
+ * Backward through time of the teacher-forced GRU causal encoder ([notes]
+ * §二.1(2) item 1, §二.2(1)).  The forward it differentiates is the one
+ * domino_draft_block runs with `teacher`: g_{-1} = 0, g_i = GRU(E[tok_i], g_{i-1}),
+ * tok_0 = x_t[b], tok_i = teacher[b, i - 1].  Given d_states, the gradient of a
+ * loss with respect to every g_i from outside the recurrence (the d_states of
+ * domino_correction_backward), it writes the gradients of W_ih [3H, d],
+ * W_hh [3H, H] and (NULL: skipped) b_ih, b_hh [3H], summed over every block
+ * and position; the embedding table is frozen.  Outputs are overwritten.
+ *
+ * x_t [batch] and teacher [batch, block] int32 (ids outside [0, V) are
+ * clamped); gru_states [batch, block, H] float32, the forward states;
+ * d_states [batch, block, H] float32; outputs float32, 4-byte aligned.
+ * workspace   device scratch of domino_gru_backward_workspace_size() bytes,
+ *             256-byte aligned.
+ * batch in 0 … 128 (0 is a no-op).  Arithmetic: float32 (the input
+ * pre-activations W_ih e of bf16 heads on the matrix cores), every sum in a
+ * fixed order.
+ */
+int domino_gru_backward(const domino_head *head, int32_t batch, const int32_t *x_t, const int32_t *teacher,
+                        const float *gru_states, const float *d_states, float *d_w_ih, float *d_w_hh,
+                        float *d_b_ih, float *d_b_hh, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes domino_gru_backward needs for `batch` blocks. */
+int domino_gru_backward_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

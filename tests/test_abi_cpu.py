@@ -302,3 +302,31 @@ def test_correction_backward_validation(lib):
     assert call(w=None) == E_WS
     assert call(wb=ws - 1) == E_WS
     assert call(B=0, x=None, g=None, G=None, dw2=None, dw1=None, w=None, wb=0) == OK
+
+
+def test_gru_backward_validation(lib):
+    h = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=256)
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_gru_backward_workspace_size(ctypes.byref(h), 2, ctypes.byref(sz)) == OK
+    ws = sz.value
+    assert ws > 0 and ws % 256 == 0
+    assert lib.domino_gru_backward_workspace_size(ctypes.byref(h), 129, ctypes.byref(sz)) == E_UNSUP
+    assert lib.domino_gru_backward_workspace_size(ctypes.byref(h), 1, None) == E_NULL
+    args = dict(B=2, x=0x20000, t=0x30000, g=0x40000, dg=0x50000, wi=0x60000, wh=0x70000, bi=0x80000, bh=0x90000,
+                w=0x100000, wb=ws)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.domino_gru_backward(ctypes.byref(h), a["B"], a["x"], a["t"], a["g"], a["dg"], a["wi"], a["wh"],
+                                       a["bi"], a["bh"], a["w"], a["wb"], None)
+
+    assert call() == E_HIP  # valid arguments, no GPU here
+    assert call(bi=None, bh=None) == E_HIP
+    assert call(B=-1) == E_SHAPE
+    assert call(B=129) == E_UNSUP
+    for k in ("x", "t", "g", "dg", "wi", "wh"):
+        assert call(**{k: None}) == E_NULL, k
+    assert call(g=0x40002) == E_ALIGN
+    assert call(w=None) == E_WS
+    assert call(wb=ws - 1) == E_WS
+    assert call(B=0, x=None, t=None, g=None, dg=None, wi=None, wh=None, w=None, wb=0) == OK
