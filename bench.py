@@ -215,7 +215,8 @@ def next_rows(args, w) -> int:
     bandwidth-bound kernel group against the 8 TB/s peak:
       train_forward: base logits + teacher-forced draft block (final logits and
                      GRU states out) + curriculum loss with both logit gradients
-                     written in place, then the backward through the correction head;
+                     written in place, then the backward through the correction head
+                     and through time of the GRU (the whole head's gradients);
       verify:        sampled-draft verification on synthetic target / draft logits;
       head_off:      base logits + base-only drafting, beside base logits + draft block."""
     import torch
@@ -267,13 +268,18 @@ def next_rows(args, w) -> int:
                                       workspace=ws)
     cl = lambda: D.domino_curriculum_loss(base, final, gold, 0.5, 0.9, loss=loss, grad_base=base,  # noqa: E731
                                           grad_final=final, workspace=lws)
-    bw = lambda: D.domino_correction_backward(head, hidden, states, final)  # noqa: E731
-    t_lm, t_tf, t_cl, t_bw = timed([lm, tf, cl, bw])
+    cbw = {}
+
+    def bw():
+        cbw["out"] = D.domino_correction_backward(head, hidden, states, final)
+
+    gb = lambda: D.domino_gru_backward(head, x_t, gold, states, cbw["out"]["d_states"])  # noqa: E731
+    t_lm, t_tf, t_cl, t_bw, t_gb = timed([lm, tf, cl, bw, gb])
     loss_bytes = 2 * B * K * V * 4 * 3  # pass 1 reads both tensors; the gradient pass reads and writes both
     out = {"train_forward": {"base_logits_ms": t_lm, "teacher_forced_draft_ms": t_tf, "curriculum_loss_ms": t_cl,
-                             "correction_backward_ms": t_bw,
+                             "correction_backward_ms": t_bw, "gru_backward_ms": t_gb,
                              "blocks_per_s": B / ((t_lm + t_tf + t_cl) * 1e-3),
-                             "with_backward_blocks_per_s": B / ((t_lm + t_tf + t_cl + t_bw) * 1e-3),
+                             "with_backward_blocks_per_s": B / ((t_lm + t_tf + t_cl + t_bw + t_gb) * 1e-3),
                              "loss_kernels_gb_s": loss_bytes / (t_cl * 1e-3) / 1e9,
                              "loss_kernels_hbm_frac": loss_bytes / (t_cl * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "loss_bytes": loss_bytes}}

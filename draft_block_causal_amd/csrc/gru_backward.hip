@@ -13,7 +13,8 @@
 //      c = W_hh g_prev + b_hh (gb_matvec_kernel, float32 states);
 //   3. per position i = K-1 … 0: gb_elem_kernel (the gate derivatives of
 //      every row of position i: da, dc and the direct part z dg of the carry)
-//      and gb_carry_kernel (carry += W_hhᵀ dc, the gradient reaching g_{i-1});
+//      and gb_carry_kernel (carry += W_hhᵀ dc, the gradient reaching g_{i-1},
+//      its 3H terms split over the waves of a workgroup);
 //   4. gb_outer_kernel twice: dW_ih = Σ da eᵀ, db_ih = Σ da and
 //      dW_hh = Σ dc g_prevᵀ, db_hh = Σ dc over every row.
 #include "common.h"
@@ -105,16 +106,37 @@ __global__ void gb_elem_kernel(int B, int K, int H, int i, const float* __restri
   carry[(size_t)b * H + j] = d_g * z;  // the direct part; gb_carry_kernel adds W_hhᵀ dc
 }
 
-// carry[b][j] += Σ_q W_hh[q][j] dc[row(b, i)][q], the sum over q in order.
+// carry[b][j] += Σ_q W_hh[q][j] dc[row(b, i)][q]: a workgroup takes 64 units j
+// (one per lane) of one block b; its 4 waves take a quarter of the 3H terms
+// each, eight loads in flight per lane, and the quarter sums are added in
+// wave order.
 template <class T>
-__global__ void gb_carry_kernel(int K, int H, int i, const typename T::elem* __restrict__ w_hh,
-                                const float* __restrict__ dc, float* __restrict__ carry) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
-  if (j >= H) return;
-  const float* d = dc + ((size_t)b * K + i) * 3 * H;
+__global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int K, int H, int i, const typename T::elem* __restrict__ w_hh,
+                                                              const float* __restrict__ dc, float* __restrict__ carry) {
+  __shared__ float part[kGbWaves][64];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int j = blockIdx.x * 64 + lane, b = blockIdx.y, G3 = 3 * H;
+  const float* d = dc + ((size_t)b * K + i) * G3;
+  const int qa = G3 * wave / kGbWaves, qb = G3 * (wave + 1) / kGbWaves;
   float acc = 0.f;
-  for (int q = 0; q < 3 * H; ++q) acc += T::to_f32(w_hh[(size_t)q * H + j]) * d[q];
-  carry[(size_t)b * H + j] += acc;
+  if (j < H) {
+    int q = qa;
+    for (; q + 8 <= qb; q += 8) {
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = T::to_f32(w_hh[(size_t)(q + u) * H + j]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += w[u] * d[q + u];
+    }
+    for (; q < qb; ++q) acc += T::to_f32(w_hh[(size_t)q * H + j]) * d[q];
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && j < H) {
+    float sum = part[0][lane];
+    for (int w = 1; w < kGbWaves; ++w) sum += part[w][lane];
+    carry[(size_t)b * H + j] += sum;
+  }
 }
 
 // out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X in type X_T);
@@ -180,8 +202,8 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
   for (int i = K - 1; i >= 0; --i) {
     hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, a, c, x_g, g.dg, carry, da, dc);
     if (i > 0)
-      hipLaunchKernelGGL(gb_carry_kernel<T>, eg, dim3(256), 0, s, K, H, i, static_cast<const E*>(g.w_hh), dc,
-                         carry);
+      hipLaunchKernelGGL(gb_carry_kernel<T>, dim3((H + 63) / 64, B), dim3(kGbThreads), 0, s, K, H, i,
+                         static_cast<const E*>(g.w_hh), dc, carry);
   }
   hipLaunchKernelGGL(gb_outer_kernel<E>, dim3((d + kGbThreads - 1) / kGbThreads, (G3 + kGbQ - 1) / kGbQ),
                      dim3(kGbThreads), 0, s, R, G3, d, da, x_e, g.d_w_ih, g.d_b_ih);
