@@ -180,32 +180,42 @@ __global__ void bw_dz_kernel(int R, int r, int S, const float* __restrict__ part
 }
 
 // dW1[q][k] = Σ_rows dz[row][q] x[row][k] for q0 .. q0 + 15; db1 from the
-// workgroups with blockIdx.x == 0.
+// workgroups with blockIdx.x == 0.  The dz values of 64 rows at a time are
+// staged in LDS (read as broadcasts).
 template <class T>
 __global__ void __launch_bounds__(kBwThreads) bw_dw1_kernel(int R, int d, int H, int r,
                                                             const typename T::elem* __restrict__ hidden,
                                                             const float* __restrict__ states,
                                                             const float* __restrict__ dz, float* __restrict__ dw1,
                                                             float* __restrict__ db1) {
+  __shared__ float zs[kBwRowsLds][kBwQDw1];
   const int k = blockIdx.x * kBwThreads + threadIdx.x, q0 = blockIdx.y * kBwQDw1, n = d + H;
   const int nq = min(kBwQDw1, r - q0);
   float acc[kBwQDw1];
 #pragma unroll
   for (int q = 0; q < kBwQDw1; ++q) acc[q] = 0.f;
-  if (k < n)
-    for (int row = 0; row < R; ++row) {
-      const float x = k < d ? T::to_f32(hidden[(size_t)row * d + k]) : states[(size_t)row * H + k - d];
-#pragma unroll
-      for (int q = 0; q < kBwQDw1; ++q)
-        if (q < nq) acc[q] += dz[(size_t)row * r + q0 + q] * x;
+  float bsum = 0.f;
+  for (int r0 = 0; r0 < R; r0 += kBwRowsLds) {
+    const int nr = min(kBwRowsLds, R - r0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kBwRowsLds * kBwQDw1; e += kBwThreads) {
+      const int rr = e / kBwQDw1, q = e % kBwQDw1;
+      zs[rr][q] = rr < nr && q < nq ? dz[(size_t)(r0 + rr) * r + q0 + q] : 0.f;
     }
+    __syncthreads();
+    if (blockIdx.x == 0 && (int)threadIdx.x < nq)
+      for (int rr = 0; rr < nr; ++rr) bsum += zs[rr][threadIdx.x];
+    if (k < n)
+      for (int rr = 0; rr < nr; ++rr) {
+        const int row = r0 + rr;
+        const float x = k < d ? T::to_f32(hidden[(size_t)row * d + k]) : states[(size_t)row * H + k - d];
+#pragma unroll
+        for (int q = 0; q < kBwQDw1; ++q) acc[q] += zs[rr][q] * x;
+      }
+  }
   if (k < n)
     for (int q = 0; q < nq; ++q) dw1[(size_t)(q0 + q) * n + k] = acc[q];
-  if (blockIdx.x == 0 && db1 && (int)threadIdx.x < nq) {
-    float sum = 0.f;
-    for (int row = 0; row < R; ++row) sum += dz[(size_t)row * r + q0 + threadIdx.x];
-    db1[q0 + threadIdx.x] = sum;
-  }
+  if (blockIdx.x == 0 && db1 && (int)threadIdx.x < nq) db1[q0 + threadIdx.x] = bsum;
 }
 
 // dg[row][j] = Σ_q dz[row][q] W1[q][d + j] for rows m0 .. m0 + 15.

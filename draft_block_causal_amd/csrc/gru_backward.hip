@@ -139,35 +139,45 @@ __global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int K, int H, int 
   }
 }
 
-// out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X in type X_T);
-// bias[q] = Σ_rows A[row][q] from the workgroups with blockIdx.x == 0.
+// out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X of type XE);
+// bias[q] = Σ_rows A[row][q] from the workgroups with blockIdx.x == 0.  The
+// A values of 64 rows at a time are staged in LDS (read as broadcasts).
+constexpr int kGbRowsLds = 64;
 template <class XE>
 __global__ void __launch_bounds__(kGbThreads) gb_outer_kernel(int R, int Q, int N, const float* __restrict__ A,
                                                               const XE* __restrict__ X, float* __restrict__ out,
                                                               float* __restrict__ bias) {
+  __shared__ float as[kGbRowsLds][kGbQ];
   const int k = blockIdx.x * kGbThreads + threadIdx.x, q0 = blockIdx.y * kGbQ;
   const int nq = min(kGbQ, Q - q0);
   float acc[kGbQ];
 #pragma unroll
   for (int q = 0; q < kGbQ; ++q) acc[q] = 0.f;
-  if (k < N)
-    for (int row = 0; row < R; ++row) {
-      float x;
-      if constexpr (sizeof(XE) == 2)
-        x = bf16_to_f32(X[(size_t)row * N + k]);
-      else
-        x = X[(size_t)row * N + k];
-#pragma unroll
-      for (int q = 0; q < kGbQ; ++q)
-        if (q < nq) acc[q] += A[(size_t)row * Q + q0 + q] * x;
+  float bsum = 0.f;
+  for (int r0 = 0; r0 < R; r0 += kGbRowsLds) {
+    const int nr = min(kGbRowsLds, R - r0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kGbRowsLds * kGbQ; e += kGbThreads) {
+      const int rr = e / kGbQ, q = e % kGbQ;
+      as[rr][q] = rr < nr && q < nq ? A[(size_t)(r0 + rr) * Q + q0 + q] : 0.f;
     }
+    __syncthreads();
+    if (blockIdx.x == 0 && (int)threadIdx.x < nq)
+      for (int rr = 0; rr < nr; ++rr) bsum += as[rr][threadIdx.x];
+    if (k < N)
+      for (int rr = 0; rr < nr; ++rr) {
+        float x;
+        if constexpr (sizeof(XE) == 2)
+          x = bf16_to_f32(X[(size_t)(r0 + rr) * N + k]);
+        else
+          x = X[(size_t)(r0 + rr) * N + k];
+#pragma unroll
+        for (int q = 0; q < kGbQ; ++q) acc[q] += as[rr][q] * x;
+      }
+  }
   if (k < N)
     for (int q = 0; q < nq; ++q) out[(size_t)(q0 + q) * N + k] = acc[q];
-  if (blockIdx.x == 0 && bias && (int)threadIdx.x < nq) {
-    float s = 0.f;
-    for (int row = 0; row < R; ++row) s += A[(size_t)row * Q + q0 + threadIdx.x];
-    bias[q0 + threadIdx.x] = s;
-  }
+  if (blockIdx.x == 0 && bias && (int)threadIdx.x < nq) bias[q0 + threadIdx.x] = bsum;
 }
 
 template <class T>
