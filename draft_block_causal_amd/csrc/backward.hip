@@ -7,8 +7,8 @@
 //   dg_i = W1[:, d:]ᵀ dz_i.
 // Launches on the caller's stream, all in float32 with every sum in a fixed
 // order (no atomics, so two calls give the same bits):
-//   1. bw_z_kernel     (R workgroups): z and u of each row, rows of W1 split
-//                      over the lanes of a wave;
+//   1. bw_z_kernel     (R x r / 64): z and u of each row, 64 outputs per
+//                      workgroup, rows of W1 split over the lanes of a wave;
 //   2. bw_dw2_kernel   (V / 256 x r / 32): dW2 and db2, one vocabulary entry
 //                      per thread, u staged in LDS 64 rows at a time;
 //   3. bw_du_kernel    (S vocabulary slices x R / 64 x r / 256): partial W2ᵀ G
@@ -17,7 +17,8 @@
 //   4. bw_dz_kernel    (R x r threads): the S partials added in slice order,
 //                      times SiLU'(z);
 //   5. bw_dw1_kernel   ((d + H) / 256 x r / 16): dW1 and db1;
-//   6. bw_dg_kernel    (H / 256 x R / 16): the state gradient.
+//   6. bw_dg_kernel    (H / 64 x R / 16): the state gradient, the r terms split
+//                      over the waves of a workgroup.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,12 +48,12 @@ __global__ void __launch_bounds__(kBwThreads) bw_z_kernel(int d, int H, int r, c
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [d + H]
-  const int row = blockIdx.x, n = d + H;
+  const int row = blockIdx.x, n = d + H, n0 = blockIdx.y * 64;  // outputs n0 .. n0 + 63 of the row
   for (int k = threadIdx.x; k < d; k += kBwThreads) xs[k] = T::to_f32(hidden[(size_t)row * d + k]);
   for (int k = threadIdx.x; k < H; k += kBwThreads) xs[d + k] = states[(size_t)row * H + k];
   __syncthreads();
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  for (int q0 = wave * 4; q0 < r; q0 += kBwWaves * 4) {
+  for (int q0 = n0 + wave * 4; q0 < min(r, n0 + 64); q0 += kBwWaves * 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int k = lane * EPF; k < n; k += 64 * EPF) {
       u32x4 w[4];
@@ -218,26 +219,43 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw1_kernel(int R, int d, int H,
   if (blockIdx.x == 0 && db1 && (int)threadIdx.x < nq) db1[q0 + threadIdx.x] = bsum;
 }
 
-// dg[row][j] = Σ_q dz[row][q] W1[q][d + j] for rows m0 .. m0 + 15.
+// dg[row][j] = Σ_q dz[row][q] W1[q][d + j] for rows m0 .. m0 + 15: a
+// workgroup takes 64 units j (one per lane); its 4 waves take a quarter of
+// the r terms each, with the 16 rows' dz in LDS, and the quarter sums are
+// added in wave order.
 template <class T>
 __global__ void __launch_bounds__(kBwThreads) bw_dg_kernel(int R, int d, int H, int r,
                                                            const typename T::elem* __restrict__ w1,
                                                            const float* __restrict__ dz, float* __restrict__ dg) {
-  const int j = blockIdx.x * kBwThreads + threadIdx.x, m0 = blockIdx.y * kBwRowsDg;
-  if (j >= H) return;
+  extern __shared__ __attribute__((aligned(16))) float zs[];  // [kBwRowsDg][r], then [kBwWaves][kBwRowsDg][64]
+  float* part = zs + kBwRowsDg * r;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int j = blockIdx.x * 64 + lane, m0 = blockIdx.y * kBwRowsDg;
   const int nr = min(kBwRowsDg, R - m0);
+  for (int e = threadIdx.x; e < kBwRowsDg * r; e += kBwThreads) {
+    const int i = e / r, q = e % r;
+    zs[e] = i < nr ? dz[(size_t)(m0 + i) * r + q] : 0.f;
+  }
+  __syncthreads();
+  const int qa = r * wave / kBwWaves, qb = r * (wave + 1) / kBwWaves;
   float acc[kBwRowsDg];
 #pragma unroll
   for (int i = 0; i < kBwRowsDg; ++i) acc[i] = 0.f;
-  for (int q = 0; q < r; ++q) {
-    const float w = T::to_f32(w1[(size_t)q * (d + H) + d + j]);
+  if (j < H)
+    for (int q = qa; q < qb; ++q) {
+      const float w = T::to_f32(w1[(size_t)q * (d + H) + d + j]);
 #pragma unroll
-    for (int i = 0; i < kBwRowsDg; ++i)
-      if (i < nr) acc[i] += dz[(size_t)(m0 + i) * r + q] * w;
-  }
+      for (int i = 0; i < kBwRowsDg; ++i) acc[i] += zs[i * r + q] * w;
+    }
 #pragma unroll
-  for (int i = 0; i < kBwRowsDg; ++i)
-    if (i < nr) dg[(size_t)(m0 + i) * H + j] = acc[i];
+  for (int i = 0; i < kBwRowsDg; ++i) part[(wave * kBwRowsDg + i) * 64 + lane] = acc[i];
+  __syncthreads();
+  if (wave == 0 && j < H)
+    for (int i = 0; i < nr; ++i) {
+      float sum = part[i * 64 + lane];
+      for (int w = 1; w < kBwWaves; ++w) sum += part[(w * kBwRowsDg + i) * 64 + lane];
+      dg[(size_t)(m0 + i) * H + j] = sum;
+    }
 }
 
 template <class T>
@@ -258,7 +276,7 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
+  hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R, (r + 63) / 64), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
                      static_cast<const E*>(a.b1), z, u);
   hipLaunchKernelGGL(bw_dw2_kernel, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
                      dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
@@ -268,9 +286,16 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
                      dz);
   hipLaunchKernelGGL(bw_dw1_kernel<T>, dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1),
                      dim3(kBwThreads), 0, s, R, d, H, r, hidden, a.states, dz, a.d_w1, a.d_b1);
-  if (a.d_states)
-    hipLaunchKernelGGL(bw_dg_kernel<T>, dim3((H + kBwThreads - 1) / kBwThreads, (R + kBwRowsDg - 1) / kBwRowsDg),
-                       dim3(kBwThreads), 0, s, R, d, H, r, w1, dz, a.d_states);
+  if (a.d_states) {
+    const size_t dg_lds = ((size_t)kBwRowsDg * r + (size_t)kBwWaves * kBwRowsDg * 64) * sizeof(float);
+    if (dg_lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_dg_kernel<T>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)dg_lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bw_dg_kernel<T>, dim3((H + 63) / 64, (R + kBwRowsDg - 1) / kBwRowsDg), dim3(kBwThreads),
+                       dg_lds, s, R, d, H, r, w1, dz, a.d_states);
+  }
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ inline BackwardPlan backward_plan(int R, int r, int V) {
   BackwardPlan p{};
   const long groups = (R + 63) / 64;
   long S = (512 + groups - 1) / groups;
-  const long smax = V / 1024 > 1 ? V / 1024 : 1;
+  const long smax = V / 512 > 1 ? V / 512 : 1;  // slices of at least 512 entries
   p.S = (int)(S < 1 ? 1 : S > smax ? smax : S);
   const size_t m = up((size_t)R * r * sizeof(float));
   p.z = 0;
