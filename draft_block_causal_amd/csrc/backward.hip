@@ -79,11 +79,18 @@ __global__ void __launch_bounds__(kBwThreads) bw_z_kernel(int d, int H, int r, c
 }
 
 // dW2[v][q0 .. q0 + 31] = Σ_rows G[row][v] u[row][q]; db2[v] = Σ_rows G[row][v] (blockIdx.y == 0).
+// ROWS_OUT: the finished 256 x 32 tile goes through LDS so that the stores
+// write whole 128-byte rows (each thread's own 32 values lie 4r bytes from its
+// neighbour's); used for up to 64 rows, where the stores dominate (at
+// Qwen3-8B shapes: one block 72 against 203 us, but 32 blocks 1.88 against
+// 1.14 ms, the tile's LDS lowering the occupancy of the longer accumulation).
+template <bool ROWS_OUT>
 __global__ void __launch_bounds__(kBwThreads) bw_dw2_kernel(int R, int V, int r, const float* __restrict__ G,
                                                             const float* __restrict__ u, float* __restrict__ dw2,
                                                             float* __restrict__ db2) {
   __shared__ float us[kBwRowsLds][kBwQDw2];
-  const int v = blockIdx.x * kBwThreads + threadIdx.x, q0 = blockIdx.y * kBwQDw2;
+  __shared__ float tile[ROWS_OUT ? kBwThreads : 1][kBwQDw2 + 1];
+  const int vb = blockIdx.x * kBwThreads, v = vb + threadIdx.x, q0 = blockIdx.y * kBwQDw2;
   const int nq = min(kBwQDw2, r - q0);
   float acc[kBwQDw2];
 #pragma unroll
@@ -105,9 +112,19 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw2_kernel(int R, int V, int r,
         for (int q = 0; q < kBwQDw2; ++q) acc[q] += g * us[rr][q];
       }
   }
-  if (v >= V) return;
-  for (int q = 0; q < nq; ++q) dw2[(size_t)v * r + q0 + q] = acc[q];
-  if (blockIdx.y == 0 && db2) db2[v] = gsum;
+  if (blockIdx.y == 0 && db2 && v < V) db2[v] = gsum;
+  if constexpr (ROWS_OUT) {
+#pragma unroll
+    for (int q = 0; q < kBwQDw2; ++q) tile[threadIdx.x][q] = acc[q];
+    __syncthreads();
+    for (int e = threadIdx.x; e < kBwThreads * kBwQDw2; e += kBwThreads) {
+      const int vl = e / kBwQDw2, q = e % kBwQDw2;
+      if (vb + vl < V && q < nq) dw2[(size_t)(vb + vl) * r + q0 + q] = tile[vl][q];
+    }
+  } else {
+    if (v >= V) return;
+    for (int q = 0; q < nq; ++q) dw2[(size_t)v * r + q0 + q] = acc[q];
+  }
 }
 
 // part[s][row][q] = Σ_{v in slice s} G[row][v] W2[v][q] for rows m0 .. m0 + 63
@@ -278,7 +295,8 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R, (r + 63) / 64), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
                      static_cast<const E*>(a.b1), z, u);
-  hipLaunchKernelGGL(bw_dw2_kernel, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
+  auto dw2_kern = R <= kBwRowsLds ? bw_dw2_kernel<true> : bw_dw2_kernel<false>;
+  hipLaunchKernelGGL(dw2_kern, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
                      dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
   hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu, (r + 255) / 256), dim3(kBwThreads),
                      0, s, R, V, r, a.grad, static_cast<const E*>(a.w2), part);
