@@ -55,8 +55,8 @@ __device__ __forceinline__ LsePart lse_add4(LsePart p, float x0, float x1, float
 // kLseThreads threads; thread 0 holds the result.  red: kLseWaves entries of
 // LDS.  Every thread of the workgroup must call it.  When the row and v0 are
 // 16-byte aligned the body reads 16 B per lane, two loads in flight per
-// thread; the (up to 3 + 2 * 4 * kLseThreads) entries past the last full
-// pair of loads are taken one by one.
+// thread, then the remaining whole 16-byte groups one load at a time; only
+// the last (at most 3) entries are taken one by one.
 __device__ inline LsePart block_lse(const float* __restrict__ row, long v0, long v1, float inv_t, LsePart* red) {
   LsePart p{-INFINITY, 0.f};
   long v = v0;
@@ -69,7 +69,13 @@ __device__ inline LsePart block_lse(const float* __restrict__ row, long v0, long
       p = lse_add4(p, a.x * inv_t, a.y * inv_t, a.z * inv_t, a.w * inv_t);
       p = lse_add4(p, b.x * inv_t, b.y * inv_t, b.z * inv_t, b.w * inv_t);
     }
-    v = v0 + nv;
+    // the remaining whole 16-byte groups, one per thread at a time
+    const long n4 = (v1 - v0) / 4;
+    for (long q = nv / 4 + threadIdx.x; q < n4; q += kLseThreads) {
+      const float4 a = r4[q];
+      p = lse_add4(p, a.x * inv_t, a.y * inv_t, a.z * inv_t, a.w * inv_t);
+    }
+    v = v0 + 4 * n4;
   }
   for (v += threadIdx.x; v < v1; v += kLseThreads) {
     const float x = row[v] * inv_t;
