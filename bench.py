@@ -310,6 +310,28 @@ def next_rows(args, w) -> int:
     return 0
 
 
+def cpu_only(args) -> int:
+    """The CPU oracle alone on one block of the workload: with every host thread
+    its BLAS uses, then limited to one thread."""
+    import domino_synth as S
+
+    w = S.get_workload(args.workload)
+    head_np, inp = S.make_workload(w, batch=1)
+    target = S.make_targets(S.make_tokens((1, w.block), w.vocab, seed=11), w.vocab, p=0.9, seed=1)
+    res = {"workload": w.name, "all_threads": cpu_baseline(w, head_np, inp, target)}
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover - threadpoolctl missing
+        threadpool_limits = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one = cpu_baseline(w, head_np, inp, target)
+        one["cores"] = 1
+        res["one_thread"] = one
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +357,9 @@ def main() -> int:
                     help="write a 512 MB buffer between steps (outside the timed events) so that every step starts "
                          "with the weights evicted from the on-die cache; value is then the mean of the per-step "
                          "HIP-event times")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="time only the CPU oracle on one block of the workload, with all host threads and with one "
+                         "(no GPU needed); prints one JSON line")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -343,6 +368,9 @@ def main() -> int:
         print(f"bench.py: this benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding of the path is a design, not an implementation.", file=sys.stderr)
         return 2
+
+    if args.cpu_only:
+        return cpu_only(args)
 
     import torch
 
