@@ -35,3 +35,14 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=300)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_cpu_only_mode_reports_both_thread_counts():
+    import json
+
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--cpu-only", "--workload", "tiny_f32_b1"],
+                         capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    line = json.loads(res.stdout.strip().splitlines()[-1])
+    assert line["all_threads"]["kind"] == "oracle" and line["all_threads"]["value"] > 0
+    assert line["one_thread"]["cores"] == 1 and line["one_thread"]["value"] > 0
