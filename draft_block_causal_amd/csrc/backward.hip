@@ -5,8 +5,8 @@
 //   dW2 = Σ_i G_i u_iᵀ, db2 = Σ_i G_i, du_i = W2ᵀ G_i,
 //   dz_i = du_i ⊙ SiLU'(z_i), dW1 = Σ_i dz_i x_iᵀ, db1 = Σ_i dz_i,
 //   dg_i = W1[:, d:]ᵀ dz_i.
-// Launches on the caller's stream, all in float32 with every sum in a fixed
-// order (no atomics, so two calls give the same bits):
+// Launches on the caller's stream, every sum in a fixed order (no atomics, so
+// two calls give the same bits).  float32 heads, all on the vector ALUs:
 //   1. bw_z_kernel     (R x r / 64): z and u of each row, 64 outputs per
 //                      workgroup, rows of W1 split over the lanes of a wave;
 //   2. bw_dw2_kernel   (V / 256 x r / 32): dW2 and db2, one vocabulary entry
@@ -19,6 +19,11 @@
 //   5. bw_dw1_kernel   ((d + H) / 256 x r / 16): dW1 and db1;
 //   6. bw_dg_kernel    (H / 64 x R / 16): the state gradient, the r terms split
 //                      over the waves of a workgroup.
+// bf16 heads replace 2 and 3 by bw_split_kernel (G re-laid along both axes,
+// db2), bw_w2t_kernel, bw_us_kernel and two launches of the tiled bf16 GEMM
+// on the matrix cores (dW2, and the du partials over vocabulary slices).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -275,6 +280,106 @@ __global__ void __launch_bounds__(kBwThreads) bw_dg_kernel(int R, int d, int H, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 heads: the two large contractions on the matrix cores.  The float32
+// operands are split as x = hi + lo (hi = x truncated to bf16, lo = the
+// remainder rounded to bf16, about 16 significant bits together) and the
+// products expanded, in the tiled bf16 GEMM:
+//   du  = G W2 = [G_hi | G_lo] [W2 ; W2]     split-K partials over vocabulary slices,
+//   dW2 = G^T u = G_hi^T u_hi + G_lo^T u_hi + G_hi^T u_lo, stored as [V][r].
+// Both GEMM operands are K-contiguous, so G, W2 and u are re-laid first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void bw_split(float x, uint32_t& h, uint32_t& l) {
+  const uint32_t t = __float_as_uint(x) & 0xFFFF0000u;
+  h = t >> 16;
+  l = f32_to_bf16_rne(x - __uint_as_float(t));
+}
+
+// One pass over G [R][V] (64 columns per workgroup, 32 rows per round):
+// gs [R][2 Vp] = hi | lo along the vocabulary (zero past V), gt [V][2 Rp] =
+// hi | lo along the rows (zero past R), and db2[v] = the column sums of G.
+__global__ void __launch_bounds__(kBwThreads) bw_split_kernel(int R, int V, int Vp, int Rp, const float* __restrict__ G,
+                                                              uint16_t* __restrict__ gs, uint16_t* __restrict__ gt,
+                                                              float* __restrict__ db2) {
+  __shared__ float t[32][65];
+  __shared__ float csum[4][64];
+  const int v0 = blockIdx.x * 64, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tv = tid >> 2, tk = (tid & 3) * 8;  // transposed stores: column tv, rows tk .. tk + 7
+  const int v = v0 + lane;
+  float colsum = 0.f;
+  for (int rc = 0; rc < Rp; rc += 32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = rc + wave * 8 + j;
+      const float g = row < R && v < V ? G[(size_t)row * V + v] : 0.f;
+      t[wave * 8 + j][lane] = g;
+      if (row < R) {
+        uint32_t h, l;
+        bw_split(g, h, l);
+        gs[(size_t)row * 2 * Vp + v] = (uint16_t)h;
+        gs[(size_t)row * 2 * Vp + Vp + v] = (uint16_t)l;
+      }
+    }
+    __syncthreads();
+    if (v0 + tv < V) {
+      uint32_t h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = t[tk + e][tv];
+        colsum += g;
+        bw_split(g, h[e], l[e]);
+      }
+      u32x4 hv, lv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hv[q] = h[2 * q] | (h[2 * q + 1] << 16);
+        lv[q] = l[2 * q] | (l[2 * q + 1] << 16);
+      }
+      uint16_t* dst = gt + (size_t)(v0 + tv) * 2 * Rp + rc + tk;
+      st16(dst, hv);
+      st16(dst + Rp, lv);
+    }
+    __syncthreads();
+  }
+  csum[tid & 3][tv] = colsum;
+  __syncthreads();
+  if (db2 && tid < 64 && v0 + tid < V) db2[v0 + tid] = (csum[0][tid] + csum[1][tid]) + (csum[2][tid] + csum[3][tid]);
+}
+
+// w2t [r][Vp] = W2^T (zero past V); 64 vocabulary rows x 32 columns per workgroup.
+__global__ void __launch_bounds__(kBwThreads) bw_w2t_kernel(int V, int r, int Vp, const uint16_t* __restrict__ w2,
+                                                            uint16_t* __restrict__ w2t) {
+  __shared__ uint16_t tw[64][34];
+  const int v0 = blockIdx.x * 64, q0 = blockIdx.y * 32, tid = threadIdx.x;
+  {
+    const int vv = tid >> 2, q8 = (tid & 3) * 8;
+    const u32x4 x = v0 + vv < V ? ld16(w2 + (size_t)(v0 + vv) * r + q0 + q8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tw[vv][q8 + 2 * q] = (uint16_t)(x[q] & 0xFFFFu);
+      tw[vv][q8 + 2 * q + 1] = (uint16_t)(x[q] >> 16);
+    }
+  }
+  __syncthreads();
+  const int q = tid >> 3, v8 = (tid & 7) * 8;
+  u32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = (uint32_t)tw[v8 + 2 * e][q] | ((uint32_t)tw[v8 + 2 * e + 1][q] << 16);
+  st16(w2t + (size_t)(q0 + q) * Vp + v0 + v8, y);
+}
+
+// us [r][3 Rp] = u_hi^T | u_hi^T | u_lo^T (zero past R).
+__global__ void bw_us_kernel(int R, int r, int Rp, const float* __restrict__ u, uint16_t* __restrict__ us) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x, q = blockIdx.y;
+  if (k >= Rp) return;
+  uint32_t h, l;
+  bw_split(k < R ? u[(size_t)k * r + q] : 0.f, h, l);
+  uint16_t* dst = us + (size_t)q * 3 * Rp + k;
+  dst[0] = (uint16_t)h;
+  dst[Rp] = (uint16_t)h;
+  dst[2 * Rp] = (uint16_t)l;
+}
+
 template <class T>
 static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   using E = typename T::elem;
@@ -295,11 +400,32 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R, (r + 63) / 64), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
                      static_cast<const E*>(a.b1), z, u);
-  auto dw2_kern = R <= kBwRowsLds ? bw_dw2_kernel<true> : bw_dw2_kernel<false>;
-  hipLaunchKernelGGL(dw2_kern, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
-                     dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
-  hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu, (r + 255) / 256), dim3(kBwThreads),
-                     0, s, R, V, r, a.grad, static_cast<const E*>(a.w2), part);
+  if (pl.mfma) {
+    if constexpr (std::is_same<T, Bf16>::value) {
+      uint16_t* gs = reinterpret_cast<uint16_t*>(ws + pl.gs);
+      uint16_t* gt = reinterpret_cast<uint16_t*>(ws + pl.gt);
+      uint16_t* w2t = reinterpret_cast<uint16_t*>(ws + pl.w2t);
+      uint16_t* us = reinterpret_cast<uint16_t*>(ws + pl.us);
+      const int Vp = pl.Vp, Rp = pl.Rp;
+      hipLaunchKernelGGL(bw_split_kernel, dim3(Vp / 64), dim3(kBwThreads), 0, s, R, V, Vp, Rp, a.grad, gs, gt,
+                         a.d_b2);
+      hipLaunchKernelGGL(bw_w2t_kernel, dim3(Vp / 64, r / 32), dim3(kBwThreads), 0, s, V, r, Vp,
+                         static_cast<const uint16_t*>(a.w2), w2t);
+      hipLaunchKernelGGL(bw_us_kernel, dim3((Rp + 255) / 256, r), dim3(256), 0, s, R, r, Rp, u, us);
+      hipError_t e = launch_gemm_bf16_tn_wrapt(us, 3 * Rp, r, gt, 2 * Rp, V, 3 * Rp, 2 * Rp, a.d_w2, r, s);
+      if (e != hipSuccess) return e;
+      e = launch_gemm_bf16_tn_splitk(gs, 2 * Vp, R, w2t, Vp, r, pl.kc, pl.S, Vp, part, r, (size_t)R * r, s);
+      if (e != hipSuccess) return e;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    auto dw2_kern = R <= kBwRowsLds ? bw_dw2_kernel<true> : bw_dw2_kernel<false>;
+    hipLaunchKernelGGL(dw2_kern, dim3((V + kBwThreads - 1) / kBwThreads, (r + kBwQDw2 - 1) / kBwQDw2),
+                       dim3(kBwThreads), 0, s, R, V, r, a.grad, u, a.d_w2, a.d_b2);
+    hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu, (r + 255) / 256),
+                       dim3(kBwThreads), 0, s, R, V, r, a.grad, static_cast<const E*>(a.w2), part);
+  }
   hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 255) / 256)), dim3(256), 0, s, R, r, pl.S, part, z,
                      dz);
   hipLaunchKernelGGL(bw_dw1_kernel<T>, dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1),

@@ -78,19 +78,40 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int BM>
+// MODE selects what a launch computes:
+//   kPlain   C = A W^T (+ bias), the XCD-grouped block order above;
+//   kSplitK  blockIdx.y = slice s of K: A columns s K .. s K + K - 1 against W
+//            columns (s K) mod w_wrap .., written to C + s c_slice (partial
+//            products; K must divide w_wrap); blocks in plain (m, n) order,
+//            since few N tiles would leave XCDs idle in the grouped order;
+//   kWrapT   W column k is read as k mod w_wrap (one wrap at most), and C is
+//            stored transposed, C[n][m] at C + n ldc + m.
+enum GemmMode { kPlain = 0, kSplitK = 1, kWrapT = 2 };
+
+template <int BM, int MODE>
 __global__ void __launch_bounds__(kGThreads, 1)
     gemm_bf16_tn_big_kernel(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W, int ldw,
                             int N, int K, const uint16_t* __restrict__ bias, float* __restrict__ C, int ldc, int num_m,
-                            int num_n) {
+                            int num_n, int w_wrap, size_t c_slice) {
   using BT = BigTile<BM>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int b = blockIdx.x;
-  const int xcd = b % kXcds, local = b / kXcds;
-  const int n_per_xcd = (num_n + kXcds - 1) / kXcds;
-  const int nl = local / num_m, mt = local - nl * num_m;
-  const int nt = nl * kXcds + xcd;
-  if (nl >= n_per_xcd || nt >= num_n) return;
+  int mt, nt;
+  if constexpr (MODE == kSplitK) {
+    mt = b % num_m;
+    nt = b / num_m;
+    const int k0 = (int)blockIdx.y * K;
+    A += k0;
+    W += k0 >= w_wrap ? k0 - w_wrap : k0;
+    C += (size_t)blockIdx.y * c_slice;
+  } else {
+    const int xcd = b % kXcds, local = b / kXcds;
+    const int n_per_xcd = (num_n + kXcds - 1) / kXcds;
+    const int nl = local / num_m;
+    mt = local - nl * num_m;
+    nt = nl * kXcds + xcd;
+    if (nl >= n_per_xcd || nt >= num_n) return;
+  }
   const int m0 = mt * BM, n0 = nt * BT::kBN;
 
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -119,10 +140,14 @@ __global__ void __launch_bounds__(kGThreads, 1)
     for (int i = 0; i < BT::kALoads; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(ag[i] + (size_t)kt * BT::kRow),
                                        (lptr_t)(sA + (wave * BT::kALoads + i) * 1024), 16, 0, 0);
+    size_t wk = (size_t)kt * BT::kRow;
+    if constexpr (MODE == kWrapT) {
+      if (kt * BT::kBK >= w_wrap) wk -= (size_t)w_wrap * 2;
+    }
 #pragma unroll
     for (int i = 0; i < BT::kWLoads; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(wg[i] + (size_t)kt * BT::kRow),
-                                       (lptr_t)(sW + (wave * BT::kWLoads + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(wg[i] + wk), (lptr_t)(sW + (wave * BT::kWLoads + i) * 1024), 16, 0,
+                                       0);
   };
   // fragment reads: row r = base + col, chunk grp -> slot grp ^ ((r >> 2) & 3) (base % 16 == 0)
   const int fslot = (grp ^ ((col >> 2) & 3)) * 16;
@@ -161,32 +186,42 @@ __global__ void __launch_bounds__(kGThreads, 1)
   for (int j = 0; j < BT::kFW; ++j) {
     const int n = n0 + wn * BT::kFW * 16 + j * 16 + col;
     if (n >= N) continue;
-    const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+    if constexpr (MODE == kWrapT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 128 + i * 16 + grp * 4 + q;
-        if (m < M) C[(size_t)m * ldc + n] = acc[i][j][q] + bv;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 128 + i * 16 + grp * 4 + q;
+          if (m < M) C[(size_t)n * ldc + m] = acc[i][j][q];
+        }
+    } else {
+      const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 128 + i * 16 + grp * 4 + q;
+          if (m < M) C[(size_t)m * ldc + n] = acc[i][j][q] + bv;
+        }
+    }
   }
 }
 
-template <int BM>
+template <int BM, int MODE>
 static hipError_t launch_big(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
-                             float* C, int ldc, hipStream_t s) {
+                             float* C, int ldc, int slices, int w_wrap, size_t c_slice, hipStream_t s) {
   using BT = BigTile<BM>;
   const int num_m = (M + BM - 1) / BM, num_n = (N + BT::kBN - 1) / BT::kBN;
   const int n_per_xcd = (num_n + kXcds - 1) / kXcds;
-  const long blocks = (long)n_per_xcd * num_m * kXcds;
-  if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
+  const long blocks = MODE == kSplitK ? (long)num_m * num_n : (long)n_per_xcd * num_m * kXcds;
+  if (blocks > 0x7FFFFFFF || slices > 65535) return hipErrorNotSupported;
   const size_t lds = (size_t)BT::kStages * BT::kStage;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_tn_big_kernel<BM>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* fn = reinterpret_cast<const void*>(gemm_bf16_tn_big_kernel<BM, MODE>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_bf16_tn_big_kernel<BM>, dim3((unsigned)blocks), dim3(kGThreads), lds, s,
-                     static_cast<const uint16_t*>(A), lda, M, static_cast<const uint16_t*>(W), ldw, N, K,
-                     static_cast<const uint16_t*>(bias), C, ldc, num_m, num_n);
+  hipLaunchKernelGGL((gemm_bf16_tn_big_kernel<BM, MODE>), dim3((unsigned)blocks, (unsigned)slices), dim3(kGThreads),
+                     lds, s, static_cast<const uint16_t*>(A), lda, M, static_cast<const uint16_t*>(W), ldw, N, K,
+                     static_cast<const uint16_t*>(bias), C, ldc, num_m, num_n, w_wrap, c_slice);
   return hipGetLastError();
 }
 
@@ -194,8 +229,24 @@ hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int
                                float* C, int ldc, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % BigTile<256>::kBK) return hipErrorNotSupported;
-  return M >= 256 ? launch_big<256>(A, lda, M, W, ldw, N, K, bias, C, ldc, s)
-                  : launch_big<128>(A, lda, M, W, ldw, N, K, bias, C, ldc, s);
+  return M >= 256 ? launch_big<256, kPlain>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s)
+                  : launch_big<128, kPlain>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
 }
 
+hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void* W, int ldw, int N, int kc,
+                                      int slices, int w_wrap, float* C, int ldc, size_t c_slice, hipStream_t s) {
+  if (M <= 0 || N <= 0 || slices <= 0) return hipSuccess;
+  if (kc <= 0 || kc % BigTile<256>::kBK || w_wrap <= 0 || w_wrap % kc) return hipErrorNotSupported;
+  return M >= 256 ? launch_big<256, kSplitK>(A, lda, M, W, ldw, N, kc, nullptr, C, ldc, slices, w_wrap, c_slice, s)
+                  : launch_big<128, kSplitK>(A, lda, M, W, ldw, N, kc, nullptr, C, ldc, slices, w_wrap, c_slice, s);
+}
+
+hipError_t launch_gemm_bf16_tn_wrapt(const void* A, int lda, int M, const void* W, int ldw, int N, int K, int w_wrap,
+                                     float* C, int ldc, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % BigTile<256>::kBK || w_wrap % BigTile<256>::kBK || w_wrap <= 0 || K > 2 * w_wrap)
+    return hipErrorNotSupported;
+  return M >= 256 ? launch_big<256, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, 0, s)
+                  : launch_big<128, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, 0, s);
+}
 }  // namespace domino

@@ -34,6 +34,13 @@ hipError_t launch_p_partials(const void* A, int M, int lda, const void* w1, int 
 // Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 32 == 0 (else hipErrorNotSupported).
 hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
                                float* C, int ldc, hipStream_t s);
+// Split-K partial products: slice s of `slices` multiplies A columns s kc ..
+// s kc + kc - 1 by W columns (s kc) mod w_wrap .. and writes C + s c_slice.
+hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void* W, int ldw, int N, int kc,
+                                      int slices, int w_wrap, float* C, int ldc, size_t c_slice, hipStream_t s);
+// C[n][m] = sum_k A[m][k] W[n][k mod w_wrap] (K <= 2 w_wrap), stored transposed.
+hipError_t launch_gemm_bf16_tn_wrapt(const void* A, int lda, int M, const void* W, int ldw, int N, int K, int w_wrap,
+                                     float* C, int ldc, hipStream_t s);
 
 struct LoopArgs {
   int dtype;
@@ -93,22 +100,55 @@ hipError_t launch_verify_sampled(int B, int K, int V, const float* target, const
 
 // Backward through the correction head (backward.hip).
 struct BackwardPlan {
-  int S;  // vocabulary slices of the du partials
-  size_t z, u, dz, part, total;  // byte offsets of [R][r], [R][r], [R][r], [S][R][r] float32; workspace bytes
+  int S;     // slices of the du partials (vocabulary slices; bf16: hi and lo halves)
+  int mfma;  // bf16 head: W2^T G and G^T u on the matrix cores
+  int kc, Vp, Rp;  // (mfma) vocabulary entries per slice, padded vocabulary, padded rows
+  // byte offsets of z, u, dz [R][r] and part [S][R][r] (float32), and with
+  // mfma of gs [R][2 Vp], gt [V][2 Rp], w2t [r][Vp], us [r][3 Rp] (bf16); workspace bytes
+  size_t z, u, dz, part, gs, gt, w2t, us, total;
 };
-inline BackwardPlan backward_plan(int R, int r, int V) {
+inline BackwardPlan backward_plan(int R, int r, int V, int dtype) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BackwardPlan p{};
-  const long groups = (R + 63) / 64;
-  long S = (512 + groups - 1) / groups;
-  const long smax = V / 512 > 1 ? V / 512 : 1;  // slices of at least 512 entries
-  p.S = (int)(S < 1 ? 1 : S > smax ? smax : S);
+  if (dtype == 1) {
+    const long bm = R >= 256 ? 256 : 128;
+    const long tiles = ((R + bm - 1) / bm) * ((r + 255) / 256);
+    long half = 128 / tiles;
+    const long hmax = (V + 511) / 512;  // slices of at least 512 entries
+    if (half > hmax) half = hmax;
+    if (half < 1) half = 1;
+    p.mfma = 1;
+    p.kc = (int)(64 * ((V + 64 * half - 1) / (64 * half)));
+    p.Vp = (int)(half * p.kc);
+    p.Rp = (R + 31) / 32 * 32;
+    p.S = (int)(2 * half);
+  } else {
+    const long groups = (R + 63) / 64;
+    long S = (512 + groups - 1) / groups;
+    const long smax = V / 512 > 1 ? V / 512 : 1;  // slices of at least 512 entries
+    p.S = (int)(S < 1 ? 1 : S > smax ? smax : S);
+  }
   const size_t m = up((size_t)R * r * sizeof(float));
-  p.z = 0;
-  p.u = m;
-  p.dz = 2 * m;
-  p.part = 3 * m;
-  p.total = 3 * m + up((size_t)p.S * R * r * sizeof(float));
+  size_t off = 0;
+  p.z = off;
+  off += m;
+  p.u = off;
+  off += m;
+  p.dz = off;
+  off += m;
+  p.part = off;
+  off += up((size_t)p.S * R * r * sizeof(float));
+  if (p.mfma) {
+    p.gs = off;
+    off += up((size_t)R * 2 * p.Vp * 2);
+    p.gt = off;
+    off += up((size_t)V * 2 * p.Rp * 2);
+    p.w2t = off;
+    off += up((size_t)r * p.Vp * 2);
+    p.us = off;
+    off += up((size_t)r * 3 * p.Rp * 2);
+  }
+  p.total = off;
   return p;
 }
 struct BackwardArgs {
