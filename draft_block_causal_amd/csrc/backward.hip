@@ -295,55 +295,74 @@ __device__ __forceinline__ void bw_split(float x, uint32_t& h, uint32_t& l) {
   l = f32_to_bf16_rne(x - __uint_as_float(t));
 }
 
-// One pass over G [R][V] (64 columns per workgroup, 32 rows per round):
+// One pass over G [R][V] (256 columns per workgroup, 32 rows per round):
 // gs [R][2 Vp] = hi | lo along the vocabulary (zero past V), gt [V][2 Rp] =
-// hi | lo along the rows (zero past R), and db2[v] = the column sums of G.
+// hi | lo along the rows (zero past R), and db2[v] = the column sums of G in
+// row order.  VEC: V % 4 == 0 and G 16-byte aligned, rows read as float4.
+template <bool VEC>
 __global__ void __launch_bounds__(kBwThreads) bw_split_kernel(int R, int V, int Vp, int Rp, const float* __restrict__ G,
                                                               uint16_t* __restrict__ gs, uint16_t* __restrict__ gt,
                                                               float* __restrict__ db2) {
-  __shared__ float t[32][65];
-  __shared__ float csum[4][64];
-  const int v0 = blockIdx.x * 64, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tv = tid >> 2, tk = (tid & 3) * 8;  // transposed stores: column tv, rows tk .. tk + 7
-  const int v = v0 + lane;
+  __shared__ __attribute__((aligned(16))) float t[32][260];
+  const int v0 = blockIdx.x * 256, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int v = v0 + lane * 4;  // this lane's 4 columns in the row-wise phase
+  const int vt = v0 + tid;      // this thread's column in the transposed phase
   float colsum = 0.f;
   for (int rc = 0; rc < Rp; rc += 32) {
+    float4 g[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = rc + wave * 8 + j;
-      const float g = row < R && v < V ? G[(size_t)row * V + v] : 0.f;
-      t[wave * 8 + j][lane] = g;
-      if (row < R) {
-        uint32_t h, l;
-        bw_split(g, h, l);
-        gs[(size_t)row * 2 * Vp + v] = (uint16_t)h;
-        gs[(size_t)row * 2 * Vp + Vp + v] = (uint16_t)l;
+      const float* src = G + (size_t)row * V + v;
+      if constexpr (VEC) {
+        g[j] = row < R && v < V ? *reinterpret_cast<const float4*>(src) : float4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        g[j].x = row < R && v < V ? src[0] : 0.f;
+        g[j].y = row < R && v + 1 < V ? src[1] : 0.f;
+        g[j].z = row < R && v + 2 < V ? src[2] : 0.f;
+        g[j].w = row < R && v + 3 < V ? src[3] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = rc + wave * 8 + j;
+      *reinterpret_cast<float4*>(&t[wave * 8 + j][lane * 4]) = g[j];
+      if (row < R && v < Vp) {
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        bw_split(g[j].x, h0, l0);
+        bw_split(g[j].y, h1, l1);
+        bw_split(g[j].z, h2, l2);
+        bw_split(g[j].w, h3, l3);
+        uint16_t* dst = gs + (size_t)row * 2 * Vp + v;
+        *reinterpret_cast<uint2*>(dst) = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+        *reinterpret_cast<uint2*>(dst + Vp) = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
       }
     }
     __syncthreads();
-    if (v0 + tv < V) {
-      uint32_t h[8], l[8];
+    if (vt < V) {
+      uint16_t* dst = gt + (size_t)vt * 2 * Rp + rc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g = t[tk + e][tv];
-        colsum += g;
-        bw_split(g, h[e], l[e]);
-      }
-      u32x4 hv, lv;
+      for (int k8 = 0; k8 < 32; k8 += 8) {
+        uint32_t h[8], l[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hv[q] = h[2 * q] | (h[2 * q + 1] << 16);
-        lv[q] = l[2 * q] | (l[2 * q + 1] << 16);
+        for (int e = 0; e < 8; ++e) {
+          const float x = t[k8 + e][tid];
+          colsum += x;
+          bw_split(x, h[e], l[e]);
+        }
+        u32x4 hv, lv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = h[2 * q] | (h[2 * q + 1] << 16);
+          lv[q] = l[2 * q] | (l[2 * q + 1] << 16);
+        }
+        st16(dst + k8, hv);
+        st16(dst + Rp + k8, lv);
       }
-      uint16_t* dst = gt + (size_t)(v0 + tv) * 2 * Rp + rc + tk;
-      st16(dst, hv);
-      st16(dst + Rp, lv);
     }
     __syncthreads();
   }
-  csum[tid & 3][tv] = colsum;
-  __syncthreads();
-  if (db2 && tid < 64 && v0 + tid < V) db2[v0 + tid] = (csum[0][tid] + csum[1][tid]) + (csum[2][tid] + csum[3][tid]);
+  if (db2 && vt < V) db2[vt] = colsum;
 }
 
 // w2t [r][Vp] = W2^T (zero past V); 64 vocabulary rows x 32 columns per workgroup.
@@ -407,8 +426,9 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
       uint16_t* w2t = reinterpret_cast<uint16_t*>(ws + pl.w2t);
       uint16_t* us = reinterpret_cast<uint16_t*>(ws + pl.us);
       const int Vp = pl.Vp, Rp = pl.Rp;
-      hipLaunchKernelGGL(bw_split_kernel, dim3(Vp / 64), dim3(kBwThreads), 0, s, R, V, Vp, Rp, a.grad, gs, gt,
-                         a.d_b2);
+      const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(a.grad) & 15u) == 0;
+      hipLaunchKernelGGL(vec ? bw_split_kernel<true> : bw_split_kernel<false>, dim3((Vp + 255) / 256),
+                         dim3(kBwThreads), 0, s, R, V, Vp, Rp, a.grad, gs, gt, a.d_b2);
       hipLaunchKernelGGL(bw_w2t_kernel, dim3(Vp / 64, r / 32), dim3(kBwThreads), 0, s, V, r, Vp,
                          static_cast<const uint16_t*>(a.w2), w2t);
       hipLaunchKernelGGL(bw_us_kernel, dim3((Rp + 255) / 256, r), dim3(256), 0, s, R, r, Rp, u, us);

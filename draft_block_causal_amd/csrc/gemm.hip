@@ -85,7 +85,8 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 //            products; K must divide w_wrap); blocks in plain (m, n) order,
 //            since few N tiles would leave XCDs idle in the grouped order;
 //   kWrapT   W column k is read as k mod w_wrap (one wrap at most), and C is
-//            stored transposed, C[n][m] at C + n ldc + m.
+//            stored transposed, C[n][m] at C + n ldc + m (c_slice != 0: C is
+//            16-byte aligned and ldc, M multiples of 4, for 16-byte stores).
 enum GemmMode { kPlain = 0, kSplitK = 1, kWrapT = 2 };
 
 template <int BM, int MODE>
@@ -187,13 +188,19 @@ __global__ void __launch_bounds__(kGThreads, 1)
     const int n = n0 + wn * BT::kFW * 16 + j * 16 + col;
     if (n >= N) continue;
     if constexpr (MODE == kWrapT) {
+      // a lane's 4 values are consecutive in C[n][:]: one 16-byte store when
+      // C and ldc allow it (c_slice != 0; then M % 4 == 0 as well)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + grp * 4;
+        if (c_slice) {
+          if (m < M) *reinterpret_cast<f32x4*>(C + (size_t)n * ldc + m) = acc[i][j];
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * 128 + i * 16 + grp * 4 + q;
-          if (m < M) C[(size_t)n * ldc + m] = acc[i][j][q];
+          for (int q = 0; q < 4; ++q)
+            if (m + q < M) C[(size_t)n * ldc + m + q] = acc[i][j][q];
         }
+      }
     } else {
       const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
@@ -246,7 +253,8 @@ hipError_t launch_gemm_bf16_tn_wrapt(const void* A, int lda, int M, const void* 
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % BigTile<256>::kBK || w_wrap % BigTile<256>::kBK || w_wrap <= 0 || K > 2 * w_wrap)
     return hipErrorNotSupported;
-  return M >= 256 ? launch_big<256, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, 0, s)
-                  : launch_big<128, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, 0, s);
+  const size_t vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && ldc % 4 == 0 && M % 4 == 0;
+  return M >= 256 ? launch_big<256, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, vec, s)
+                  : launch_big<128, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, vec, s);
 }
 }  // namespace domino
