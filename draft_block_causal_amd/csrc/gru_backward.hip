@@ -10,7 +10,9 @@
 //      previous state (zero at i = 0);
 //   2. the pre-activations of every row, independent of the backward:
 //      a = W_ih e + b_ih (the tiled matrix-core GEMM on the gathered rows) and
-//      c = W_hh g_prev + b_hh (gb_matvec_kernel, float32 states);
+//      c = W_hh g_prev + b_hh (float32 states: gb_matvec_kernel; bf16 heads:
+//      the states split hi / lo by gb_hilo_kernel, split-K partials of the
+//      tiled GEMM, added in slice order with the bias by gb_csum_kernel);
 //   3. per position i = K-1 … 0: gb_elem_kernel (the gate derivatives of
 //      every row of position i: da, dc and the direct part z dg of the carry)
 //      and gb_carry_kernel (carry += W_hhᵀ dc, the gradient reaching g_{i-1},
@@ -76,6 +78,27 @@ __global__ void __launch_bounds__(kGbThreads) gb_matvec_kernel(int N, int n, con
       if (lane == 0 && q0 + j < N) out[(size_t)row * N + q0 + j] = s + (bias ? T::to_f32(bias[q0 + j]) : 0.f);
     }
   }
+}
+
+// xs[row][:] = hi | lo of x_g[row][:] (hi truncated to bf16, lo the rest
+// rounded to bf16), the matrix-core operand for c = W_hh g_prev.
+__global__ void gb_hilo_kernel(int R, int H, const float* __restrict__ x_g, uint16_t* __restrict__ xs) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x, row = blockIdx.y;
+  if (k >= H) return;
+  const float x = x_g[(size_t)row * H + k];
+  const uint32_t t = __float_as_uint(x) & 0xFFFF0000u;
+  xs[(size_t)row * 2 * H + k] = (uint16_t)(t >> 16);
+  xs[(size_t)row * 2 * H + H + k] = (uint16_t)f32_to_bf16_rne(x - __uint_as_float(t));
+}
+
+// c[row][q] = Σ_s cpart[s][row][q] (slice order) + b_hh[q].
+__global__ void gb_csum_kernel(long n, int G3, int S, const float* __restrict__ cpart,
+                               const uint16_t* __restrict__ bias, float* __restrict__ c) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += cpart[(size_t)s * n + e];
+  c[e] = v + (bias ? bf16_to_f32(bias[e % G3]) : 0.f);
 }
 
 // Gate derivatives of the rows of position i, one thread per (b, unit j).
@@ -198,14 +221,27 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
                      static_cast<const E*>(g.embed), g.states, x_e, x_g, tok);
   hipError_t e = launch_panel_gemm(g.dtype, x_e, d, R, g.w_ih, d, G3, d, g.b_ih, a, G3, num_cu, s);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)H * sizeof(float);
-  if (lds > 65536) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gb_matvec_kernel<T>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (pl.S > 0) {
+    // bf16: c = [g_hi | g_lo] [W_hh ; W_hh]^T + b_hh as split-K partials on the matrix cores
+    uint16_t* xs = reinterpret_cast<uint16_t*>(ws + pl.xs);
+    float* cpart = reinterpret_cast<float*>(ws + pl.cpart);
+    hipLaunchKernelGGL(gb_hilo_kernel, dim3((H + 255) / 256, R), dim3(256), 0, s, R, H, x_g, xs);
+    e = launch_gemm_bf16_tn_splitk(xs, 2 * H, R, g.w_hh, H, G3, 2 * H / pl.S, pl.S, H, cpart, G3,
+                                   (size_t)R * G3, s);
     if (e != hipSuccess) return e;
+    const long n = (long)R * G3;
+    hipLaunchKernelGGL(gb_csum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, G3, pl.S, cpart,
+                       static_cast<const uint16_t*>(g.b_hh), c);
+  } else {
+    const size_t lds = (size_t)H * sizeof(float);
+    if (lds > 65536) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(gb_matvec_kernel<T>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(gb_matvec_kernel<T>, dim3(R, (G3 + 63) / 64), dim3(kGbThreads), lds, s, G3, H,
+                       static_cast<const E*>(g.w_hh), static_cast<const E*>(g.b_hh), x_g, c);
   }
-  hipLaunchKernelGGL(gb_matvec_kernel<T>, dim3(R, (G3 + 63) / 64), dim3(kGbThreads), lds, s, G3, H,
-                     static_cast<const E*>(g.w_hh), static_cast<const E*>(g.b_hh), x_g, c);
   e = launch_fill_u64(reinterpret_cast<unsigned long long*>(carry), (B * H + 1) / 2, s);
   if (e != hipSuccess) return e;
   const dim3 eg((H + 255) / 256, B);

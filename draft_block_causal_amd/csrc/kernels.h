@@ -164,6 +164,10 @@ hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
 // Backward through time of the teacher-forced GRU (gru_backward.hip).
 struct GruBackwardPlan {
   size_t x_e, x_g, a, c, da, dc, carry, tok, total;  // byte offsets; workspace bytes
+  // bf16 heads: c = W_hh g_prev on the matrix cores, g_prev split hi | lo
+  // (xs [R][2H] bf16) and S split-K partials (cpart [S][R][3H] float32)
+  int S;
+  size_t xs, cpart;
 };
 inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -186,6 +190,19 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   off += up(((size_t)B * H + 1) / 2 * 8);
   p.tok = off;
   off += up(R * 4);
+  if (elem == 2) {
+    // slices of K = 2H: kc = H / half, a multiple of 32 that divides H, with
+    // about 512 workgroups over the R x 3H output tiles
+    const long bm = R >= 256 ? 256 : 128;
+    const long tiles = (((long)R + bm - 1) / bm) * (((long)G3 + 255) / 256);
+    long half = 1;
+    while (4 * half * tiles <= 512 && H % (2 * half) == 0 && (H / (2 * half)) % 32 == 0) half *= 2;
+    p.S = (int)(2 * half);
+    p.xs = off;
+    off += up(R * 2 * H * 2);
+    p.cpart = off;
+    off += up((size_t)p.S * R * G3 * 4);
+  }
   p.total = off;
   return p;
 }

@@ -60,7 +60,8 @@ def _run(dev, w, batch, seed):
     return out
 
 
-@pytest.mark.parametrize("name,batch", [("tiny_stress_b4", 4), ("qwen3_8b_b1_greedy", 1), ("qwen3_8b_b1_greedy", 2)])
+@pytest.mark.parametrize("name,batch", [("tiny_stress_b4", 4), ("qwen3_8b_b1_greedy", 1), ("qwen3_8b_b1_greedy", 2),
+                                        ("qwen3_8b_b1_greedy", 20)])
 def test_gru_backward_matches_oracle(dev, name, batch):
     _run(dev, S.get_workload(name), batch, seed=batch + 50)
 
