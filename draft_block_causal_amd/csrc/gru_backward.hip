@@ -15,8 +15,9 @@
 //      tiled GEMM, added in slice order with the bias by gb_csum_kernel);
 //   3. per position i = K-1 … 0: gb_elem_kernel (the gate derivatives of
 //      every row of position i: da, dc and the direct part z dg of the carry)
-//      and gb_carry_kernel (carry += W_hhᵀ dc, the gradient reaching g_{i-1},
-//      its 3H terms split over the waves of a workgroup);
+//      and gb_carry_kernel (W_hhᵀ dc, the rest of the gradient reaching
+//      g_{i-1}, its 3H terms split over P workgroups and their waves, the P
+//      partial sums added by the next gb_elem_kernel);
 //   4. gb_outer_kernel twice: dW_ih = Σ da eᵀ, db_ih = Σ da and
 //      dW_hh = Σ dc g_prevᵀ, db_hh = Σ dc over every row.
 #include "common.h"
@@ -102,9 +103,12 @@ __global__ void gb_csum_kernel(long n, int G3, int S, const float* __restrict__ 
 }
 
 // Gate derivatives of the rows of position i, one thread per (b, unit j).
-__global__ void gb_elem_kernel(int B, int K, int H, int i, const float* __restrict__ a, const float* __restrict__ c,
-                               const float* __restrict__ x_g, const float* __restrict__ dg, float* __restrict__ carry,
-                               float* __restrict__ da, float* __restrict__ dc) {
+// The carry reaching this position is carry[0] (the direct part) plus the P
+// partial sums carry[1 .. P] of the previous gb_carry_kernel, in that order.
+__global__ void gb_elem_kernel(int B, int K, int H, int i, int P, const float* __restrict__ a,
+                               const float* __restrict__ c, const float* __restrict__ x_g,
+                               const float* __restrict__ dg, float* __restrict__ carry, float* __restrict__ da,
+                               float* __restrict__ dc) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
   if (j >= H) return;
   const size_t row = (size_t)b * K + i, G3 = 3 * (size_t)H;
@@ -114,7 +118,10 @@ __global__ void gb_elem_kernel(int B, int K, int H, int i, const float* __restri
   const float z = sigmoidf_(ar[H + j] + cr[H + j]);
   const float n = tanhf(ar[2 * H + j] + r * cr[2 * H + j]);
   const float gp = x_g[row * H + j];
-  const float d_g = dg[row * H + j] + carry[(size_t)b * H + j];
+  const size_t BH = (size_t)B * H;
+  float cin = carry[(size_t)b * H + j];
+  for (int p = 1; p <= P; ++p) cin += carry[p * BH + (size_t)b * H + j];
+  const float d_g = dg[row * H + j] + cin;
   const float d_n = d_g * (1.f - z);
   const float d_z = d_g * (gp - n);
   const float d_pn = d_n * (1.f - n * n);
@@ -129,18 +136,20 @@ __global__ void gb_elem_kernel(int B, int K, int H, int i, const float* __restri
   carry[(size_t)b * H + j] = d_g * z;  // the direct part; gb_carry_kernel adds W_hhᵀ dc
 }
 
-// carry[b][j] += Σ_q W_hh[q][j] dc[row(b, i)][q]: a workgroup takes 64 units j
-// (one per lane) of one block b; its 4 waves take a quarter of the 3H terms
-// each, eight loads in flight per lane, and the quarter sums are added in
-// wave order.
+// carry[1 + p][b][j] = Σ_q W_hh[q][j] dc[row(b, i)][q] over group p
+// (blockIdx.z) of the 3H terms: a workgroup takes 64 units j (one per lane)
+// of one block b; its 4 waves take a quarter of the group each, eight loads
+// in flight per lane, and the quarter sums are added in wave order.
 template <class T>
-__global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int K, int H, int i, const typename T::elem* __restrict__ w_hh,
+__global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int B, int K, int H, int i,
+                                                              const typename T::elem* __restrict__ w_hh,
                                                               const float* __restrict__ dc, float* __restrict__ carry) {
   __shared__ float part[kGbWaves][64];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int j = blockIdx.x * 64 + lane, b = blockIdx.y, G3 = 3 * H;
   const float* d = dc + ((size_t)b * K + i) * G3;
-  const int qa = G3 * wave / kGbWaves, qb = G3 * (wave + 1) / kGbWaves;
+  const int parts = (int)gridDim.z * kGbWaves, idx = (int)blockIdx.z * kGbWaves + wave;
+  const int qa = (int)((long)G3 * idx / parts), qb = (int)((long)G3 * (idx + 1) / parts);
   float acc = 0.f;
   if (j < H) {
     int q = qa;
@@ -158,7 +167,7 @@ __global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int K, int H, int 
   if (wave == 0 && j < H) {
     float sum = part[0][lane];
     for (int w = 1; w < kGbWaves; ++w) sum += part[w][lane];
-    carry[(size_t)b * H + j] += sum;
+    carry[(1 + blockIdx.z) * (size_t)B * H + (size_t)b * H + j] = sum;
   }
 }
 
@@ -242,13 +251,15 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
     hipLaunchKernelGGL(gb_matvec_kernel<T>, dim3(R, (G3 + 63) / 64), dim3(kGbThreads), lds, s, G3, H,
                        static_cast<const E*>(g.w_hh), static_cast<const E*>(g.b_hh), x_g, c);
   }
-  e = launch_fill_u64(reinterpret_cast<unsigned long long*>(carry), (B * H + 1) / 2, s);
+  const int P = pl.carry_parts;
+  e = launch_fill_u64(reinterpret_cast<unsigned long long*>(carry), (int)(((size_t)(1 + P) * B * H + 1) / 2), s);
   if (e != hipSuccess) return e;
   const dim3 eg((H + 255) / 256, B);
   for (int i = K - 1; i >= 0; --i) {
-    hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, a, c, x_g, g.dg, carry, da, dc);
+    hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, i == K - 1 ? 0 : P, a, c, x_g, g.dg,
+                       carry, da, dc);
     if (i > 0)
-      hipLaunchKernelGGL(gb_carry_kernel<T>, dim3((H + 63) / 64, B), dim3(kGbThreads), 0, s, K, H, i,
+      hipLaunchKernelGGL(gb_carry_kernel<T>, dim3((H + 63) / 64, B, P), dim3(kGbThreads), 0, s, B, K, H, i,
                          static_cast<const E*>(g.w_hh), dc, carry);
   }
   hipLaunchKernelGGL(gb_outer_kernel<E>, dim3((d + kGbThreads - 1) / kGbThreads, (G3 + kGbQ - 1) / kGbQ),

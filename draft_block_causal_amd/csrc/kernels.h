@@ -164,6 +164,7 @@ hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
 // Backward through time of the teacher-forced GRU (gru_backward.hip).
 struct GruBackwardPlan {
   size_t x_e, x_g, a, c, da, dc, carry, tok, total;  // byte offsets; workspace bytes
+  int carry_parts;  // P
   // bf16 heads: c = W_hh g_prev on the matrix cores, g_prev split hi | lo
   // (xs [R][2H] bf16) and S split-K partials (cpart [S][R][3H] float32)
   int S;
@@ -186,8 +187,15 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   off += up(R * G3 * 4);
   p.dc = off;
   off += up(R * G3 * 4);
+  {
+    // groups of the 3H terms of W_hh^T dc (the carry is [1 + P][B][H]: the
+    // direct part, then one partial sum per group), about 256 workgroups
+    const long wgs = ((long)H + 63) / 64 * B;
+    const long P = 256 / wgs;
+    p.carry_parts = (int)(P < 1 ? 1 : P > 8 ? 8 : P);
+  }
   p.carry = off;
-  off += up(((size_t)B * H + 1) / 2 * 8);
+  off += up(((size_t)(1 + p.carry_parts) * B * H + 1) / 2 * 8);
   p.tok = off;
   off += up(R * 4);
   if (elem == 2) {
