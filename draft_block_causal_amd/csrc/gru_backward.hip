@@ -28,6 +28,7 @@ namespace domino {
 constexpr int kGbThreads = 256;
 constexpr int kGbWaves = kGbThreads / 64;
 constexpr int kGbQ = 16;  // output rows per thread in the outer-product sums
+constexpr int kGbCarryNB = kGruCarryBlocks;  // blocks per carry workgroup from 8 blocks up
 
 // x_e[row][:] = E[tok(row)][:] (head dtype) and x_g[row][:] = states[b][i - 1][:] (zero at i = 0).
 template <class T>
@@ -138,19 +139,25 @@ __global__ void gb_elem_kernel(int B, int K, int H, int i, int P, const float* _
 
 // carry[1 + p][b][j] = Σ_q W_hh[q][j] dc[row(b, i)][q] over group p
 // (blockIdx.z) of the 3H terms: a workgroup takes 64 units j (one per lane)
-// of one block b; its 4 waves take a quarter of the group each, eight loads
-// in flight per lane, and the quarter sums are added in wave order.
-template <class T>
+// of NB blocks b (each W_hh value loaded once for the NB blocks); its 4 waves
+// take a quarter of the group each, eight loads in flight per lane, and the
+// quarter sums are added in wave order.
+template <class T, int NB>
 __global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int B, int K, int H, int i,
                                                               const typename T::elem* __restrict__ w_hh,
                                                               const float* __restrict__ dc, float* __restrict__ carry) {
-  __shared__ float part[kGbWaves][64];
+  __shared__ float part[kGbWaves][NB][64];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int j = blockIdx.x * 64 + lane, b = blockIdx.y, G3 = 3 * H;
-  const float* d = dc + ((size_t)b * K + i) * G3;
+  const int j = blockIdx.x * 64 + lane, b0 = blockIdx.y * NB, G3 = 3 * H;
+  const int nb = min(NB, B - b0);
   const int parts = (int)gridDim.z * kGbWaves, idx = (int)blockIdx.z * kGbWaves + wave;
   const int qa = (int)((long)G3 * idx / parts), qb = (int)((long)G3 * (idx + 1) / parts);
-  float acc = 0.f;
+  const float* d[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) d[t] = dc + ((size_t)(b0 + min(t, nb - 1)) * K + i) * G3;
+  float acc[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) acc[t] = 0.f;
   if (j < H) {
     int q = qa;
     for (; q + 8 <= qb; q += 8) {
@@ -158,17 +165,25 @@ __global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int B, int K, int 
 #pragma unroll
       for (int u = 0; u < 8; ++u) w[u] = T::to_f32(w_hh[(size_t)(q + u) * H + j]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += w[u] * d[q + u];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int t = 0; t < NB; ++t) acc[t] += w[u] * d[t][q + u];
     }
-    for (; q < qb; ++q) acc += T::to_f32(w_hh[(size_t)q * H + j]) * d[q];
+    for (; q < qb; ++q) {
+      const float w = T::to_f32(w_hh[(size_t)q * H + j]);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) acc[t] += w * d[t][q];
+    }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int t = 0; t < NB; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
-  if (wave == 0 && j < H) {
-    float sum = part[0][lane];
-    for (int w = 1; w < kGbWaves; ++w) sum += part[w][lane];
-    carry[(1 + blockIdx.z) * (size_t)B * H + (size_t)b * H + j] = sum;
-  }
+  if (wave == 0 && j < H)
+    for (int t = 0; t < nb; ++t) {
+      float sum = part[0][t][lane];
+      for (int w = 1; w < kGbWaves; ++w) sum += part[w][t][lane];
+      carry[(1 + blockIdx.z) * (size_t)B * H + (size_t)(b0 + t) * H + j] = sum;
+    }
 }
 
 // out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X of type XE);
@@ -259,8 +274,9 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
     hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, i == K - 1 ? 0 : P, a, c, x_g, g.dg,
                        carry, da, dc);
     if (i > 0)
-      hipLaunchKernelGGL(gb_carry_kernel<T>, dim3((H + 63) / 64, B, P), dim3(kGbThreads), 0, s, B, K, H, i,
-                         static_cast<const E*>(g.w_hh), dc, carry);
+      hipLaunchKernelGGL((B >= kGbCarryNB ? gb_carry_kernel<T, kGbCarryNB> : gb_carry_kernel<T, 1>),
+                         dim3((H + 63) / 64, B >= kGbCarryNB ? (B + kGbCarryNB - 1) / kGbCarryNB : B, P),
+                         dim3(kGbThreads), 0, s, B, K, H, i, static_cast<const E*>(g.w_hh), dc, carry);
   }
   hipLaunchKernelGGL(gb_outer_kernel<E>, dim3((d + kGbThreads - 1) / kGbThreads, (G3 + kGbQ - 1) / kGbQ),
                      dim3(kGbThreads), 0, s, R, G3, d, da, x_e, g.d_w_ih, g.d_b_ih);

@@ -162,6 +162,7 @@ struct BackwardArgs {
 hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
 
 // Backward through time of the teacher-forced GRU (gru_backward.hip).
+constexpr int kGruCarryBlocks = 8;  // blocks sharing each W_hh load in the carry, from 8 blocks up
 struct GruBackwardPlan {
   size_t x_e, x_g, a, c, da, dc, carry, tok, total;  // byte offsets; workspace bytes
   int carry_parts;  // P
@@ -190,7 +191,7 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   {
     // groups of the 3H terms of W_hh^T dc (the carry is [1 + P][B][H]: the
     // direct part, then one partial sum per group), about 256 workgroups
-    const long wgs = ((long)H + 63) / 64 * B;
+    const long wgs = ((long)H + 63) / 64 * (B >= kGruCarryBlocks ? (B + kGruCarryBlocks - 1) / kGruCarryBlocks : B);
     const long P = 256 / wgs;
     p.carry_parts = (int)(P < 1 ? 1 : P > 8 ? 8 : P);
   }
