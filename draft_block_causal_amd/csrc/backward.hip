@@ -214,12 +214,18 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw1_kernel(int R, int d, int H,
   __shared__ float zs[kBwRowsLds][kBwQDw1];
   const int k = blockIdx.x * kBwThreads + threadIdx.x, q0 = blockIdx.y * kBwQDw1, n = d + H;
   const int nq = min(kBwQDw1, r - q0);
+  // rows of group blockIdx.z; with several groups the sums are partials
+  const int ga = (int)((long)R * blockIdx.z / gridDim.z), gb = (int)((long)R * (blockIdx.z + 1) / gridDim.z);
+  if (gridDim.z > 1) {
+    dw1 += (size_t)blockIdx.z * r * n;
+    if (db1) db1 += (size_t)blockIdx.z * r;
+  }
   float acc[kBwQDw1];
 #pragma unroll
   for (int q = 0; q < kBwQDw1; ++q) acc[q] = 0.f;
   float bsum = 0.f;
-  for (int r0 = 0; r0 < R; r0 += kBwRowsLds) {
-    const int nr = min(kBwRowsLds, R - r0);
+  for (int r0 = ga; r0 < gb; r0 += kBwRowsLds) {
+    const int nr = min(kBwRowsLds, gb - r0);
     __syncthreads();
     for (int e = threadIdx.x; e < kBwRowsLds * kBwQDw1; e += kBwThreads) {
       const int rr = e / kBwQDw1, q = e % kBwQDw1;
@@ -239,6 +245,15 @@ __global__ void __launch_bounds__(kBwThreads) bw_dw1_kernel(int R, int d, int H,
   if (k < n)
     for (int q = 0; q < nq; ++q) dw1[(size_t)(q0 + q) * n + k] = acc[q];
   if (blockIdx.x == 0 && db1 && (int)threadIdx.x < nq) db1[q0 + threadIdx.x] = bsum;
+}
+
+// out[e] = Σ_g part[g][e] in group order (dW1 and db1 from row groups).
+__global__ void bw_gsum_kernel(long n, int G, const float* __restrict__ part, float* __restrict__ out) {
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float v = 0.f;
+  for (int g = 0; g < G; ++g) v += part[(size_t)g * n + e];
+  out[e] = v;
 }
 
 // dg[row][j] = Σ_q dz[row][q] W1[q][d + j] for rows m0 .. m0 + 15: a
@@ -448,8 +463,22 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 255) / 256)), dim3(256), 0, s, R, r, pl.S, part, z,
                      dz);
-  hipLaunchKernelGGL(bw_dw1_kernel<T>, dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1),
-                     dim3(kBwThreads), 0, s, R, d, H, r, hidden, a.states, dz, a.d_w1, a.d_b1);
+  {
+    const int G1 = pl.G1;
+    float* w1out = G1 > 1 ? reinterpret_cast<float*>(ws + pl.dw1p) : a.d_w1;
+    float* b1out = G1 > 1 ? (a.d_b1 ? reinterpret_cast<float*>(ws + pl.db1p) : nullptr) : a.d_b1;
+    hipLaunchKernelGGL(bw_dw1_kernel<T>,
+                       dim3((d + H + kBwThreads - 1) / kBwThreads, (r + kBwQDw1 - 1) / kBwQDw1, G1),
+                       dim3(kBwThreads), 0, s, R, d, H, r, hidden, a.states, dz, w1out, b1out);
+    if (G1 > 1) {
+      const long n1 = (long)r * (d + H);
+      hipLaunchKernelGGL(bw_gsum_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, n1, G1, w1out,
+                         a.d_w1);
+      if (a.d_b1)
+        hipLaunchKernelGGL(bw_gsum_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, (long)r, G1, b1out,
+                           a.d_b1);
+    }
+  }
   if (a.d_states) {
     const size_t dg_lds = ((size_t)kBwRowsDg * r + (size_t)kBwWaves * kBwRowsDg * 64) * sizeof(float);
     if (dg_lds > 65536) {

@@ -106,8 +106,13 @@ struct BackwardPlan {
   // byte offsets of z, u, dz [R][r] and part [S][R][r] (float32), and with
   // mfma of gs [R][2 Vp], gt [V][2 Rp], w2t [r][Vp], us [r][3 Rp] (bf16); workspace bytes
   size_t z, u, dz, part, gs, gt, w2t, us, total;
+  // dW1, db1: the rows split over G1 groups (G1 > 1: partial sums dw1p
+  // [G1][r][n1] and db1p [G1][r] float32, added in group order)
+  int G1;
+  size_t dw1p, db1p;
 };
-inline BackwardPlan backward_plan(int R, int r, int V, int dtype) {
+constexpr int kBwDw1Rows = 128;  // rows per dW1 group
+inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BackwardPlan p{};
   if (dtype == 1) {
@@ -147,6 +152,16 @@ inline BackwardPlan backward_plan(int R, int r, int V, int dtype) {
     off += up((size_t)r * p.Vp * 2);
     p.us = off;
     off += up((size_t)r * 3 * p.Rp * 2);
+  }
+  {
+    const int g = (R + kBwDw1Rows - 1) / kBwDw1Rows;
+    p.G1 = g < 1 ? 1 : g > 8 ? 8 : g;
+  }
+  if (p.G1 > 1) {
+    p.dw1p = off;
+    off += up((size_t)p.G1 * r * n1 * 4);
+    p.db1p = off;
+    off += up((size_t)p.G1 * r * 4);
   }
   p.total = off;
   return p;
