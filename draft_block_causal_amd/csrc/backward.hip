@@ -14,8 +14,8 @@
 //   3. bw_du_kernel    (S vocabulary slices x R / 64 x r / 256): partial W2ᵀ G
 //                      over a slice for 64 rows (G and W2 staged in LDS,
 //                      16 x 4 register tiles), W2 read once per 64 rows;
-//   4. bw_dz_kernel    (R x r threads): the S partials added in slice order,
-//                      times SiLU'(z);
+//   4. bw_dz_kernel    (R r / 64): the S partials added, a quarter of the
+//                      slices per wave, times SiLU'(z);
 //   5. bw_dw1_kernel   ((d + H) / 256 x r / 16): dW1 and db1;
 //   6. bw_dg_kernel    (H / 64 x R / 16): the state gradient, the r terms split
 //                      over the waves of a workgroup.
@@ -191,15 +191,34 @@ __global__ void __launch_bounds__(kBwThreads) bw_du_kernel(int R, int V, int r, 
   }
 }
 
-// dz = (Σ_s part[s]) ⊙ SiLU'(z), the slices added in order.
-__global__ void bw_dz_kernel(int R, int r, int S, const float* __restrict__ part, const float* __restrict__ z,
-                             float* __restrict__ dz) {
-  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (long)R * r) return;
+// dz = (Σ_s part[s]) ⊙ SiLU'(z): 64 entries per workgroup, each wave adds a
+// quarter of the slices in order (eight loads in flight), and the quarter
+// sums are added in wave order.
+__global__ void __launch_bounds__(kBwThreads) bw_dz_kernel(int R, int r, int S, const float* __restrict__ part,
+                                                           const float* __restrict__ z, float* __restrict__ dz) {
+  __shared__ float ps[kBwWaves][64];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const long n = (long)R * r, e = (long)blockIdx.x * 64 + lane;
+  const int sa = S * wave / kBwWaves, sb = S * (wave + 1) / kBwWaves;
   float du = 0.f;
-  for (int s = 0; s < S; ++s) du += part[(size_t)s * R * r + e];
-  const float zz = z[e], sg = sigmoidf_(zz);
-  dz[e] = du * sg * (1.f + zz * (1.f - sg));
+  if (e < n) {
+    int s = sa;
+    for (; s + 8 <= sb; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(s + u) * n + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) du += v[u];
+    }
+    for (; s < sb; ++s) du += part[(size_t)s * n + e];
+  }
+  ps[wave][lane] = du;
+  __syncthreads();
+  if (wave == 0 && e < n) {
+    const float t = (ps[0][lane] + ps[1][lane]) + (ps[2][lane] + ps[3][lane]);
+    const float zz = z[e], sg = sigmoidf_(zz);
+    dz[e] = t * sg * (1.f + zz * (1.f - sg));
+  }
 }
 
 // dW1[q][k] = Σ_rows dz[row][q] x[row][k] for q0 .. q0 + 15; db1 from the
@@ -461,8 +480,8 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bw_du_kernel<T>, dim3(pl.S, (R + kBwRowsDu - 1) / kBwRowsDu, (r + 255) / 256),
                        dim3(kBwThreads), 0, s, R, V, r, a.grad, static_cast<const E*>(a.w2), part);
   }
-  hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 255) / 256)), dim3(256), 0, s, R, r, pl.S, part, z,
-                     dz);
+  hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 63) / 64)), dim3(kBwThreads), 0, s, R, r, pl.S,
+                     part, z, dz);
   {
     const int G1 = pl.G1;
     float* w1out = G1 > 1 ? reinterpret_cast<float*>(ws + pl.dw1p) : a.d_w1;
