@@ -33,8 +33,13 @@ in the design notes):
     G from a Philox4x32-10 counter generator (counter = (v>>2, i, b, offset),
     key = (seed lo32, seed hi32), word = output[v & 3],
     U = ((word >> 9) + 1/2) * 2^-23, G = -ln(-ln U)).
-  * The token decision is taken on the score rounded to float32 (the
-    kernel's precision); ties go to the lowest vocabulary index.
+  * The token decision is taken on the score rounded to float32, and ties
+    go to the lowest vocabulary index.  The contract compares free-running
+    tokens exactly except at near-ties (top-2 margin below 2e-2); rounding a
+    score of magnitude below ~100 to float32 moves it by under 1e-5, so the
+    rounding can change a decision only where the margin is far inside that
+    band, where any token within 2e-2 of the top is correct.  Deciding on the
+    rounded score fixes which of several exactly equal float32 values wins.
   * Acceptance length: the bare length of the longest matching prefix.
   * Verification of a sampled draft (the pages report T = 1 decoding, verified
     in parallel by the target model, without the rule): standard speculative
@@ -45,10 +50,39 @@ in the design notes):
     U_i is the Philox word of entry 0 at counter (0, i, b, offset) mapped as
     for the Gumbel noise; the resampling noise uses offset + 1.
 
-Pins: every function here is checked by ``tests/test_oracle_pins.py``
-against something other than itself (closed forms, brute force, invariants,
-torch / rocRAND library routines, statistics).  No function is parity
-unpinned.
+Pins (``tests/test_oracle_pins.py``), each against something other than the
+function itself:
+  as_f64, base_logits      hand-worked product, one-hot rows, torch linear on
+                           bf16-widened data
+  sigmoid, silu            values at 0, 1 and the tails worked with math
+  gru_cell                 torch GRUCell over several steps, zero-weight closed
+                           form, scalar hand case
+  correction_logits        torch linear/silu composition, concatenation order
+  philox4x32_10            rocRAND's header-only engine built with g++
+  philox_words             counter layout, uniformity and serial-pair chi^2
+  gumbel_noise             uniform-map endpoints, chi^2 of Gumbel-max draws
+                           against the tempered softmax
+  sampling_scores          chi^2 at T = 1 and 0.5, T -> 0+ equals greedy
+  pick_token, top2_margin  hand cases with ties
+  draft_block              brute-force enumeration of every token sequence on
+                           a micro head, an independent teacher-forced chain,
+                           residual invariants
+  base_draft               hand case, equality with draft_block at zero W2
+  curriculum_*, cross_entropy, position_weights
+                           torch cross_entropy, closed form log V, limits at
+                           lambda = 0 / 1, hand case, autograd gradients
+  correction_backward, gru_backward
+                           torch autograd of the same compositions
+  accept_len               all 6561 pairs at V = 3, K = 4; geometric closed form
+  uniform01                the uniform behind the Gumbel noise of entry 0
+  softmax                  two-entry closed form 1 / (1 + e^{a/T}), torch
+                           softmax at T = 0.5, 0.8, 1.5
+  verify_sampled           first emission distributed as the target (chi^2),
+                           acceptance rate sum min(p_t, p_d), residual support,
+                           equal distributions, zero target mass (the expected
+                           probabilities written out independently)
+``tests/test_oracle_mutations.py`` plants a mistake in each of these and
+checks that the pins reject it.
 """
 from __future__ import annotations
 

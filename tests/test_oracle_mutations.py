@@ -28,6 +28,9 @@ MUTATIONS = {
     "philox_lane": ("lane = np.broadcast_to(v & np.uint64(3), shape)",
                     "lane = np.broadcast_to((v >> np.uint64(1)) & np.uint64(3), shape)"),
     "temperature_ignored": ("return logits / temperature + gumbel_noise", "return logits + gumbel_noise"),
+    "softmax_ignores_temperature": ("x = as_f64(logits) / temperature", "x = as_f64(logits)"),
+    "verify_uniform_wrong_lane": ("w = philox_words(seed, offset, b, i, 0).astype(np.float64)",
+                                  "w = philox_words(seed, offset, b, i, 1).astype(np.float64)"),
     "verify_ratio_inverted": ("if not (uniform01(seed, offset, b, i) * pd[y] < pt[y]):",
                               "if not (uniform01(seed, offset, b, i) * pt[y] < pd[y]):"),
     "verify_residual_reversed": ("q = softmax(tl[b, n], temperature) - softmax(dl[b, n], temperature)",

@@ -468,6 +468,18 @@ def test_uniform_map_endpoints():
     assert g.min() >= -math.log(-math.log(lo)) - 1e-12 and g.max() <= -math.log(-math.log(hi)) + 1e-12
 
 
+def test_verify_uniform_is_the_gumbel_uniform_of_entry_zero():
+    # the acceptance uniform U_i is the uniform behind the Gumbel noise of
+    # vocabulary entry 0 at the same counter: -ln(-ln U_i) equals that noise
+    for seed, off in ((0, 0), (0xDEAD_BEEF_0123, 9), (2 ** 64 - 1, 2 ** 32 - 1)):
+        b, i = np.arange(5)[:, None], np.arange(7)[None, :]
+        u = O.uniform01(seed, off, b, i)
+        assert ((u > 0) & (u < 1)).all()
+        np.testing.assert_array_equal(-np.log(-np.log(u)), O.gumbel_noise(seed, off, b, i, 0))
+        # and it is not the uniform of another entry of the same word
+        assert not np.array_equal(-np.log(-np.log(u)), O.gumbel_noise(seed, off, b, i, 1))
+
+
 def test_gumbel_max_matches_softmax_chi2():
     L = np.array([0.3, -1.2, 2.0, 0.0, 1.1, -0.4, 0.9, 1.6])
     for T in (1.0, 0.5):
@@ -562,9 +574,37 @@ def test_head_parameter_count_matches_pages():
 # draft token from p_d with an independent generator and running the oracle
 # once per trial (its own Philox stream decides acceptance and resampling).
 # ---------------------------------------------------------------------------
+def _tempered_probs(logits, T):
+    """softmax(L / T) written out independently of the oracle: exp(L / T - max) normalised."""
+    x = np.asarray(logits, dtype=np.float64) / T
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def test_softmax_two_entry_closed_form():
+    # logits [0, a] at temperature T: p_0 = 1 / (1 + e^{a/T}), p_1 = 1 - p_0
+    for a in (-2.0, 0.3, 1.7):
+        for T in (0.25, 0.5, 1.0, 1.5, 4.0):
+            p = O.softmax(np.array([0.0, a]), T)
+            p0 = 1.0 / (1.0 + math.exp(a / T))
+            assert abs(p[0] - p0) < 1e-15 and abs(p[1] - (1.0 - p0)) < 1e-15, (a, T, p)
+
+
+def test_softmax_matches_torch_at_several_temperatures():
+    rng = np.random.default_rng(17)
+    L = rng.normal(0, 2, (3, 4, 37))
+    for T in (0.5, 0.8, 1.5):
+        want = torch.softmax(torch.from_numpy(L) / T, dim=-1).numpy()
+        np.testing.assert_allclose(O.softmax(L, T), want, rtol=1e-12, atol=1e-15)
+    # bf16 bit patterns are widened before the division
+    bits = S.f32_to_bf16_bits(rng.normal(0, 1, 64).astype(np.float32))
+    want = torch.softmax(torch.from_numpy(bits.astype(np.int32) << 16).view(torch.float32).double() / 0.7, dim=-1)
+    np.testing.assert_allclose(O.softmax(bits, 0.7), want.numpy(), rtol=1e-12, atol=1e-15)
+
+
 def _verify_trials(t_logits, d_logits, T, n, seed0=1000):
     rng = np.random.default_rng(7)
-    pd = O.softmax(d_logits, T)
+    pd = _tempered_probs(d_logits, T)
     V = pd.size
     emitted = np.zeros(V)
     accepted = 0
@@ -587,7 +627,7 @@ def test_verify_first_emission_follows_target_and_acceptance_rate():
     d = np.array([-0.2, 0.9, 0.4, -0.7, 0.5])
     T, n = 0.8, 6000
     emp, acc, _ = _verify_trials(t, d, T, n)
-    pt, pd = O.softmax(t, T), O.softmax(d, T)
+    pt, pd = _tempered_probs(t, T), _tempered_probs(d, T)
     sd = np.sqrt(pt * (1 - pt) / n)
     assert np.all(np.abs(emp - pt) < 5 * sd + 1e-9), (emp, pt)
     p_acc = np.minimum(pt, pd).sum()
@@ -599,7 +639,7 @@ def test_verify_residual_draw_is_positive_part():
     d = np.array([0.0, 1.5, 0.0, 0.5])
     T, n = 1.0, 4000
     _, _, res = _verify_trials(t, d, T, n)
-    q = np.maximum(O.softmax(t, T) - O.softmax(d, T), 0.0)
+    q = np.maximum(_tempered_probs(t, T) - _tempered_probs(d, T), 0.0)
     q /= q.sum()
     m = res.sum()
     assert m > 500
