@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the Domino draft-head hot path on one MI355X.
 
-One step = one draft block call on the Qwen3-8B-shaped head at B = 1:
+One step = one draft call on the Qwen3-8B-shaped head at B = 1:
 domino_base_logits (frozen LM head over the 16 positions) + domino_draft_block
-(GRU + low-rank correction + greedy pick, 16 serial positions) +
-domino_accept_len (against synthetic targets).  Inputs are resident in HBM
-before the timed region.  Prints one JSON line.
+(GRU + low-rank correction + greedy pick, 16 serial positions).  Inputs are
+resident in HBM before the timed region.  domino_accept_len is timed on its
+own, on targets derived from the run's draft.  The run checks its own output
+(status word, token range, and block 0 against the oracle by the replay rule
+in the CPU-baseline leg) and exits non-zero if a check fails.  Prints one JSON
+line.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--workload qwen3_8b_b1_greedy]
     python bench.py --sweep 1,2,4,8,16,32,64,128 [--steps 30]   # concurrency sweep of one head
@@ -49,6 +52,34 @@ def lmhead_flops(B: int, K: int, d: int, V: int) -> int:
     return 2 * B * K * d * V
 
 
+def block_algorithmic_bytes(B: int, K: int, d: int, V: int, H: int, r: int, elem: int) -> int:
+    """Compulsory HBM bytes of one draft call (base logits + draft block) over B
+    blocks: every weight once (the LM head, W2, W_ih, W_hh, W1 and the biases;
+    a tied embedding is the LM head), the gathered embedding rows, the hidden
+    states in, the float32 base logits written and read back once, x_t in and
+    the tokens out.  Re-reads of per-position weights across the 16 positions
+    are a schedule's choice and are not counted."""
+    weights = (V * d + V * r + 3 * H * d + 3 * H * H + r * (d + H)) * elem
+    biases = (3 * H * 2 + r + V) * elem
+    acts = B * K * d * elem * 2 + 2 * B * K * V * 4 + B * 4 + B * K * 4
+    return weights + biases + acts
+
+
+def block_flops(B: int, K: int, d: int, V: int, H: int, r: int) -> int:
+    """Multiply-adds x 2 of one draft call: the LM head, W2, the GRU's two
+    products and W1, for every block position."""
+    M = B * K
+    return 2 * M * (V * d + V * r + 3 * H * (d + H) + r * (d + H))
+
+
+def block_floor_us(B: int, K: int, d: int, V: int, H: int, r: int, elem: int) -> float:
+    """Roofline floor of one draft call: the larger of its compulsory bytes at
+    the HBM peak and its FLOPs at the dense bf16 matrix-core peak."""
+    t_hbm = block_algorithmic_bytes(B, K, d, V, H, r, elem) / (HBM_PEAK_GBS * 1e9)
+    t_mfma = block_flops(B, K, d, V, H, r) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return max(t_hbm, t_mfma) * 1e6
+
+
 def measured_traffic(kernel_hash: str):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -62,8 +93,28 @@ def measured_traffic(kernel_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, head_np, inp, target, min_seconds: float = 10.0):
-    """The CPU oracle, as it is, on a bounded sample of the same workload."""
+def replay_mismatches(O, f, hidden, x_t, gpu_tokens, w, tol: float = 2e-2):
+    """Positions of one block where the GPU's free-running token breaks the
+    replay rule: the oracle is run teacher-forced on the GPU's own tokens, and
+    each GPU token must be the oracle's pick, or, where the oracle's top-2 score
+    margin is below tol, score within tol of the top.  Returns a list of
+    (position, gpu token, oracle token)."""
+    rep = O.draft_block(f, hidden, x_t, teacher=gpu_tokens, temperature=w.temperature, seed=w.philox_seed)
+    bad = []
+    for i in range(gpu_tokens.shape[1]):
+        s = rep["scores"][0, i]
+        y, best = int(gpu_tokens[0, i]), O.pick_token(s)
+        if y == best:
+            continue
+        if not (0 <= y < s.size and O.top2_margin(s) < tol and s[y] > s.max() - tol):
+            bad.append((i, y, best))
+    return bad
+
+
+def cpu_baseline(w, head_np, inp, min_seconds: float = 10.0, gpu_tokens=None):
+    """The CPU oracle, as it is, on a bounded sample of the same workload.  When
+    the GPU's tokens of block 0 are given, they are also checked against the
+    oracle by the replay rule (result in "gpu_block0_check")."""
     import oracle as O
 
     try:
@@ -80,20 +131,25 @@ def cpu_baseline(w, head_np, inp, target, min_seconds: float = 10.0):
     while True:
         base = O.base_logits(hid, f["lm_head"])
         out = O.draft_block(f, hid, inp["x_t"][:1], temperature=w.temperature, seed=w.philox_seed, base=base)
-        O.accept_len(out["tokens"], target[:1])
         n += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or n >= 1000:
             break
-    return {"value": n / el, "unit": "draft blocks/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} x one {w.name} block (B=1): float64 numpy base logits + 16-position loop + "
-                      f"accept_len, {el:.1f} s wall"}
+    res = {"value": n / el, "unit": "draft blocks/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} x one {w.name} block (B=1): float64 numpy base logits + 16-position loop, "
+                     f"{el:.1f} s wall"}
+    if gpu_tokens is not None:
+        bad = replay_mismatches(O, f, hid, inp["x_t"][:1], gpu_tokens[:1], w)
+        res["gpu_block0_check"] = {"rule": "replay (tokens equal except at top-2 margin < 2e-2)",
+                                   "positions": int(gpu_tokens.shape[1]), "mismatches": bad,
+                                   "equal_to_free_running_oracle": int((out["tokens"][0] == gpu_tokens[0]).sum())}
+    return res
 
 
 def sweep(args, w, batches) -> int:
     """Draft blocks/s of one head at several batch sizes (blocks per call): the
     concurrency axis of the pages' serving measurements. Each row times
-    base logits + draft block + accept_len on the first B blocks of one input set."""
+    base logits + draft block on the first B blocks of one input set."""
     import torch
 
     import domino_synth as S
@@ -110,14 +166,11 @@ def sweep(args, w, batches) -> int:
         D.domino_prepare_gru_table(head)
     hidden_all = S.to_torch(inp["hidden"], dev)
     x_all = S.to_torch(inp["x_t"], dev)
-    target_all = S.to_torch(S.make_targets(S.make_tokens((Bmax, w.block), w.vocab, seed=11), w.vocab, p=0.9,
-                                           seed=1), dev)
     rows = []
     for B in batches:
-        hidden, x_t, target = hidden_all[:B], x_all[:B], target_all[:B]
+        hidden, x_t = hidden_all[:B], x_all[:B]
         base = torch.empty((B, w.block, w.vocab), dtype=torch.float32, device=dev)
         tokens = torch.empty((B, w.block), dtype=torch.int32, device=dev)
-        accept = torch.empty((B,), dtype=torch.int32, device=dev)
         ws = torch.empty(D.domino_workspace_size(head, B), dtype=torch.uint8, device=dev)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
@@ -131,7 +184,6 @@ def sweep(args, w, batches) -> int:
                                  tokens=tokens, workspace=ws)
             if e:
                 e[2].record()
-            D.domino_accept_len(tokens, target, accept)
 
         for _ in range(args.warmup):
             step()
@@ -145,7 +197,11 @@ def sweep(args, w, batches) -> int:
                      "lm_head_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
                      "draft_block_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))})
         print(f"sweep B={B}: {rows[-1]['blocks_per_s']:.1f} blocks/s, {ms:.4f} ms/call", file=sys.stderr, flush=True)
-        del base, tokens, accept, ws
+        st = int(D.domino_draft_status(head, B, ws).cpu().numpy()[0])
+        if st != 0 or int(tokens.min()) < 0:
+            print(f"bench.py: sweep B={B}: a loop gave up (status {st})", file=sys.stderr)
+            return 3
+        del base, tokens, ws
     print(json.dumps({"metric": "draft blocks/s vs blocks per call (concurrency sweep)", "unit": "draft blocks/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
                       "data": "synthetic (seeded Gaussian weights and hidden states)",
@@ -317,15 +373,14 @@ def cpu_only(args) -> int:
 
     w = S.get_workload(args.workload)
     head_np, inp = S.make_workload(w, batch=1)
-    target = S.make_targets(S.make_tokens((1, w.block), w.vocab, seed=11), w.vocab, p=0.9, seed=1)
-    res = {"workload": w.name, "all_threads": cpu_baseline(w, head_np, inp, target)}
+    res = {"workload": w.name, "all_threads": cpu_baseline(w, head_np, inp)}
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover - threadpoolctl missing
         threadpool_limits = None
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            one = cpu_baseline(w, head_np, inp, target)
+            one = cpu_baseline(w, head_np, inp)
         one["cores"] = 1
         res["one_thread"] = one
     print(json.dumps(res), flush=True)
@@ -398,16 +453,13 @@ def main() -> int:
     if args.next_rows:
         return next_rows(args, w)
     head_np, inp = S.make_workload(w)
-    B, K, V, d, H = w.batch, w.block, w.vocab, w.d, w.gru_hidden
+    B, K, V, d, H, r = w.batch, w.block, w.vocab, w.d, w.gru_hidden, w.rank
     tensors = {k: S.to_torch(v, dev) for k, v in head_np.items() if not (k == "embed" and w.tied)}
     if w.tied:
         tensors["embed"] = tensors["lm_head"]
     head = D.Head(tensors, block=K)
     hidden = S.to_torch(inp["hidden"], dev)
     x_t = S.to_torch(inp["x_t"], dev)
-    synth_draft = S.make_tokens((B, K), V, seed=11)
-    target_np = S.make_targets(synth_draft, V, p=0.9, seed=1)
-    target = S.to_torch(target_np, dev)
     base = torch.empty((B, K, V), dtype=torch.float32, device=dev)
     tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
     accept = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -424,11 +476,11 @@ def main() -> int:
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    ev_draft = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     def step(i=None):
+        """One draft call: base logits (A1) + the draft block (A2-A5)."""
         if i is not None:
             ev[i][0].record()
         D.domino_base_logits(head, hidden, base)
@@ -436,9 +488,6 @@ def main() -> int:
             ev[i][1].record()
         D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature, seed=w.philox_seed,
                              tokens=tokens, workspace=ws)
-        if i is not None:
-            ev_draft[i].record()
-        D.domino_accept_len(tokens, target, accept)
         if i is not None:
             ev_end[i].record()
 
@@ -455,8 +504,34 @@ def main() -> int:
     step_ms = np.array([a.elapsed_time(e) for (a, _), e in zip(ev, ev_end)])
     ms_per_step = float(step_ms.mean()) if args.cold else (t1 - t0) * 1e3 / args.steps
     lm_all = np.array([a.elapsed_time(b) for a, b in ev])
-    draft_all = np.array([b.elapsed_time(c) for (_, b), c in zip(ev, ev_draft)])
+    draft_all = np.array([b.elapsed_time(c) for (_, b), c in zip(ev, ev_end)])
     lm_ms, draft_ms = float(lm_all.mean()), float(draft_all.mean())
+
+    # the run's own output: every loop completed and every token is a valid id
+    status = int(D.domino_draft_status(head, B, ws).cpu().numpy()[0])
+    tok_np = tokens.cpu().numpy()
+    failures = []
+    if status != 0:
+        failures.append(f"draft status {status}: a loop gave up")
+    if tok_np.min() < 0 or tok_np.max() >= V:
+        failures.append(f"tokens outside [0, V): min {tok_np.min()}, max {tok_np.max()}")
+
+    # acceptance length (A6), timed on its own, against targets derived from
+    # this run's draft: each position keeps the drafted token with probability
+    # 0.9, else a uniform token (seeded)
+    target_np = S.make_targets(tok_np, V, p=0.9, seed=1)
+    target = S.to_torch(target_np, dev)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        D.domino_accept_len(tokens, target, accept)
+    ea.record()
+    for _ in range(args.steps):
+        D.domino_accept_len(tokens, target, accept)
+    eb.record()
+    torch.cuda.synchronize()
+    accept_ms = ea.elapsed_time(eb) / args.steps
+    acc_np = accept.cpu().numpy()
+
     pct = lambda x: {"p10": float(np.percentile(x, 10)), "p50": float(np.percentile(x, 50)),  # noqa: E731
                      "p90": float(np.percentile(x, 90))}
     elem = 2 if w.dtype == "bf16" else 4
@@ -480,7 +555,13 @@ def main() -> int:
                  % ((256, 256) if M >= 256 else (128, 128)))
     else:
         kname = "panel_gemm_kernel (LM head, f32)"
-    roof.update({"kernel": kname, "avg_launch_ms": lm_ms})
+    floor_us = block_floor_us(B, K, d, V, H, r, elem)
+    roof.update({"kernel": kname, "avg_launch_ms": lm_ms,
+                 # the whole draft call against its own roofline floor (compulsory
+                 # bytes at 8 TB/s or FLOPs at the bf16 peak, whichever is larger)
+                 "block_floor_us": floor_us, "block_frac": floor_us * 1e-3 / ms_per_step,
+                 "block_algorithmic_bytes": block_algorithmic_bytes(B, K, d, V, H, r, elem),
+                 "block_flops": block_flops(B, K, d, V, H, r)})
 
     result = {
         "metric": METRIC,
@@ -502,6 +583,9 @@ def main() -> int:
         "gru_table_prepare_ms": prepare_ms,
         "lm_head_ms": lm_ms,
         "draft_block_ms": draft_ms,
+        "accept_len_ms": accept_ms,
+        "accept_len_mean": float(acc_np.mean()),
+        "draft_status": status,
         "step_ms_events": pct(step_ms),
         "lm_head_ms_events": pct(lm_all),
         "draft_block_ms_events": pct(draft_all),
@@ -509,8 +593,16 @@ def main() -> int:
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, head_np, inp, target_np)
+        cb = cpu_baseline(w, head_np, inp, gpu_tokens=tok_np)
+        result["cpu_baseline"] = cb
+        if cb["gpu_block0_check"]["mismatches"]:
+            failures.append(f"block 0 breaks the replay rule at {cb['gpu_block0_check']['mismatches']}")
+    if failures:
+        result["failures"] = failures
     print(json.dumps(result), flush=True)
+    if failures:
+        print("bench.py: the run's own output failed its checks: " + "; ".join(failures), file=sys.stderr)
+        return 3
     return 0
 
 

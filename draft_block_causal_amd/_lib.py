@@ -41,6 +41,7 @@ EXPORTED = [
     "domino_workspace_size",
     "domino_base_logits",
     "domino_draft_block",
+    "domino_draft_status",
     "domino_accept_len",
     "domino_verify_sampled",
     "domino_verify_workspace_size",
@@ -108,6 +109,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
         "domino_base_logits": (ctypes.c_int, [HP, I32, P, P, P]),
         "domino_draft_block": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P, SZ, P]),
+        "domino_draft_status": (ctypes.c_int, [HP, I32, P, SZ, P, P]),
         "domino_accept_len": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "domino_verify_sampled": (ctypes.c_int, [I32, I32, I32, P, P, P, F, U64, U32, P, P, P, SZ, P]),
         "domino_verify_workspace_size": (SZ, [I32, I32, I32]),
@@ -276,6 +278,20 @@ def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: torch.Tens
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(tokens), _ptr(logits), _ptr(gru_states),
         _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return tokens
+
+
+def domino_draft_status(head: Head, batch: int, workspace: torch.Tensor, status: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """The status word of the last draft call on `workspace` (a one-element int32
+    device tensor): 0 = every block's loop completed, 1 = a loop gave up."""
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=head.device)
+    _need(status, "status", torch.int32, (1,), head.device)
+    if workspace.dtype != torch.uint8 or workspace.device != head.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    _check("domino_draft_status", load_library().domino_draft_status(
+        head.ref, int(batch), _ptr(workspace), workspace.numel(), _ptr(status), _stream_ptr(stream)))
+    return status
 
 
 def domino_accept_len(draft: torch.Tensor, target: torch.Tensor, accept: Optional[torch.Tensor] = None,

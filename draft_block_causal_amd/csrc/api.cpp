@@ -39,6 +39,17 @@ int loop_mode() {
   return 0;
 }
 
+// DOMINO_DEBUG_SPIN_LIMIT=n sets the polls a wait of the on-chip loops makes
+// before giving up (test hook: 0 makes every wait give up at its first check).
+unsigned int spin_limit() {
+  const char* m = std::getenv("DOMINO_DEBUG_SPIN_LIMIT");
+  if (!m || !*m) return domino::kDefaultSpinLimit;
+  char* end = nullptr;
+  const unsigned long v = std::strtoul(m, &end, 10);
+  if (end == m || *end != '\0' || v > domino::kDefaultSpinLimit) return domino::kDefaultSpinLimit;
+  return (unsigned int)v;
+}
+
 }  // namespace
 
 extern "C" int domino_base_logits(const domino_head* h, int32_t batch, const void* hidden, float* base_logits,
@@ -105,7 +116,27 @@ extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const voi
   a.max_wg = domino::kMaxLoopWorkgroups;
   a.ks = w.ks;
   a.num_cu = num_cu;
+  a.call_status = reinterpret_cast<unsigned int*>(a.keys + (size_t)batch * h->block + 1);
+  a.spin_limit = spin_limit();
+  a.clear_words = batch * h->block + 2;
   return hip_status(domino::launch_draft_loop(a, loop_mode(), static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int domino_draft_status(const domino_head* h, int32_t batch, const void* workspace,
+                                   size_t workspace_bytes, int32_t* status, void* stream) {
+  int st = domino::check_head(h);
+  if (st != DOMINO_OK) return st;
+  if (batch < 1) return DOMINO_ERR_SHAPE;
+  if (batch > domino::kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
+  if (!status) return DOMINO_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return DOMINO_ERR_ALIGN;
+  const domino::WorkspaceLayout w = domino::workspace_layout(h, batch);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < w.total)
+    return DOMINO_ERR_WORKSPACE;
+  const unsigned char* word = static_cast<const unsigned char*>(workspace) + w.keys +
+                              ((size_t)batch * h->block + 1) * sizeof(unsigned long long);
+  return hip_status(hipMemcpyAsync(status, word, sizeof(int32_t), hipMemcpyDeviceToDevice,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int domino_prepare_gru_table(const domino_head* h, float* table, void* stream) {

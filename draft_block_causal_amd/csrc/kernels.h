@@ -72,6 +72,14 @@ struct LoopArgs {
   int max_wg;
   int ks;
   int num_cu;
+  // the call's status word (keys + K B + 1 of the whole call): 0 while every
+  // block's loop completes, 1 once one gave up; cleared by the call's first launch
+  unsigned int* call_status;
+  // polls a wait of the on-chip loops makes before giving up; 0 makes every
+  // wait give up at its first check (a host-forced give-up for tests)
+  unsigned int spin_limit;
+  // key words the single-block loop's pre-loop launch clears (keys + control words)
+  int clear_words;
 };
 
 // Runs the K-position loop.  mode: 0 = default (three kernels per position),
@@ -89,6 +97,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s);
 size_t b1_exchange_words(int H, int r, int max_wg);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
+constexpr unsigned int kDefaultSpinLimit = 1u << 20;  // about a second of polling
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
 
 // Sampled-draft verification (verify.hip): accept[b] and next[b] from the

@@ -946,7 +946,10 @@ __device__ bool reduce_keys(const DevLoop<T>& p, int step, int G, int* picked) {
 
 template <class T>
 __device__ void loop_failed(const DevLoop<T>& p) {
-  if (threadIdx.x == 0) atomicOr(p.ctrl, 1u);
+  if (threadIdx.x == 0) {
+    atomicOr(p.ctrl, 1u);
+    atomicOr(p.ctrl + 2, 1u);  // the call's status word (the next 64-bit control word)
+  }
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < p.B * p.K; i += gridDim.x * blockDim.x) p.tokens[i] = -1;
 }
 
@@ -1147,6 +1150,9 @@ static hipError_t b1_per_block(const LoopArgs& a, hipStream_t s) {
   if (a.dtype != 1 || !b1_supported(a1)) return hipErrorNotSupported;
   const size_t K = (size_t)a.K;
   for (int b = 0; b < a.B; ++b) {
+    // block 0's pre-loop launch clears the whole key region, the call's status
+    // word included; later blocks clear their own keys and control word only
+    a1.clear_words = b == 0 ? a.K * a.B + 2 : a.K + 1;
     a1.hidden = static_cast<const uint16_t*>(a.hidden) + b * K * a.d;
     a1.base = a.base + b * K * a.V;
     a1.x_t = a.x_t + b;
@@ -1187,14 +1193,14 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
     // loop-invariant hidden half of the first correction projection (+ b1)
     // as K-slice partials that u_kernel adds up
     e = launch_p_partials(a.hidden, a.B * a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, ps, a.keys,
-                          a.K * a.B + 1, nullptr, 0, s);
+                          a.K * a.B + 2, nullptr, 0, s);
     if (e != hipSuccess) return e;
     DevLoop<T> q = p;
     q.S = ps.S;
     return multi_kernel_loop<T, MT>(q, a.num_cu, s);
   }
   // keys [K, B] and the control words start at zero on every call
-  e = launch_fill_u64(a.keys, a.K * a.B + 1, s);
+  e = launch_fill_u64(a.keys, a.K * a.B + 2, s);
   if (e != hipSuccess) return e;
   // loop-invariant hidden half of the first correction projection (+ b1)
   e = launch_panel_gemm(a.dtype, a.hidden, a.d, a.B * a.K, a.w1, a.d + a.H, a.r, a.d, a.b1, a.P, a.r, a.num_cu, s);

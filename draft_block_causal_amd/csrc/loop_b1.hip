@@ -47,6 +47,7 @@
 // streams that keeps compute units busy only delays the loop; a wait gives up
 // after about a second, so even a loop that cannot complete ends.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -61,7 +62,6 @@ constexpr int kWaves = 4;
 constexpr int kNR = 10;  // W2 tiles per wave, held in registers
 constexpr int kUnitWGs = 8;
 constexpr int kUnitMax = 128;  // GRU units per unit workgroup (H <= 1024)
-constexpr unsigned int kSpinLimit = 1u << 20;
 constexpr int kMaxWgTiles = kNR * kWaves;  // W2 tiles per workgroup
 
 
@@ -84,7 +84,9 @@ struct Params {
   uint32_t rng_b;  // the block's index in the sampler's counter
   float *logits, *states;
   int32_t* tokens;
-  unsigned int* status;
+  unsigned int* status;       // this launch's give-up flag: the other workgroups leave at their next poll
+  unsigned int* call_status;  // the call's status word (see domino_draft_status)
+  unsigned int spin_limit;    // polls before a wait gives up; 0: every wait gives up at once
   unsigned long long* x_hh;   // [2][G][2 segments][16]
   unsigned long long* x_g;    // [2][H]
   unsigned long long* x_pu;   // [2][kUnitWGs][r]
@@ -110,7 +112,8 @@ __device__ __forceinline__ bool gave_up(const unsigned int* status) {
 // is reached or another workgroup gave up.
 template <int N>
 __device__ __forceinline__ bool settle_all(const unsigned long long* const (&src)[N], uint32_t tag,
-                                          const unsigned int* status, unsigned long long (&x)[N]) {
+                                          const unsigned int* status, unsigned int limit,
+                                          unsigned long long (&x)[N]) {
   // every exit follows a check of every load, so no load is left in flight
   // (a later wait would otherwise cover this wave's pending stores too)
   unsigned int spins = 0;
@@ -118,8 +121,8 @@ __device__ __forceinline__ bool settle_all(const unsigned long long* const (&src
     bool done = true;
 #pragma unroll
     for (int q = 0; q < N; ++q) done &= !src[q] || (uint32_t)(x[q] >> 32) == tag;
-    if (done) return true;
-    if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) return false;
+    if (done && limit != 0u) return true;
+    if (++spins > limit || ((spins & 63u) == 0u && gave_up(status))) return false;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int q = 0; q < N; ++q)
@@ -132,11 +135,11 @@ __device__ __forceinline__ bool settle_all(const unsigned long long* const (&src
 // loads (and tag-checks) its words of a published block, so that the whole
 // grid does not re-poll thousands of words per round.
 __device__ __forceinline__ bool wait_sentinels(const unsigned long long* src0, int n, size_t stride, uint32_t tag,
-                                               const unsigned int* status) {
+                                               const unsigned int* status, unsigned int limit) {
   const int lane = threadIdx.x & 63;
   const unsigned long long* src[1] = {lane < n ? src0 + (size_t)lane * stride : nullptr};
   unsigned long long x[1] = {src[0] ? ld_word(src[0]) : 0ull};
-  return settle_all(src, tag, status, x);
+  return settle_all(src, tag, status, limit, x);
 }
 
 // Argmax key carrying the position tag: score (32) | tag (8) | 0xFFFFFF - v (24).
@@ -183,7 +186,8 @@ __device__ __forceinline__ unsigned long long wave_max(unsigned long long x) {
 // Max over the G keys published for one position, on one wave; every load of a
 // lane is in flight before the first is checked.
 __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int G, uint32_t tag,
-                                            const unsigned int* status, unsigned long long& best) {
+                                            const unsigned int* status, unsigned int limit,
+                                            unsigned long long& best) {
   constexpr int kMaxPer = 4;  // G <= 256
   const int lane = threadIdx.x & 63;
   unsigned long long k[kMaxPer];
@@ -199,8 +203,8 @@ __device__ __forceinline__ bool gather_keys(const unsigned long long* keys, int 
     bool done = true;
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) done &= !src[q] || key_tagged(k[q], tag);
-    if (done) break;
-    if (++spins > kSpinLimit || ((spins & 63u) == 0u && gave_up(status))) {
+    if (done && limit != 0u) break;
+    if (++spins > limit || ((spins & 63u) == 0u && gave_up(status))) {
       ok = false;
       break;
     }
@@ -438,7 +442,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
           tok = p.x_t[0];
         } else {
           unsigned long long best;
-          ok &= gather_keys(p.x_key + (size_t)(par ^ 1) * G, G, step, p.status, best);
+          ok &= gather_keys(p.x_key + (size_t)(par ^ 1) * G, G, step, p.status, p.spin_limit, best);
           const int picked = key_index(best);
           if (w == 0 && lane == 0) p.tokens[step - 1] = picked;
           tok = p.teacher ? p.teacher[step - 1] : picked;
@@ -465,7 +469,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         float a3[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) a3[q] = trow[q * H + j];
-        ok &= settle_all(hsrc, tag, p.status, hx);
+        ok &= settle_all(hsrc, tag, p.status, p.spin_limit, hx);
         float c3[3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
@@ -512,8 +516,9 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     for (int q = 0; q < kLbPer; ++q)
       if (tid + q * kThreads < nv)
         lbs[tid + q * kThreads] = t_lo * 16 + tid + q * kThreads < V ? lbr[q] + b2s[tid + q * kThreads] : -INFINITY;
-    if (wave == 0) ok &= wait_sentinels(p.x_pu + (size_t)par * kUnitWGs * r, kUnitWGs, r, tag, p.status);
-    if (do_hh && wave == 1) ok &= wait_sentinels(p.x_g + (size_t)par * H, kUnitWGs, units, tag, p.status);
+    if (wave == 0) ok &= wait_sentinels(p.x_pu + (size_t)par * kUnitWGs * r, kUnitWGs, r, tag, p.status, p.spin_limit);
+    if (do_hh && wave == 1)
+      ok &= wait_sentinels(p.x_g + (size_t)par * H, kUnitWGs, units, tag, p.status, p.spin_limit);
     if (__syncthreads_or(!ok)) {
       ok = false;
       break;
@@ -532,7 +537,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
         src[kUnitWGs + q] = do_hh && tid + q * kThreads < H ? p.x_g + (size_t)par * H + tid + q * kThreads : nullptr;
 #pragma unroll
       for (int q = 0; q < kUnitWGs + kPer; ++q) x[q] = src[q] ? ld_word(src[q]) : 0ull;
-      ok &= settle_all(src, tag, p.status, x);
+      ok &= settle_all(src, tag, p.status, p.spin_limit, x);
       if (tid < r) {
         float s = 0.f;  // the shares carry P as well
 #pragma unroll
@@ -631,11 +636,14 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
 
   if (ok && w == 0 && wave == kWaves - 1) {  // the token of the last position
     unsigned long long best;
-    ok &= gather_keys(p.x_key + (size_t)((p.K - 1) & 1) * G, G, p.K, p.status, best);
+    ok &= gather_keys(p.x_key + (size_t)((p.K - 1) & 1) * G, G, p.K, p.status, p.spin_limit, best);
     if (lane == 0 && ok) p.tokens[p.K - 1] = key_index(best);
   }
   if (!ok) {
-    if (tid == 0) atomicOr(p.status, 1u);
+    if (tid == 0) {
+      atomicOr(p.status, 1u);
+      atomicOr(p.call_status, 1u);
+    }
     if (w == 0)
       for (int i = tid; i < p.K; i += kThreads) p.tokens[i] = -1;
   }
@@ -653,12 +661,59 @@ struct PreArgs {
 
 static hipError_t launch_pre(const PreArgs& q, hipStream_t s) {
   const LoopArgs& a = *q.a;
-  return launch_p_partials(a.hidden, a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, q.shape, a.keys, a.K * a.B + 1,
+  return launch_p_partials(a.hidden, a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, q.shape, a.keys, a.clear_words,
                            a.xpart, (int)a.xwords, s);
 }
 
+// The loop's workgroups wait on one another, so two such loops must never
+// hold compute units at the same time: one loop could then wait for
+// workgroups that cannot start until the other ends.  Within the process,
+// every loop launch is ordered after the previous one on the same device,
+// whatever stream either runs on: the launch first waits on an event recorded
+// after the previous loop, then records it again after its own.  Under stream
+// capture the ordering is the graph's (the event is neither waited on nor
+// recorded).  Loops of other processes on the same device are not ordered by
+// this; their bounded waits then give up instead of hanging.
+class LoopOrder {
+ public:
+  static LoopOrder& get() {
+    static LoopOrder o;
+    return o;
+  }
+  // Enqueues `launch` on s after every earlier loop launch of this device.
+  template <class F>
+  hipError_t run(hipStream_t s, F&& launch) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) return launch();
+    std::lock_guard<std::mutex> lock(mu_);
+    if (!ev_[dev]) {
+      e = hipEventCreateWithFlags(&ev_[dev], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        ev_[dev] = nullptr;
+        return e;
+      }
+    } else if ((e = hipStreamWaitEvent(s, ev_[dev], 0)) != hipSuccess) {
+      return e;
+    }
+    e = launch();
+    if (e != hipSuccess) return e;
+    return hipEventRecord(ev_[dev], s);
+  }
+
+ private:
+  static constexpr int kMaxDev = 64;
+  std::mutex mu_;
+  hipEvent_t ev_[kMaxDev] = {};
+};
+
 // Checks that the loop kernel fits one workgroup per CU, then launches the
-// pre-loop kernel and the loop.
+// pre-loop kernel and the loop, ordered after earlier loops of the device.
 template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
 static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q, hipStream_t s) {
   auto kern = draft_b1_kernel<UHW, NR, RK, SAMPLED, LOGITS>;
@@ -669,10 +724,12 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q,
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
-  e = launch_pre(q, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
-  return hipGetLastError();
+  return LoopOrder::get().run(s, [&]() -> hipError_t {
+    hipError_t e2 = launch_pre(q, s);
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
+    return hipGetLastError();
+  });
 }
 
 template <int UHW, int NR, int RK>
@@ -774,6 +831,8 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.states = a.states;
   p.tokens = a.tokens;
   p.status = reinterpret_cast<unsigned int*>(a.keys + (size_t)a.K * a.B);
+  p.call_status = a.call_status;
+  p.spin_limit = a.spin_limit;
   unsigned long long* x = a.xpart;
   p.x_hh = x;
   x += 2 * (size_t)a.max_wg * 2 * 16;

@@ -26,6 +26,15 @@
  *     results (never out-of-bounds accesses for token ids: the kernels clamp).
  *   - Thread safety: calls may be made from several host threads on different
  *     streams; each concurrent draft_block call needs its own workspace.
+ *   - domino_draft_block's single-block schedule (one block per call, or two,
+ *     with a GRU input table at the pages' shapes) runs one workgroup on every
+ *     compute unit, and those workgroups wait on one another.  The library
+ *     orders every such launch of a process after the previous one on the same
+ *     device, whatever streams they are issued on, so they never share the
+ *     compute units (under stream capture the graph's own order applies).
+ *     Work of other processes can still hold compute units; every wait of the
+ *     loop is bounded (about a second), and a loop that gives up reports it
+ *     through domino_draft_status and leaves -1 in its block's tokens.
  */
 #ifndef DOMINO_H_
 #define DOMINO_H_
@@ -163,12 +172,28 @@ int domino_base_logits(const domino_head *head, int32_t batch, const void *hidde
  * Arithmetic: float32 throughout; bf16 weights are multiplied in bf16 by the
  * matrix cores with float32 accumulation, and float32 activations are fed to
  * them as a bf16 (high, low) pair so they keep about 16 significant bits.
+ * Completion: the schedules whose workgroups wait on one another (see the
+ * conventions above) give up a wait after about a second; the call's status
+ * word (domino_draft_status) is then 1 and every token of the block whose
+ * loop gave up is -1, which is never a valid token id.  A call that returns
+ * DOMINO_OK and whose status word reads 0 drafted every block.
  */
 int domino_draft_block(const domino_head *head, int32_t batch, const void *hidden,
                        const float *base_logits, const int32_t *x_t, const int32_t *teacher,
                        float temperature, uint64_t seed, uint32_t offset, int32_t *tokens,
                        float *logits, float *gru_states, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * Status of the last domino_draft_block call that used `workspace` for `batch`
+ * blocks of this head: enqueues on `stream` a copy of the call's status word
+ * into status[0] (device memory, int32): 0 = every block's loop completed,
+ * 1 = a loop gave up a wait (its block's tokens are -1).  Stream-ordered after
+ * the draft call when issued on the same stream; the workspace must not have
+ * been reused in between.
+ */
+int domino_draft_status(const domino_head *head, int32_t batch, const void *workspace, size_t workspace_bytes,
+                        int32_t *status, void *stream);
 
 /*
  * Acceptance length of each draft row ([notes] §一.1 item 1): the number of

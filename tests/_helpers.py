@@ -15,6 +15,13 @@ import oracle as O
 # scales the GRU moves the logits by less than the logit tolerance.
 LOGIT_TOL = 2e-2
 STATE_TOL = 1e-3
+# Diagnostic bounds, far tighter than the contract: the measured errors are
+# ~1e-5 (logits) and ~1e-7 (states).  Feeding a float32 activation to the
+# matrix cores as one bf16 value instead of a (high, low) pair would add
+# ~3e-4 rms to the logits and ~1e-3 at the tails, which the contract's 2e-2
+# would not see; these bounds do.
+LOGIT_DIAG_TOL = 5e-3
+STATE_DIAG_TOL = 1e-4
 
 _cache: dict = {}
 
@@ -73,7 +80,7 @@ def device_head(w: S.Workload, device):
     return ent["dev"]
 
 
-def check_replay(gpu_tokens: np.ndarray, replay: dict, tol: float = LOGIT_TOL):
+def check_replay(gpu_tokens: np.ndarray, replay: dict, tol: float = LOGIT_TOL, block_ids=None):
     """Free-running tokens versus the oracle re-run teacher-forced on those tokens.
 
     Position (b, i) passes if the GPU token is the oracle's pick, or if the
@@ -92,7 +99,8 @@ def check_replay(gpu_tokens: np.ndarray, replay: dict, tol: float = LOGIT_TOL):
                 continue
             margin = float(O.top2_margin(s))
             ok = margin < tol and s[y] > s.max() - tol
-            assert ok, (f"block {b} position {i}: GPU token {y} (score {s[y]:.6f}) vs oracle {best} "
+            bid = b if block_ids is None else int(block_ids[b])
+            assert ok, (f"block {bid} position {i}: GPU token {y} (score {s[y]:.6f}) vs oracle {best} "
                         f"(score {s[best]:.6f}, top-2 margin {margin:.3g})")
             ties += 1
     return ties, B * K

@@ -135,6 +135,25 @@ def test_draft_block_validation(lib):
     assert _draft(lib, bad) == E_SHAPE
 
 
+def test_draft_status_validation(lib):
+    h = fake_head()
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_workspace_size(ctypes.byref(h), 2, ctypes.byref(sz)) == OK
+    ws = 0x100000
+
+    def st(batch=2, w=ws, nbytes=sz.value, out=0x2000, head=h):
+        return lib.domino_draft_status(ctypes.byref(head), batch, w, nbytes, out, None)
+
+    assert st(batch=0) == E_SHAPE
+    assert st(batch=129) == E_UNSUP
+    assert st(out=None) == E_NULL
+    assert st(out=0x2002) == E_ALIGN
+    assert st(w=None) == E_WS
+    assert st(w=ws + 16) == E_WS
+    assert st(nbytes=sz.value - 1) == E_WS
+    assert st(head=fake_head(d=100)) == E_SHAPE
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour without a GPU")
 def test_valid_call_without_gpu_reports_hip_error(lib):
     h = fake_head()

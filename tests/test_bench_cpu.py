@@ -46,3 +46,22 @@ def test_cpu_only_mode_reports_both_thread_counts():
     line = json.loads(res.stdout.strip().splitlines()[-1])
     assert line["all_threads"]["kind"] == "oracle" and line["all_threads"]["value"] > 0
     assert line["one_thread"]["cores"] == 1 and line["one_thread"]["value"] > 0
+
+
+def test_whole_call_bytes_flops_and_floors_at_the_workloads():
+    # compulsory bytes of one draft call: each weight once, gathered embedding
+    # rows, hidden in, float32 base logits written and read, x_t in, tokens out
+    q8 = dict(K=16, d=4096, V=151936, H=1024, r=256, elem=2)
+    assert bench.block_algorithmic_bytes(1, **q8) == 1_376_556_356
+    assert bench.block_algorithmic_bytes(32, **q8) == 1_987_566_976
+    assert bench.block_algorithmic_bytes(128, **q8) == 3_879_728_896
+    assert bench.block_algorithmic_bytes(8, 16, 2560, 151936, 1024, 256, 2) == 1_036_769_056
+    # per block: LM head 19.915 G, W2 1.245 G, GRU 0.503 G, W1 0.042 G
+    per_block = bench.block_flops(1, 16, 4096, 151936, 1024, 256)
+    assert abs(per_block - (19.915e9 + 1.245e9 + 0.503e9 + 0.042e9)) < 0.01e9
+    # floors: one Qwen3-8B block is HBM-bound (172.1 us), 32 and 128 blocks
+    # are matrix-core-bound (277.8 and 1,111 us)
+    assert abs(bench.block_floor_us(1, **q8) - 172.07) < 0.05
+    assert abs(bench.block_floor_us(32, **q8) - 277.8) < 0.1
+    assert abs(bench.block_floor_us(128, **q8) - 1111.1) < 0.5
+    assert abs(bench.block_floor_us(8, 16, 2560, 151936, 1024, 256, 2) - 129.6) < 0.1
