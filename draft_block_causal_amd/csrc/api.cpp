@@ -72,6 +72,14 @@ extern "C" int domino_draft_block(const domino_head* h, int32_t batch, const voi
   int st = domino::check_draft_args(h, batch, hidden, base_logits, x_t, temperature, tokens, logits, gru_states,
                                     workspace, workspace_bytes);
   if (st != DOMINO_OK || batch == 0) return st;
+  return domino::enqueue_draft_block(h, batch, hidden, base_logits, x_t, teacher, temperature, seed, offset, tokens,
+                                     logits, gru_states, workspace, stream);
+}
+
+int domino::enqueue_draft_block(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                                const int32_t* x_t, const int32_t* teacher, float temperature, uint64_t seed,
+                                uint32_t offset, int32_t* tokens, float* logits, float* gru_states, void* workspace,
+                                void* stream) {
   const int num_cu = device_cu_count();
   if (num_cu <= 0) return DOMINO_ERR_HIP;
   const domino::WorkspaceLayout w = domino::workspace_layout(h, batch);

@@ -77,9 +77,9 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   return w;
 }
 
-int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
-                     const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
-                     const float* gru_states, const void* workspace, size_t workspace_bytes) {
+int check_draft_io(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                   const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
+                   const float* gru_states) {
   int st = check_head(h);
   if (st != DOMINO_OK) return st;
   if (batch < 0) return DOMINO_ERR_SHAPE;
@@ -89,6 +89,14 @@ int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, co
   if (!hidden || !base_logits || !x_t || !tokens) return DOMINO_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(base_logits) || !aligned16(tokens)) return DOMINO_ERR_ALIGN;
   if ((logits && !aligned16(logits)) || (gru_states && !aligned16(gru_states))) return DOMINO_ERR_ALIGN;
+  return DOMINO_OK;
+}
+
+int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                     const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
+                     const float* gru_states, const void* workspace, size_t workspace_bytes) {
+  int st = check_draft_io(h, batch, hidden, base_logits, x_t, temperature, tokens, logits, gru_states);
+  if (st != DOMINO_OK || batch == 0) return st;
   const WorkspaceLayout w = workspace_layout(h, batch);
   if (!workspace) return DOMINO_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DOMINO_ERR_WORKSPACE;

@@ -28,6 +28,10 @@ int elem_size(int dtype);
 int check_head(const domino_head* h);
 int gru_ksplit(int d);
 WorkspaceLayout workspace_layout(const domino_head* h, int batch);
+// Everything domino_draft_block checks except the workspace.
+int check_draft_io(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                   const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
+                   const float* gru_states);
 int check_draft_args(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
                      const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
                      const float* gru_states, const void* workspace, size_t workspace_bytes);
@@ -51,5 +55,13 @@ int check_gru_backward_args(const domino_head* h, int32_t batch, const int32_t* 
 int check_verify_args(int32_t batch, int32_t block, int32_t vocab, const float* target_logits,
                       const float* draft_logits, const int32_t* draft, float temperature, const int32_t* accept,
                       const int32_t* next_token, const void* workspace, size_t workspace_bytes);
+
+// Enqueues a draft call whose arguments passed check_draft_io, over a
+// workspace of at least workspace_layout(h, batch).total bytes, 256-byte
+// aligned (api.cpp).  Returns a domino_status.
+int enqueue_draft_block(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
+                        const int32_t* x_t, const int32_t* teacher, float temperature, uint64_t seed,
+                        uint32_t offset, int32_t* tokens, float* logits, float* gru_states, void* workspace,
+                        void* stream);
 
 }  // namespace domino
