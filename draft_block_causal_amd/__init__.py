@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     domino_curriculum_loss,
     domino_debug_philox,
     domino_draft_block,
+    domino_draft_block_noalloc,
     domino_draft_status,
     domino_gru_backward,
     domino_gru_table_size,

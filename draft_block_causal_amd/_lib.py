@@ -42,6 +42,7 @@ EXPORTED = [
     "domino_base_logits",
     "domino_draft_block",
     "domino_draft_status",
+    "domino_draft_block_noalloc",
     "domino_accept_len",
     "domino_verify_sampled",
     "domino_verify_workspace_size",
@@ -110,6 +111,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_base_logits": (ctypes.c_int, [HP, I32, P, P, P]),
         "domino_draft_block": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P, SZ, P]),
         "domino_draft_status": (ctypes.c_int, [HP, I32, P, SZ, P, P]),
+        "domino_draft_block_noalloc": (ctypes.c_int, [HP, I32, P, P, P, P, F, U64, U32, P, P, P, P]),
         "domino_accept_len": (ctypes.c_int, [I32, I32, P, P, P, P]),
         "domino_verify_sampled": (ctypes.c_int, [I32, I32, I32, P, P, P, F, U64, U32, P, P, P, SZ, P]),
         "domino_verify_workspace_size": (SZ, [I32, I32, I32]),
@@ -277,6 +279,30 @@ def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: torch.Tens
         head.ref, B, _ptr(hidden), _ptr(base_logits), _ptr(x_t), _ptr(teacher), float(temperature),
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(tokens), _ptr(logits), _ptr(gru_states),
         _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return tokens
+
+
+def domino_draft_block_noalloc(head: Head, hidden: torch.Tensor, base_logits: torch.Tensor, x_t: torch.Tensor,
+                               tokens: torch.Tensor, teacher: Optional[torch.Tensor] = None, temperature: float = 0.0,
+                               seed: int = 0, offset: int = 0, logits: Optional[torch.Tensor] = None,
+                               gru_states: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """domino_draft_block over the library's fixed scratch array: no workspace,
+    and nothing is allocated (the caller passes every output, tokens included)."""
+    B, K, dev = hidden.shape[0], head.block, head.device
+    _need(hidden, "hidden", head.dtype, (B, K, head.d), dev)
+    _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
+    _need(x_t, "x_t", torch.int32, (B,), dev)
+    _need(tokens, "tokens", torch.int32, (B, K), dev)
+    if teacher is not None:
+        _need(teacher, "teacher", torch.int32, (B, K), dev)
+    if logits is not None:
+        _need(logits, "logits", torch.float32, (B, K, head.vocab), dev)
+    if gru_states is not None:
+        _need(gru_states, "gru_states", torch.float32, (B, K, head.gru_hidden), dev)
+    _check("domino_draft_block_noalloc", load_library().domino_draft_block_noalloc(
+        head.ref, B, _ptr(hidden), _ptr(base_logits), _ptr(x_t), _ptr(teacher), float(temperature),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF, _ptr(tokens), _ptr(logits), _ptr(gru_states),
+        _stream_ptr(stream)))
     return tokens
 
 

@@ -185,6 +185,25 @@ int domino_draft_block(const domino_head *head, int32_t batch, const void *hidde
                        void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * serving loops or harnesses that forbid allocation): domino_draft_block with
+ * the same arguments except the workspace.  Its scratch is a fixed device
+ * array of 16 MiB inside the library (one per device, held until the process
+ * ends), enough for up to 32 blocks of a Qwen3-8B-shaped head; a call whose
+ * domino_workspace_size exceeds 16 MiB returns DOMINO_ERR_UNSUPPORTED before
+ * anything is enqueued.  The call allocates nothing.  Every call on a device
+ * shares that device's array: calls that overlap on one device (different
+ * streams, or host threads, without ordering between them) race and give
+ * undefined results.  Each call clears what must start at zero.  Outputs,
+ * arguments and errors are those of domino_draft_block; a loop that gives up
+ * leaves -1 in its block's tokens.
+ */
+int domino_draft_block_noalloc(const domino_head *head, int32_t batch, const void *hidden,
+                               const float *base_logits, const int32_t *x_t, const int32_t *teacher,
+                               float temperature, uint64_t seed, uint32_t offset, int32_t *tokens, float *logits,
+                               float *gru_states, void *stream);
+
+/*
  * Status of the last domino_draft_block call that used `workspace` for `batch`
  * blocks of this head: enqueues on `stream` a copy of the call's status word
  * into status[0] (device memory, int32): 0 = every block's loop completed,

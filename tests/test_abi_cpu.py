@@ -154,12 +154,36 @@ def test_draft_status_validation(lib):
     assert st(head=fake_head(d=100)) == E_SHAPE
 
 
+def test_draft_block_noalloc_validation(lib):
+    # the same argument checks as domino_draft_block, and a call whose scratch
+    # would exceed the library's fixed 16 MiB array is refused on the host
+    q8 = fake_head(d=4096, vocab=151936, gru_hidden=1024, rank=256)
+
+    def na(h, batch=1, hidden=0x20000, base=0x30000, x_t=0x40000, temp=0.0, tokens=0x50000):
+        return lib.domino_draft_block_noalloc(ctypes.byref(h), batch, hidden, base, x_t, None, temp, 0, 0, tokens,
+                                              None, None, None)
+
+    assert na(q8, batch=-1) == E_SHAPE
+    assert na(q8, batch=129) == E_UNSUP
+    assert na(q8, temp=-1.0) == E_ARG
+    assert na(q8, hidden=None) == E_NULL
+    assert na(q8, tokens=0x50004) == E_ALIGN
+    assert na(q8, batch=0) == OK
+    sz = ctypes.c_size_t(0)
+    assert lib.domino_workspace_size(ctypes.byref(q8), 64, ctypes.byref(sz)) == OK and sz.value > 16 << 20
+    assert na(q8, batch=64) == E_UNSUP
+    assert na(q8, batch=128) == E_UNSUP
+    assert lib.domino_workspace_size(ctypes.byref(q8), 32, ctypes.byref(sz)) == OK and sz.value <= 16 << 20
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the behaviour without a GPU")
 def test_valid_call_without_gpu_reports_hip_error(lib):
     h = fake_head()
     assert _draft(lib, h) == E_HIP
     assert lib.domino_base_logits(ctypes.byref(h), 1, 0x20000, 0x30000, None) == E_HIP
     assert lib.domino_accept_len(4, 16, 0x1000, 0x2000, 0x3000, None) == E_HIP
+    assert lib.domino_draft_block_noalloc(ctypes.byref(h), 1, 0x20000, 0x30000, 0x40000, None, 0.0, 0, 0, 0x50000,
+                                          None, None, None) == E_HIP
 
 
 def test_base_logits_and_accept_validation(lib):
