@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdomino.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "verify.hip", "base_draft.hip",
+SOURCES = ["kernels.hip", "rowstream.hip", "gemm.hip", "loop.hip", "loop_b1.hip", "loop_bn.hip", "verify.hip", "base_draft.hip",
            "loss.hip", "backward.hip", "gru_backward.hip", "noalloc.hip", "api.cpp", "validate.cpp"]
 
 HIPCC_FLAGS = [

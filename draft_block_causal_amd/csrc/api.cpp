@@ -29,13 +29,15 @@ int device_cu_count() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DOMINO_OK : DOMINO_ERR_HIP; }
 
-// DOMINO_LOOP=persistent | multi selects the loop schedule (default: three
-// kernels per position).
+// DOMINO_LOOP selects the loop schedule: persistent (the cooperative kernel,
+// B <= 32), multi (three kernels per position), blocks (the several-block
+// on-chip loop also for two blocks); default: the library's choice.
 int loop_mode() {
   const char* m = std::getenv("DOMINO_LOOP");
   if (!m) return 0;
   if (std::strcmp(m, "persistent") == 0) return 1;
   if (std::strcmp(m, "multi") == 0) return 2;
+  if (std::strcmp(m, "blocks") == 0) return 3;
   return 0;
 }
 

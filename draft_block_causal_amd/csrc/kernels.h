@@ -96,6 +96,15 @@ bool b1_supported(const LoopArgs& a);
 hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s);
 size_t b1_exchange_words(int H, int r, int max_wg);
 
+// The several-block loop with on-chip weights (loop_bn.hip), up to 32 blocks
+// per launch (a call of more blocks runs launches of about equal size, each
+// with its own pre-loop kernel): bn_supported() tells whether it takes these
+// arguments (host-side checks only); bn_exchange_words() is the exchange
+// region it needs for `batch` blocks.
+bool bn_supported(const LoopArgs& a);
+hipError_t launch_draft_bn(const LoopArgs& a, hipStream_t s);
+size_t bn_exchange_words(int batch, int max_wg, int H, int r);
+
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
 constexpr unsigned int kDefaultSpinLimit = 1u << 20;  // about a second of polling
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);

@@ -1140,6 +1140,8 @@ static hipError_t persistent_loop(const DevLoop<T>& p, int num_cu, int max_wg, h
 
 // Blocks per call up to which the single-block loop runs once per block.
 constexpr int kB1PerBlockMax = 2;
+// Blocks per call up to which the several-block on-chip loop is the default.
+constexpr int kBnDefaultMax = 16;
 
 // Block b of a bf16 call as a call of its own (row pointers offset, the
 // sampler keyed by b); hipErrorNotSupported before any launch if the
@@ -1218,6 +1220,18 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
 
 template <class T>
 static hipError_t loop_t(const LoopArgs& a, int mode, hipStream_t s) {
+  // several blocks of a bf16 head with its GRU input table: the on-chip loop
+  // for several blocks per launch, from 3 to 16 blocks (one launch; measured
+  // at Qwen3 shapes: 8 blocks 253 us against 443 us for the per-position
+  // kernels, 32 blocks in two launches 706 against 624 us), or for any count
+  // from 2 when forced
+  if ((mode == 0 && a.B >= 3 && a.B <= kBnDefaultMax) || mode == 3) {
+    if (bn_supported(a)) {
+      const hipError_t e = launch_draft_bn(a, s);
+      if (e != hipErrorNotSupported) return e;
+      (void)hipGetLastError();  // the grid cannot be co-resident here: use another schedule
+    }
+  }
   if (a.B <= 16) return run_loop<T, 1>(a, mode, s);
   if (a.B <= 32) return run_loop<T, 2>(a, mode, s);
   if (a.B <= 64) return run_loop<T, 4>(a, mode, s);

@@ -51,9 +51,11 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "xchg.h"
 
 namespace domino {
 namespace b1 {
+using namespace xchg;
 
 // One wave per SIMD: each wave may use 512 registers (256 VGPRs + 256 AGPRs),
 // which is where the workgroup's whole share of W2 lives.
@@ -92,96 +94,6 @@ struct Params {
   unsigned long long* x_pu;   // [2][kUnitWGs][r]
   unsigned long long* x_key;  // [2][G]
 };
-
-__device__ __forceinline__ unsigned long long ld_word(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_word(unsigned long long* p, unsigned long long w) {
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_f32(unsigned long long* p, float v, uint32_t tag) {
-  put_word(p, ((unsigned long long)tag << 32) | __float_as_uint(v));
-}
-__device__ __forceinline__ bool gave_up(const unsigned int* status) {
-  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-}
-
-// Polls the words src[q] (skipping null entries) until each carries `tag` in
-// its high word; x[q] holds the last value read (preloaded by the caller, so
-// all first loads are in flight together).  Bounded: false if the spin limit
-// is reached or another workgroup gave up.
-template <int N>
-__device__ __forceinline__ bool settle_all(const unsigned long long* const (&src)[N], uint32_t tag,
-                                          const unsigned int* status, unsigned int limit,
-                                          unsigned long long (&x)[N]) {
-  // every exit follows a check of every load, so no load is left in flight
-  // (a later wait would otherwise cover this wave's pending stores too)
-  unsigned int spins = 0;
-  while (true) {
-    bool done = true;
-#pragma unroll
-    for (int q = 0; q < N; ++q) done &= !src[q] || (uint32_t)(x[q] >> 32) == tag;
-    if (done && limit != 0u) return true;
-    if (++spins > limit || ((spins & 63u) == 0u && gave_up(status))) return false;
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int q = 0; q < N; ++q)
-      if (src[q] && (uint32_t)(x[q] >> 32) != tag) x[q] = ld_word(src[q]);
-  }
-}
-
-// Lanes 0..n-1 of one wave poll one word each, src0 + lane * stride, until it
-// carries `tag`: a cheap "probably all there" signal before every thread
-// loads (and tag-checks) its words of a published block, so that the whole
-// grid does not re-poll thousands of words per round.
-__device__ __forceinline__ bool wait_sentinels(const unsigned long long* src0, int n, size_t stride, uint32_t tag,
-                                               const unsigned int* status, unsigned int limit) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long* src[1] = {lane < n ? src0 + (size_t)lane * stride : nullptr};
-  unsigned long long x[1] = {src[0] ? ld_word(src[0]) : 0ull};
-  return settle_all(src, tag, status, limit, x);
-}
-
-// Argmax key carrying the position tag: score (32) | tag (8) | 0xFFFFFF - v (24).
-__device__ __forceinline__ unsigned long long b1_key(float s, uint32_t v, uint32_t tag) {
-  uint32_t u = __float_as_uint(s);
-  if (u == 0x80000000u) u = 0u;
-  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)o << 32) | ((unsigned long long)(tag & 0xFFu) << 24) |
-         (unsigned long long)(0xFFFFFFu - v);
-}
-__device__ __forceinline__ bool key_tagged(unsigned long long k, uint32_t tag) {
-  return k != 0ull && ((uint32_t)(k >> 24) & 0xFFu) == (tag & 0xFFu);
-}
-__device__ __forceinline__ int key_index(unsigned long long k) { return (int)(0xFFFFFFu - (uint32_t)(k & 0xFFFFFFull)); }
-
-// 64-bit max across lanes with DPP moves (no LDS round trips): within each
-// 16-lane row by rotations of 8 and 4 and two quad swaps, then across the
-// four rows with lane reads (the result is wave-uniform).
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long x) {
-  const unsigned lo = __builtin_amdgcn_update_dpp(0u, (unsigned)x, CTRL, 0xF, 0xF, false);
-  const unsigned hi = __builtin_amdgcn_update_dpp(0u, (unsigned)(x >> 32), CTRL, 0xF, 0xF, false);
-  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-  return o > x ? o : x;
-}
-__device__ __forceinline__ unsigned long long row_max16(unsigned long long x) {
-  x = dpp_max_step<0x128>(x);  // row_ror:8
-  x = dpp_max_step<0x124>(x);  // row_ror:4
-  x = dpp_max_step<0x4E>(x);   // quad_perm [2,3,0,1]
-  return dpp_max_step<0xB1>(x);  // quad_perm [1,0,3,2]
-}
-__device__ __forceinline__ unsigned long long wave_max(unsigned long long x) {
-  x = row_max16(x);
-  unsigned long long m = 0ull;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const unsigned long long y = ((unsigned long long)__builtin_amdgcn_readlane((unsigned)(x >> 32), row * 16) << 32) |
-                                 __builtin_amdgcn_readlane((unsigned)x, row * 16);
-    m = y > m ? y : m;
-  }
-  return m;
-}
 
 // Max over the G keys published for one position, on one wave; every load of a
 // lane is in flight before the first is checked.
@@ -238,7 +150,7 @@ __device__ __forceinline__ int hh_partial_offset(const Params& p, int row, int o
 // workgroup's range or the vocabulary carry a bias of -inf and never win.
 template <bool SAMPLED>
 __device__ __forceinline__ unsigned long long entry_key(float L, float inv_temp, float noise, uint32_t v, uint32_t tag) {
-  return b1_key(SAMPLED ? L * inv_temp + noise : L, v, tag);
+  return tagged_key(SAMPLED ? L * inv_temp + noise : L, v, tag);
 }
 
 struct Lds {
@@ -664,53 +576,6 @@ static hipError_t launch_pre(const PreArgs& q, hipStream_t s) {
   return launch_p_partials(a.hidden, a.K, a.d, a.w1, a.d + a.H, a.r, a.b1, a.ppart, q.shape, a.keys, a.clear_words,
                            a.xpart, (int)a.xwords, s);
 }
-
-// The loop's workgroups wait on one another, so two such loops must never
-// hold compute units at the same time: one loop could then wait for
-// workgroups that cannot start until the other ends.  Within the process,
-// every loop launch is ordered after the previous one on the same device,
-// whatever stream either runs on: the launch first waits on an event recorded
-// after the previous loop, then records it again after its own.  Under stream
-// capture the ordering is the graph's (the event is neither waited on nor
-// recorded).  Loops of other processes on the same device are not ordered by
-// this; their bounded waits then give up instead of hanging.
-class LoopOrder {
- public:
-  static LoopOrder& get() {
-    static LoopOrder o;
-    return o;
-  }
-  // Enqueues `launch` on s after every earlier loop launch of this device.
-  template <class F>
-  hipError_t run(hipStream_t s, F&& launch) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(s, &cap);
-    if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return launch();
-    std::lock_guard<std::mutex> lock(mu_);
-    if (!ev_[dev]) {
-      e = hipEventCreateWithFlags(&ev_[dev], hipEventDisableTiming);
-      if (e != hipSuccess) {
-        ev_[dev] = nullptr;
-        return e;
-      }
-    } else if ((e = hipStreamWaitEvent(s, ev_[dev], 0)) != hipSuccess) {
-      return e;
-    }
-    e = launch();
-    if (e != hipSuccess) return e;
-    return hipEventRecord(ev_[dev], s);
-  }
-
- private:
-  static constexpr int kMaxDev = 64;
-  std::mutex mu_;
-  hipEvent_t ev_[kMaxDev] = {};
-};
 
 // Checks that the loop kernel fits one workgroup per CU, then launches the
 // pre-loop kernel and the loop, ordered after earlier loops of the device.

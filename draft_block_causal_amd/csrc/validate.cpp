@@ -68,8 +68,10 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   // tagged exchange words of the persistent loop: partials, GRU state, u, keys,
   // each double-buffered by position parity
   const size_t multi = 2 * ((ks + 1) * B * 3 * H + B * H + B * r + (size_t)kMaxLoopWorkgroups * B);
-  const size_t single = 2 * ((size_t)kMaxLoopWorkgroups * 2 * 16 + H + 8 * r + (size_t)kMaxLoopWorkgroups);
+  const size_t single = b1_exchange_words((int)H, (int)r, kMaxLoopWorkgroups);
+  const size_t blocks = bn_exchange_words(batch, kMaxLoopWorkgroups, (int)H, (int)r);
   w.xwords = multi > single ? multi : single;
+  if (blocks > w.xwords) w.xwords = blocks;
   w.xchg = off;
   off += up256(w.xwords * sizeof(unsigned long long));
   w.total = off;

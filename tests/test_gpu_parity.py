@@ -243,16 +243,68 @@ def test_qwen3_4b_b8_tied(dev):
     _parity(S.get_workload("qwen3_4b_b8_tied"), dev, sampled=True)
 
 
+def _bn_head(batch, **kw):
+    # GRU width 1024 and rank 256 (what the several-block on-chip loop takes),
+    # a small ragged vocabulary and fan-in scaled weights, so the recurrence
+    # moves the logits by O(1)
+    base = dict(name=f"bn_b{batch}", batch=batch, block=16, d=256, vocab=20011, gru_hidden=1024, rank=256,
+                dtype="bf16", tied=False, temperature=0.0, init="fanin")
+    base.update(kw)
+    return S.Workload(**base)
+
+
+@pytest.mark.parametrize("batch,temperature,mode", [
+    (3, 0.0, "default"), (5, 1.0, "default"), (8, 0.0, "default"), (16, 0.6, "default"), (17, 1.0, "blocks"),
+    (2, 0.0, "blocks"), (2, 1.3, "blocks"),
+])
+def test_several_block_loop(dev, batch, temperature, mode, monkeypatch):
+    """The several-block on-chip loop (GRU input table): partial and full
+    8-block passes, a call split into two launches (17 blocks), two blocks when
+    forced, greedy and sampled, logits and states written."""
+    if mode == "default":
+        monkeypatch.delenv("DOMINO_LOOP", raising=False)
+    else:
+        monkeypatch.setenv("DOMINO_LOOP", mode)
+    _parity(_bn_head(batch, temperature=temperature, philox_seed=21 + batch), dev, table=True)
+
+
+@pytest.mark.parametrize("batch,temperature", [(8, 0.0), (13, 1.0), (32, 1.0)])
+def test_several_block_loop_tokens_only(dev, batch, temperature, monkeypatch):
+    """The same loop without the logits and states outputs (the serving path):
+    every block's tokens by the replay rule against the oracle."""
+    import draft_block_causal_amd as D
+
+    monkeypatch.setenv("DOMINO_LOOP", "blocks")
+    w = _bn_head(batch, temperature=temperature, philox_seed=5)
+    head_np, inp = workload_arrays(w)
+    f = head_f64(w)
+    head = device_head(w, dev)
+    D.domino_prepare_gru_table(head)
+    try:
+        hidden_t = _t(inp["hidden"], dev)
+        base = D.domino_base_logits(head, hidden_t)
+        tok = D.domino_draft_block(head, hidden_t, base, _t(inp["x_t"], dev), temperature=w.temperature,
+                                   seed=w.philox_seed).cpu().numpy()
+    finally:
+        head.set_gru_input_table(None)
+    assert tok.min() >= 0 and tok.max() < w.vocab
+    hid = O.as_f64(inp["hidden"])
+    rep = O.draft_block(f, hid, inp["x_t"], teacher=tok, temperature=w.temperature, seed=w.philox_seed)
+    ties, n = check_replay(tok, rep)
+    log(f"{w.name}: tokens-only replay, near-ties {ties}/{n}")
+
+
 def test_qwen3_8b_b128_accept(dev):
-    """The 128-block workload as one composition: the GPU drafts every block
-    (each replayed against the oracle), the targets are derived from that draft
+    """The 128-block workload as one composition, as the benchmark runs it (GRU
+    input table): the GPU drafts every block (each replayed against the
+    oracle), the targets are derived from that draft
     (each position kept with probability 0.9, else a uniform token), and
     domino_accept_len scores the GPU's own draft tensor, bit-exact against the
     oracle on the same arrays."""
     import draft_block_causal_amd as D
 
     w = S.get_workload("qwen3_8b_b128_accept")
-    tok_np, tok_dev = _parity(w, dev, sampled=True)
+    tok_np, tok_dev = _parity(w, dev, sampled=True, table=True)
     target = S.make_targets(tok_np, w.vocab, p=0.9, seed=1)
     acc = D.domino_accept_len(tok_dev, _t(target, dev)).cpu().numpy()
     want = O.accept_len(tok_np, target)

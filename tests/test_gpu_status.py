@@ -37,12 +37,14 @@ def _draft(D, head, inp, batch, ws, dev, temperature=0.0):
     return tok.cpu().numpy(), int(st.cpu().numpy()[0])
 
 
-@pytest.mark.parametrize("batch", [1, 2])
-def test_single_block_loop_give_up_is_reported(dev, batch, monkeypatch):
+@pytest.mark.parametrize("batch", [1, 2, 8, 20])
+def test_on_chip_loop_give_up_is_reported(dev, batch, monkeypatch):
+    # one block: the single-block loop; two: it once per block; 8 and 20: the
+    # several-block loop (20 blocks: two launches)
     import draft_block_causal_amd as D
 
-    monkeypatch.delenv("DOMINO_LOOP", raising=False)
-    w = S.get_workload("qwen3_8b_b1_greedy").with_(batch=batch)
+    monkeypatch.setenv("DOMINO_LOOP", "blocks" if batch > 2 else "default")
+    w = S.get_workload("qwen3_8b_b32_t1").with_(batch=batch, temperature=0.0)
     _, inp = workload_arrays(w, batch)
     head = device_head(w, dev)
     D.domino_prepare_gru_table(head)
