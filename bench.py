@@ -1,10 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the Domino draft-head hot path on one MI355X.
 
-One step = one draft call on the Qwen3-8B-shaped head at B = 1:
-domino_base_logits (frozen LM head over the 16 positions) + domino_draft_block
-(GRU + low-rank correction + greedy pick, 16 serial positions).  Inputs are
-resident in HBM before the timed region.  domino_accept_len is timed on its
+One step = one draft call on the Qwen3-8B-shaped head at B = 1: the frozen LM
+head over the 16 positions (base logits) + the draft block (GRU + low-rank
+correction + greedy pick, 16 serial positions).  Where the single-block loop
+can form the base logits itself (one block of a bf16 head with its GRU input
+table), the step is the one call domino_draft_block(base_logits=None);
+otherwise, or with --unfused, domino_base_logits then domino_draft_block.
+Inputs are resident in HBM before the timed region, which holds the steps
+alone (no event records between them); a second pass with HIP events gives
+the per-call breakdown.  domino_accept_len is timed on its
 own, on targets derived from the run's draft.  The run checks its own output
 (status word, token range, and block 0 against the oracle by the replay rule
 in the CPU-baseline leg) and exits non-zero if a check fails.  Prints one JSON
@@ -33,11 +38,15 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f) for f in ("rowstream.hip", "common.h")]
+# the single-block loop that forms the base logits itself
+FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_b1_fused_traffic.json")
+FUSED_KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f)
+                        for f in ("loop_b1.hip", "common.h", "xchg.h", "kernels.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -52,16 +61,18 @@ def lmhead_flops(B: int, K: int, d: int, V: int) -> int:
     return 2 * B * K * d * V
 
 
-def block_algorithmic_bytes(B: int, K: int, d: int, V: int, H: int, r: int, elem: int) -> int:
+def block_algorithmic_bytes(B: int, K: int, d: int, V: int, H: int, r: int, elem: int,
+                            base_in_hbm: bool = True) -> int:
     """Compulsory HBM bytes of one draft call (base logits + draft block) over B
     blocks: every weight once (the LM head, W2, W_ih, W_hh, W1 and the biases;
     a tied embedding is the LM head), the gathered embedding rows, the hidden
-    states in, the float32 base logits written and read back once, x_t in and
-    the tokens out.  Re-reads of per-position weights across the 16 positions
-    are a schedule's choice and are not counted."""
+    states in, the float32 base logits written and read back once (not when
+    the call forms them on chip: base_in_hbm=False), x_t in and the tokens out.
+    Re-reads of per-position weights across the 16 positions are a schedule's
+    choice and are not counted."""
     weights = (V * d + V * r + 3 * H * d + 3 * H * H + r * (d + H)) * elem
     biases = (3 * H * 2 + r + V) * elem
-    acts = B * K * d * elem * 2 + 2 * B * K * V * 4 + B * 4 + B * K * 4
+    acts = B * K * d * elem * 2 + (2 * B * K * V * 4 if base_in_hbm else 0) + B * 4 + B * K * 4
     return weights + biases + acts
 
 
@@ -72,19 +83,20 @@ def block_flops(B: int, K: int, d: int, V: int, H: int, r: int) -> int:
     return 2 * M * (V * d + V * r + 3 * H * (d + H) + r * (d + H))
 
 
-def block_floor_us(B: int, K: int, d: int, V: int, H: int, r: int, elem: int) -> float:
+def block_floor_us(B: int, K: int, d: int, V: int, H: int, r: int, elem: int, base_in_hbm: bool = True) -> float:
     """Roofline floor of one draft call: the larger of its compulsory bytes at
     the HBM peak and its FLOPs at the dense bf16 matrix-core peak."""
-    t_hbm = block_algorithmic_bytes(B, K, d, V, H, r, elem) / (HBM_PEAK_GBS * 1e9)
+    t_hbm = block_algorithmic_bytes(B, K, d, V, H, r, elem, base_in_hbm) / (HBM_PEAK_GBS * 1e9)
     t_mfma = block_flops(B, K, d, V, H, r) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     return max(t_hbm, t_mfma) * 1e6
 
 
-def measured_traffic(kernel_hash: str):
-    """HBM bytes per LM-head launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch of a kernel (the LM head by default) from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel source; else
+    None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -190,9 +202,12 @@ def sweep(args, w, batches) -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(ev[i])
+            step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for i in range(args.steps):  # the breakdown, in a pass of its own
+            step(ev[i])
+        torch.cuda.synchronize()
         rows.append({"batch": B, "blocks_per_s": B / (ms * 1e-3), "ms_per_call": ms, "ms_per_block": ms / B,
                      "lm_head_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
                      "draft_block_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))})
@@ -366,6 +381,14 @@ def next_rows(args, w) -> int:
     return 0
 
 
+def forms_base_logits(w, B: int, table: bool) -> bool:
+    """Whether the draft call can form the base logits itself at these shapes
+    (the library's own rule: one block of at most 16 positions of a bf16 head
+    with its GRU input table, d 2560 or 4096, H 1024, r 256)."""
+    return (B == 1 and w.dtype == "bf16" and table and w.block <= 16 and w.d in (2560, 4096)
+            and w.gru_hidden == 1024 and w.rank == 256)
+
+
 def cpu_only(args) -> int:
     """The CPU oracle alone on one block of the workload: with every host thread
     its BLAS uses, then limited to one thread."""
@@ -415,6 +438,9 @@ def main() -> int:
     ap.add_argument("--cpu-only", action="store_true",
                     help="time only the CPU oracle on one block of the workload, with all host threads and with one "
                          "(no GPU needed); prints one JSON line")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time domino_base_logits + domino_draft_block even where the draft call can form the base "
+                         "logits itself")
     ap.add_argument("--no-table", action="store_true",
                     help="do not build the per-head GRU input table (W_ih E^T + b_ih); the loop then multiplies "
                          "by W_ih at every position")
@@ -475,37 +501,48 @@ def main() -> int:
         prepare_ms = e0.elapsed_time(e1)
     torch.cuda.synchronize()
 
+    fused = forms_base_logits(w, B, not args.no_table) and not args.unfused
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     def step(i=None):
-        """One draft call: base logits (A1) + the draft block (A2-A5)."""
+        """One draft call: base logits (A1) + the draft block (A2-A5); fused, the
+        draft call forms the base logits itself."""
         if i is not None:
             ev[i][0].record()
-        D.domino_base_logits(head, hidden, base)
+        if not fused:
+            D.domino_base_logits(head, hidden, base)
         if i is not None:
             ev[i][1].record()
-        D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature, seed=w.philox_seed,
-                             tokens=tokens, workspace=ws)
+        D.domino_draft_block(head, hidden, None if fused else base, x_t, temperature=w.temperature,
+                             seed=w.philox_seed, tokens=tokens, workspace=ws)
         if i is not None:
             ev_end[i].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed region: the steps alone (an event record between launches costs
+    # GPU time of its own); cold runs take the per-step event times instead
     t0 = time.perf_counter()
+    if not args.cold:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # the per-call breakdown, in a pass of its own, with HIP events on the stream
+    # the calls run on (torch's current stream)
     for i in range(args.steps):
         if flush is not None:
             flush.fill_(i & 255)
         step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     step_ms = np.array([a.elapsed_time(e) for (a, _), e in zip(ev, ev_end)])
     ms_per_step = float(step_ms.mean()) if args.cold else (t1 - t0) * 1e3 / args.steps
     lm_all = np.array([a.elapsed_time(b) for a, b in ev])
     draft_all = np.array([b.elapsed_time(c) for (_, b), c in zip(ev, ev_end)])
-    lm_ms, draft_ms = float(lm_all.mean()), float(draft_all.mean())
+    lm_ms, draft_ms = (None if fused else float(lm_all.mean())), float(draft_all.mean())
 
     # the run's own output: every loop completed and every token is a valid id
     status = int(D.domino_draft_status(head, B, ws).cpu().numpy()[0])
@@ -540,7 +577,17 @@ def main() -> int:
     khash = kernel_source_hash()
     traffic = measured_traffic(khash)
     M = B * K
-    if flops / alg > RIDGE_FLOP_PER_BYTE:
+    if fused:
+        # the dominant kernel is the loop that streams the LM head itself: the
+        # whole call's compulsory bytes (no base logits in HBM) over the draft
+        # call's event time (its short pre-launch included)
+        alg = block_algorithmic_bytes(B, K, d, V, H, r, elem, base_in_hbm=False)
+        achieved = alg / (draft_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": measured_traffic(kernel_source_hash(FUSED_KERNEL_SOURCES), FUSED_TRAFFIC_FILE),
+                "algorithmic_bytes": alg}
+    elif flops / alg > RIDGE_FLOP_PER_BYTE:
         achieved = flops / (lm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic, "algorithmic_flops": flops}
@@ -548,19 +595,23 @@ def main() -> int:
         achieved = alg / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": alg}
-    if M <= 32:
+    if fused:
+        kname = ("draft_b1_kernel<8,10,8,%s,false,%d> (the LM head streamed into an on-chip base-logit table, "
+                 "then the 16-position loop, one launch; the events also bracket the pre-loop launch)"
+                 % ("true" if w.temperature > 0 else "false", d * 2 // 4 // 64))
+    elif M <= 32:
         kname = "rowstream_gemm_kernel (LM head, K split over 8 waves, row-contiguous non-temporal loads)"
     elif w.dtype == "bf16":
         kname = ("gemm_bf16_tn_big_kernel<%d> (LM head, %dx256 tiles, LDS-DMA operand loads)"
                  % ((256, 256) if M >= 256 else (128, 128)))
     else:
         kname = "panel_gemm_kernel (LM head, f32)"
-    floor_us = block_floor_us(B, K, d, V, H, r, elem)
-    roof.update({"kernel": kname, "avg_launch_ms": lm_ms,
+    floor_us = block_floor_us(B, K, d, V, H, r, elem, base_in_hbm=not fused)
+    roof.update({"kernel": kname, "avg_launch_ms": draft_ms if fused else lm_ms,
                  # the whole draft call against its own roofline floor (compulsory
                  # bytes at 8 TB/s or FLOPs at the bf16 peak, whichever is larger)
                  "block_floor_us": floor_us, "block_frac": floor_us * 1e-3 / ms_per_step,
-                 "block_algorithmic_bytes": block_algorithmic_bytes(B, K, d, V, H, r, elem),
+                 "block_algorithmic_bytes": block_algorithmic_bytes(B, K, d, V, H, r, elem, base_in_hbm=not fused),
                  "block_flops": block_flops(B, K, d, V, H, r)})
 
     result = {
@@ -579,7 +630,8 @@ def main() -> int:
         "data": "synthetic (seeded Gaussian weights and hidden states; no datasets or checkpoints)",
         "config": {"workload": w.name, "batch": B, "block": K, "d": d, "vocab": V, "gru_hidden": H,
                    "rank": w.rank, "temperature": w.temperature, "tied": w.tied, "parallelism": "none (1 GPU)",
-                   "gru_input_table": not args.no_table},
+                   "gru_input_table": not args.no_table,
+                   "base_logits": "formed inside the draft call" if fused else "domino_base_logits, then the draft call"},
         "gru_table_prepare_ms": prepare_ms,
         "lm_head_ms": lm_ms,
         "draft_block_ms": draft_ms,
@@ -587,7 +639,7 @@ def main() -> int:
         "accept_len_mean": float(acc_np.mean()),
         "draft_status": status,
         "step_ms_events": pct(step_ms),
-        "lm_head_ms_events": pct(lm_all),
+        "lm_head_ms_events": None if fused else pct(lm_all),
         "draft_block_ms_events": pct(draft_all),
         "cold": bool(args.cold),
         "roofline": roof,

@@ -252,14 +252,18 @@ def domino_base_logits(head: Head, hidden: torch.Tensor, base_logits: Optional[t
     return base_logits
 
 
-def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: torch.Tensor, x_t: torch.Tensor,
+def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: Optional[torch.Tensor], x_t: torch.Tensor,
                        teacher: Optional[torch.Tensor] = None, temperature: float = 0.0, seed: int = 0,
                        offset: int = 0, tokens: Optional[torch.Tensor] = None,
                        logits: Optional[torch.Tensor] = None, gru_states: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """base_logits=None: the call forms the base logits itself (one block of a
+    bf16 head with its GRU input table; other shapes raise DominoError with
+    DOMINO_ERR_UNSUPPORTED)."""
     B, K, dev = hidden.shape[0], head.block, head.device
     _need(hidden, "hidden", head.dtype, (B, K, head.d), dev)
-    _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
+    if base_logits is not None:
+        _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
     _need(x_t, "x_t", torch.int32, (B,), dev)
     if teacher is not None:
         _need(teacher, "teacher", torch.int32, (B, K), dev)
@@ -282,15 +286,17 @@ def domino_draft_block(head: Head, hidden: torch.Tensor, base_logits: torch.Tens
     return tokens
 
 
-def domino_draft_block_noalloc(head: Head, hidden: torch.Tensor, base_logits: torch.Tensor, x_t: torch.Tensor,
-                               tokens: torch.Tensor, teacher: Optional[torch.Tensor] = None, temperature: float = 0.0,
-                               seed: int = 0, offset: int = 0, logits: Optional[torch.Tensor] = None,
-                               gru_states: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+def domino_draft_block_noalloc(head: Head, hidden: torch.Tensor, base_logits: Optional[torch.Tensor],
+                               x_t: torch.Tensor, tokens: torch.Tensor, teacher: Optional[torch.Tensor] = None,
+                               temperature: float = 0.0, seed: int = 0, offset: int = 0,
+                               logits: Optional[torch.Tensor] = None, gru_states: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
     """domino_draft_block over the library's fixed scratch array: no workspace,
     and nothing is allocated (the caller passes every output, tokens included)."""
     B, K, dev = hidden.shape[0], head.block, head.device
     _need(hidden, "hidden", head.dtype, (B, K, head.d), dev)
-    _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
+    if base_logits is not None:
+        _need(base_logits, "base_logits", torch.float32, (B, K, head.vocab), dev)
     _need(x_t, "x_t", torch.int32, (B,), dev)
     _need(tokens, "tokens", torch.int32, (B, K), dev)
     if teacher is not None:

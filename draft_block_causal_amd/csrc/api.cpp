@@ -105,6 +105,7 @@ int domino::enqueue_draft_block(const domino_head* h, int32_t batch, const void*
   a.b2 = h->b2;
   a.hidden = hidden;
   a.base = base_logits;
+  a.lm_head = h->lm_head;
   a.x_t = x_t;
   a.teacher = teacher;
   a.sampled = temperature > 0.f ? 1 : 0;
@@ -129,6 +130,12 @@ int domino::enqueue_draft_block(const domino_head* h, int32_t batch, const void*
   a.call_status = reinterpret_cast<unsigned int*>(a.keys + (size_t)batch * h->block + 1);
   a.spin_limit = spin_limit();
   a.clear_words = batch * h->block + 2;
+  if (!base_logits) {
+    // the single-block loop forms the base logits itself; a device whose grid
+    // it cannot hold (fewer than 200 compute units) has no other schedule for it
+    const hipError_t e = domino::launch_draft_b1(a, static_cast<hipStream_t>(stream));
+    return e == hipErrorNotSupported ? DOMINO_ERR_UNSUPPORTED : hip_status(e);
+  }
   return hip_status(domino::launch_draft_loop(a, loop_mode(), static_cast<hipStream_t>(stream)));
 }
 

@@ -47,7 +47,8 @@ struct LoopArgs {
   int B, K, d, V, H, r;
   const void *embed, *w_ih, *w_hh, *b_ih, *b_hh, *w1, *b1, *w2, *b2;
   const void* hidden;
-  const float* base;
+  const float* base;     // [B, K, V], or null: the single-block loop forms the base logits from lm_head
+  const void* lm_head;   // [V, d] (read only where base is null)
   const int32_t* x_t;
   const int32_t* teacher;
   float inv_temp;

@@ -1239,6 +1239,7 @@ static hipError_t loop_t(const LoopArgs& a, int mode, hipStream_t s) {
 }
 
 hipError_t launch_draft_loop(const LoopArgs& a, int mode, hipStream_t s) {
+  if (!a.base) return a.B == 1 ? launch_draft_b1(a, s) : hipErrorNotSupported;  // only it forms the base logits
   if (a.dtype == 1) return loop_t<Bf16>(a, mode, s);
   return loop_t<F32>(a, mode, s);
 }

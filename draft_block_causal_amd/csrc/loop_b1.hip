@@ -51,6 +51,8 @@
 
 #include "common.h"
 #include "kernels.h"
+#include <hip/hip_ext.h>
+
 #include "xchg.h"
 
 namespace domino {
@@ -65,6 +67,15 @@ constexpr int kNR = 10;  // W2 tiles per wave, held in registers
 constexpr int kUnitWGs = 8;
 constexpr int kUnitMax = 128;  // GRU units per unit workgroup (H <= 1024)
 constexpr int kMaxWgTiles = kNR * kWaves;  // W2 tiles per workgroup
+constexpr int kStreamPositions = 16;       // positions of a block whose base logits the kernel can form itself
+// LM-head widths the kernel streams (64-B steps per wave-quarter of a row):
+// d = 2560 and d = 4096 (the Qwen3-4B and Qwen3-8B hidden sizes)
+constexpr int kStreamKw4B = 2560 * 2 / kWaves / 64;
+constexpr int kStreamKw8B = 4096 * 2 / kWaves / 64;
+constexpr int kUHW = 8;  // W_hh k-steps per wave: the only shape a grid of 200..256 workgroups takes
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+constexpr int kWaitVmem0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters left alone
 
 
 struct Params {
@@ -75,7 +86,8 @@ struct Params {
   int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
   const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
   const float* table;     // [V][3H]: W_ih E[v] + b_ih
-  const float* base;   // [K][V]
+  const float* base;   // [K][V], or null: the kernel forms its range's base logits itself
+  const uint16_t *lm_head, *hidden;  // [V][d], [K][d] (base == null)
   const float* ppart;  // [S][K][r]: P = W1[:, :d] h + b1 = sum over s of ppart[s] (b1 in s = 0)
   int S;
   const int32_t *x_t, *teacher;
@@ -154,12 +166,12 @@ __device__ __forceinline__ unsigned long long entry_key(float L, float inv_temp,
 }
 
 struct Lds {
-  int pool, ghl, utile, lbs, b2s, gum, uhl, gs_prev, zero, red, total;
+  int pool, ghl, utile, lbs, b2s, gum, uhl, gs_prev, zero, red, lb, total;
 };
 
 // The pool holds a unit workgroup's W1 columns, or a W_hh owner's k-steps,
 // both as matrix-core fragments [.. 16-row tiles][.. k-steps][64 lanes][16 B].
-__host__ __device__ inline Lds lds_layout(int U_hh, int H, int r) {
+__host__ __device__ inline Lds lds_layout(int U_hh, int H, int r, bool fused) {
   Lds L{};
   int off = 0;
   L.pool = off;
@@ -183,6 +195,8 @@ __host__ __device__ inline Lds lds_layout(int U_hh, int H, int r) {
   off += 16;  // 16 zero bytes: the A operand of the lanes of rows 2-15
   L.red = off;
   off += kWaves * 2 * 16 * 4;
+  L.lb = off;
+  off += fused ? kStreamPositions * kMaxWgTiles * 16 * 4 : 0;  // base logits + b2 of every position (fused)
   L.total = off;
   return L;
 }
@@ -202,7 +216,110 @@ __device__ __forceinline__ u32x4 row_frag(const uint16_t* hl, int n, int k0, int
   return ld16(col < 2 ? static_cast<const void*>(hl + col * n + k0 + grp * 8) : zero);
 }
 
-template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
+// Bytes of LDS the fused base-logit stream borrows from the pool: each
+// wave's transposition tile and two reduction buffers.
+__host__ __device__ constexpr int stream_scratch_bytes() { return kWaves * 16 * 512 + 2 * kWaves * 16 * 17 * 4; }
+
+// Base logits of this workgroup's vocabulary range for every position
+// ([notes] §二.1(1): the frozen LM head over the block's hidden states, in one
+// pass): lb[i][e] = sum_k hidden[i][k] W_lm[16 t_lo + e][k] + b2[16 t_lo + e]
+// (-inf past the vocabulary).  W_lm's rows are read once, from HBM, the way
+// it streams best: each wave takes a quarter of K (KW 64-B steps of each
+// row), and a load instruction covers 512 contiguous bytes of each of two rows,
+// read non-temporally through buffer descriptors sized to the valid rows (rows
+// past V read zero); a quarter of K that 512 B does not divide goes in 256-B
+// passes of four rows.  The wave writes its slices into a private LDS tile
+// (16-B chunks XOR-swizzled by row) and reads them back as matrix-core
+// operands against the 16 positions' hidden states held in registers; the
+// four waves' partial sums are added in LDS in a fixed order.  The next tile's
+// loads are in flight while a tile is multiplied.
+template <int KW>
+__device__ void stream_base(const Params& p, int t_lo, int nt, unsigned char* scratch, float* lb) {
+  constexpr int kSlice = KW * 64;
+  constexpr int kPass = kSlice % 512 == 0 ? 512 : 256;
+  constexpr int kPasses = kSlice / kPass;
+  constexpr int kChunks = kPass / 16;
+  constexpr int kRowsPerLoad = 64 / kChunks;
+  constexpr int kLoadsPerPass = 16 / kRowsPerLoad;
+  constexpr int kStepsPerPass = kPass / 64;
+  static_assert(kSlice % kPass == 0 && kPasses * kLoadsPerPass == KW, "stream shape");
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int V = p.V, d = p.d;
+  unsigned char* tile = scratch + wave * 16 * kPass;
+  float* red = reinterpret_cast<float*>(scratch + kWaves * 16 * 512);
+  u32x4 af[KW];
+  {
+    const bool live = col < p.K;
+    const unsigned char* arow =
+        reinterpret_cast<const unsigned char*>(p.hidden + (size_t)(live ? col : 0) * d) + wave * kSlice + grp * 16;
+#pragma unroll
+    for (int s = 0; s < KW; ++s) af[s] = live ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
+  }
+  const int row_bytes = d * 2;
+  const int lrow = lane / kChunks, lchunk = lane % kChunks;
+  const int voff = lrow * row_bytes + wave * kSlice + lchunk * 16;
+  auto stage = [&](int j, u32x4 (&dst)[KW]) {
+    const int t = t_lo + j;
+    const int rows = j < nt ? min(16, V - t * 16) : 0;
+    const uint16_t* base = p.lm_head + (j < nt ? (size_t)t * 16 * d : 0);
+#pragma unroll
+    for (int jj = 0; jj < kLoadsPerPass; ++jj) {
+      const int rj =
+          jj == 0 ? min(rows, kRowsPerLoad) : min(max(rows - jj * kRowsPerLoad, 0), kRowsPerLoad);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base + (rj > 0 ? (size_t)jj * kRowsPerLoad * d : 0)), (short)0, rj * row_bytes,
+          kRsrcWord3);
+#pragma unroll
+      for (int q = 0; q < kPasses; ++q)
+        dst[q * kLoadsPerPass + jj] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + q * kPass, 0, kLoadNonTemporal);
+    }
+  };
+  auto process = [&](int j, const u32x4 (&w)[KW], float* rb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+#pragma unroll
+      for (int jj = 0; jj < kLoadsPerPass; ++jj) {
+        const int r = jj * kRowsPerLoad + lrow;
+        st16(tile + r * kPass + ((lchunk ^ (r & 15)) << 4), w[q * kLoadsPerPass + jj]);
+      }
+#pragma unroll
+      for (int ss = 0; ss < kStepsPerPass; ++ss) {
+        const u32x4 b = ld16(tile + col * kPass + (((ss * 4 + grp) ^ col) << 4));
+        acc = mma16<Bf16>(acc, af[q * kStepsPerPass + ss], b);
+      }
+    }
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) rb[(wave * 16 + grp * 4 + jq) * 17 + col] = acc[jq];
+    __syncthreads();
+    // thread: position tid / 16, entry tid % 16 of the tile
+    const int m = tid >> 4, c = tid & 15, v = (t_lo + j) * 16 + c;
+    float sum = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) sum += rb[(wv * 16 + m) * 17 + c];
+    lb[m * kMaxWgTiles * 16 + j * 16 + c] = v < V ? sum + (p.b2 ? bf16_to_f32(p.b2[v]) : 0.f) : -INFINITY;
+  };
+  u32x4 w0[KW], w1[KW];
+  int j = 0;
+  stage(0, w0);
+  // the scheduling barriers keep each prefetch ahead of the tile in hand
+  while (j < nt) {
+    stage(j + 1, w1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(j, w0, red);
+    if (++j >= nt) break;
+    stage(j + 1, w0);
+    __builtin_amdgcn_sched_barrier(0);
+    process(j, w1, red + kWaves * 16 * 17);
+    ++j;
+  }
+  // slots without a tile never win
+  for (int i = tid; i < kStreamPositions * kMaxWgTiles * 16; i += kThreads)
+    if (i % (kMaxWgTiles * 16) >= nt * 16) lb[i] = -INFINITY;
+}
+
+template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS, int SKW>
 __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ unsigned long long s_key[kWaves];
@@ -212,7 +329,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   const int grp = lane >> 4, col = lane & 15;
   const int H = p.H, V = p.V, r = p.r;
   const int T3 = (3 * H) >> 4;
-  const Lds L = lds_layout(p.U_hh, H, r);
+  const Lds L = lds_layout(p.U_hh, H, r, SKW > 0);
   unsigned char* pool = smem + L.pool;
   uint16_t* ghl = reinterpret_cast<uint16_t*>(smem + L.ghl);
   uint16_t* utile = reinterpret_cast<uint16_t*>(smem + L.utile);
@@ -223,6 +340,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   float* lbs = reinterpret_cast<float*>(smem + L.lbs);
   float* b2s = reinterpret_cast<float*>(smem + L.b2s);
   float* gum = reinterpret_cast<float*>(smem + L.gum);
+  float* lbt = reinterpret_cast<float*>(smem + L.lb);
   const int units = H / kUnitWGs;
   const int ksu = units / 32;  // k-steps of a unit workgroup's W1 columns
   const bool unit_wg = w < kUnitWGs;
@@ -241,6 +359,12 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     }
   }
   const int nt = t_hi - t_lo;
+  // fused: the base logits of the range for every position first, while the
+  // registers and the pool are still free
+  if constexpr (SKW > 0) {
+    stream_base<SKW>(p, t_lo, nt, pool, lbt);
+    __syncthreads();
+  }
   // W2: tile s * kWaves + wave of this workgroup's range, 8 k-step fragments each
   u32x4 w2r[NR][RK];
 #pragma unroll
@@ -259,13 +383,16 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   for (int q = 0; q < 3; ++q)
 #pragma unroll
     for (int o = 0; o < 3; ++o) hoff[q][o] = -1;
+  // The pool's fragments go straight from memory into LDS (no registers,
+  // every load of a wave in flight at once): fragment f of wave f % kWaves,
+  // lane ln's 16 bytes at pool + f KB + 16 ln.
   if (unit_wg) {
     // W1[:, d + w*units : d + (w+1)*units] as fragments of 16 rows x 32 columns
-    for (int j = tid; j < (r / 16) * ksu * 64; j += kThreads) {
-      const int f = j >> 6, ln = j & 63;
+    for (int f = wave; f < (r / 16) * ksu; f += kWaves) {
       const int rt = f / ksu, ks = f - rt * ksu;
-      const int row = rt * 16 + (ln & 15), c0 = ks * 32 + (ln >> 4) * 8;
-      st16(pool + (size_t)j * 16, ld16(p.w1 + (size_t)row * (p.d + H) + p.d + w * units + c0));
+      const int row = rt * 16 + (lane & 15), c0 = ks * 32 + (lane >> 4) * 8;
+      __builtin_amdgcn_global_load_lds((gptr_t)(p.w1 + (size_t)row * (p.d + H) + p.d + w * units + c0),
+                                       (lptr_t)(pool + (size_t)f * 1024), 16, 0, 0);
     }
     if (tid < units && p.b_hh)
 #pragma unroll
@@ -276,17 +403,20 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
 #pragma unroll
         for (int o = 0; o < 3; ++o) hoff[q][o] = hh_partial_offset(p, q * H + w * units + tid, o, G);
   } else {
-    for (int j = tid; j < p.U_hh * 64; j += kThreads) {
-      const long gu = hh0 + (j >> 6);
-      const int ln = j & 63;
-      u32x4 v = {0, 0, 0, 0};
+    // k-steps past the end of W_hh are zeros
+    for (int f = wave; f < p.U_hh; f += kWaves) {
+      const long gu = hh0 + f;
       if (gu < total_hh) {
         const int t = (int)(gu / p.KH), s = (int)(gu % p.KH);
-        v = ld16(p.w_hh + (size_t)(t * 16 + (ln & 15)) * H + s * 32 + (ln >> 4) * 8);
+        __builtin_amdgcn_global_load_lds(
+            (gptr_t)(p.w_hh + (size_t)(t * 16 + (lane & 15)) * H + s * 32 + (lane >> 4) * 8),
+            (lptr_t)(pool + (size_t)f * 1024), 16, 0, 0);
+      } else {
+        st16(pool + ((size_t)f * 64 + lane) * 16, u32x4{0, 0, 0, 0});
       }
-      st16(pool + (size_t)j * 16, v);
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the direct-to-LDS loads have landed (the barrier below publishes them)
   const int nv = nt * 16;  // vocabulary entries of this workgroup: [t_lo * 16, t_lo * 16 + nv)
   for (int i = tid; i < nv; i += kThreads) {
     const int v = t_lo * 16 + i;
@@ -324,6 +454,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     constexpr int kLbPer = (kMaxWgTiles * 16 + kThreads - 1) / kThreads;
     float lbr[kLbPer];
     auto load_base = [&]() {
+      if constexpr (SKW > 0) return;
 #pragma unroll
       for (int q = 0; q < kLbPer; ++q) {
         const int i = tid + q * kThreads, v = t_lo * 16 + i;
@@ -424,10 +555,11 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
 
     // ---------- C(i): u, W2 tiles, argmax ----------
     const bool do_hh = !unit_wg && step + 1 < p.K && hh0 < total_hh;
+    if constexpr (SKW == 0)
 #pragma unroll
-    for (int q = 0; q < kLbPer; ++q)
-      if (tid + q * kThreads < nv)
-        lbs[tid + q * kThreads] = t_lo * 16 + tid + q * kThreads < V ? lbr[q] + b2s[tid + q * kThreads] : -INFINITY;
+      for (int q = 0; q < kLbPer; ++q)
+        if (tid + q * kThreads < nv)
+          lbs[tid + q * kThreads] = t_lo * 16 + tid + q * kThreads < V ? lbr[q] + b2s[tid + q * kThreads] : -INFINITY;
     if (wave == 0) ok &= wait_sentinels(p.x_pu + (size_t)par * kUnitWGs * r, kUnitWGs, r, tag, p.status, p.spin_limit);
     if (do_hh && wave == 1)
       ok &= wait_sentinels(p.x_g + (size_t)par * H, kUnitWGs, units, tag, p.status, p.spin_limit);
@@ -473,7 +605,8 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
     for (int k = 0; k < RK; ++k) ua[k] = row_frag(utile, r, k * 32, col, grp, zero);
     float bias[NR];  // Lb + b2 of the row-0 lanes' entries, read while the products run
 #pragma unroll
-    for (int s = 0; s < NR; ++s) bias[s] = lbs[min((s * kWaves + wave) * 16 + col, kMaxWgTiles * 16 - 1)];
+    for (int s = 0; s < NR; ++s)
+      bias[s] = (SKW > 0 ? lbt + step * kMaxWgTiles * 16 : lbs)[min((s * kWaves + wave) * 16 + col, kMaxWgTiles * 16 - 1)];
     f32x4 acc[NR];
 #pragma unroll
     for (int s = 0; s < NR; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -579,9 +712,9 @@ static hipError_t launch_pre(const PreArgs& q, hipStream_t s) {
 
 // Checks that the loop kernel fits one workgroup per CU, then launches the
 // pre-loop kernel and the loop, ordered after earlier loops of the device.
-template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS>
+template <int UHW, int NR, int RK, bool SAMPLED, bool LOGITS, int SKW>
 static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q, hipStream_t s) {
-  auto kern = draft_b1_kernel<UHW, NR, RK, SAMPLED, LOGITS>;
+  auto kern = draft_b1_kernel<UHW, NR, RK, SAMPLED, LOGITS, SKW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -589,30 +722,30 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q,
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
-  return LoopOrder::get().run(s, [&]() -> hipError_t {
+  return LoopOrder::get().run(s, [&](hipEvent_t stop) -> hipError_t {
     hipError_t e2 = launch_pre(q, s);
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
+    hipExtLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, nullptr, stop, 0, p);
     return hipGetLastError();
   });
 }
 
-template <int UHW, int NR, int RK>
+template <int UHW, int NR, int RK, int SKW>
 static hipError_t launch_flags(const Params& p, int G, size_t lds, const PreArgs& q, hipStream_t s) {
   if (p.sampled)
-    return p.logits ? launch_t<UHW, NR, RK, true, true>(p, G, lds, q, s)
-                    : launch_t<UHW, NR, RK, true, false>(p, G, lds, q, s);
-  return p.logits ? launch_t<UHW, NR, RK, false, true>(p, G, lds, q, s)
-                  : launch_t<UHW, NR, RK, false, false>(p, G, lds, q, s);
+    return p.logits ? launch_t<UHW, NR, RK, true, true, SKW>(p, G, lds, q, s)
+                    : launch_t<UHW, NR, RK, true, false, SKW>(p, G, lds, q, s);
+  return p.logits ? launch_t<UHW, NR, RK, false, true, SKW>(p, G, lds, q, s)
+                  : launch_t<UHW, NR, RK, false, false, SKW>(p, G, lds, q, s);
 }
 
-template <int NR, int RK>
-static hipError_t launch_uhw(const Params& p, int uhw, int G, size_t lds, const PreArgs& q, hipStream_t s) {
-  switch (uhw) {
-    case 2: return launch_flags<2, NR, RK>(p, G, lds, q, s);
-    case 4: return launch_flags<4, NR, RK>(p, G, lds, q, s);
-    case 6: return launch_flags<6, NR, RK>(p, G, lds, q, s);
-    case 8: return launch_flags<8, NR, RK>(p, G, lds, q, s);
+// skw: 64-B steps of a quarter of an LM-head row (0: the base logits are an input)
+template <int UHW, int NR, int RK>
+static hipError_t launch_skw(const Params& p, int skw, int G, size_t lds, const PreArgs& q, hipStream_t s) {
+  switch (skw) {
+    case 0: return launch_flags<UHW, NR, RK, 0>(p, G, lds, q, s);
+    case kStreamKw4B: return launch_flags<UHW, NR, RK, kStreamKw4B>(p, G, lds, q, s);
+    case kStreamKw8B: return launch_flags<UHW, NR, RK, kStreamKw8B>(p, G, lds, q, s);
     default: return hipErrorNotSupported;
   }
 }
@@ -625,7 +758,7 @@ size_t b1_exchange_words(int H, int r, int max_wg) {
 
 namespace b1 {
 struct Plan {
-  int G, KH, U_hh, ntiles, ut;
+  int G, KH, U_hh, ntiles, ut, skw;
   size_t lds;
 };
 
@@ -642,7 +775,7 @@ static bool make_plan(const LoopArgs& a, Plan& pl) {
   const int T3 = 3 * a.H / 16;
   const long need = ((long)T3 * pl.KH + (pl.G - kUnitWGs) - 1) / (pl.G - kUnitWGs);  // over the W_hh owners
   pl.U_hh = (int)((need + 2 * kWaves - 1) / (2 * kWaves) * (2 * kWaves));           // UHW even
-  if (pl.U_hh > pl.KH || pl.U_hh / kWaves > 8) return false;  // a range spans at most two tiles
+  if (pl.U_hh != kUHW * kWaves || pl.U_hh > pl.KH) return false;  // a range spans at most two tiles
   pl.ntiles = (a.V + 15) / 16;
   // the unit workgroups take ut tiles each, the others share the rest; every
   // workgroup's tiles must fit its waves' registers
@@ -650,7 +783,17 @@ static bool make_plan(const LoopArgs& a, Plan& pl) {
   const int rest = pl.ntiles - kUnitWGs * pl.ut;
   const int per_other = (rest + (pl.G - kUnitWGs) - 1) / (pl.G - kUnitWGs);
   if (per_other > kWaves * kNR) return false;
-  pl.lds = (size_t)lds_layout(pl.U_hh, a.H, a.r).total;
+  // no base logits: the kernel forms them (LM-head widths it streams, a block
+  // of at most kStreamPositions, a pool the stream's LDS fits in)
+  pl.skw = 0;
+  if (!a.base) {
+    pl.skw = a.d * 2 / kWaves / 64;
+    if (!a.lm_head || a.K > kStreamPositions || a.d % (kWaves * 32) != 0 ||
+        (pl.skw != kStreamKw4B && pl.skw != kStreamKw8B))
+      return false;
+    if (lds_layout(pl.U_hh, a.H, a.r, true).ghl < stream_scratch_bytes()) return false;
+  }
+  pl.lds = (size_t)lds_layout(pl.U_hh, a.H, a.r, pl.skw > 0).total;
   return pl.lds <= 160 * 1024 - 256;
 }
 }  // namespace b1
@@ -666,7 +809,6 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   Plan pl;
   if (!make_plan(a, pl)) return hipErrorNotSupported;
   const int G = pl.G, KH = pl.KH, U_hh = pl.U_hh, ntiles = pl.ntiles, ut = pl.ut;
-  const Lds L = lds_layout(U_hh, a.H, a.r);
   Params p{};
   p.d = a.d;
   p.V = a.V;
@@ -684,6 +826,8 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.b2 = static_cast<const uint16_t*>(a.b2);
   p.table = a.table;
   p.base = a.base;
+  p.lm_head = static_cast<const uint16_t*>(a.lm_head);
+  p.hidden = static_cast<const uint16_t*>(a.hidden);
   p.ppart = a.ppart;
   p.x_t = a.x_t;
   p.teacher = a.teacher;
@@ -709,7 +853,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   PreArgs q{&a, {}};
   if (!p_split_shape(a.d, a.r, q.shape)) return hipErrorNotSupported;
   p.S = q.shape.S;
-  return launch_uhw<NR, RK>(p, U_hh / kWaves, G, L.total, q, s);
+  return launch_skw<kUHW, NR, RK>(p, pl.skw, G, pl.lds, q, s);
 }
 
 }  // namespace domino

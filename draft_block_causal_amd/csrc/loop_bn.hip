@@ -48,6 +48,8 @@
 
 #include "common.h"
 #include "kernels.h"
+#include <hip/hip_ext.h>
+
 #include "xchg.h"
 
 namespace domino {
@@ -175,13 +177,16 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
     for (int s = 0; s < kKH; ++s) whh[tt][s] = ld16(p.w_hh + (size_t)row * kH + s * 32 + grp * 8);
     bhh[tt] = p.b_hh ? bf16_to_f32(p.b_hh[row]) : 0.f;
   }
-  // W1[:, d + u0 .. d + u0 + 63] as fragments (u-row tile rt, k-step ks)
-  for (int j = tid; j < kW1Frags * 64; j += kThreads) {
-    const int f = j >> 6, ln = j & 63;
+  // W1[:, d + u0 .. d + u0 + 63] as fragments (u-row tile rt, k-step ks),
+  // straight from memory into LDS (every load of a wave in flight at once):
+  // fragment f by wave f % kWaves, lane ln's 16 bytes at w1f + f KB + 16 ln
+  for (int f = wave; f < kW1Frags; f += kWaves) {
     const int rt = f >> 1, ks = f & 1;
-    st16(w1f + (size_t)j * 16,
-         ld16(p.w1 + (size_t)(rt * 16 + (ln & 15)) * (p.d + kH) + p.d + u0 + ks * 32 + (ln >> 4) * 8));
+    __builtin_amdgcn_global_load_lds(
+        (gptr_t)(p.w1 + (size_t)(rt * 16 + (lane & 15)) * (p.d + kH) + p.d + u0 + ks * 32 + (lane >> 4) * 8),
+        (lptr_t)(w1f + (size_t)f * 1024), 16, 0, 0);
   }
+  DOMINO_BN_WAIT_VM0();  // landed before the barrier below publishes them
   // position 0: g_{-1} = 0, so W_hh g + b_hh = b_hh
   for (int j = tid; j < B * 3 * kUnits; j += kThreads) {
     const int q = (j / kUnits) % 3, k = j % kUnits;
@@ -698,14 +703,14 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, const LoopArgs& a
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kThreads, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
-  return LoopOrder::get().run(s, [&]() -> hipError_t {
+  return LoopOrder::get().run(s, [&](hipEvent_t stop) -> hipError_t {
     // before the loop: the key region's words that must start at zero (this
     // launch's status word, and for the first launch of a call the call's
     // status word), the exchange words, and P as K-slice partials
     hipError_t e2 = launch_p_partials(hidden, p.B * p.K, a.d, a.w1, a.d + kH, kR, a.b1, a.ppart, ps, a.keys,
                                       clear_words, a.xpart, (int)xwords, s);
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, p);
+    hipExtLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, nullptr, stop, 0, p);
     return hipGetLastError();
   });
 }

@@ -79,6 +79,11 @@ WorkspaceLayout workspace_layout(const domino_head* h, int batch) {
   return w;
 }
 
+bool forms_base_logits(const domino_head* h, int32_t batch) {
+  return batch == 1 && h->dtype == DOMINO_BF16 && h->gru_input_table && h->block <= 16 &&
+         (h->d == 2560 || h->d == 4096) && h->gru_hidden == 1024 && h->rank == 256;
+}
+
 int check_draft_io(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
                    const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,
                    const float* gru_states) {
@@ -88,8 +93,9 @@ int check_draft_io(const domino_head* h, int32_t batch, const void* hidden, cons
   if (batch > kMaxBatch) return DOMINO_ERR_UNSUPPORTED;
   if (!std::isfinite(temperature) || temperature < 0.f) return DOMINO_ERR_ARG;
   if (batch == 0) return DOMINO_OK;
-  if (!hidden || !base_logits || !x_t || !tokens) return DOMINO_ERR_NULL;
-  if (!aligned16(hidden) || !aligned16(base_logits) || !aligned16(tokens)) return DOMINO_ERR_ALIGN;
+  if (!hidden || !x_t || !tokens) return DOMINO_ERR_NULL;
+  if (!base_logits && !forms_base_logits(h, batch)) return DOMINO_ERR_UNSUPPORTED;
+  if (!aligned16(hidden) || (base_logits && !aligned16(base_logits)) || !aligned16(tokens)) return DOMINO_ERR_ALIGN;
   if ((logits && !aligned16(logits)) || (gru_states && !aligned16(gru_states))) return DOMINO_ERR_ALIGN;
   return DOMINO_OK;
 }

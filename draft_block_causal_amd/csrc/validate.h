@@ -28,6 +28,10 @@ int elem_size(int dtype);
 int check_head(const domino_head* h);
 int gru_ksplit(int d);
 WorkspaceLayout workspace_layout(const domino_head* h, int batch);
+// Whether a draft call of these shapes may leave the base logits to the
+// single-block loop (base_logits == NULL): one block of at most 16 positions of
+// a bf16 head with its GRU input table, d = 2560 or 4096, H = 1024, r = 256.
+bool forms_base_logits(const domino_head* h, int32_t batch);
 // Everything domino_draft_block checks except the workspace.
 int check_draft_io(const domino_head* h, int32_t batch, const void* hidden, const float* base_logits,
                    const int32_t* x_t, float temperature, int32_t* tokens, const float* logits,

@@ -139,18 +139,23 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 // never hold compute units at the same time: one loop could then wait for
 // workgroups that cannot start until the other ends.  Within the process,
 // every loop launch is ordered after the previous one on the same device,
-// whatever stream either runs on: the launch first waits on an event recorded
-// after the previous loop, then records it again after its own.  Under stream
-// capture the ordering is the graph's (the event is neither waited on nor
-// recorded).  Loops of other processes on the same device are not ordered by
-// this; their bounded waits then give up instead of hanging.
+// whatever stream either runs on: the launch first waits on an event that
+// marks the end of the previous loop, then hands the event to its own loop
+// kernel, whose dispatch records it as it completes (an extended launch with a
+// stop event: no marker of its own on the stream, which costs ~2 us between
+// back-to-back calls).  Under stream capture the ordering is the graph's (the
+// event is neither waited on nor recorded: the launch gets a null event).
+// Loops of other processes on the same device are not ordered by this; their
+// bounded waits then give up instead of hanging.
 class LoopOrder {
  public:
   static LoopOrder& get() {
     static LoopOrder o;
     return o;
   }
-  // Enqueues `launch` on s after every earlier loop launch of this device.
+  // Enqueues `launch(stop)` on s after every earlier loop launch of this
+  // device; `launch` passes `stop` as the stop event of its loop kernel's
+  // extended launch (hipExtLaunchKernelGGL), or ignores a null one.
   template <class F>
   hipError_t run(hipStream_t s, F&& launch) {
     int dev = 0;
@@ -160,7 +165,7 @@ class LoopOrder {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     e = hipStreamIsCapturing(s, &cap);
     if (e != hipSuccess) return e;
-    if (cap != hipStreamCaptureStatusNone) return launch();
+    if (cap != hipStreamCaptureStatusNone) return launch(static_cast<hipEvent_t>(nullptr));
     std::lock_guard<std::mutex> lock(mu_);
     if (!ev_[dev]) {
       e = hipEventCreateWithFlags(&ev_[dev], hipEventDisableTiming);
@@ -171,9 +176,7 @@ class LoopOrder {
     } else if ((e = hipStreamWaitEvent(s, ev_[dev], 0)) != hipSuccess) {
       return e;
     }
-    e = launch();
-    if (e != hipSuccess) return e;
-    return hipEventRecord(ev_[dev], s);
+    return launch(ev_[dev]);
   }
 
  private:

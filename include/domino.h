@@ -162,13 +162,20 @@ int domino_base_logits(const domino_head *head, int32_t batch, const void *hidde
  *   counter (v >> 2, i, b, offset), key (seed low 32 bits, seed high 32 bits),
  *   word = output lane (v & 3), U = ((word >> 9) + 0.5) * 2^-23.
  *
- * hidden      [batch, K, d] head dtype          base_logits [batch, K, V] float32
+ * hidden      [batch, K, d] head dtype          base_logits [batch, K, V] float32, or NULL
  * x_t         [batch] int32                     teacher     [batch, K] int32 or NULL
  * tokens      [batch, K] int32 (output)
  * logits      [batch, K, V] float32 or NULL (output: the corrected logits L_i)
  * gru_states  [batch, K, H] float32 or NULL (output: g_i)
  * workspace   device scratch of at least domino_workspace_size() bytes,
  *             256-byte aligned; its contents are overwritten.
+ * base_logits == NULL: the call forms base_logits[b, i] = lm_head hidden[b, i]
+ *   itself, inside the draft loop (the LM head is read once, and the base
+ *   logits never reach device memory).  Only for batch == 1, K <= 16, a bf16
+ *   head with its GRU input table, d = 2560 or 4096, H = 1024, r = 256, on a
+ *   device of at least 200 compute units; otherwise DOMINO_ERR_UNSUPPORTED
+ *   (shapes: before anything is enqueued).  The products are summed in another
+ *   order than domino_base_logits': the logits agree to float32 rounding.
  * Arithmetic: float32 throughout; bf16 weights are multiplied in bf16 by the
  * matrix cores with float32 accumulation, and float32 activations are fed to
  * them as a bf16 (high, low) pair so they keep about 16 significant bits.

@@ -135,6 +135,24 @@ def test_draft_block_validation(lib):
     assert _draft(lib, bad) == E_SHAPE
 
 
+def test_draft_block_without_base_logits_validation(lib):
+    # base_logits == NULL asks the single-block loop to form the base logits:
+    # one block of a bf16 head with its GRU input table, d 2560 or 4096,
+    # H 1024, r 256, K <= 16; anything else is refused before any GPU call
+    q8 = dict(d=4096, vocab=151936, gru_hidden=1024, rank=256, gru_input_table=0x900000)
+    assert _draft(lib, fake_head(**q8), base=None, batch=2) == E_UNSUP
+    assert _draft(lib, fake_head(**dict(q8, gru_input_table=None)), base=None) == E_UNSUP
+    assert _draft(lib, fake_head(**dict(q8, d=2048)), base=None) == E_UNSUP
+    assert _draft(lib, fake_head(**dict(q8, block=17)), base=None) == E_UNSUP
+    assert _draft(lib, fake_head(**dict(q8, rank=128)), base=None) == E_UNSUP
+    assert _draft(lib, fake_head(**dict(q8, dtype=0, d=2048)), base=None) == E_UNSUP
+    assert _draft(lib, fake_head(**q8), base=None, batch=0) == OK
+    assert _draft(lib, fake_head(**q8), base=None, hidden=None) == E_NULL
+    if not torch.cuda.is_available():
+        assert _draft(lib, fake_head(**q8), base=None) == E_HIP
+        assert _draft(lib, fake_head(**dict(q8, d=2560)), base=None) == E_HIP
+
+
 def test_draft_status_validation(lib):
     h = fake_head()
     sz = ctypes.c_size_t(0)

@@ -28,6 +28,11 @@ def test_traffic_record_matches_current_source_or_is_ignored():
     got = bench.measured_traffic(bench.kernel_source_hash())
     assert got is None or abs(got / bench.lmhead_algorithmic_bytes(1, 16, 4096, 151936, 2) - 1.0) < 0.01
     assert bench.measured_traffic("0" * 64) is None
+    # the single-block loop that streams the LM head itself: within 10 % of
+    # the call's compulsory bytes without base logits in HBM
+    fused = bench.measured_traffic(bench.kernel_source_hash(bench.FUSED_KERNEL_SOURCES), bench.FUSED_TRAFFIC_FILE)
+    alg = bench.block_algorithmic_bytes(1, 16, 4096, 151936, 1024, 256, 2, base_in_hbm=False)
+    assert fused is None or abs(fused / alg - 1.0) < 0.1
 
 
 def test_more_than_one_gpu_is_refused():
@@ -65,3 +70,18 @@ def test_whole_call_bytes_flops_and_floors_at_the_workloads():
     assert abs(bench.block_floor_us(32, **q8) - 277.8) < 0.1
     assert abs(bench.block_floor_us(128, **q8) - 1111.1) < 0.5
     assert abs(bench.block_floor_us(8, 16, 2560, 151936, 1024, 256, 2) - 129.6) < 0.1
+    # one block whose call forms the base logits on chip: 16 x V float32
+    # written and read back no more (2 x 9,723,904 bytes less)
+    assert bench.block_algorithmic_bytes(1, **q8, base_in_hbm=False) == 1_376_556_356 - 2 * 16 * 151936 * 4
+    assert abs(bench.block_floor_us(1, **q8, base_in_hbm=False) - 169.64) < 0.05
+
+
+def test_fused_step_rule_matches_the_library():
+    import domino_synth as S
+
+    q8 = S.get_workload("qwen3_8b_b1_greedy")
+    assert bench.forms_base_logits(q8, 1, True)
+    assert not bench.forms_base_logits(q8, 1, False)  # no GRU input table
+    assert not bench.forms_base_logits(q8, 2, True)
+    assert bench.forms_base_logits(S.get_workload("qwen3_4b_b8_tied"), 1, True)
+    assert not bench.forms_base_logits(S.get_workload("tiny_f32_b1"), 1, True)

@@ -73,7 +73,7 @@ def _sampled_checks(w, f, inp, teacher, base_gpu, logits_tf, states_tf, n=4096, 
     return err, serr, lerr
 
 
-def _parity(w, dev, check_blocks=None, sampled=False, table=False, chunk=16):
+def _parity(w, dev, check_blocks=None, sampled=False, table=False, chunk=16, fused=False):
     import draft_block_causal_amd as D
 
     log(f"{w.name}: generating inputs")
@@ -83,17 +83,19 @@ def _parity(w, dev, check_blocks=None, sampled=False, table=False, chunk=16):
     if table:
         D.domino_prepare_gru_table(head)
     try:
-        return _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled, chunk)
+        return _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled, chunk, fused)
     finally:
         head.set_gru_input_table(None)
 
 
-def _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled, chunk):
+def _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled, chunk, fused=False):
     """GPU base logits, a teacher-forced and a free-running draft of every block;
     the oracle re-runs the blocks in `check_blocks` (default: all of them) in
     chunks of `chunk` blocks: base logits, teacher-forced logits and GRU states,
-    and the free-running tokens by the replay rule.  Returns the free-running
-    tokens (numpy) and the device tensor that holds them."""
+    and the free-running tokens by the replay rule.  `fused`: the draft calls
+    get no base logits and form them themselves (the drafted logits then check
+    those).  Returns the free-running tokens (numpy) and the device tensor that
+    holds them."""
     B, K, V = inp["hidden"].shape[0], w.block, w.vocab
     hidden_t = _t(inp["hidden"], dev)
     x_t = _t(inp["x_t"], dev)
@@ -101,8 +103,9 @@ def _parity_run(D, w, dev, head, head_np, inp, f, check_blocks, sampled, chunk):
     teacher_t = _t(teacher, dev)
     log(f"{w.name}: GPU base logits + teacher-forced + free-running")
     base = D.domino_base_logits(head, hidden_t)
-    tok_tf, log_tf, st_tf = _gpu_block(D, head, hidden_t, base, x_t, teacher_t, w, dev)
-    tok_fr_t, log_fr, st_fr = _gpu_block(D, head, hidden_t, base, x_t, None, w, dev)
+    draft_base = None if fused else base
+    tok_tf, log_tf, st_tf = _gpu_block(D, head, hidden_t, draft_base, x_t, teacher_t, w, dev)
+    tok_fr_t, log_fr, st_fr = _gpu_block(D, head, hidden_t, draft_base, x_t, None, w, dev)
     torch.cuda.synchronize()
     base_g = base.cpu().numpy()
     tok_tf, log_tf, st_tf = tok_tf.cpu().numpy(), log_tf.cpu().numpy(), st_tf.cpu().numpy()
@@ -195,6 +198,30 @@ def test_qwen3_8b_b1_gru_table(dev, temperature):
 
 def test_qwen3_4b_b1_tied_gru_table(dev):
     _parity(S.get_workload("qwen3_4b_b8_tied").with_(batch=1), dev, table=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("qwen3_8b_b1_greedy", dict(temperature=0.0)),
+    ("qwen3_8b_b1_greedy", dict(temperature=1.0, philox_seed=9)),
+    ("qwen3_4b_b8_tied", dict(batch=1)),
+    # a ragged last vocabulary tile and a short block
+    ("qwen3_8b_b1_greedy", dict(vocab=150001, block=7, temperature=1.0, philox_seed=3)),
+])
+def test_draft_forms_base_logits(dev, name, kw):
+    # no base logits passed: the single-block loop streams the LM head itself
+    _parity(S.get_workload(name).with_(**kw), dev, table=True, fused=True)
+
+
+def test_draft_forms_base_logits_refuses_other_shapes(dev):
+    import draft_block_causal_amd as D
+
+    w = S.get_workload("tiny_stress_b4")
+    head_np, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    hidden_t = _t(inp["hidden"], dev)
+    with pytest.raises(D.DominoError) as e:
+        D.domino_draft_block(head, hidden_t, None, _t(inp["x_t"], dev))
+    assert e.value.status == -8
 
 
 @pytest.mark.parametrize("case", ["qwen3_8b_b32_t1", "qwen3_4b_b8_tied", "tiny_stress_b4", "small_b17", "small_b65"])
