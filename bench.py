@@ -185,15 +185,17 @@ def sweep(args, w, batches) -> int:
         tokens = torch.empty((B, w.block), dtype=torch.int32, device=dev)
         ws = torch.empty(D.domino_workspace_size(head, B), dtype=torch.uint8, device=dev)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        fused = forms_base_logits(w, B, not args.no_table) and not args.unfused
 
         def step(e=None):
             if e:
                 e[0].record()
-            D.domino_base_logits(head, hidden, base)
+            if not fused:
+                D.domino_base_logits(head, hidden, base)
             if e:
                 e[1].record()
-            D.domino_draft_block(head, hidden, base, x_t, temperature=w.temperature, seed=w.philox_seed,
-                                 tokens=tokens, workspace=ws)
+            D.domino_draft_block(head, hidden, None if fused else base, x_t, temperature=w.temperature,
+                                 seed=w.philox_seed, tokens=tokens, workspace=ws)
             if e:
                 e[2].record()
 
@@ -209,7 +211,8 @@ def sweep(args, w, batches) -> int:
             step(ev[i])
         torch.cuda.synchronize()
         rows.append({"batch": B, "blocks_per_s": B / (ms * 1e-3), "ms_per_call": ms, "ms_per_block": ms / B,
-                     "lm_head_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                     "base_logits": "inside the draft call" if fused else "domino_base_logits",
+                     "lm_head_ms": None if fused else float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
                      "draft_block_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))})
         print(f"sweep B={B}: {rows[-1]['blocks_per_s']:.1f} blocks/s, {ms:.4f} ms/call", file=sys.stderr, flush=True)
         st = int(D.domino_draft_status(head, B, ws).cpu().numpy()[0])
@@ -381,6 +384,36 @@ def next_rows(args, w) -> int:
     return 0
 
 
+def read_calibration(args) -> int:
+    """GB/s of one plain streaming read of 151936 x 4096 bf16 (the Qwen3-8B LM
+    head's bytes), HIP events over --steps launches after --warmup; the XOR the
+    kernel returns is checked against the host's."""
+    import torch
+
+    import draft_block_causal_amd as D
+
+    nbytes = 151936 * 4096 * 2
+    g = torch.Generator().manual_seed(5)
+    host = torch.randint(-(1 << 31), (1 << 31) - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    buf = host.to("cuda:0")
+    sink = torch.empty((2048,), dtype=torch.int32, device="cuda:0")
+    for _ in range(args.warmup):
+        D.domino_debug_read_stream(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        D.domino_debug_read_stream(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    print(json.dumps({"read_calibration_bytes": nbytes, "launches": args.steps, "ms": ms,
+                      "gb_s": nbytes / (ms * 1e-3) / 1e9, "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "xor_ok": got == want}), flush=True)
+    return 0 if got == want else 3
+
+
 def forms_base_logits(w, B: int, table: bool) -> bool:
     """Whether the draft call can form the base logits itself at these shapes
     (the library's own rule: one block of at most 16 positions of a bf16 head
@@ -420,6 +453,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run a plain device-to-device copy of 1 GiB five times; its "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-traffic counters of the LM head")
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="instead of the benchmark, time a plain streaming read (domino_debug_read_stream) of a "
+                         "buffer the size of the Qwen3-8B LM head: the read bandwidth the HBM-bound kernels can reach")
     ap.add_argument("--sweep", default=None, metavar="B1,B2,...",
                     help="concurrency sweep: the workload's head at each batch size in the list (e.g. "
                          "1,2,4,8,16,32,64,128); prints one JSON line with a row per batch size instead of the "
@@ -458,6 +494,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.read_calibration:
+        return read_calibration(args)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)

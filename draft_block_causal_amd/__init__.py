@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     domino_correction_backward,
     domino_curriculum_loss,
     domino_debug_philox,
+    domino_debug_read_stream,
     domino_draft_block,
     domino_draft_block_noalloc,
     domino_draft_status,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdomino.so")
 
 DOMINO_F32 = 0
 DOMINO_BF16 = 1
+READ_STREAM_SINK = 2048  # entries of domino_debug_read_stream's sink
 
 _STATUS = {
     0: "DOMINO_OK",
@@ -54,6 +55,7 @@ EXPORTED = [
     "domino_correction_backward_workspace_size",
     "domino_gru_backward",
     "domino_gru_backward_workspace_size",
+    "domino_debug_read_stream",
     "domino_debug_philox",
 ]
 
@@ -123,6 +125,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "domino_correction_backward_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
         "domino_gru_backward": (ctypes.c_int, [HP, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
         "domino_gru_backward_workspace_size": (ctypes.c_int, [HP, I32, ctypes.POINTER(SZ)]),
+        "domino_debug_read_stream": (ctypes.c_int, [P, SZ, P, P]),
         "domino_debug_philox": (ctypes.c_int, [U64, U32, I32, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -473,6 +476,20 @@ def domino_gru_backward(head: Head, x_t: torch.Tensor, teacher: torch.Tensor, gr
         head.ref, B, _ptr(x_t), _ptr(teacher), _ptr(gru_states), _ptr(d_states), _ptr(out["d_w_ih"]),
         _ptr(out["d_w_hh"]), _ptr(out["d_b_ih"]), _ptr(out["d_b_hh"]), _ptr(ws), ws.numel(), _stream_ptr(stream)))
     return out
+
+
+def domino_debug_read_stream(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One plain streaming read of `buf` (a contiguous device tensor whose byte
+    size is a multiple of 16); returns sink, 2048 int32 (device) whose XOR is
+    the XOR of the buffer's 32-bit words."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty((READ_STREAM_SINK,), dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, (READ_STREAM_SINK,), buf.device)
+    _check("domino_debug_read_stream", load_library().domino_debug_read_stream(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream_ptr(stream)))
+    return sink
 
 
 def domino_debug_philox(seed: int, offset: int, b: int, pos: int, v0: int, n: int,

@@ -315,6 +315,13 @@ extern "C" int domino_base_draft(int32_t batch, int32_t block, int32_t vocab, co
                                               workspace, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int domino_debug_read_stream(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!sink || (bytes > 0 && !buf)) return DOMINO_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return DOMINO_ERR_ALIGN;
+  if ((bytes & 15u) || bytes > ((size_t)1 << 40)) return DOMINO_ERR_SHAPE;
+  return hip_status(domino::launch_read_stream(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int domino_debug_philox(uint64_t seed, uint32_t offset, int32_t b, int32_t pos, int32_t v0, int32_t n,
                                    uint32_t* out, void* stream) {
   if (n < 0 || n > (1 << 26) || b < 0 || pos < 0 || v0 < 0) return DOMINO_ERR_SHAPE;

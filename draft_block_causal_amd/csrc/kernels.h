@@ -277,6 +277,8 @@ hipError_t launch_curriculum_loss(int B, int K, int V, const float* base, const 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s);
 
+constexpr int kReadGrid = 2048;  // workgroups of the calibration read (entries of its sink)
+hipError_t launch_read_stream(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_debug_philox(uint64_t seed, uint32_t offset, int b, int pos, int v0, int n, uint32_t* out,
                                hipStream_t s);
 

@@ -14,6 +14,7 @@
 //   finalize_tokens keys -> token ids.
 //   accept_len      longest matching prefix ([notes] §一.1 item 1).
 //   debug_philox    the sampler's random words (test hook).
+//   read_stream     a plain read of a buffer (calibration of the read bandwidth).
 // The serial loop itself lives in loop.hip.
 #include <algorithm>
 
@@ -236,6 +237,36 @@ __global__ void debug_philox_kernel(uint64_t seed, uint32_t offset, int b, int p
   if (j < n) out[j] = philox_word(seed, offset, (uint32_t)b, (uint32_t)pos, (uint32_t)(v0 + j));
 }
 
+// Calibration stream: each workgroup reads a contiguous range of the buffer
+// with 16-B non-temporal loads, kReadInflight per thread in flight, and writes
+// the XOR of its range's 32-bit words to sink[workgroup] (a plain store: one
+// address updated by every workgroup would serialize them).
+constexpr int kReadInflight = 8;
+__global__ void __launch_bounds__(256) read_stream_kernel(const unsigned char* __restrict__ buf, size_t per_wg,
+                                                          size_t total, uint32_t* __restrict__ sink) {
+  __shared__ uint32_t part[4];
+  const size_t lo = (size_t)blockIdx.x * per_wg;
+  const size_t hi = lo + per_wg < total ? lo + per_wg : total;
+  constexpr size_t kStride = 256 * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t a0 = lo + threadIdx.x * 16; a0 < hi; a0 += kStride * kReadInflight) {
+    u32x4 v[kReadInflight];
+#pragma unroll
+    for (int i = 0; i < kReadInflight; ++i) {
+      const size_t a = a0 + (size_t)i * kStride;
+      v[i] = a < hi ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + a)) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kReadInflight; ++i) acc ^= v[i];
+  }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x ^= (uint32_t)__shfl_xor((int)x, m, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -342,6 +373,14 @@ hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, 
 hipError_t launch_accept_len(int B, int K, const int32_t* draft, const int32_t* target, int32_t* accept,
                              hipStream_t s) {
   hipLaunchKernelGGL(accept_len_kernel, dim3((B + 255) / 256), dim3(256), 0, s, B, K, draft, target, accept);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_stream(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  // bytes per workgroup, rounded up to 4 KiB (a multiple of 16: every load stays in range)
+  const size_t per = ((bytes + kReadGrid - 1) / kReadGrid + 4095) / 4096 * 4096;
+  hipLaunchKernelGGL(read_stream_kernel, dim3(kReadGrid), dim3(256), 0, s, static_cast<const unsigned char*>(buf),
+                     per, bytes, sink);
   return hipGetLastError();
 }
 

@@ -385,6 +385,18 @@ int domino_gru_backward(const domino_head *head, int32_t batch, const int32_t *x
 int domino_gru_backward_workspace_size(const domino_head *head, int32_t batch, size_t *bytes);
 
 /*
+ * Calibration hook: reads `bytes` bytes at `buf` (device memory) once, the way
+ * the LM-head streams read (16-byte non-temporal loads, several in flight per
+ * thread, a contiguous range for each of 2048 workgroups), and stores into
+ * sink[j] (device memory, 2048 uint32) the XOR of the 32-bit words workgroup
+ * j read, so the XOR of the 2048 entries is the XOR of the buffer.  Timing it
+ * gives the read bandwidth a plain stream reaches on the device, the practical
+ * ceiling of the HBM-bound kernels.  buf 16-byte aligned, bytes a multiple of
+ * 16 (0 … 2^40).
+ */
+int domino_debug_read_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/*
  * Test hook: out[j] = the Philox word that domino_draft_block uses for
  * vocabulary entry v0 + j of position pos of block b (see above).
  * out: device buffer of n uint32.  n in 0 … 2^26.

@@ -204,6 +204,15 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
                                           None, None, None) == E_HIP
 
 
+def test_read_stream_validation(lib):
+    assert lib.domino_debug_read_stream(0x10000, 64, None, None) == E_NULL
+    assert lib.domino_debug_read_stream(None, 64, 0x2000, None) == E_NULL
+    assert lib.domino_debug_read_stream(0x10008, 64, 0x2000, None) == E_ALIGN
+    assert lib.domino_debug_read_stream(0x10000, 64, 0x2002, None) == E_ALIGN
+    assert lib.domino_debug_read_stream(0x10000, 72, 0x2000, None) == E_SHAPE
+    assert lib.domino_debug_read_stream(0x10000, (1 << 40) + 16, 0x2000, None) == E_SHAPE
+
+
 def test_base_logits_and_accept_validation(lib):
     h = fake_head()
     assert lib.domino_base_logits(ctypes.byref(h), -1, 0x20000, 0x30000, None) == E_SHAPE

@@ -556,6 +556,20 @@ def test_philox_words_bit_exact(dev, seed, offset, b, pos, v0, n):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 * 3 + 16, 10 << 20, (64 << 20) + 48])
+def test_read_stream_xor(dev, nbytes):
+    # the read-bandwidth calibration kernel reads every byte once: its XOR of
+    # the 32-bit words matches the host's (ragged ranges included)
+    import draft_block_causal_amd as D
+
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev)
+    sink = D.domino_debug_read_stream(buf)
+    want = int(np.bitwise_xor.reduce(host)) if nbytes else 0
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))) == want
+
+
 def test_accept_len_bit_exact_edges(dev):
     import draft_block_causal_amd as D
 
