@@ -38,6 +38,7 @@ int loop_mode() {
   if (std::strcmp(m, "persistent") == 0) return 1;
   if (std::strcmp(m, "multi") == 0) return 2;
   if (std::strcmp(m, "blocks") == 0) return 3;
+  if (std::strcmp(m, "perblock") == 0) return 4;  // never the several-block loop: one block at a time up to two
   return 0;
 }
 

@@ -1221,11 +1221,12 @@ static hipError_t run_loop(const LoopArgs& a, int mode, hipStream_t s) {
 template <class T>
 static hipError_t loop_t(const LoopArgs& a, int mode, hipStream_t s) {
   // several blocks of a bf16 head with its GRU input table: the on-chip loop
-  // for several blocks per launch, from 3 to 16 blocks (one launch; measured
-  // at Qwen3 shapes: 8 blocks 253 us against 443 us for the per-position
-  // kernels, 32 blocks in two launches 706 against 624 us), or for any count
-  // from 2 when forced
-  if ((mode == 0 && a.B >= 3 && a.B <= kBnDefaultMax) || mode == 3) {
+  // for several blocks per launch, from 2 to 16 blocks (one launch; measured
+  // at Qwen3 shapes: 2 blocks 202 us against 307 us for the single-block loop
+  // run twice, 8 blocks 253 us against 443 us for the per-position kernels,
+  // 32 blocks in two launches 787 against 614 us), or for any count from 2
+  // when forced
+  if ((mode == 0 && a.B >= 2 && a.B <= kBnDefaultMax) || mode == 3) {
     if (bn_supported(a)) {
       const hipError_t e = launch_draft_bn(a, s);
       if (e != hipErrorNotSupported) return e;

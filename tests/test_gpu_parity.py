@@ -239,10 +239,16 @@ def test_batched_gru_table(dev, case, monkeypatch):
 
 
 @pytest.mark.parametrize("batch,temperature", [(2, 1.0), (3, 0.0)])
-def test_qwen3_8b_few_blocks_gru_table(dev, batch, temperature, monkeypatch):
-    # two or three blocks with the GRU input table: the single-block loop runs
-    # once per block, its sampler keyed by each block's own index
-    monkeypatch.delenv("DOMINO_LOOP", raising=False)
+@pytest.mark.parametrize("mode", ["default", "perblock"])
+def test_qwen3_8b_few_blocks_gru_table(dev, batch, temperature, mode, monkeypatch):
+    # two or three Qwen3-8B blocks with the GRU input table: by default the
+    # several-block loop; forced, the single-block loop once per block (two
+    # blocks; three take the per-position kernels), its sampler keyed by each
+    # block's own index
+    if mode == "default":
+        monkeypatch.delenv("DOMINO_LOOP", raising=False)
+    else:
+        monkeypatch.setenv("DOMINO_LOOP", mode)
     w = S.get_workload("qwen3_8b_b1_greedy").with_(batch=batch, temperature=temperature, philox_seed=9)
     _parity(w, dev, table=True)
 
