@@ -80,6 +80,25 @@ constexpr int kHhStride = kH + 8;           // g operand rows for W_hh, bf16 (20
 constexpr int kGStride = kUnits + 8;        // g operand rows for the W1 share, bf16 (144 B)
 constexpr int kW1Frags = (kR / 16) * (kUnits / 32);  // W1 column fragments of a unit workgroup (32)
 
+// g of two adjacent GRU units in one exchange word: {tag (16 bits), g_a, g_b}
+// with each state rounded to its top 24 float32 bits (sign, exponent, 15
+// mantissa bits; nearest).  The W_hh products take g as a bf16 high/low pair,
+// whose two halves keep 16 significant bits together, and a 24-bit value's
+// high and low halves are exact, so the products see the same precision from
+// half the bytes: F's gather of every block's g is the largest read of a unit
+// workgroup per position.
+__device__ __forceinline__ uint32_t round_f24(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;  // nearest, ties to even (|g| < 1: no overflow)
+}
+__device__ __forceinline__ unsigned long long pack_g2(float a, float b, uint32_t tag) {
+  return ((unsigned long long)(tag & 0xFFFFu) << 48) | ((unsigned long long)round_f24(a) << 24) | round_f24(b);
+}
+__device__ __forceinline__ float unpack_g2_a(uint32_t lo, uint32_t hi) {
+  return __uint_as_float(((hi & 0xFFFFu) << 16) | ((lo >> 24) << 8));
+}
+__device__ __forceinline__ float unpack_g2_b(uint32_t lo) { return __uint_as_float((lo & 0xFFFFFFu) << 8); }
+
 struct Params {
   int B, K, V, d, ntiles, S, Gv;
   const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
@@ -97,7 +116,7 @@ struct Params {
   unsigned int* call_status;  // the call's status word
   unsigned int spin_limit;
   unsigned long long* x_key;  // [2][B][Gv]
-  unsigned long long* x_g;    // [2][B][H]
+  unsigned long long* x_g;    // [2][B][H / 2]: g of two adjacent units per word (pack_g2)
   unsigned long long* x_pu;   // [2][kUnitWGs][B][r]
   unsigned long long* x_u;    // [2][B][r]
 };
@@ -117,7 +136,7 @@ __host__ __device__ inline UnitLds unit_lds(int B) {
   L.hha = off;
   off += 16 * kHhStride * 2;  // g_i of every unit, one group at a time, for W_hh
   L.stg = off;
-  off += kGroup * kH * 8;  // the x_g words of one group, as loaded (tagged)
+  off += ng * kGroup * kH * 4;  // the x_g words of every block, as loaded (tagged, two states a word)
   L.c = off;
   off += B * 3 * kUnits * 4;  // W_hh g + b_hh of this workgroup's gate rows [B][3][kUnits]
   L.g = off;
@@ -151,8 +170,7 @@ template <int NG>
 __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
   constexpr int kNB4 = (NG * kGroup + kWaves - 1) / kWaves;  // blocks per wave in the key gather / gates
   const int u = blockIdx.x;
-  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-  const int grp = lane >> 4, col = lane & 15;
+  const int wave = wave_id();
   const int B = p.B, K = p.K, V = p.V, Gv = p.Gv;
   const int u0 = u * kUnits;
   const UnitLds L = unit_lds(B);
@@ -164,6 +182,7 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
   float* gl = reinterpret_cast<float*>(smem + L.g);
   int* s_tok = reinterpret_cast<int*>(smem + L.tok);
 
+  int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   // ---- resident weights: W_hh rows of this workgroup's gates in registers.
   // Tile t = wave * kHhTiles + tt (of 12): gate q = t / 4, units
   // u0 + (t % 4) * 16 + col; k-step s covers inputs 32 s .. 32 s + 31.
@@ -200,6 +219,14 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
   for (int step = 0; step < K; ++step) {
     const uint32_t tag = step + 1;
     const int par = step & 1;
+    // the lane's indices re-derived from an opaque copy at every position: the
+    // addresses built from them are then recomputed where they are used
+    // instead of being kept live (and spilled, with a wait at every reload)
+    // across the loop next to the resident W_hh rows
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    grp = lane >> 4;
+    col = lane & 15;
     // ---------- A: tokens of position step - 1 ----------
     if (step == 0) {
       for (int b = tid; b < B; b += kThreads) s_tok[b] = min(max(p.x_t[b], 0), V - 1);
@@ -288,7 +315,10 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
           const float g = (1.f - zg) * ng + zg * gl[b * kUnits + lane];
           gl[b * kUnits + lane] = g;
           p.states[((size_t)b * K + step) * kH + u0 + lane] = g;
-          put_f32(p.x_g + ((size_t)par * B + b) * kH + u0 + lane, g, tag);
+          // even lanes publish their unit's and the next unit's g in one word
+          const float g_next = __shfl_down(g, 1, 64);
+          if ((lane & 1) == 0)
+            put_word(p.x_g + ((size_t)par * B + b) * (kH / 2) + ((u0 + lane) >> 1), pack_g2(g, g_next, tag));
           uint16_t hi, lo;
           split_bf16(g, hi, lo);
           uint16_t* row = ghl + (size_t)((b >> 3) * 16 + 2 * (b & 7)) * kGStride + lane;
@@ -377,64 +407,65 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
     }
     // ---------- F: W_hh g_i + b_hh for position step + 1, 8 blocks per pass ----------
     if (step + 1 < K) {
+      // every block's x_g words straight into LDS at once (no registers): 1 KB
+      // chunks, chunk j = block j / 4, words (j % 4) 128 .. + 127; wave w
+      // loads chunks NG 8 w .. NG 8 w + NG 8 - 1 and loads again any chunk
+      // that still holds a word without this position's tag
+      constexpr int kCh = NG * 8;  // chunks per wave
+      const unsigned long long* xg = p.x_g + (size_t)par * B * (kH / 2);
+      unsigned int pending = 0;  // bit c: chunk kCh wave + c still to check
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) {
+        const int j = wave * kCh + c;
+        if ((j >> 2) < B) {
+          __builtin_amdgcn_global_load_lds((gptr_t)(xg + (size_t)j * 128 + lane * 2), (lptr_t)(stg + j * 1024), 16, 0,
+                                           kCoherentLoad);
+          pending |= 1u << c;
+        }
+      }
+      unsigned int spins = 0;
+      while (true) {
+        DOMINO_BN_WAIT_VM0();
+        unsigned int missing = 0;
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) {
+          if (pending & (1u << c)) {
+            const u32x4 w = ld16(stg + (wave * kCh + c) * 1024 + lane * 16);
+            const bool bad = (w[1] >> 16) != (tag & 0xFFFFu) || (w[3] >> 16) != (tag & 0xFFFFu);
+            if (__builtin_amdgcn_ballot_w64(bad) != 0ull) missing |= 1u << c;
+          }
+        }
+        pending = missing;
+        if (pending == 0u && p.spin_limit != 0u) break;
+        if (++spins > p.spin_limit || ((spins & 63u) == 0u && gave_up(p.status))) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) {
+          const int j = wave * kCh + c;
+          if (pending & (1u << c))
+            __builtin_amdgcn_global_load_lds((gptr_t)(xg + (size_t)j * 128 + lane * 2), (lptr_t)(stg + j * 1024), 16, 0,
+                                             kCoherentLoad);
+        }
+      }
+      if (__syncthreads_or(!ok)) {
+        ok = false;
+        break;
+      }
 #pragma unroll
       for (int gb = 0; gb < NG; ++gb) {
         if (gb * kGroup < B) {
-          // the group's x_g words straight into LDS (no registers): 1 KB
-          // chunks, chunk j = block j / 8, words (j % 8) 128 .. + 127; wave w
-          // loads chunks 16 w .. 16 w + 15 and loads again any chunk that
-          // still holds a word without this position's tag
           const int nb = min(kGroup, B - gb * kGroup);
-          const unsigned long long* xg = p.x_g + ((size_t)par * B + gb * kGroup) * kH;
-          unsigned int pending = 0;  // bit c: chunk 16 wave + c still to check
-#pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            const int j = wave * 16 + c;
-            if ((j >> 3) < nb) {
-              __builtin_amdgcn_global_load_lds((gptr_t)(xg + (size_t)j * 128 + lane * 2), (lptr_t)(stg + j * 1024), 16,
-                                               0, kCoherentLoad);
-              pending |= 1u << c;
-            }
-          }
-          unsigned int spins = 0;
-          while (true) {
-            DOMINO_BN_WAIT_VM0();
-            unsigned int missing = 0;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-              if (pending & (1u << c)) {
-                const u32x4 w = ld16(stg + (wave * 16 + c) * 1024 + lane * 16);
-                const bool bad = w[1] != tag || w[3] != tag;
-                if (__builtin_amdgcn_ballot_w64(bad) != 0ull) missing |= 1u << c;
-              }
-            }
-            pending = missing;
-            if (pending == 0u && p.spin_limit != 0u) break;
-            if (++spins > p.spin_limit || ((spins & 63u) == 0u && gave_up(p.status))) {
-              ok = false;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-              const int j = wave * 16 + c;
-              if (pending & (1u << c))
-                __builtin_amdgcn_global_load_lds((gptr_t)(xg + (size_t)j * 128 + lane * 2), (lptr_t)(stg + j * 1024),
-                                                 16, 0, kCoherentLoad);
-            }
-          }
-          if (__syncthreads_or(!ok)) {
-            ok = false;
-            break;
-          }
           // float32 -> bf16 high and low rows: thread takes inputs 4 tid .. 4 tid + 3
 #pragma unroll
           for (int bl = 0; bl < kGroup; ++bl) {
             if (bl < nb) {
-              const u32x4 w0 = ld16(stg + (size_t)bl * kH * 8 + tid * 32);
-              const u32x4 w1 = ld16(stg + (size_t)bl * kH * 8 + tid * 32 + 16);
-              const float x[4] = {__uint_as_float(w0[0]), __uint_as_float(w0[2]), __uint_as_float(w1[0]),
-                                  __uint_as_float(w1[2])};
+              // words 2 tid, 2 tid + 1 of the block: units 4 tid .. 4 tid + 3
+              const u32x4 w = ld16(stg + (size_t)(gb * kGroup + bl) * kH * 4 + tid * 16);
+              const float x[4] = {unpack_g2_a(w[0], w[1]), unpack_g2_b(w[0]), unpack_g2_a(w[2], w[3]),
+                                  unpack_g2_b(w[2])};
               uint16_t hi[4], lo[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) split_bf16(x[e], hi[e], lo[e]);
@@ -466,7 +497,6 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
           __syncthreads();  // hha is refilled by the next group
         }
       }
-      if (!ok) break;
     }
   }
 
@@ -689,7 +719,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_bn_kernel(Params p) {
 
 // Words of the exchange region for B blocks with Gv vocabulary workgroups.
 inline size_t exchange_words(int B, int Gv) {
-  return 2 * (size_t)B * ((size_t)Gv + kH + (size_t)kUnitWGs * kR + kR);
+  return 2 * (size_t)B * ((size_t)Gv + kH / 2 + (size_t)kUnitWGs * kR + kR);
 }
 
 template <int NG, bool SAMPLED, bool LOGITS>
@@ -803,7 +833,7 @@ hipError_t launch_draft_bn(const LoopArgs& a, hipStream_t s) {
     p.x_key = x;
     x += 2 * (size_t)nb * Gv;
     p.x_g = x;
-    x += 2 * (size_t)nb * kH;
+    x += 2 * (size_t)nb * (kH / 2);
     p.x_pu = x;
     x += 2 * (size_t)kUnitWGs * nb * kR;
     p.x_u = x;
