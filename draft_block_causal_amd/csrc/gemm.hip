@@ -250,7 +250,7 @@ hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void*
                                       int slices, int w_wrap, float* C, int ldc, size_t c_slice, hipStream_t s) {
   if (M <= 0 || N <= 0 || slices <= 0) return hipSuccess;
   if (kc <= 0 || kc % BigTile<256>::kBK || w_wrap <= 0 || w_wrap % kc) return hipErrorNotSupported;
-  return M >= 256 ? launch_big<256, kSplitK>(A, lda, M, W, ldw, N, kc, nullptr, C, ldc, slices, w_wrap, c_slice, s)
+  return M >= 256 ? launch_big<256, kSplitK, 8>(A, lda, M, W, ldw, N, kc, nullptr, C, ldc, slices, w_wrap, c_slice, s)
                   : launch_big<128, kSplitK>(A, lda, M, W, ldw, N, kc, nullptr, C, ldc, slices, w_wrap, c_slice, s);
 }
 
@@ -260,7 +260,7 @@ hipError_t launch_gemm_bf16_tn_wrapt(const void* A, int lda, int M, const void* 
   if (K % BigTile<256>::kBK || w_wrap % BigTile<256>::kBK || w_wrap <= 0 || K > 2 * w_wrap)
     return hipErrorNotSupported;
   const size_t vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && ldc % 4 == 0 && M % 4 == 0;
-  return M >= 256 ? launch_big<256, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, vec, s)
+  return M >= 256 ? launch_big<256, kWrapT, 8>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, vec, s)
                   : launch_big<128, kWrapT>(A, lda, M, W, ldw, N, K, nullptr, C, ldc, 1, w_wrap, vec, s);
 }
 }  // namespace domino
