@@ -107,6 +107,7 @@ hipError_t launch_draft_bn(const LoopArgs& a, hipStream_t s);
 size_t bn_exchange_words(int batch, int max_wg, int H, int r);
 
 hipError_t launch_fill_u64(unsigned long long* p, int n, hipStream_t s);
+hipError_t launch_fill2_u64(unsigned long long* z0, int n0, unsigned long long* z1, int n1, hipStream_t s);
 constexpr unsigned int kDefaultSpinLimit = 1u << 20;  // about a second of polling
 hipError_t launch_finalize_tokens(int B, int K, const unsigned long long* keys, int32_t* tokens, hipStream_t s);
 

@@ -206,6 +206,17 @@ __global__ void __launch_bounds__(kPreWaves * 64)
   }
 }
 
+// z0[0..n0) and z1[0..n1) set to zero (grid-stride)
+__global__ void __launch_bounds__(256) fill2_u64_kernel(unsigned long long* z0, int n0, unsigned long long* z1,
+                                                        int n1) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n0 + n1; i += gridDim.x * blockDim.x) {
+    if (i < n0)
+      z0[i] = 0ull;
+    else
+      z1[i - n0] = 0ull;
+  }
+}
+
 __global__ void fill_u64_kernel(unsigned long long* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0ull;
@@ -354,6 +365,13 @@ hipError_t launch_p_partials(const void* A, int M, int lda, const void* w1, int 
   hipLaunchKernelGGL(p_partials_kernel, dim3(ps.S * (r / 16), gy), dim3(kPreWaves * 64), 0, s,
                      static_cast<const uint16_t*>(A), M, lda, static_cast<const uint16_t*>(w1), ldw, r,
                      static_cast<const uint16_t*>(b1), ppart, ps.waves, z0, n0, z1, n1);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill2_u64(unsigned long long* z0, int n0, unsigned long long* z1, int n1, hipStream_t s) {
+  const int n = n0 + n1;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill2_u64_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, s, z0, n0, z1, n1);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ constexpr int kStreamPositions = 16;       // positions of a block whose base lo
 constexpr int kStreamKw4B = 2560 * 2 / kWaves / 64;
 constexpr int kStreamKw8B = 4096 * 2 / kWaves / 64;
 constexpr int kUHW = 8;  // W_hh k-steps per wave: the only shape a grid of 200..256 workgroups takes
+constexpr int kPRows = 256 / kUnitWGs;  // rows of P = W1[:, :d] h + b1 a unit workgroup forms (fused; r = 256)
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 constexpr int kWaitVmem0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters left alone
@@ -84,7 +85,7 @@ struct Params {
   int U_hh;    // W_hh k-steps per W_hh owner (multiple of 2 * kWaves)
   int ntiles;  // ceil(V / 16)
   int ut;      // W2 tiles of a unit workgroup (the others share the remainder evenly)
-  const uint16_t *w_hh, *b_hh, *w1, *w2, *b2;
+  const uint16_t *w_hh, *b_hh, *w1, *w2, *b2, *b1;
   const float* table;     // [V][3H]: W_ih E[v] + b_ih
   const float* base;   // [K][V], or null: the kernel forms its range's base logits itself
   const uint16_t *lm_head, *hidden;  // [V][d], [K][d] (base == null)
@@ -166,7 +167,7 @@ __device__ __forceinline__ unsigned long long entry_key(float L, float inv_temp,
 }
 
 struct Lds {
-  int pool, ghl, utile, lbs, b2s, gum, uhl, gs_prev, zero, red, lb, total;
+  int pool, ghl, utile, lbs, b2s, gum, uhl, gs_prev, zero, red, lb, px, total;
 };
 
 // The pool holds a unit workgroup's W1 columns, or a W_hh owner's k-steps,
@@ -197,6 +198,8 @@ __host__ __device__ inline Lds lds_layout(int U_hh, int H, int r, bool fused) {
   off += kWaves * 2 * 16 * 4;
   L.lb = off;
   off += fused ? kStreamPositions * kMaxWgTiles * 16 * 4 : 0;  // base logits + b2 of every position (fused)
+  L.px = off;
+  off += fused ? kStreamPositions * kPRows * 4 : 0;  // a unit workgroup's rows of P for every position (fused)
   L.total = off;
   return L;
 }
@@ -223,7 +226,11 @@ __host__ __device__ constexpr int stream_scratch_bytes() { return kWaves * 16 * 
 // Base logits of this workgroup's vocabulary range for every position
 // ([notes] §二.1(1): the frozen LM head over the block's hidden states, in one
 // pass): lb[i][e] = sum_k hidden[i][k] W_lm[16 t_lo + e][k] + b2[16 t_lo + e]
-// (-inf past the vocabulary).  W_lm's rows are read once, from HBM, the way
+// (-inf past the vocabulary); then, for a unit workgroup u (nx = 2), rows
+// 32 u .. 32 u + 31 of the hidden half of the first correction projection,
+// px[i][c] = sum_k hidden[i][k] W1[32 u + c][k] + b1[32 u + c]
+// ([notes] §二.1(2) item 2: the hidden state's share of the bottleneck
+// input), streamed the same way as two more tiles.  W_lm's rows are read once, from HBM, the way
 // it streams best: each wave takes a quarter of K (KW 64-B steps of each
 // row), and a load instruction covers 512 contiguous bytes of each of two rows,
 // read non-temporally through buffer descriptors sized to the valid rows (rows
@@ -234,7 +241,8 @@ __host__ __device__ constexpr int stream_scratch_bytes() { return kWaves * 16 * 
 // four waves' partial sums are added in LDS in a fixed order.  The next tile's
 // loads are in flight while a tile is multiplied.
 template <int KW>
-__device__ void stream_base(const Params& p, int t_lo, int nt, unsigned char* scratch, float* lb) {
+__device__ void stream_base(const Params& p, int t_lo, int nt, int nx, int x_row0, unsigned char* scratch, float* lb,
+                            float* px) {
   constexpr int kSlice = KW * 64;
   constexpr int kPass = kSlice % 512 == 0 ? 512 : 256;
   constexpr int kPasses = kSlice / kPass;
@@ -256,19 +264,24 @@ __device__ void stream_base(const Params& p, int t_lo, int nt, unsigned char* sc
 #pragma unroll
     for (int s = 0; s < KW; ++s) af[s] = live ? ld16(arow + s * 64) : u32x4{0, 0, 0, 0};
   }
-  const int row_bytes = d * 2;
   const int lrow = lane / kChunks, lchunk = lane % kChunks;
-  const int voff = lrow * row_bytes + wave * kSlice + lchunk * 16;
+  const int ldw1 = d + p.H;  // W1 row length (hidden half first)
   auto stage = [&](int j, u32x4 (&dst)[KW]) {
-    const int t = t_lo + j;
-    const int rows = j < nt ? min(16, V - t * 16) : 0;
-    const uint16_t* base = p.lm_head + (j < nt ? (size_t)t * 16 * d : 0);
+    // tile j < nt: LM head rows 16 (t_lo + j) ..; nt <= j < nt + nx: W1 rows
+    // x_row0 + 16 (j - nt) ..; later: nothing (every load reads zero)
+    const bool lm = j < nt, w1t = !lm && j < nt + nx;
+    const int rows = lm ? min(16, V - (t_lo + j) * 16) : w1t ? 16 : 0;
+    const int ld = lm ? d : ldw1;
+    const uint16_t* base = lm ? p.lm_head + (size_t)(t_lo + j) * 16 * d
+                              : w1t ? p.w1 + (size_t)(x_row0 + 16 * (j - nt)) * ldw1 : p.lm_head;
+    const int row_bytes = ld * 2;
+    const int voff = lrow * row_bytes + wave * kSlice + lchunk * 16;
 #pragma unroll
     for (int jj = 0; jj < kLoadsPerPass; ++jj) {
       const int rj =
           jj == 0 ? min(rows, kRowsPerLoad) : min(max(rows - jj * kRowsPerLoad, 0), kRowsPerLoad);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(base + (rj > 0 ? (size_t)jj * kRowsPerLoad * d : 0)), (short)0, rj * row_bytes,
+          const_cast<uint16_t*>(base + (rj > 0 ? (size_t)jj * kRowsPerLoad * ld : 0)), (short)0, rj * row_bytes,
           kRsrcWord3);
 #pragma unroll
       for (int q = 0; q < kPasses; ++q)
@@ -294,21 +307,28 @@ __device__ void stream_base(const Params& p, int t_lo, int nt, unsigned char* sc
     for (int jq = 0; jq < 4; ++jq) rb[(wave * 16 + grp * 4 + jq) * 17 + col] = acc[jq];
     __syncthreads();
     // thread: position tid / 16, entry tid % 16 of the tile
-    const int m = tid >> 4, c = tid & 15, v = (t_lo + j) * 16 + c;
+    const int m = tid >> 4, c = tid & 15;
     float sum = 0.f;
 #pragma unroll
     for (int wv = 0; wv < kWaves; ++wv) sum += rb[(wv * 16 + m) * 17 + c];
-    lb[m * kMaxWgTiles * 16 + j * 16 + c] = v < V ? sum + (p.b2 ? bf16_to_f32(p.b2[v]) : 0.f) : -INFINITY;
+    if (j < nt) {
+      const int v = (t_lo + j) * 16 + c;
+      lb[m * kMaxWgTiles * 16 + j * 16 + c] = v < V ? sum + (p.b2 ? bf16_to_f32(p.b2[v]) : 0.f) : -INFINITY;
+    } else {
+      const int row = x_row0 + 16 * (j - nt) + c;
+      px[m * kPRows + 16 * (j - nt) + c] = sum + (p.b1 ? bf16_to_f32(p.b1[row]) : 0.f);
+    }
   };
   u32x4 w0[KW], w1[KW];
+  const int ntot = nt + nx;
   int j = 0;
   stage(0, w0);
   // the scheduling barriers keep each prefetch ahead of the tile in hand
-  while (j < nt) {
+  while (j < ntot) {
     stage(j + 1, w1);
     __builtin_amdgcn_sched_barrier(0);
     process(j, w0, red);
-    if (++j >= nt) break;
+    if (++j >= ntot) break;
     stage(j + 1, w0);
     __builtin_amdgcn_sched_barrier(0);
     process(j, w1, red + kWaves * 16 * 17);
@@ -341,6 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   float* b2s = reinterpret_cast<float*>(smem + L.b2s);
   float* gum = reinterpret_cast<float*>(smem + L.gum);
   float* lbt = reinterpret_cast<float*>(smem + L.lb);
+  float* pxt = reinterpret_cast<float*>(smem + L.px);
   const int units = H / kUnitWGs;
   const int ksu = units / 32;  // k-steps of a unit workgroup's W1 columns
   const bool unit_wg = w < kUnitWGs;
@@ -362,7 +383,7 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
   // fused: the base logits of the range for every position first, while the
   // registers and the pool are still free
   if constexpr (SKW > 0) {
-    stream_base<SKW>(p, t_lo, nt, pool, lbt);
+    stream_base<SKW>(p, t_lo, nt, unit_wg ? kPRows / 16 : 0, w * kPRows, pool, lbt, pxt);
     __syncthreads();
   }
   // W2: tile s * kWaves + wave of this workgroup's range, 8 k-step fragments each
@@ -503,9 +524,14 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       constexpr int kRtPerWave = 256 / 16 / kWaves;  // r / 16 / kWaves with r = 256
       float pslice[kRtPerWave];
 #pragma unroll
-      for (int i = 0; i < kRtPerWave; ++i)
-        pslice[i] = w < p.S && grp == 0 ? p.ppart[((size_t)w * p.K + step) * r + (wave * kRtPerWave + i) * 16 + col]
-                                        : 0.f;
+      for (int i = 0; i < kRtPerWave; ++i) {
+        const int row = (wave * kRtPerWave + i) * 16 + col;
+        if constexpr (SKW > 0)  // rows w kPRows .. of P, formed in the stream
+          pslice[i] = grp == 0 && row >= w * kPRows && row < (w + 1) * kPRows ? pxt[step * kPRows + row - w * kPRows]
+                                                                              : 0.f;
+        else
+          pslice[i] = w < p.S && grp == 0 ? p.ppart[((size_t)w * p.K + step) * r + row] : 0.f;
+      }
       if (tid < units) {
         const int j = w * units + tid;
         const float* trow = p.table + (size_t)s_tok * 3 * H;
@@ -723,7 +749,9 @@ static hipError_t launch_t(const Params& p, int G, size_t lds, const PreArgs& q,
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorNotSupported;
   return LoopOrder::get().run(s, [&](hipEvent_t stop) -> hipError_t {
-    hipError_t e2 = launch_pre(q, s);
+    // the loop that forms P itself needs only the clears before it
+    hipError_t e2 = SKW > 0 ? launch_fill2_u64(q.a->keys, q.a->clear_words, q.a->xpart, (int)q.a->xwords, s)
+                            : launch_pre(q, s);
     if (e2 != hipSuccess) return e2;
     hipExtLaunchKernelGGL(kern, dim3(G), dim3(kThreads), lds, s, nullptr, stop, 0, p);
     return hipGetLastError();
@@ -780,6 +808,10 @@ static bool make_plan(const LoopArgs& a, Plan& pl) {
   // the unit workgroups take ut tiles each, the others share the rest; every
   // workgroup's tiles must fit its waves' registers
   pl.ut = std::min(kWaves * kNR, pl.ntiles / pl.G);
+  // forming the base logits, a unit workgroup also streams its kPRows rows of
+  // W1's hidden half (as many bytes as kPRows / 16 LM-head tiles): it takes
+  // that many fewer vocabulary tiles
+  if (!a.base) pl.ut = std::max(0, pl.ut - kPRows / 16);
   const int rest = pl.ntiles - kUnitWGs * pl.ut;
   const int per_other = (rest + (pl.G - kUnitWGs) - 1) / (pl.G - kUnitWGs);
   if (per_other > kWaves * kNR) return false;
@@ -824,6 +856,7 @@ hipError_t launch_draft_b1(const LoopArgs& a, hipStream_t s) {
   p.w1 = static_cast<const uint16_t*>(a.w1);
   p.w2 = static_cast<const uint16_t*>(a.w2);
   p.b2 = static_cast<const uint16_t*>(a.b2);
+  p.b1 = static_cast<const uint16_t*>(a.b1);
   p.table = a.table;
   p.base = a.base;
   p.lm_head = static_cast<const uint16_t*>(a.lm_head);
