@@ -29,8 +29,11 @@ constexpr int kXcds = 8;
 // staging registers) through a ring of kStages K tiles of 32 (4 x 32 KB for
 // BM = 256, 6 x 24 KB for BM = 128), so the loads of a tile are issued
 // kStages - 1 tiles before use.  An LDS row is 64 bytes (4 chunks of 16 B);
-// chunk c of row r sits in slot c ^ ((r >> 2) & 3), which makes the 16-row
-// fragment reads conflict-free.  Same XCD-grouped block order as above.  The
+// chunk c of row r sits in slot c ^ ((r >> 1) & 3): a 16-B read is served 8
+// lanes (128 B, all 32 banks) at a time, and the 8 lanes of a fragment read
+// (rows r .. r + 7, one chunk) then touch 8 different 16-B bank groups (two
+// rows share a 128-B line; the XOR separates rows r and r + 2).  Same
+// XCD-grouped block order as above.  The
 // operand fill into LDS is what bounds it: BM x 256 outputs per (BM + 256) x
 // 64 B filled per K step.
 // ---------------------------------------------------------------------------
@@ -123,8 +126,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
   const int wm = wave / BT::kWavesN, wn = wave % BT::kWavesN;
 
   // DMA: load i of this wave covers tile rows 16 * (wave * loads + i) + lane / 4,
-  // LDS slot lane & 3 of that row, i.e. global chunk (lane & 3) ^ ((lane >> 4) & 3)
-  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // LDS slot lane & 3 of that row, i.e. global chunk (lane & 3) ^ ((lane >> 3) & 3)
+  const int dchunk = (lane & 3) ^ ((lane >> 3) & 3);
   const unsigned char* ag[BT::kALoads];
   const unsigned char* wg[BT::kWLoads];
 #pragma unroll
@@ -153,8 +156,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
       __builtin_amdgcn_global_load_lds((gptr_t)(wg[i] + wk), (lptr_t)(sW + (wave * BT::kWLoads + i) * 1024), 16, 0,
                                        0);
   };
-  // fragment reads: row r = base + col, chunk grp -> slot grp ^ ((r >> 2) & 3) (base % 16 == 0)
-  const int fslot = (grp ^ ((col >> 2) & 3)) * 16;
+  // fragment reads: row r = base + col, chunk grp -> slot grp ^ ((r >> 1) & 3) (base % 16 == 0)
+  const int fslot = (grp ^ ((col >> 1) & 3)) * 16;
 
   f32x4 acc[8][BT::kFW];
 #pragma unroll
