@@ -73,6 +73,10 @@ constexpr int kR = 256;                     // correction rank this loop takes
 constexpr int kRK = kR / 32;                // k-steps of a W2 row (8)
 constexpr int kNR = 10;                     // W2 tiles per wave of a vocabulary workgroup
 constexpr int kMaxEntries = kNR * kWaves * 16;  // vocabulary entries of a vocabulary workgroup (640)
+// LDS row stride (floats) of the per-block base-logit and noise tables: M reads
+// blocks 2 g and 2 g + 2 in the same half-wave, and a stride of 8 mod 16 puts
+// those rows on opposite halves of the 32 banks (640 put them on the same)
+constexpr int kCombStride = kMaxEntries + 8;
 constexpr int kGroup = 8;                   // blocks per matrix-core pass
 constexpr int kMaxB = 16;                   // blocks per launch
 constexpr int kUStride = kR + 8;            // u operand rows in LDS, bf16 (528 B: conflict-free 16-B reads)
@@ -154,9 +158,9 @@ __host__ __device__ inline VocabLds vocab_lds(int B, bool noise) {
   VocabLds L{};
   int off = 0;
   L.comb = off;
-  off += B * kMaxEntries * 4;  // base + b2 (scaled, + noise when sampling) per block and entry
+  off += B * kCombStride * 4;  // base + b2 (scaled, + noise when sampling) per block and entry
   L.noise = off;
-  off += noise ? B * kMaxEntries * 4 : 0;  // Gumbel noise kept apart when logits are written too
+  off += noise ? B * kCombStride * 4 : 0;  // Gumbel noise kept apart when logits are written too
   L.utile = off;
   off += ng * 16 * kUStride * 2;  // u of every block, per group: 16 rows (block, hi | lo)
   L.b2s = off;
@@ -566,7 +570,7 @@ __device__ void vocab_role(const Params& p, unsigned char* smem, bool& ok) {
   }
   for (int e = tid; e < kMaxEntries; e += kThreads) b2s[e] = e < nv && v0 + e < V && p.b2 ? bf16_to_f32(p.b2[v0 + e]) : 0.f;
   // slots past the range (or the vocabulary) never win: their combined bias is -inf
-  for (int j = tid; j < B * kMaxEntries; j += kThreads) {
+  for (int j = tid; j < B * kCombStride; j += kThreads) {
     comb[j] = -INFINITY;
     if (kNoise) noise[j] = 0.f;
   }
@@ -588,20 +592,25 @@ __device__ void vocab_role(const Params& p, unsigned char* smem, bool& ok) {
         for (int q = 0; q < 4; ++q) lb[q] = v0 + e + q < V ? brow[q] : 0.f;
         u32x4 words = {0u, 0u, 0u, 0u};
         if constexpr (SAMPLED) words = philox4(p.seed, p.offset, p.rng_b + (uint32_t)b, (uint32_t)step, (uint32_t)((v0 + e) >> 2));
-        float* cb = comb + (size_t)b * kMaxEntries + e;
+        // one 16-B store per thread and table (four 4-B stores 16 B apart
+        // would put lanes l, l + 8, l + 16, l + 24 on one bank)
+        f32x4 cv, nv4 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 b2v = *reinterpret_cast<const f32x4*>(b2s + e);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bool live = v0 + e + q < V;
-          const float x = lb[q] + b2s[e + q];
+          const float x = lb[q] + b2v[q];
           if constexpr (!SAMPLED) {
-            cb[q] = live ? x : -INFINITY;
+            cv[q] = live ? x : -INFINITY;
           } else if constexpr (kNoise) {
-            cb[q] = live ? x : -INFINITY;
-            noise[(size_t)b * kMaxEntries + e + q] = gumbel_from_word(words[q]);
+            cv[q] = live ? x : -INFINITY;
+            nv4[q] = gumbel_from_word(words[q]);
           } else {
-            cb[q] = live ? x * p.inv_temp + gumbel_from_word(words[q]) : -INFINITY;
+            cv[q] = live ? x * p.inv_temp + gumbel_from_word(words[q]) : -INFINITY;
           }
         }
+        *reinterpret_cast<f32x4*>(comb + (size_t)b * kCombStride + e) = cv;
+        if constexpr (kNoise) *reinterpret_cast<f32x4*>(noise + (size_t)b * kCombStride + e) = nv4;
       }
     }
     // ---------- W: u of every block ----------
@@ -658,14 +667,14 @@ __device__ void vocab_role(const Params& p, unsigned char* smem, bool& ok) {
           asm volatile("" : "+v"(e));  // keeps per-tile constants inside the position loop
           const uint32_t v = (uint32_t)(v0 + e);
           const float d0 = acc[s][0] + acc[s][1], d1 = acc[s][2] + acc[s][3];
-          const float x0 = comb[(size_t)c0 * kMaxEntries + e], x1 = comb[(size_t)c1 * kMaxEntries + e];
+          const float x0 = comb[(size_t)c0 * kCombStride + e], x1 = comb[(size_t)c1 * kCombStride + e];
           float s0, s1;
           if constexpr (!SAMPLED) {
             s0 = d0 + x0;
             s1 = d1 + x1;
           } else if constexpr (kNoise) {
-            s0 = (d0 + x0) * p.inv_temp + noise[(size_t)c0 * kMaxEntries + e];
-            s1 = (d1 + x1) * p.inv_temp + noise[(size_t)c1 * kMaxEntries + e];
+            s0 = (d0 + x0) * p.inv_temp + noise[(size_t)c0 * kCombStride + e];
+            s1 = (d1 + x1) * p.inv_temp + noise[(size_t)c1 * kCombStride + e];
           } else {
             s0 = d0 * p.inv_temp + x0;
             s1 = d1 * p.inv_temp + x1;
