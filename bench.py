@@ -38,6 +38,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f) for f in ("rowstream.hip", "common.h")]
+# the tiled LM-head GEMM (256-row tiles, many blocks)
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_gemm_traffic.json")
+GEMM_KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f)
+                       for f in ("gemm.hip", "common.h", "kernels.h")]
 # the single-block loop that forms the base logits itself
 FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "draft_b1_fused_traffic.json")
 FUSED_KERNEL_SOURCES = [os.path.join(ROOT, "draft_block_causal_amd", "csrc", f)
@@ -91,16 +95,18 @@ def block_floor_us(B: int, K: int, d: int, V: int, H: int, r: int, elem: int, ba
     return max(t_hbm, t_mfma) * 1e6
 
 
-def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE):
+def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE, rows=None):
     """HBM bytes per launch of a kernel (the LM head by default) from the committed
-    rocprofv3 counter runs, if they were taken on the current kernel source; else
-    None."""
+    rocprofv3 counter runs, if they were taken on the current kernel source (and,
+    when `rows` is given, on a launch of that many rows); else None."""
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_hash:
+        return None
+    if rows is not None and t.get("rows") != rows:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -612,9 +618,14 @@ def main() -> int:
     elem = 2 if w.dtype == "bf16" else 4
     alg = lmhead_algorithmic_bytes(B, K, d, V, elem)
     flops = lmhead_flops(B, K, d, V)
-    khash = kernel_source_hash()
-    traffic = measured_traffic(khash)
     M = B * K
+    # the counter record of the kernel that forms the base logits at this row count
+    if M <= 32:
+        traffic = measured_traffic(kernel_source_hash(), TRAFFIC_FILE, rows=M)
+    elif w.dtype == "bf16" and M >= 256:
+        traffic = measured_traffic(kernel_source_hash(GEMM_KERNEL_SOURCES), GEMM_TRAFFIC_FILE, rows=M)
+    else:
+        traffic = None
     if fused:
         # the dominant kernel is the loop that streams the LM head itself: the
         # whole call's compulsory bytes (no base logits in HBM) over the draft
