@@ -95,10 +95,10 @@ def block_floor_us(B: int, K: int, d: int, V: int, H: int, r: int, elem: int, ba
     return max(t_hbm, t_mfma) * 1e6
 
 
-def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE, rows=None):
+def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE, workload=None):
     """HBM bytes per launch of a kernel (the LM head by default) from the committed
     rocprofv3 counter runs, if they were taken on the current kernel source (and,
-    when `rows` is given, on a launch of that many rows); else None."""
+    when `workload` is given, on that workload's shapes); else None."""
     try:
         with open(path) as f:
             t = json.load(f)
@@ -106,7 +106,7 @@ def measured_traffic(kernel_hash: str, path: str = TRAFFIC_FILE, rows=None):
         return None
     if t.get("kernel_source_sha256") != kernel_hash:
         return None
-    if rows is not None and t.get("rows") != rows:
+    if workload is not None and t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -619,11 +619,11 @@ def main() -> int:
     alg = lmhead_algorithmic_bytes(B, K, d, V, elem)
     flops = lmhead_flops(B, K, d, V)
     M = B * K
-    # the counter record of the kernel that forms the base logits at this row count
+    # the counter record of the kernel that forms the base logits, taken on this workload
     if M <= 32:
-        traffic = measured_traffic(kernel_source_hash(), TRAFFIC_FILE, rows=M)
+        traffic = measured_traffic(kernel_source_hash(), TRAFFIC_FILE, workload=w.name)
     elif w.dtype == "bf16" and M >= 256:
-        traffic = measured_traffic(kernel_source_hash(GEMM_KERNEL_SOURCES), GEMM_TRAFFIC_FILE, rows=M)
+        traffic = measured_traffic(kernel_source_hash(GEMM_KERNEL_SOURCES), GEMM_TRAFFIC_FILE, workload=w.name)
     else:
         traffic = None
     if fused:

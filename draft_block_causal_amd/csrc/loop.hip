@@ -508,7 +508,7 @@ __device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0);
 // token-to-token path: by the workgroups x >= gx_w2, which do nothing else,
 // when the grid has them, else by the W2 workgroups before their tiles
 // (unit q in workgroup q mod the grid size).
-template <class T, int MT, int NS, bool VEC>
+template <class T, int MT, int NS, bool VEC, int D>
 __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step, int gx_w2) {
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
@@ -680,20 +680,23 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
     }
   };
 
-  // (t is kept in a scalar register: the descriptors built from it must be)
-  Stage s0, s1;
+  // A ring of D register stages: the tiles D - 1 strides ahead are in flight
+  // while a tile is multiplied (every load unconditional, so the compiler's
+  // count of loads in flight stays exact).  (t is kept in a scalar register:
+  // the descriptors built from it must be.)
+  Stage st[D];
   int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
-  load(t, s0);
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) load(t + i * stride, st[i]);
   while (t < ntiles) {
-    load(t + stride, s1);
-    __builtin_amdgcn_sched_barrier(0);
-    process(t, s0);
-    t = __builtin_amdgcn_readfirstlane(t + stride);
-    if (t >= ntiles) break;
-    load(t + stride, s0);
-    __builtin_amdgcn_sched_barrier(0);
-    process(t, s1);
-    t = __builtin_amdgcn_readfirstlane(t + stride);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      load(t + (D - 1) * stride, st[(i + D - 1) % D]);
+      __builtin_amdgcn_sched_barrier(0);
+      process(t, st[i]);
+      t = __builtin_amdgcn_readfirstlane(t + stride);
+      if (t >= ntiles) break;
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -1056,11 +1059,18 @@ struct W2Launch {
   bool fused_hh;  // the kernel forms W_hh g for the next position
 };
 
+// register stages of W2 tiles per wave in the streaming kernel (Qwen3-8B,
+// draft call at 32 / 128 blocks: 0.622 / 1.40 ms with 2 stages, 0.690 / 1.79
+// with 3, 0.711 / 2.07 with 4: more registers cost occupancy, and at 32 blocks
+// the W_hh units then no longer fit in workgroups of their own)
+constexpr int kW2Stages = 2;
+
 template <class T, int MW, int NS>
 static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int ntiles = (p.V + 15) / 16;
   const size_t lds = w2_stream_lds_bytes<T, MW>(p.r);
-  auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true> : w2_stream_kernel<T, MW, NS, false>;
+  auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true, kW2Stages>
+                            : w2_stream_kernel<T, MW, NS, false, kW2Stages>;
   // one workgroup per compute unit for each slice of 16 MW batch rows: each
   // wave then streams ~ntiles / (4 #CU) tiles, which amortises staging u and
   // the key reduction (measured at Qwen3 shapes, B = 8 / 32 / 128: 19 / 26 /

@@ -28,13 +28,14 @@ def test_traffic_record_matches_current_source_or_is_ignored():
     got = bench.measured_traffic(bench.kernel_source_hash())
     assert got is None or abs(got / bench.lmhead_algorithmic_bytes(1, 16, 4096, 151936, 2) - 1.0) < 0.01
     assert bench.measured_traffic("0" * 64) is None
-    # a record only counts for the row count it was taken at
-    assert bench.measured_traffic(bench.kernel_source_hash(), rows=16) == got
-    assert bench.measured_traffic(bench.kernel_source_hash(), rows=32) is None
+    # a record only counts for the workload it was taken on (the tiny float32
+    # head has 16 rows too)
+    assert bench.measured_traffic(bench.kernel_source_hash(), workload="qwen3_8b_b1_greedy") == got
+    assert bench.measured_traffic(bench.kernel_source_hash(), workload="tiny_f32_b1") is None
     # the tiled GEMM at 32 blocks (512 rows): W_lm fetched about once, the
     # float32 output written with partial-line overhead; within 1.0 .. 1.3 x
     gemm = bench.measured_traffic(bench.kernel_source_hash(bench.GEMM_KERNEL_SOURCES), bench.GEMM_TRAFFIC_FILE,
-                                  rows=512)
+                                  workload="qwen3_8b_b32_t1")
     alg32 = bench.lmhead_algorithmic_bytes(32, 16, 4096, 151936, 2)
     assert gemm is None or 1.0 <= gemm / alg32 < 1.3
     # the single-block loop that streams the LM head itself: within 10 % of
