@@ -22,7 +22,8 @@ constexpr int kXcds = 8;
 // Big-tile kernel: block tile BM x 256 (BM = 256, or 128 for 33 .. 255 rows),
 // NW = 4 or 8 waves.  BM = 256: a 2 x 2 grid of 128 x 128 wave tiles (4 waves)
 // or a 2 x 4 grid of 128 x 64 (8 waves, two per SIMD); BM = 128: four
-// 128 x 64 wave tiles side by side.  Accumulators live in
+// 128 x 64 wave tiles side by side (4 waves) or a 2 x 4 grid of 64 x 64
+// (8 waves).  Accumulators live in
 // AGPRs (one wave per SIMD may use 512 registers, two 256).  Per 32-wide K step a wave
 // reads 8 A and 8 (or 4) W fragments from LDS for 64 (or 32) products.
 // Operands go from HBM straight into LDS (global_load_lds, 16 B per lane, no
@@ -52,7 +53,8 @@ struct BigTile {
   static constexpr int kPerStage = kALoads + kWLoads;     // DMA instructions of one stage per wave
   static constexpr int kWavesN = BM == 256 && NW == 4 ? 2 : 4;  // wave grid (NW / kWavesN) x kWavesN
   static constexpr int kFW = kBN / kWavesN / 16;          // W fragments per wave (8 or 4)
-  static_assert(BM == 256 || (BM == 128 && NW == 4), "block height");
+  static constexpr int kFA = BM / (NW / kWavesN) / 16;    // A fragments per wave (8, or 4 for 128 x 256 / 8)
+  static_assert(BM == 256 || BM == 128, "block height");
   static_assert(NW == 4 || NW == 8, "waves");
   static_assert((kStages - 2) * kPerStage < 64, "vector-memory count field");
 };
@@ -91,6 +93,12 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 #define DOMINO_WAIT_VM_LGK0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
 template <int PER, int MAXA>
 __device__ __forceinline__ void wait_stages_lgk0(int ahead) {
+  if constexpr (MAXA >= 4) {
+    if (ahead >= 4) {
+      DOMINO_WAIT_VM_LGK0(4 * PER);
+      return;
+    }
+  }
   if constexpr (MAXA >= 3) {
     if (ahead >= 3) {
       DOMINO_WAIT_VM_LGK0(3 * PER);
@@ -181,9 +189,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
   // fragment reads: row r = base + col, chunk grp -> slot grp ^ ((r >> 1) & 3) (base % 16 == 0)
   const int fslot = (grp ^ ((col >> 1) & 3)) * 16;
 
-  f32x4 acc[8][BT::kFW];
+  f32x4 acc[BT::kFA][BT::kFW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < BT::kFA; ++i)
 #pragma unroll
     for (int j = 0; j < BT::kFW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -210,9 +218,9 @@ __global__ void __launch_bounds__(NW * 64, 1)
       __builtin_amdgcn_sched_barrier(0);
       const unsigned char* sA = smem + (kt % BT::kStages) * BT::kStage;
       const unsigned char* sW = sA + BM * BT::kRow;
-      u32x4 af[8], wf[BT::kFW];
+      u32x4 af[BT::kFA], wf[BT::kFW];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) af[i] = ld16(sA + (wm * 128 + i * 16 + col) * BT::kRow + fslot);
+      for (int i = 0; i < BT::kFA; ++i) af[i] = ld16(sA + (wm * BT::kFA * 16 + i * 16 + col) * BT::kRow + fslot);
 #pragma unroll
       for (int j = 0; j < BT::kFW; ++j) wf[j] = ld16(sW + (wn * BT::kFW * 16 + j * 16 + col) * BT::kRow + fslot);
       if (kt + BT::kStages - 1 < nk) issue(kt + BT::kStages - 1);
@@ -223,7 +231,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < BT::kFA; ++i)
 #pragma unroll
         for (int j = 0; j < BT::kFW; ++j) acc[i][j] = mma16<Bf16>(acc[i][j], af[i], wf[j]);
       __builtin_amdgcn_sched_barrier(0);
@@ -238,17 +246,17 @@ __global__ void __launch_bounds__(NW * 64, 1)
     if (kt + BT::kStages - 1 < nk) issue(kt + BT::kStages - 1);
     const unsigned char* sA = smem + (kt % BT::kStages) * BT::kStage;
     const unsigned char* sW = sA + BM * BT::kRow;
-    u32x4 af[8], wf[BT::kFW];
+    u32x4 af[BT::kFA], wf[BT::kFW];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = ld16(sA + (wm * 128 + i * 16 + col) * BT::kRow + fslot);
+    for (int i = 0; i < BT::kFA; ++i) af[i] = ld16(sA + (wm * BT::kFA * 16 + i * 16 + col) * BT::kRow + fslot);
 #pragma unroll
     for (int j = 0; j < BT::kFW; ++j) wf[j] = ld16(sW + (wn * BT::kFW * 16 + j * 16 + col) * BT::kRow + fslot);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < BT::kFA; ++i)
 #pragma unroll
       for (int j = 0; j < BT::kFW; ++j) acc[i][j] = mma16<Bf16>(acc[i][j], af[i], wf[j]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + BT::kFW, 0);  // all fragment reads first,
-    __builtin_amdgcn_sched_group_barrier(0x008, 8 * BT::kFW, 0);  // then the products
+    __builtin_amdgcn_sched_group_barrier(0x100, BT::kFA + BT::kFW, 0);  // all fragment reads first,
+    __builtin_amdgcn_sched_group_barrier(0x008, BT::kFA * BT::kFW, 0);  // then the products
   }
 
 #pragma unroll
@@ -259,8 +267,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
       // a lane's 4 values are consecutive in C[n][:]: one 16-byte store when
       // C and ldc allow it (c_slice != 0; then M % 4 == 0 as well)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = m0 + wm * 128 + i * 16 + grp * 4;
+      for (int i = 0; i < BT::kFA; ++i) {
+        const int m = m0 + wm * BT::kFA * 16 + i * 16 + grp * 4;
         if (c_slice) {
           if (m < M) *reinterpret_cast<f32x4*>(C + (size_t)n * ldc + m) = acc[i][j];
         } else {
@@ -272,10 +280,10 @@ __global__ void __launch_bounds__(NW * 64, 1)
     } else {
       const float bv = bias ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < BT::kFA; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * 128 + i * 16 + grp * 4 + q;
+          const int m = m0 + wm * BT::kFA * 16 + i * 16 + grp * 4 + q;
           if (m < M) C[(size_t)m * ldc + n] = acc[i][j][q] + bv;
         }
     }
@@ -307,8 +315,13 @@ hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int
   // 256 x 256 tiles with two waves per SIMD: one wave's fragment reads run
   // beside the other's products (Qwen3-8B LM head, 512 rows: 0.831 -> 0.802 ms
   // against one wave per SIMD)
-  return M >= 256 ? launch_big<256, kPlain, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s)
-                  : launch_big<128, kPlain>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
+  // 33 .. 255 rows: 128 x 256 tiles, with 8 waves and the ping-pong loop for
+  // long rows (Qwen3-8B LM head, K = 4096, at 48 / 64 / 128 rows: 0.359 /
+  // 0.367 / 0.389 -> 0.330 / 0.334 / 0.352 ms), else 4 waves (Qwen3-4B, K =
+  // 2560, 128 rows: 0.217 ms against 0.220 with 8)
+  if (M >= 256) return launch_big<256, kPlain, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
+  return K >= 4096 ? launch_big<128, kPlain, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s)
+                   : launch_big<128, kPlain, 4>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
 }
 
 hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void* W, int ldw, int N, int kc,

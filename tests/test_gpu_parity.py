@@ -422,18 +422,20 @@ def test_lm_head_row_slices_sharing_w(dev, batch, vocab, d):
     assert err <= LOGIT_TOL, f"base logits err {err}"
 
 
-@pytest.mark.parametrize("batch,vocab", [(3, 20001), (13, 65531), (19, 5003)])
-def test_lm_head_tile_shapes(dev, batch, vocab):
+@pytest.mark.parametrize("batch,vocab,d", [(3, 20001, 256), (13, 65531, 256), (19, 5003, 256), (5, 20001, 4096),
+                                           (19, 9001, 4096)])
+def test_lm_head_tile_shapes(dev, batch, vocab, d):
     """Base logits through both shapes of the many-row matrix-core kernel.
 
     48 rows (one partial M tile) and 208 rows (two) take 128 x 256 tiles, 304
     rows take 256 x 256 tiles; every vocabulary is larger than the row-streaming
-    kernel takes and ends in a partial tile.  All rows of the last 600 columns
-    and 3000 random columns are checked against the oracle.
+    kernel takes and ends in a partial tile.  At d = 4096 the 128-row tiles run
+    with 8 waves (80 rows here).  All rows of the last 600 columns and 3000
+    random columns are checked against the oracle.
     """
     import draft_block_causal_amd as D
 
-    w = S.Workload(f"lm_head_b{batch}_v{vocab}", batch, 16, 256, vocab, 32, 32, "bf16", False, 0.0)
+    w = S.Workload(f"lm_head_b{batch}_v{vocab}_d{d}", batch, 16, d, vocab, 32, 32, "bf16", False, 0.0)
     log(f"{w.name}: generating inputs")
     head_np, inp = workload_arrays(w)
     head = device_head(w, dev)
