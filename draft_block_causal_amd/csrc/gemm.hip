@@ -41,10 +41,10 @@ constexpr int kXcds = 8;
 // into registers alone, with no LDS and no products, takes 0.365 ms for the
 // Qwen3-8B LM head at 512 rows, and through the LDS DMA path 0.49 ms.
 // ---------------------------------------------------------------------------
-template <int BM, int NW = 4>
+template <int BM, int NW = 4, int BN = 256>
 struct BigTile {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kBN = 256, kBK = 32;
+  static constexpr int kBN = BN, kBK = 32;
   static constexpr int kRow = kBK * 2;                    // 64 bytes of K per LDS row
   static constexpr int kStage = (BM + kBN) * kRow;        // bytes per ring stage
   static constexpr int kStages = BM == 256 ? 4 : 6;       // 128 KB or 144 KB of LDS
@@ -55,6 +55,7 @@ struct BigTile {
   static constexpr int kFW = kBN / kWavesN / 16;          // W fragments per wave (8 or 4)
   static constexpr int kFA = BM / (NW / kWavesN) / 16;    // A fragments per wave (8, or 4 for 128 x 256 / 8)
   static_assert(BM == 256 || BM == 128, "block height");
+  static_assert(BN == 256 || BN == 128, "block width");
   static_assert(NW == 4 || NW == 8, "waves");
   static_assert((kStages - 2) * kPerStage < 64, "vector-memory count field");
 };
@@ -125,12 +126,12 @@ __device__ __forceinline__ void wait_stages_lgk0(int ahead) {
 //            16-byte aligned and ldc, M multiples of 4, for 16-byte stores).
 enum GemmMode { kPlain = 0, kSplitK = 1, kWrapT = 2 };
 
-template <int BM, int MODE, int NW>
+template <int BM, int MODE, int NW, int BN>
 __global__ void __launch_bounds__(NW * 64, 1)
     gemm_bf16_tn_big_kernel(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W, int ldw,
                             int N, int K, const uint16_t* __restrict__ bias, float* __restrict__ C, int ldc, int num_m,
                             int num_n, int w_wrap, size_t c_slice) {
-  using BT = BigTile<BM, NW>;
+  using BT = BigTile<BM, NW, BN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int b = blockIdx.x;
   int mt, nt;
@@ -290,38 +291,61 @@ __global__ void __launch_bounds__(NW * 64, 1)
   }
 }
 
-template <int BM, int MODE, int NW = 4>
+template <int BM, int MODE, int NW = 4, int BN = 256>
 static hipError_t launch_big(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
                              float* C, int ldc, int slices, int w_wrap, size_t c_slice, hipStream_t s) {
-  using BT = BigTile<BM, NW>;
+  using BT = BigTile<BM, NW, BN>;
   const int num_m = (M + BM - 1) / BM, num_n = (N + BT::kBN - 1) / BT::kBN;
   const int n_per_xcd = (num_n + kXcds - 1) / kXcds;
   const long blocks = MODE == kSplitK ? (long)num_m * num_n : (long)n_per_xcd * num_m * kXcds;
   if (blocks > 0x7FFFFFFF || slices > 65535) return hipErrorNotSupported;
   const size_t lds = (size_t)BT::kStages * BT::kStage;
-  const void* fn = reinterpret_cast<const void*>(gemm_bf16_tn_big_kernel<BM, MODE, NW>);
+  const void* fn = reinterpret_cast<const void*>(gemm_bf16_tn_big_kernel<BM, MODE, NW, BN>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_bf16_tn_big_kernel<BM, MODE, NW>), dim3((unsigned)blocks, (unsigned)slices), dim3(BT::kThreads),
+  hipLaunchKernelGGL((gemm_bf16_tn_big_kernel<BM, MODE, NW, BN>), dim3((unsigned)blocks, (unsigned)slices), dim3(BT::kThreads),
                      lds, s, static_cast<const uint16_t*>(A), lda, M, static_cast<const uint16_t*>(W), ldw, N, K,
                      static_cast<const uint16_t*>(bias), C, ldc, num_m, num_n, w_wrap, c_slice);
   return hipGetLastError();
 }
 
+// One M tile (M <= BM): num_n BM x 256 tiles on num_cu CUs (one workgroup
+// each) take ceil(num_n / num_cu) rounds.  When the last round would hold at
+// most half the CUs, its tiles run as twice as many BM x 128 tiles in a second
+// launch: each moves (BM + 128) / (BM + 256) of a wide tile's operand bytes
+// per K step, so the last round takes 2/3 (BM = 128) or 3/4 (BM = 256) of the
+// time, with no partial sums (Qwen3-4B LM head, 128 rows: 0.217 -> 0.203 ms;
+// Qwen3-8B, 48 / 64 / 128 rows: 0.332 / 0.337 / 0.354 -> 0.315 / 0.320 /
+// 0.331 ms).
+template <int BM, int NW>
+static hipError_t launch_one_m_tile(const void* A, int lda, int M, const void* W, int ldw, int N, int K,
+                                    const void* bias, float* C, int ldc, int num_cu, hipStream_t s) {
+  const int num_n = (N + 255) / 256;
+  const int tail = num_cu > 0 ? num_n % num_cu : 0;
+  if (M > BM || num_n < num_cu || tail == 0 || 2 * tail > num_cu)
+    return launch_big<BM, kPlain, NW>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
+  const int n_full = (num_n - tail) * 256;  // columns in the full rounds
+  hipError_t e = launch_big<BM, kPlain, NW>(A, lda, M, W, ldw, n_full, K, bias, C, ldc, 1, 0, 0, s);
+  if (e != hipSuccess) return e;
+  return launch_big<BM, kPlain, NW, 128>(A, lda, M, static_cast<const uint16_t*>(W) + (size_t)n_full * ldw, ldw,
+                                         N - n_full, K, bias ? static_cast<const uint16_t*>(bias) + n_full : nullptr,
+                                         C + n_full, ldc, 1, 0, 0, s);
+}
+
 hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
-                               float* C, int ldc, hipStream_t s) {
+                               float* C, int ldc, int num_cu, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % BigTile<256>::kBK) return hipErrorNotSupported;
   // 256 x 256 tiles with two waves per SIMD: one wave's fragment reads run
   // beside the other's products (Qwen3-8B LM head, 512 rows: 0.831 -> 0.802 ms
   // against one wave per SIMD)
-  // 33 .. 255 rows: 128 x 256 tiles, with 8 waves and the ping-pong loop for
+  if (M >= 256) return launch_one_m_tile<256, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
+  // 33 .. 255 rows: 128-row tiles, with 8 waves and the ping-pong loop for
   // long rows (Qwen3-8B LM head, K = 4096, at 48 / 64 / 128 rows: 0.359 /
   // 0.367 / 0.389 -> 0.330 / 0.334 / 0.352 ms), else 4 waves (Qwen3-4B, K =
   // 2560, 128 rows: 0.217 ms against 0.220 with 8)
-  if (M >= 256) return launch_big<256, kPlain, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
-  return K >= 4096 ? launch_big<128, kPlain, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s)
-                   : launch_big<128, kPlain, 4>(A, lda, M, W, ldw, N, K, bias, C, ldc, 1, 0, 0, s);
+  return K >= 4096 ? launch_one_m_tile<128, 8>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s)
+                   : launch_one_m_tile<128, 4>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
 }
 
 hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void* W, int ldw, int N, int kc,

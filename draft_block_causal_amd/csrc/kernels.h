@@ -31,9 +31,10 @@ hipError_t launch_p_partials(const void* A, int M, int lda, const void* w1, int 
                              float* ppart, const PSplit& ps, unsigned long long* z0, int n0, unsigned long long* z1,
                              int n1, hipStream_t s);
 
-// Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 32 == 0 (else hipErrorNotSupported).
+// Tiled bf16 matrix-core GEMM, C = A W^T (+bias), K % 32 == 0 (else hipErrorNotSupported);
+// num_cu: compute units of the device (sizes the last round of tiles).
 hipError_t launch_gemm_bf16_tn(const void* A, int lda, int M, const void* W, int ldw, int N, int K, const void* bias,
-                               float* C, int ldc, hipStream_t s);
+                               float* C, int ldc, int num_cu, hipStream_t s);
 // Split-K partial products: slice s of `slices` multiplies A columns s kc ..
 // s kc + kc - 1 by W columns (s kc) mod w_wrap .. and writes C + s c_slice.
 hipError_t launch_gemm_bf16_tn_splitk(const void* A, int lda, int M, const void* W, int ldw, int N, int kc,

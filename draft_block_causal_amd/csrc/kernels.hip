@@ -349,7 +349,7 @@ hipError_t launch_panel_gemm(int dtype, const void* A, int lda, int M, const voi
     if (e != hipErrorNotSupported) return e;
   }
   if (dtype == 1) {  // many rows: tiled matrix-core GEMM (W read once per XCD, re-used from L2)
-    const hipError_t e = launch_gemm_bf16_tn(A, lda, M, W, ldw, N, K, bias, C, ldc, s);
+    const hipError_t e = launch_gemm_bf16_tn(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);
     if (e != hipErrorNotSupported) return e;
   }
   if (dtype == 1) return panel_gemm_t<Bf16>(A, lda, M, W, ldw, N, K, bias, C, ldc, num_cu, s);

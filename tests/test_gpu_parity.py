@@ -451,6 +451,33 @@ def test_lm_head_tile_shapes(dev, batch, vocab, d):
     assert err <= LOGIT_TOL, f"base logits err {err}"
 
 
+@pytest.mark.parametrize("name,batch", [("qwen3_8b_b1_greedy", 8), ("qwen3_4b_b8_tied", 8), ("qwen3_8b_b1_greedy", 16)])
+def test_lm_head_narrow_last_round(dev, name, batch):
+    """128 or 256 rows against the full Qwen3 vocabulary: 594 tiles of M x 256
+    on 256 compute units leave a last round of 82, which runs as 163 tiles of
+    M x 128 in a second launch (8 waves at d = 4096, 4 at d = 2560), checked
+    against the oracle at every fifth column past the full rounds (all
+    rows), the 300 columns on either side of that boundary, and 4000 random
+    columns."""
+    import draft_block_causal_amd as D
+
+    w = S.get_workload(name).with_(batch=batch)
+    head_np, inp = workload_arrays(w)
+    head = device_head(w, dev)
+    base = D.domino_base_logits(head, _t(inp["hidden"], dev))
+    torch.cuda.synchronize()
+    V = w.vocab
+    got = base.cpu().numpy().reshape(batch * w.block, V)
+    n_full = (((V + 255) // 256) // 256) * 256 * 256  # columns of the full rounds on 256 CUs
+    cols = np.unique(np.concatenate([np.arange(n_full, V, 5), np.arange(n_full - 300, n_full + 300),
+                                     np.arange(V - 300, V), np.random.default_rng(5).integers(0, V, 4000)]))
+    hid = O.as_f64(inp["hidden"]).reshape(batch * w.block, -1)
+    ref = O.base_logits(hid, O.as_f64(head_np["lm_head"][cols]))
+    err = np.abs(got[:, cols] - ref).max()
+    log(f"{name} x {batch} blocks: {cols.size} columns x {batch * w.block} rows, max err {err:.2e}")
+    assert err <= LOGIT_DIAG_TOL, f"base logits err {err}"
+
+
 def test_sampled_small_temperature_and_ties(dev):
     _parity(_small("bf16", temperature=0.37, philox_seed=99), dev)
 
