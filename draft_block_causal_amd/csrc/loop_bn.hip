@@ -231,6 +231,25 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
     lane = tid & 63;
     grp = lane >> 4;
     col = lane & 15;
+    // P_i = W1[:, :d] h_i + b1 for the u rows this workgroup adds up in E
+    // (thread: row tid % 16 of blocks tid / 16 + 16 m): it does not depend on
+    // the tokens, so its loads are issued before the key polls and are in
+    // flight with them (issued after the gather, they added a second memory
+    // round trip to every position)
+    // The first kPReg slices are loaded into registers of their own (a
+    // runtime trip count made the compiler wait for each load before the
+    // next); they are added in slice order after the gather, then any further
+    // slices (d > 4096) one by one.
+    constexpr int kPairs = (NG * kGroup + 15) / 16;
+    constexpr int kPReg = 8;
+    float pr[kPairs][kPReg];
+#pragma unroll
+    for (int m = 0; m < kPairs; ++m) {
+      const int b = (tid >> 4) + m * 16, row = u * 16 + (tid & 15);
+#pragma unroll
+      for (int sl = 0; sl < kPReg; ++sl)
+        pr[m][sl] = b < B && sl < p.S ? p.ppart[((size_t)sl * B * K + (size_t)b * K + step) * kR + row] : 0.f;
+    }
     // ---------- A: tokens of position step - 1 ----------
     if (step == 0) {
       for (int b = tid; b < B; b += kThreads) s_tok[b] = min(max(p.x_t[b], 0), V - 1);
@@ -286,16 +305,15 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
       ok = false;
       break;
     }
-    // P_i = W1[:, :d] h_i + b1 for the u rows this workgroup adds up in E:
-    // loaded now, used there (thread: row tid % 16 of blocks tid / 16 + 16 m)
-    constexpr int kPairs = (NG * kGroup + 15) / 16;
     float pv[kPairs];
 #pragma unroll
     for (int m = 0; m < kPairs; ++m) {
       const int b = (tid >> 4) + m * 16, row = u * 16 + (tid & 15);
       float sum = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < kPReg; ++sl) sum += pr[m][sl];  // slices past S are zero
       if (b < B)
-        for (int sl = 0; sl < p.S; ++sl) sum += p.ppart[((size_t)sl * B * K + (size_t)b * K + step) * kR + row];
+        for (int sl = kPReg; sl < p.S; ++sl) sum += p.ppart[((size_t)sl * B * K + (size_t)b * K + step) * kR + row];
       pv[m] = sum;
     }
     // ---------- B: gates of this workgroup's units (thread: unit lane, blocks wave + 4 m) ----------
