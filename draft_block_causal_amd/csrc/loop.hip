@@ -845,18 +845,24 @@ __global__ void __launch_bounds__(256) u_kernel(DevLoop<T> p, int step) {
   const int b = m0 + (threadIdx.x >> 4), q = t * 16 + (threadIdx.x & 15);
   const size_t row = ((size_t)b * p.K + step) * p.r + q;
   // P (whole, or its S slices added in order) is read before the product, so
-  // that its loads are in flight with the product's
-  float ph = 0.f;
-  if (b < p.B) {
-    if (p.S > 0)
-      for (int sl = 0; sl < p.S; ++sl) ph += p.ppart[(size_t)sl * p.B * p.K * p.r + row];
-    else
-      ph = p.P[row];
-  }
+  // that its loads are in flight with the product's: the first kPReg slices
+  // each into a register of its own (with a runtime trip count the compiler
+  // waits for each load before issuing the next), added after the product
+  constexpr int kPReg = 8;
+  float pr[kPReg];
+#pragma unroll
+  for (int sl = 0; sl < kPReg; ++sl)
+    pr[sl] = b < p.B && (sl < p.S || (sl == 0 && p.S == 0))
+                 ? (p.S > 0 ? p.ppart[(size_t)sl * p.B * p.K * p.r + row] : p.P[row])
+                 : 0.f;
   // batch row b's state at this position: states[b][step][:], row stride K * H
   const float sum = block_rows_dot<T>(p.w1 + p.d, p.d + p.H, t * 16, p.states + (size_t)step * p.H, p.K * p.H, m0,
                                       p.B, p.H);
   if (b < p.B) {
+    float ph = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kPReg; ++sl) ph += pr[sl];  // slices past S are zero
+    for (int sl = kPReg; sl < p.S; ++sl) ph += p.ppart[(size_t)sl * p.B * p.K * p.r + row];
     const float pre = ph + sum;
     p.u[(size_t)b * p.r + q] = pre * sigmoidf_(pre);
   }
