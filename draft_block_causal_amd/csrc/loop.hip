@@ -748,7 +748,25 @@ __global__ void __launch_bounds__(256) gates_kernel(DevLoop<T> p, int step) {
   const int H = p.H, G3 = 3 * H, KS = p.KS;
   const int b = blockIdx.y, j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= H) return;
+  // the loads that do not depend on the token first, so that they are in
+  // flight with the token's key load and the table row read after it
   float a3[3], c3[3] = {0.f, 0.f, 0.f};
+  float gp = 0.f;
+  if (step > 0) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) c3[q] = p.part_hh[(size_t)b * G3 + q * H + j];
+    gp = p.states[((size_t)b * p.K + step - 1) * H + j];
+  }
+  // b_hh loaded unconditionally (from W_hh, 3H x H elements, when there is
+  // no bias) and selected after: a load on one side of a branch made the
+  // compiler wait for every load in flight after each
+  const typename T::elem* bsrc = p.b_hh ? p.b_hh : p.w_hh;
+  float bh[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const float v = T::to_f32(bsrc[q * H + j]);
+    bh[q] = p.b_hh ? v : 0.f;
+  }
   if (p.table) {
     const float* trow = p.table + (size_t)step_token(p, step, b) * G3;
 #pragma unroll
@@ -761,14 +779,8 @@ __global__ void __launch_bounds__(256) gates_kernel(DevLoop<T> p, int step) {
       a3[q] = x + (p.b_ih ? T::to_f32(p.b_ih[q * H + j]) : 0.f);
     }
   }
-  float gp = 0.f;
-  if (step > 0) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q) c3[q] = p.part_hh[(size_t)b * G3 + q * H + j];
-    gp = p.states[((size_t)b * p.K + step - 1) * H + j];
-  }
-#pragma unroll
-  for (int q = 0; q < 3; ++q) c3[q] += p.b_hh ? T::to_f32(p.b_hh[q * H + j]) : 0.f;
+  for (int q = 0; q < 3; ++q) c3[q] += bh[q];
   const float rg = sigmoidf_(a3[0] + c3[0]);
   const float zg = sigmoidf_(a3[1] + c3[1]);
   const float ng = tanhf(a3[2] + rg * c3[2]);
