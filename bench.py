@@ -634,7 +634,8 @@ def main() -> int:
         achieved = alg / (draft_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "traffic": measured_traffic(kernel_source_hash(FUSED_KERNEL_SOURCES), FUSED_TRAFFIC_FILE),
+                "traffic": measured_traffic(kernel_source_hash(FUSED_KERNEL_SOURCES), FUSED_TRAFFIC_FILE,
+                                            workload=w.name),
                 "algorithmic_bytes": alg}
     elif flops / alg > RIDGE_FLOP_PER_BYTE:
         achieved = flops / (lm_ms * 1e-3) / 1e12

@@ -40,7 +40,8 @@ def test_traffic_record_matches_current_source_or_is_ignored():
     assert gemm is None or 1.0 <= gemm / alg32 < 1.3
     # the single-block loop that streams the LM head itself: within 10 % of
     # the call's compulsory bytes without base logits in HBM
-    fused = bench.measured_traffic(bench.kernel_source_hash(bench.FUSED_KERNEL_SOURCES), bench.FUSED_TRAFFIC_FILE)
+    fused = bench.measured_traffic(bench.kernel_source_hash(bench.FUSED_KERNEL_SOURCES), bench.FUSED_TRAFFIC_FILE,
+                                   workload="qwen3_8b_b1_greedy")
     alg = bench.block_algorithmic_bytes(1, 16, 4096, 151936, 1024, 256, 2, base_in_hbm=False)
     assert fused is None or abs(fused / alg - 1.0) < 0.1
 
