@@ -499,6 +499,18 @@ __device__ bool w2_sample_block(const DevLoop<T>& p, int step, int bx, int nbx, 
 // ---------------------------------------------------------------------------
 template <class T>
 __device__ void hh_unit(const DevLoop<T>& p, int step, int t, int m0);
+template <class T, int NT, int MT>
+__device__ void hh_block(const DevLoop<T>& p, int step, int n0, int m0, float* red);
+// W_hh tiling of the W2 launch's units: 16 NT gate rows x 16 MT batch rows,
+// and the LDS bytes of their reduction.  64 x 32 only where the W2 tile loop
+// already runs two waves per SIMD (64-row slices); with 16- and 32-row
+// slices 32 x 16 (more accumulators would take the launch from three waves
+// per SIMD to two).
+template <int MW>
+struct HhTiling {
+  static constexpr int NT = MW >= 4 ? 4 : 2, MT = MW >= 4 ? 2 : 1;
+  static constexpr size_t kRedBytes = (size_t)4 * 16 * MT * (16 * NT + 1) * sizeof(float);
+};
 
 // VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
 // logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
@@ -524,14 +536,18 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
   // (trip counts are uniform over the workgroup: hh_unit synchronises it)
   const int hx = gridDim.x - gx_w2;  // W_hh-only workgroups per batch slice
   if (hh_step > 0) {
-    const int t3 = (3 * p.H) >> 4;
-    const int units = t3 * ((B + 15) >> 4);
+    // units of HhTiling<MT>::NT x ::MT 16-row tiles; the reduction uses the
+    // LDS that u is staged into below
+    using HT = HhTiling<MT>;
+    const int tn = (3 * p.H + 16 * HT::NT - 1) / (16 * HT::NT);
+    const int units = tn * ((B + 16 * HT::MT - 1) / (16 * HT::MT));
+    float* hred = reinterpret_cast<float*>(smem);
     if (hx == 0) {
       for (int unit = blockIdx.y * gridDim.x + blockIdx.x; unit < units; unit += gridDim.x * gridDim.y)
-        hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+        hh_block<T, HT::NT, HT::MT>(p, hh_step, (unit % tn) * 16 * HT::NT, (unit / tn) * 16 * HT::MT, hred);
     } else if ((int)blockIdx.x >= gx_w2) {
       for (int unit = blockIdx.y * hx + (blockIdx.x - gx_w2); unit < units; unit += hx * gridDim.y)
-        hh_unit(p, hh_step, unit % t3, (unit / t3) * 16);
+        hh_block<T, HT::NT, HT::MT>(p, hh_step, (unit % tn) * 16 * HT::NT, (unit / tn) * 16 * HT::MT, hred);
     }
   }
   if ((int)blockIdx.x >= gx_w2) return;
@@ -896,6 +912,102 @@ __global__ void __launch_bounds__(256) hh_kernel(DevLoop<T> p, int step) {
   hh_unit(p, step, blockIdx.x, blockIdx.y * 16);
 }
 
+// W_hh g_{step-1} for gate rows n0 .. n0 + 16 NT - 1 and batch rows m0 ..
+// m0 + 16 MT - 1 (one workgroup; every thread must call it; red: LDS for
+// 4 x 16 MT x (16 NT + 1) floats).  A unit of 16 rows x 16 rows reads its
+// 16 state rows (64 KB at H = 1024) for 16 gate rows of W_hh (32 KB); this
+// one reads 16 MT state rows for 16 NT gate rows, so the states are read
+// 3H / (16 NT) times per position instead of 3H / 16 (Qwen3 heads, 128
+// blocks: 147 MB of cache traffic a position with 16 x 16 units, 49 MB with
+// 64 x 32).  Same sums as hh_unit, in the same order: each wave one
+// contiguous quarter of K in step order, the four partials added in wave
+// order.  U steps of loads are in flight at once (addresses clamped, so
+// every load is unconditional).
+template <class T, int NT, int MT>
+__device__ void hh_block(const DevLoop<T>& p, int step, int n0, int m0, float* red) {
+  using E = typename T::elem;
+  constexpr int EPF = T::kPer16B;
+  constexpr int KSTEP = 4 * EPF;
+  // steps of loads in flight, within the registers of the W2 launch's tile loop
+  constexpr int U = 2;
+  const int H = p.H, G3 = 3 * H;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+  const int nsteps = H / KSTEP, per_wave = (nsteps + 3) / 4;
+  const int s_begin = wave * per_wave, s_end = min(nsteps, s_begin + per_wave);
+  const unsigned char* wrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    wrow[nt] = reinterpret_cast<const unsigned char*>(p.w_hh + (size_t)min(n0 + nt * 16 + col, G3 - 1) * H) + grp * 16;
+  const float* X = p.states + (size_t)(step - 1) * H;
+  const float* xrow[MT];
+  bool xlive[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int b = m0 + mt * 16 + col;
+    xlive[mt] = b < p.B;
+    xrow[mt] = X + (size_t)min(b, p.B - 1) * p.K * H + grp * EPF;
+  }
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_begin; s0 < s_end; s0 += U) {
+    u32x4 w[U][NT];
+    float x[U][MT][EPF];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, s_end - 1);  // past s_end: a repeated step, multiplied by zero below
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = ld16(wrow[nt] + (size_t)s * KSTEP * sizeof(E));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < EPF; e += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(xrow[mt] + s * KSTEP + e);
+          x[u][mt][e] = v[0];
+          x[u][mt][e + 1] = v[1];
+          x[u][mt][e + 2] = v[2];
+          x[u][mt][e + 3] = v[3];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = s0 + u < s_end;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float xs[EPF];
+#pragma unroll
+        for (int e = 0; e < EPF; ++e) xs[e] = in && xlive[mt] ? x[u][mt][e] : 0.f;
+        ActFrag<T> a;
+        a.from_f32(xs);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = a.mma(acc[nt][mt], w[u][nt]);
+      }
+    }
+  }
+  // partials [wave][batch row][gate row]
+  constexpr int RS = 16 * NT + 1;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[(wave * 16 * MT + mt * 16 + grp * 4 + j) * RS + nt * 16 + col] = acc[nt][mt][j];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * MT * 16 * NT; i += blockDim.x) {
+    const int mm = i / (16 * NT), nn = i - mm * (16 * NT);
+    const int b = m0 + mm, n = n0 + nn;
+    float sum = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) sum += red[(wv * 16 * MT + mm) * RS + nn];
+    if (b < p.B && n < G3) p.part_hh[(size_t)b * G3 + n] = sum;
+  }
+  __syncthreads();  // red is reused by the caller
+}
+
+
 // ---------------------------------------------------------------------------
 // three-kernels-per-position schedule
 // ---------------------------------------------------------------------------
@@ -1086,7 +1198,7 @@ constexpr int kW2Stages = 2;
 template <class T, int MW, int NS>
 static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int ntiles = (p.V + 15) / 16;
-  const size_t lds = w2_stream_lds_bytes<T, MW>(p.r);
+  const size_t lds = std::max(w2_stream_lds_bytes<T, MW>(p.r), HhTiling<MW>::kRedBytes);
   auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true, kW2Stages>
                             : w2_stream_kernel<T, MW, NS, false, kW2Stages>;
   // one workgroup per compute unit for each slice of 16 MW batch rows: each
@@ -1103,7 +1215,8 @@ static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), 256, lds) !=
       hipSuccess)
     per_cu = 1;
-  const long units = (long)(3 * p.H / 16) * ((p.B + 15) / 16);
+  using HT = HhTiling<MW>;
+  const long units = (long)((3 * p.H + 16 * HT::NT - 1) / (16 * HT::NT)) * ((p.B + 16 * HT::MT - 1) / (16 * HT::MT));
   const long hx = (units + gy - 1) / gy;
   const bool own = (long)(gx + hx) * gy <= (long)per_cu * num_cu;
   return {kern, lds, dim3(gx + (own ? (int)hx : 0), gy), gx, true};
