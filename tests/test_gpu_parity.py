@@ -368,6 +368,15 @@ def test_batch_tile_boundaries(dev, batch, mode, monkeypatch):
     _parity(_small("bf16", batch=batch, vocab=777, block=3, d=96, gru_hidden=64), dev)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_w_hh_units_partial_gate_tile(dev, dtype, monkeypatch):
+    # 65 blocks on the three-kernel schedule: the W2 launch forms W_hh g in
+    # units of 64 gate rows x 32 batch rows; with H = 32 the 96 gate rows end
+    # inside the second unit, and the last batch group holds one block
+    monkeypatch.setenv("DOMINO_LOOP", "multi")
+    _parity(_small(dtype, batch=65, vocab=777, block=3, d=96, gru_hidden=32), dev)
+
+
 def test_lm_head_more_tiles_than_lds(dev):
     """Base logits when a workgroup finishes more 16-row tiles than it can hold.
 
