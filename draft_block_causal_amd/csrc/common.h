@@ -133,12 +133,13 @@ __device__ __forceinline__ u32x4 philox4(uint64_t seed, uint32_t offset, uint32_
   uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t lo0 = 0xD2511F53u * x0, hi0 = __umulhi(0xD2511F53u, x0);
-    const uint32_t lo1 = 0xCD9E8D57u * x2, hi1 = __umulhi(0xCD9E8D57u, x2);
-    x0 = hi1 ^ x1 ^ k0;
-    x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
-    x3 = lo0;
+    // each product as one 64-bit result (one v_mad_u64_u32 instead of a
+    // low and a high multiply)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0, p1 = (uint64_t)0xCD9E8D57u * x2;
+    x0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+    x1 = (uint32_t)p1;
+    x2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+    x3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

@@ -514,13 +514,14 @@ struct HhTiling {
 
 // VEC (V % 16 == 0: no partial tile, rows 16-B aligned): a lane's four base
 // logits are one 16-B load and its four b2 entries one 8-B (bf16) load.
+// LG: the logits are stored too (the caller asked for them).
 // Workgroups x < gx_w2 of each batch slice stream W2.  hh_step > 0: the
 // 3H/16 x ceil(B/16) 16 x 16 units of W_hh g for position hh_step (g of this
 // position is final) are formed here too, which takes that product off the
 // token-to-token path: by the workgroups x >= gx_w2, which do nothing else,
 // when the grid has them, else by the W2 workgroups before their tiles
 // (unit q in workgroup q mod the grid size).
-template <class T, int MT, int NS, bool VEC, int D>
+template <class T, int MT, int NS, bool VEC, int D, bool LG>
 __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, int hh_step, int gx_w2) {
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
@@ -608,6 +609,16 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
         live > 0 ? ((live - 1) * K * V + V) * 4 : 0, kRsrcWord3);
   }
   const int boff = eb * K * V * 4;
+  // the logits (when the caller asks for them) share that layout: rows past
+  // the batch, and with a null pointer every row, lie past the descriptor's
+  // end, where stores are dropped
+  __amdgpu_buffer_rsrc_t lrs[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int live = p.logits ? min(max(B - (m0 + mt * 16), 0), 16) : 0;
+    lrs[mt] = __builtin_amdgcn_make_buffer_rsrc(p.logits + (live > 0 ? ((size_t)(m0 + mt * 16) * K + step) * V : 0),
+                                                (short)0, live > 0 ? ((live - 1) * K * V + V) * 4 : 0, kRsrcWord3);
+  }
   const __amdgpu_buffer_rsrc_t b2rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<E*>(p.b2 ? p.b2 : p.w2), (short)0, p.b2 ? V * (int)sizeof(E) : 0, kRsrcWord3);
 
@@ -660,15 +671,25 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // u's operands come from LDS in the order (K step, slice, part); kAhead
+    // reads stay in flight ahead of the product that takes them (read one at a
+    // time, every product waited out a read's latency), the order pinned by
+    // scheduling barriers
+    constexpr int kF = NS * MT * NPARTS, kAhead = kF < 8 ? kF : 8;
+    auto frag = [&](int i) {
+      const int kb = i / (MT * NPARTS), mt = (i / NPARTS) % MT, q = i % NPARTS;
+      return ld16(smem + (q * rows + mt * 16 + col) * lds_stride + grp * 16 + kb * 64);
+    };
+    u32x4 a[kF];
 #pragma unroll
-    for (int kb = 0; kb < NS; ++kb)
+    for (int i = 0; i < kAhead; ++i) a[i] = frag(i);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int q = 0; q < NPARTS; ++q) {
-          const u32x4 a = ld16(smem + (q * rows + mt * 16 + col) * lds_stride + grp * 16 + kb * 64);
-          acc[mt] = mma16<T>(acc[mt], a, st.w[kb]);
-        }
+    for (int i = 0; i < kF; ++i) {
+      if (i + kAhead < kF) a[i + kAhead] = frag(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[(i / NPARTS) % MT] = mma16<T>(acc[(i / NPARTS) % MT], a[i], st.w[i / (MT * NPARTS)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int v0 = t * 16 + 4 * eq;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -680,17 +701,40 @@ __global__ void __launch_bounds__(256) w2_stream_kernel(DevLoop<T> p, int step, 
       // give no key): loads that only one side of a branch consumed would make
       // the compiler wait for them before the next prefetch reuses the registers
       const int b = m0 + mt * 16 + eb;
-      u32x4 words = {0u, 0u, 0u, 0u};
-      if (p.sampled) words = philox4(p.seed, p.offset, (uint32_t)b, (uint32_t)step, (uint32_t)(v0 >> 2));
-      const size_t o = ((size_t)b * K + step) * V;
+      float L[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L[i] = st.base[mt][i] + (d[i] + st.b2[i]);
+      // stores through the descriptor: no per-lane branch (entries past V get
+      // an offset past its end)
+      if constexpr (LG) {
+        if constexpr (VEC) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(L[0]), __float_as_uint(L[1]), __float_as_uint(L[2]), __float_as_uint(L[3])},
+              lrs[mt], boff + v0 * 4, 0, 0);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L[i]), lrs[mt],
+                                                  v0 + i < V ? boff + (v0 + i) * 4 : (int)0x80000000u, 0, 0);
+        }
+      }
+      // one uniform branch for the four entries' scores
+      float sc[4];
+      if (p.sampled) {
+        const u32x4 words = philox4(p.seed, p.offset, (uint32_t)b, (uint32_t)step, (uint32_t)(v0 >> 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = L[i] * p.inv_temp + gumbel_from_word(words[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = L[i];
+      }
+      // lanes of rows past the batch keep keys that are never merged (the
+      // reduction below skips those rows); entries past V (a partial last
+      // tile) give no key
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int v = v0 + i;
-        const bool ok = b < B && v < V;
-        const float L = st.base[mt][i] + (d[i] + st.b2[i]);
-        if (p.logits && ok) p.logits[o + v] = L;
-        const float s = p.sampled ? L * p.inv_temp + gumbel_from_word(words[i]) : L;
-        const unsigned long long k = ok ? argmax_key(s, (uint32_t)v) : 0ull;
+        unsigned long long k = argmax_key(sc[i], (uint32_t)(v0 + i));
+        if constexpr (!VEC) k = v0 + i < V ? k : 0ull;
         best[mt] = k > best[mt] ? k : best[mt];
       }
     }
@@ -1199,8 +1243,12 @@ template <class T, int MW, int NS>
 static W2Launch<T, MW> w2_stream_plan(const DevLoop<T>& p, int num_cu) {
   const int ntiles = (p.V + 15) / 16;
   const size_t lds = std::max(w2_stream_lds_bytes<T, MW>(p.r), HhTiling<MW>::kRedBytes);
-  auto kern = p.V % 16 == 0 ? w2_stream_kernel<T, MW, NS, true, kW2Stages>
-                            : w2_stream_kernel<T, MW, NS, false, kW2Stages>;
+  // (a kernel of its own stores the logits: a store that might be in flight
+  // costs the tile loop exact waits on its prefetches)
+  auto kern = p.V % 16 == 0 ? (p.logits ? w2_stream_kernel<T, MW, NS, true, kW2Stages, true>
+                                        : w2_stream_kernel<T, MW, NS, true, kW2Stages, false>)
+                            : (p.logits ? w2_stream_kernel<T, MW, NS, false, kW2Stages, true>
+                                        : w2_stream_kernel<T, MW, NS, false, kW2Stages, false>);
   // one workgroup per compute unit for each slice of 16 MW batch rows: each
   // wave then streams ~ntiles / (4 #CU) tiles, which amortises staging u and
   // the key reduction (measured at Qwen3 shapes, B = 8 / 32 / 128: 19 / 26 /
