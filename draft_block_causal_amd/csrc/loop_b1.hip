@@ -566,11 +566,22 @@ __global__ void __launch_bounds__(kThreads, 1) draft_b1_kernel(Params p) {
       f32x4 acc[kRtPerWave];
 #pragma unroll
       for (int i = 0; i < kRtPerWave; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < ksu; ++ks) {
+      // (the plan admits H = kUnitWGs kUnitMax only, so ksu = kKsu) a
+      // k-step's operand reads are all issued before its products: read one
+      // at a time, each product waited out a read's latency (all k-steps'
+      // reads at once would not fit in the registers left)
+      constexpr int kKsu = kUnitMax / 32;
+#pragma unroll
+      for (int ks = 0; ks < kKsu; ++ks) {
         const u32x4 a = row_frag(uhl, units, ks * 32, col, grp, zero);
+        u32x4 wf[kRtPerWave];
 #pragma unroll
         for (int i = 0; i < kRtPerWave; ++i)
-          acc[i] = mma16<Bf16>(acc[i], a, ld16(pool + ((size_t)((wave * kRtPerWave + i) * ksu + ks) * 64 + lane) * 16));
+          wf[i] = ld16(pool + ((size_t)((wave * kRtPerWave + i) * kKsu + ks) * 64 + lane) * 16);
+#pragma unroll
+        for (int i = 0; i < kRtPerWave; ++i) acc[i] = mma16<Bf16>(acc[i], a, wf[i]);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRtPerWave + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kRtPerWave, 0);
       }
       if (grp == 0)
 #pragma unroll

@@ -358,14 +358,22 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
         f32x4 acc[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // every operand read is issued before the first product (read one
+        // at a time, each product waited out a read's latency)
+        u32x4 a[2], wf[2][4];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 a = ld16(reinterpret_cast<const unsigned char*>(ghl) +
-                               (size_t)(gb * 16 + col) * kGStride * 2 + ks * 64 + grp * 16);
+          a[ks] = ld16(reinterpret_cast<const unsigned char*>(ghl) + (size_t)(gb * 16 + col) * kGStride * 2 + ks * 64 +
+                       grp * 16);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[t] = mma16<Bf16>(acc[t], a, ld16(w1f + ((size_t)((wave * 4 + t) * 2 + ks) * 64 + lane) * 16));
+          for (int t = 0; t < 4; ++t) wf[ks][t] = ld16(w1f + ((size_t)((wave * 4 + t) * 2 + ks) * 64 + lane) * 16);
         }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[t] = mma16<Bf16>(acc[t], a[ks], wf[ks][t]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         const int b0 = gb * kGroup + 2 * grp;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -501,12 +509,33 @@ __device__ void unit_role(const Params& p, unsigned char* smem, bool& ok) {
           f32x4 acc[kHhTiles];
 #pragma unroll
           for (int tt = 0; tt < kHhTiles; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          auto rd = [&](int s) {
+            return ld16(reinterpret_cast<const unsigned char*>(hha) + (size_t)col * kHhStride * 2 + s * 64 + grp * 16);
+          };
+          if constexpr (NG > 1) {
+            // two groups: the state operand of k-step s + 3 is read while
+            // step s is multiplied (order pinned by scheduling barriers;
+            // 16 blocks: draft call 0.738 -> 0.724 ms; with one group the
+            // pinned order measured slower, 0.552 -> 0.559 ms at 8 blocks)
+            constexpr int kAhead = 3;
+            u32x4 a[kKH];
 #pragma unroll
-          for (int s = 0; s < kKH; ++s) {
-            const u32x4 a = ld16(reinterpret_cast<const unsigned char*>(hha) + (size_t)col * kHhStride * 2 + s * 64 +
-                                 grp * 16);
+            for (int s = 0; s < kAhead; ++s) a[s] = rd(s);
 #pragma unroll
-            for (int tt = 0; tt < kHhTiles; ++tt) acc[tt] = mma16<Bf16>(acc[tt], a, whh[tt][s]);
+            for (int s = 0; s < kKH; ++s) {
+              if (s + kAhead < kKH) a[s + kAhead] = rd(s + kAhead);
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int tt = 0; tt < kHhTiles; ++tt) acc[tt] = mma16<Bf16>(acc[tt], a[s], whh[tt][s]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < kKH; ++s) {
+              const u32x4 a = rd(s);
+#pragma unroll
+              for (int tt = 0; tt < kHhTiles; ++tt) acc[tt] = mma16<Bf16>(acc[tt], a, whh[tt][s]);
+            }
           }
           const int b0 = gb * kGroup + 2 * grp;
 #pragma unroll
