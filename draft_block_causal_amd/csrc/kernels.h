@@ -206,6 +206,13 @@ struct GruBackwardPlan {
   // (xs [R][2H] bf16) and S split-K partials (cpart [S][R][3H] float32)
   int S;
   size_t xs, cpart;
+  // bf16 heads: the weight gradients on the matrix cores, operands re-laid
+  // with the rows (padded to Rp, a multiple of 32) along K: daT [3H][2 Rp]
+  // (da hi | lo), eT [d][2 Rp] (the embedding rows twice), dcT [3H][3 Rp]
+  // (dc hi | hi | lo), gT [H][3 Rp] (g_prev hi | lo | hi), and the bias
+  // sums' per-64-row partials bpart [2][Rp / 64][3H]
+  int Rp;
+  size_t daT, eT, dcT, gT, bpart;
 };
 inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -247,6 +254,18 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
     off += up(R * 2 * H * 2);
     p.cpart = off;
     off += up((size_t)p.S * R * G3 * 4);
+    p.Rp = (int)((R + 31) / 32 * 32);
+    const size_t Rp = (size_t)p.Rp;
+    p.daT = off;
+    off += up(G3 * 2 * Rp * 2);
+    p.eT = off;
+    off += up((size_t)d * 2 * Rp * 2);
+    p.dcT = off;
+    off += up(G3 * 3 * Rp * 2);
+    p.gT = off;
+    off += up((size_t)H * 3 * Rp * 2);
+    p.bpart = off;
+    off += up(2 * ((Rp + 63) / 64) * G3 * 4);
   }
   p.total = off;
   return p;

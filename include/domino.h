@@ -373,9 +373,11 @@ int domino_correction_backward_workspace_size(const domino_head *head, int32_t b
  * d_states [batch, block, H] float32; outputs float32, 4-byte aligned.
  * workspace   device scratch of domino_gru_backward_workspace_size() bytes,
  *             256-byte aligned.
- * batch in 0 … 128 (0 is a no-op).  Arithmetic: float32 (the input
- * pre-activations W_ih e of bf16 heads on the matrix cores), every sum in a
- * fixed order.
+ * batch in 0 … 128 (0 is a no-op).  Arithmetic: float32, every sum in a
+ * fixed order; for bf16 heads the input pre-activations W_ih e, and from
+ * 128 rows (batch x block) on the two weight gradients, run on the matrix
+ * cores, float32 factors split as bf16 hi + lo (the lo·lo term dropped, about
+ * 2^-16 relative).
  */
 int domino_gru_backward(const domino_head *head, int32_t batch, const int32_t *x_t, const int32_t *teacher,
                         const float *gru_states, const float *d_states, float *d_w_ih, float *d_w_hh,

@@ -61,9 +61,32 @@ def _run(dev, w, batch, seed):
 
 
 @pytest.mark.parametrize("name,batch", [("tiny_stress_b4", 4), ("qwen3_8b_b1_greedy", 1), ("qwen3_8b_b1_greedy", 2),
-                                        ("qwen3_8b_b1_greedy", 20)])
+                                        ("qwen3_8b_b1_greedy", 9), ("qwen3_8b_b1_greedy", 20)])
 def test_gru_backward_matches_oracle(dev, name, batch):
+    # (from 128 rows the bf16 weight gradients run on the matrix cores; 9
+    # blocks: 144 rows, padded to 160 along the GEMMs' K)
     _run(dev, S.get_workload(name), batch, seed=batch + 50)
+
+
+def _small_bf16():
+    # every matrix-core tile of the weight gradients partial: 3H = 192, d = 96, H = 64
+    return S.Workload(name="small_bf16", batch=3, block=5, d=96, vocab=777, gru_hidden=64, rank=32, dtype="bf16",
+                      tied=False, temperature=0.0, init="fanin")
+
+
+@pytest.mark.parametrize("batch", [3, 27, 40])
+def test_gru_backward_small_bf16_head(dev, batch):
+    # 15 rows (float32 outer products); 135 and 200 rows on the matrix cores
+    # (K padded to 160 / 224: the last 64-row tile holds 7 / 8 rows)
+    _run(dev, _small_bf16(), batch, seed=batch + 80)
+
+
+def test_gru_backward_repeatable_bf16(dev):
+    w = S.get_workload("qwen3_8b_b1_greedy")
+    a = _run(dev, w, 9, seed=62)
+    b = _run(dev, w, 9, seed=62)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
 
 
 def test_gru_backward_repeatable(dev):
