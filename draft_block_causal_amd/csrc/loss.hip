@@ -111,14 +111,14 @@ __global__ void __launch_bounds__(kLseThreads) loss_grad_kernel(int K, int V, co
       if (grad_base) {
         const float4 x = *reinterpret_cast<const float4*>(base + o + v);
         *reinterpret_cast<float4*>(grad_base + o + v) =
-            float4{cb * (expf(x.x - l.x) - h0), cb * (expf(x.y - l.x) - h1), cb * (expf(x.z - l.x) - h2),
-                   cb * (expf(x.w - l.x) - h3)};
+            float4{cb * (exp_hw(x.x - l.x) - h0), cb * (exp_hw(x.y - l.x) - h1), cb * (exp_hw(x.z - l.x) - h2),
+                   cb * (exp_hw(x.w - l.x) - h3)};
       }
       if (grad_final) {
         const float4 x = *reinterpret_cast<const float4*>(final_ + o + v);
         *reinterpret_cast<float4*>(grad_final + o + v) =
-            float4{cf * (expf(x.x - l.y) - h0), cf * (expf(x.y - l.y) - h1), cf * (expf(x.z - l.y) - h2),
-                   cf * (expf(x.w - l.y) - h3)};
+            float4{cf * (exp_hw(x.x - l.y) - h0), cf * (exp_hw(x.y - l.y) - h1), cf * (exp_hw(x.z - l.y) - h2),
+                   cf * (exp_hw(x.w - l.y) - h3)};
       }
     }
     vs = v0 + 4 * n4;
@@ -127,11 +127,11 @@ __global__ void __launch_bounds__(kLseThreads) loss_grad_kernel(int K, int V, co
     const float hot = v == y ? 1.f : 0.f;
     if (grad_base) {
       const float x = base[o + v];
-      grad_base[o + v] = cb * (expf(x - l.x) - hot);
+      grad_base[o + v] = cb * (exp_hw(x - l.x) - hot);
     }
     if (grad_final) {
       const float x = final_[o + v];
-      grad_final[o + v] = cf * (expf(x - l.y) - hot);
+      grad_final[o + v] = cf * (exp_hw(x - l.y) - hot);
     }
   }
 }

@@ -75,8 +75,8 @@ __global__ void __launch_bounds__(kVThreads) verify_draw_kernel(int K, int V, in
   // accept test of every drafted position; n = the first that fails
   for (int i = tid; i < K; i += kVThreads) {
     const int y = min(max(tokens[(size_t)b * K + i], 0), V - 1);
-    const float pt = expf(target[((size_t)b * (K + 1) + i) * V + y] * inv_t - lse_t[i]);
-    const float pd = expf(draft[((size_t)b * K + i) * V + y] * inv_t - lse_d[i]);
+    const float pt = exp_hw(target[((size_t)b * (K + 1) + i) * V + y] * inv_t - lse_t[i]);
+    const float pd = exp_hw(draft[((size_t)b * K + i) * V + y] * inv_t - lse_d[i]);
     const float u = uniform_from_word(philox_word(seed, offset, (uint32_t)b, (uint32_t)i, 0u));
     if (!(u * pd < pt)) atomicMin(&s_n, i);
   }
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(kVThreads) verify_draw_kernel(int K, int V, in
     const float g = gumbel_from_word(philox_word(seed, offset + 1u, (uint32_t)b, (uint32_t)n, (uint32_t)v));
     float sc;
     if (n < K) {
-      const float q = expf(tr[v] * inv_t - lt) - expf(dr[v] * inv_t - ld);
+      const float q = exp_hw(tr[v] * inv_t - lt) - exp_hw(dr[v] * inv_t - ld);
       sc = q > 0.f ? logf(q) + g : -INFINITY;
     } else {
       sc = tr[v] * inv_t + g;
