@@ -972,8 +972,10 @@ __device__ void hh_block(const DevLoop<T>& p, int step, int n0, int m0, float* r
   using E = typename T::elem;
   constexpr int EPF = T::kPer16B;
   constexpr int KSTEP = 4 * EPF;
-  // steps of loads in flight, within the registers of the W2 launch's tile loop
-  constexpr int U = 2;
+  // steps of loads in flight: 128 VGPRs of operands, within the registers of
+  // the W2 launch's tile loop (2 steps before: Qwen3-8B draft call at 128
+  // blocks 1.033 -> 1.021 ms, unchanged at 32)
+  constexpr int U = 128 / (4 * NT + MT * EPF) < 1 ? 1 : 128 / (4 * NT + MT * EPF);
   const int H = p.H, G3 = 3 * H;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int grp = lane >> 4, col = lane & 15;
