@@ -248,7 +248,7 @@ extern "C" int domino_correction_backward_workspace_size(const domino_head* h, i
   if (st != DOMINO_OK) return st;
   if (batch < 0) return DOMINO_ERR_SHAPE;
   if (batch > domino::kMaxBatch || h->rank > 512) return DOMINO_ERR_UNSUPPORTED;
-  *bytes = batch == 0 ? 0 : domino::backward_plan(batch * h->block, h->rank, h->vocab, h->dtype, h->d + h->gru_hidden).total;
+  *bytes = batch == 0 ? 0 : domino::backward_plan(batch * h->block, h->rank, h->vocab, h->dtype, h->d + h->gru_hidden, h->gru_hidden).total;
   return DOMINO_OK;
 }
 
@@ -278,7 +278,7 @@ extern "C" int domino_correction_backward(const domino_head* h, int32_t batch, c
   a.d_b1 = d_b1;
   a.d_states = d_states;
   a.workspace = workspace;
-  a.plan = domino::backward_plan(a.R, a.r, a.V, a.dtype, a.d + a.H);
+  a.plan = domino::backward_plan(a.R, a.r, a.V, a.dtype, a.d + a.H, a.H);
   return hip_status(domino::launch_correction_backward(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -43,6 +43,159 @@ __device__ __forceinline__ float bw_wave_sum(float x) {
   return x;
 }
 
+// bf16 heads: z and u of 16 rows (blockIdx.y) x 16 bottleneck rows
+// (blockIdx.x) on the matrix cores, [h ; g] against W1's rows: the hidden
+// part with exact bf16 operands, the state part split hi + lo (as in the
+// loop's u).  The K steps of each part are split over the four waves in
+// order, kZuU steps of loads in flight per wave, and the wave partials added
+// in wave order.  d and H multiples of 32.
+constexpr int kZuU = 8;
+__global__ void __launch_bounds__(kBwThreads) bw_zu_kernel(int R, int d, int H, int r,
+                                                           const uint16_t* __restrict__ hidden,
+                                                           const float* __restrict__ states,
+                                                           const uint16_t* __restrict__ w1,
+                                                           const uint16_t* __restrict__ b1, float* __restrict__ z,
+                                                           float* __restrict__ u) {
+  __shared__ float red[kBwWaves][16][17];
+  const int q0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
+  const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int n = d + H;
+  // (rows past R and W1 rows past r read clamped rows; their outputs are not stored)
+  const int row = min(m0 + col, R - 1), qrow = min(q0 + col, r - 1);
+  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(w1 + (size_t)qrow * n) + grp * 16;
+  const unsigned char* hrow = reinterpret_cast<const unsigned char*>(hidden + (size_t)row * d) + grp * 16;
+  const float* grow = states + (size_t)row * H + grp * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int ns = d / 32, per = (ns + kBwWaves - 1) / kBwWaves, sb = wave * per, se = min(ns, sb + per);
+    for (int s0 = sb; s0 < se; s0 += kZuU) {
+      u32x4 w[kZuU], a[kZuU];
+#pragma unroll
+      for (int i = 0; i < kZuU; ++i) {
+        const int st = min(s0 + i, se - 1);  // past se: a repeated step, its A operand zeroed below
+        w[i] = ld16(wrow + (size_t)st * 64);
+        a[i] = ld16(hrow + (size_t)st * 64);
+      }
+#pragma unroll
+      for (int i = 0; i < kZuU; ++i) {
+        const u32x4 ai = s0 + i < se ? a[i] : u32x4{0, 0, 0, 0};
+        acc = mma16<Bf16>(acc, ai, w[i]);
+      }
+    }
+  }
+  {
+    const int ns = H / 32, per = (ns + kBwWaves - 1) / kBwWaves, sb = wave * per, se = min(ns, sb + per);
+    const unsigned char* wg = wrow + (size_t)d * 2;
+    for (int s0 = sb; s0 < se; s0 += kZuU) {
+      u32x4 w[kZuU];
+      float x[kZuU][8];
+#pragma unroll
+      for (int i = 0; i < kZuU; ++i) {
+        const int st = min(s0 + i, se - 1);
+        w[i] = ld16(wg + (size_t)st * 64);
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(grow + (size_t)st * 32);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(grow + (size_t)st * 32 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[i][e] = v0[e];
+          x[i][e + 4] = v1[e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kZuU; ++i) {
+        float xs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xs[e] = s0 + i < se ? x[i][e] : 0.f;
+        ActFrag<Bf16> a;
+        a.from_f32(xs);
+        acc = a.mma(acc, w[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wave][grp * 4 + j][col] = acc[j];
+  __syncthreads();
+  const int mm = threadIdx.x >> 4, nn = threadIdx.x & 15;  // 256 threads: 16 x 16 outputs
+  const int m = m0 + mm, q = q0 + nn;
+  if (m < R && q < r) {
+    float sum = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kBwWaves; ++wv) sum += red[wv][mm][nn];
+    const float zz = sum + (b1 ? bf16_to_f32(b1[q]) : 0.f);
+    z[(size_t)m * r + q] = zz;
+    u[(size_t)m * r + q] = zz * sigmoidf_(zz);
+  }
+}
+
+// bf16 heads, for dg on the matrix cores: w1gT[j][q] = W1[q][d + j] (the
+// state columns of W1, transposed so that the product's K, the bottleneck
+// rows, is contiguous), one 64 x 64 tile per workgroup through LDS.
+__global__ void __launch_bounds__(kBwThreads) bw_w1gt_kernel(int d, int H, int r, const uint16_t* __restrict__ w1,
+                                                             uint16_t* __restrict__ w1gT) {
+  __shared__ uint16_t t[64][66];
+  const int j0 = blockIdx.x * 64, q0 = blockIdx.y * 64, tid = threadIdx.x;
+  const int n = d + H;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int qq = (tid >> 6) + 4 * i, jj = tid & 63;
+    t[qq][jj] = q0 + qq < r && j0 + jj < H ? w1[(size_t)(q0 + qq) * n + d + j0 + jj] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int jj = (tid >> 6) + 4 * i, qq = tid & 63;
+    if (j0 + jj < H && q0 + qq < r) w1gT[(size_t)(j0 + jj) * r + q0 + qq] = t[qq][jj];
+  }
+}
+
+// bf16 heads: dg = dz W1[:, d:] for 16 rows (blockIdx.y) x 64 state columns
+// (blockIdx.x, 16 per wave) on the matrix cores, dz split hi + lo, every K
+// step's loads issued first.  r a multiple of 32.
+__global__ void __launch_bounds__(kBwThreads) bw_dgm_kernel(int R, int H, int r, const float* __restrict__ dz,
+                                                            const uint16_t* __restrict__ w1gT,
+                                                            float* __restrict__ dg) {
+  const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int m0 = blockIdx.y * 16, j0 = blockIdx.x * 64 + wave * 16;
+  if (j0 >= H) return;  // (uniform over the wave; no barrier below)
+  const int row = min(m0 + col, R - 1), jrow = min(j0 + col, H - 1);
+  const float* arow = dz + (size_t)row * r + grp * 8;
+  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(w1gT + (size_t)jrow * r) + grp * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kU = 8;
+  const int ns = r / 32;
+  for (int s0 = 0; s0 < ns; s0 += kU) {
+    u32x4 w[kU];
+    float x[kU][8];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int st = min(s0 + i, ns - 1);  // past ns: a repeated step, its A operand zeroed below
+      w[i] = ld16(wrow + (size_t)st * 64);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(arow + (size_t)st * 32);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(arow + (size_t)st * 32 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[i][e] = v0[e];
+        x[i][e + 4] = v1[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      float xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = s0 + i < ns ? x[i][e] : 0.f;
+      ActFrag<Bf16> a;
+      a.from_f32(xs);
+      acc = a.mma(acc, w[i]);
+    }
+  }
+  const int j = j0 + col;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int m = m0 + grp * 4 + jj;
+    if (m < R && j < H) dg[(size_t)m * H + j] = acc[jj];
+  }
+}
+
 // z = W1 [h ; g] + b1 and u = SiLU(z) for row `row`; x staged in LDS.
 template <class T>
 __global__ void __launch_bounds__(kBwThreads) bw_z_kernel(int d, int H, int r, const typename T::elem* __restrict__ hidden,
@@ -451,8 +604,15 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R, (r + 63) / 64), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states, w1,
-                     static_cast<const E*>(a.b1), z, u);
+  if (std::is_same<T, Bf16>::value && d % 32 == 0 && H % 32 == 0) {
+    // on the matrix cores (Qwen3-8B, 32 blocks: 80 us as float32 vector dot products)
+    hipLaunchKernelGGL(bw_zu_kernel, dim3((r + 15) / 16, (R + 15) / 16), dim3(kBwThreads), 0, s, R, d, H, r,
+                       reinterpret_cast<const uint16_t*>(hidden), a.states, reinterpret_cast<const uint16_t*>(w1),
+                       static_cast<const uint16_t*>(a.b1), z, u);
+  } else {
+    hipLaunchKernelGGL(bw_z_kernel<T>, dim3(R, (r + 63) / 64), dim3(kBwThreads), lds, s, d, H, r, hidden, a.states,
+                       w1, static_cast<const E*>(a.b1), z, u);
+  }
   if (pl.mfma) {
     if constexpr (std::is_same<T, Bf16>::value) {
       uint16_t* gs = reinterpret_cast<uint16_t*>(ws + pl.gs);
@@ -498,7 +658,14 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
                            a.d_b1);
     }
   }
-  if (a.d_states) {
+  if (a.d_states && pl.w1gT) {
+    // on the matrix cores (Qwen3-8B, 32 blocks: 35 us for the float32 vector kernel)
+    uint16_t* w1gT = reinterpret_cast<uint16_t*>(ws + pl.w1gT);
+    hipLaunchKernelGGL(bw_w1gt_kernel, dim3((H + 63) / 64, (r + 63) / 64), dim3(kBwThreads), 0, s, d, H, r,
+                       static_cast<const uint16_t*>(a.w1), w1gT);
+    hipLaunchKernelGGL(bw_dgm_kernel, dim3((H + 63) / 64, (R + 15) / 16), dim3(kBwThreads), 0, s, R, H, r, dz, w1gT,
+                       a.d_states);
+  } else if (a.d_states) {
     const size_t dg_lds = ((size_t)kBwRowsDg * r + (size_t)kBwWaves * kBwRowsDg * 64) * sizeof(float);
     if (dg_lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bw_dg_kernel<T>),

@@ -131,9 +131,12 @@ struct BackwardPlan {
   // [G1][r][n1] and db1p [G1][r] float32, added in group order)
   int G1;
   size_t dw1p, db1p;
+  // bf16 heads with r % 32 == 0: W1's state columns transposed, w1gT [H][r]
+  // bf16, for dg on the matrix cores (0: the float32 kernel)
+  size_t w1gT;
 };
 constexpr int kBwDw1Rows = 128;  // rows per dW1 group
-inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1) {
+inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1, int H) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BackwardPlan p{};
   if (dtype == 1) {
@@ -183,6 +186,11 @@ inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1) {
     off += up((size_t)p.G1 * r * n1 * 4);
     p.db1p = off;
     off += up((size_t)p.G1 * r * 4);
+  }
+  p.w1gT = 0;
+  if (dtype == 1 && r % 32 == 0) {
+    p.w1gT = off;
+    off += up((size_t)H * r * 2);
   }
   p.total = off;
   return p;

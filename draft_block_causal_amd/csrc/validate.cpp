@@ -182,7 +182,7 @@ int check_backward_args(const domino_head* h, int32_t batch, const void* hidden,
   for (const void* q : {(const void*)gru_states, (const void*)grad_final, (const void*)d_w2, (const void*)d_b2,
                         (const void*)d_w1, (const void*)d_b1, (const void*)d_states})
     if (reinterpret_cast<uintptr_t>(q) & 3u) return DOMINO_ERR_ALIGN;
-  const BackwardPlan pl = backward_plan(batch * h->block, h->rank, h->vocab, h->dtype, h->d + h->gru_hidden);
+  const BackwardPlan pl = backward_plan(batch * h->block, h->rank, h->vocab, h->dtype, h->d + h->gru_hidden, h->gru_hidden);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < pl.total)
     return DOMINO_ERR_WORKSPACE;
   return DOMINO_OK;

@@ -58,6 +58,22 @@ def test_backward_matches_oracle(dev, name, batch):
     _run(dev, S.get_workload(name), batch, seed=batch + 3)
 
 
+def test_backward_small_bf16_head(dev):
+    # 15 rows and 2 bottleneck-row tiles of z: partial row tiles on the
+    # matrix-core path of the bf16 head (d = 96, H = 64, r = 32, V = 777)
+    w = S.Workload(name="small_bf16", batch=3, block=5, d=96, vocab=777, gru_hidden=64, rank=32, dtype="bf16",
+                   tied=False, temperature=0.0, init="fanin")
+    _run(dev, w, 3, seed=17)
+
+
+def test_backward_repeatable_bf16(dev):
+    w = S.get_workload("qwen3_8b_b1_greedy")
+    a = _run(dev, w, 2, seed=19)
+    b = _run(dev, w, 2, seed=19)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_backward_repeatable(dev):
     w = S.get_workload("tiny_stress_b4")
     a = _run(dev, w, 4, seed=9)
