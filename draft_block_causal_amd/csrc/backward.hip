@@ -22,6 +22,7 @@
 // bf16 heads replace 2 and 3 by bw_split_kernel (G re-laid along both axes,
 // db2), bw_w2t_kernel, bw_us_kernel and two launches of the tiled bf16 GEMM
 // on the matrix cores (dW2, and the du partials over vocabulary slices).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -642,7 +643,38 @@ static hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(bw_dz_kernel, dim3((unsigned)(((long)R * r + 63) / 64)), dim3(kBwThreads), 0, s, R, r, pl.S,
                      part, z, dz);
-  {
+  if (pl.w1m) {
+    // dW1 on the matrix cores: [dz_hi | dz_lo] [h | h]^T for the hidden
+    // columns, [dz_hi | dz_lo | dz_hi] [g_hi | g_hi | g_lo]^T for the state
+    // columns, as S1 split-K slices added in slice order (Qwen3-8B, 32
+    // blocks: 73 + 12 us with the float32 row groups)
+    const int Rp = pl.Rp, S1 = pl.S1, tiles = (Rp + 63) / 64, n1 = d + H;
+    uint16_t* dzT = reinterpret_cast<uint16_t*>(ws + pl.dzT);
+    uint16_t* hT = reinterpret_cast<uint16_t*>(ws + pl.hT);
+    uint16_t* gT = reinterpret_cast<uint16_t*>(ws + pl.gT);
+    float* bp1 = reinterpret_cast<float*>(ws + pl.bp1);
+    KJobs jobs{};
+    jobs.j[0] = {dz, dzT, a.d_b1 ? bp1 : nullptr, r, 3, 0, 0b010u};
+    jobs.j[1] = {hidden, hT, nullptr, d, 2, 1, 0b00u};
+    jobs.j[2] = {a.states, gT, nullptr, H, 3, 0, 0b100u};
+    hipError_t e = launch_rows_to_k(R, Rp, jobs, 3, std::max(std::max(r, d), H), s);
+    if (e != hipSuccess) return e;
+    e = launch_tile_colsums(tiles, r, bp1, a.d_b1, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+    float* w1out = S1 > 1 ? reinterpret_cast<float*>(ws + pl.dw1p) : a.d_w1;
+    e = S1 > 1 ? launch_gemm_bf16_tn_splitk(dzT, 3 * Rp, r, hT, 2 * Rp, d, 2 * Rp / S1, S1, 2 * Rp, w1out, n1,
+                                            (size_t)r * n1, s)
+               : launch_gemm_bf16_tn(dzT, 3 * Rp, r, hT, 2 * Rp, d, 2 * Rp, nullptr, w1out, n1, 0, s);
+    if (e != hipSuccess) return e;
+    e = S1 > 1 ? launch_gemm_bf16_tn_splitk(dzT, 3 * Rp, r, gT, 3 * Rp, H, 3 * Rp / S1, S1, 3 * Rp, w1out + d, n1,
+                                            (size_t)r * n1, s)
+               : launch_gemm_bf16_tn(dzT, 3 * Rp, r, gT, 3 * Rp, H, 3 * Rp, nullptr, w1out + d, n1, 0, s);
+    if (e != hipSuccess) return e;
+    if (S1 > 1) {
+      const long nw = (long)r * n1;
+      hipLaunchKernelGGL(bw_gsum_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, nw, S1, w1out, a.d_w1);
+    }
+  } else {
     const int G1 = pl.G1;
     float* w1out = G1 > 1 ? reinterpret_cast<float*>(ws + pl.dw1p) : a.d_w1;
     float* b1out = G1 > 1 ? (a.d_b1 ? reinterpret_cast<float*>(ws + pl.db1p) : nullptr) : a.d_b1;

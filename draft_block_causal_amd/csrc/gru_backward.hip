@@ -241,19 +241,10 @@ __global__ void __launch_bounds__(kGbThreads) gb_outer_kernel(int R, int Q, int 
 // rounded to bf16, else hi = x truncated to bf16 (for bf16 X, x itself).  One
 // 64 x 64 tile of X per workgroup through LDS; with `bpart`, the tile's
 // column sums (its rows in order) go to bpart[blockIdx.y][n].
-struct GbTJob {
-  const void* X;  // [R][N], float32 or (bf16) bf16
-  uint16_t* Y;
-  float* bpart;
-  int N, nparts, bf16;
-  unsigned lo_parts;
-};
-struct GbTJobs {
-  GbTJob j[4];
-};
-__global__ void __launch_bounds__(256) gb_tsplit_kernel(int R, int Rp, GbTJobs jobs) {
+// (KJob, KJobs: kernels.h)
+__global__ void __launch_bounds__(256) gb_tsplit_kernel(int R, int Rp, KJobs jobs) {
   __shared__ float t[64][65];
-  const GbTJob& jb = jobs.j[blockIdx.z];
+  const KJob& jb = jobs.j[blockIdx.z];
   const int N = jb.N, n0 = blockIdx.x * 64, r0 = blockIdx.y * 64, tid = threadIdx.x;
   if (n0 >= N) return;  // (uniform over the workgroup)
   {
@@ -304,6 +295,20 @@ __global__ void gb_bsum_kernel(int tiles, int N, const float* __restrict__ bpart
   float sum = 0.f;
   for (int i = 0; i < tiles; ++i) sum += bpart[(size_t)i * N + n];
   bias[n] = sum;
+}
+
+hipError_t launch_rows_to_k(int R, int Rp, const KJobs& jobs, int njobs, int nmax, hipStream_t s) {
+  if (R <= 0 || njobs <= 0) return hipSuccess;
+  if (njobs > 4 || Rp % 32 || Rp < R) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gb_tsplit_kernel, dim3((nmax + 63) / 64, (Rp + 63) / 64, njobs), dim3(256), 0, s, R, Rp, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_colsums(int tiles, int N, const float* bpart0, float* sum0, const float* bpart1, float* sum1,
+                               hipStream_t s) {
+  if (N <= 0 || (!sum0 && !sum1)) return hipSuccess;
+  hipLaunchKernelGGL(gb_bsum_kernel, dim3((N + 255) / 256, 2), dim3(256), 0, s, tiles, N, bpart0, sum0, bpart1, sum1);
+  return hipGetLastError();
 }
 
 // Rows (blocks x positions) from which bf16 heads take the weight gradients
@@ -371,16 +376,15 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
     uint16_t* gT = reinterpret_cast<uint16_t*>(ws + pl.gT);
     float* bpart = reinterpret_cast<float*>(ws + pl.bpart);
     float* bpart_hh = bpart + (size_t)tiles * G3;
-    GbTJobs jobs{};
+    KJobs jobs{};
     jobs.j[0] = {da, daT, g.d_b_ih ? bpart : nullptr, G3, 2, 0, 0b10u};
     jobs.j[1] = {x_e, eT, nullptr, d, 2, 1, 0b00u};
     jobs.j[2] = {dc, dcT, g.d_b_hh ? bpart_hh : nullptr, G3, 3, 0, 0b100u};
     jobs.j[3] = {x_g, gT, nullptr, H, 3, 0, 0b010u};
-    const int nmax = std::max(std::max(G3, d), H);
-    hipLaunchKernelGGL(gb_tsplit_kernel, dim3((nmax + 63) / 64, tiles, 4), dim3(256), 0, s, R, Rp, jobs);
-    if (g.d_b_ih || g.d_b_hh)
-      hipLaunchKernelGGL(gb_bsum_kernel, dim3((G3 + 255) / 256, 2), dim3(256), 0, s, tiles, G3, bpart, g.d_b_ih,
-                         bpart_hh, g.d_b_hh);
+    e = launch_rows_to_k(R, Rp, jobs, 4, std::max(std::max(G3, d), H), s);
+    if (e != hipSuccess) return e;
+    e = launch_tile_colsums(tiles, G3, bpart, g.d_b_ih, bpart_hh, g.d_b_hh, s);
+    if (e != hipSuccess) return e;
     e = launch_gemm_bf16_tn(daT, 2 * Rp, G3, eT, 2 * Rp, d, 2 * Rp, nullptr, g.d_w_ih, d, num_cu, s);
     if (e != hipSuccess) return e;
     e = launch_gemm_bf16_tn(dcT, 3 * Rp, G3, gT, 3 * Rp, H, 3 * Rp, nullptr, g.d_w_hh, H, num_cu, s);

@@ -134,7 +134,14 @@ struct BackwardPlan {
   // bf16 heads with r % 32 == 0: W1's state columns transposed, w1gT [H][r]
   // bf16, for dg on the matrix cores (0: the float32 kernel)
   size_t w1gT;
+  // bf16 heads from kBwW1MfmaRows rows (d, H, r multiples of 32): dW1 on the
+  // matrix cores, S1 split-K slices (partials in dw1p when S1 > 1), operands
+  // dzT [r][3 Rp] (dz hi | lo | hi), hT [d][2 Rp], gT [H][3 Rp] (g hi | hi |
+  // lo), db1 tile sums bp1 [Rp / 64][r]
+  int w1m, S1;
+  size_t dzT, hT, gT, bp1;
 };
+constexpr int kBwW1MfmaRows = 128;
 constexpr int kBwDw1Rows = 128;  // rows per dW1 group
 inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1, int H) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -192,6 +199,26 @@ inline BackwardPlan backward_plan(int R, int r, int V, int dtype, int n1, int H)
     p.w1gT = off;
     off += up((size_t)H * r * 2);
   }
+  const int d = n1 - H;
+  p.w1m = dtype == 1 && R >= kBwW1MfmaRows && r % 32 == 0 && d % 32 == 0 && H % 32 == 0;
+  if (p.w1m) {
+    const size_t Rp = (size_t)p.Rp;
+    // the largest slice count within the dW1 partial buffer dividing Rp / 32
+    p.S1 = 1;
+    for (int sl = p.G1; sl > 1; --sl)
+      if ((p.Rp / 32) % sl == 0) {
+        p.S1 = sl;
+        break;
+      }
+    p.dzT = off;
+    off += up((size_t)r * 3 * Rp * 2);
+    p.hT = off;
+    off += up((size_t)d * 2 * Rp * 2);
+    p.gT = off;
+    off += up((size_t)H * 3 * Rp * 2);
+    p.bp1 = off;
+    off += up((Rp + 63) / 64 * (size_t)r * 4);
+  }
   p.total = off;
   return p;
 }
@@ -207,6 +234,27 @@ hipError_t launch_correction_backward(const BackwardArgs& a, hipStream_t s);
 
 // Backward through time of the teacher-forced GRU (gru_backward.hip).
 constexpr int kGruCarryBlocks = 8;  // blocks sharing each W_hh load in the carry, from 8 blocks up
+// Rows-to-K re-layout for the matrix-core weight gradients (gru_backward.hip):
+// job j of a launch, Y[n][p Rp + r] = part p of X[r][n] as bf16 for r < R
+// (zero up to Rp, a multiple of 32); bit p of lo_parts set: the remainder
+// x - hi rounded to bf16, else hi = x truncated to bf16 (bf16 X: x itself);
+// with bpart, each 64-row tile's column sums in row order, bpart[tile][n].
+struct KJob {
+  const void* X;  // [R][N] row-major: float32, or bf16 when bf16 = 1
+  uint16_t* Y;    // [N][nparts Rp]
+  float* bpart;
+  int N, nparts, bf16;
+  unsigned lo_parts;
+};
+struct KJobs {
+  KJob j[4];
+};
+// njobs <= 4; nmax: the largest N of the jobs.
+hipError_t launch_rows_to_k(int R, int Rp, const KJobs& jobs, int njobs, int nmax, hipStream_t s);
+// sum_i[n] = bpart_i[0][n] + ... + bpart_i[tiles - 1][n] in tile order (sum_i nullptr: skipped).
+hipError_t launch_tile_colsums(int tiles, int N, const float* bpart0, float* sum0, const float* bpart1, float* sum1,
+                               hipStream_t s);
+
 struct GruBackwardPlan {
   size_t x_e, x_g, a, c, da, dc, carry, tok, total;  // byte offsets; workspace bytes
   int carry_parts;  // P

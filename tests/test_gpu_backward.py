@@ -53,17 +53,22 @@ def _run(dev, w, batch, seed):
 
 
 @pytest.mark.parametrize("name,batch", [("tiny_stress_b4", 4), ("qwen3_8b_b1_greedy", 1), ("qwen3_8b_b1_greedy", 2),
-                                        ("qwen3_8b_b1_greedy", 20)])
+                                        ("qwen3_8b_b1_greedy", 9), ("qwen3_8b_b1_greedy", 20),
+                                        ("qwen3_8b_b1_greedy", 32)])
 def test_backward_matches_oracle(dev, name, batch):
+    # from 128 rows dW1 runs on the matrix cores: 9 blocks in one K slice (K
+    # padded 144 -> 160 rows), 20 in two, 32 in four
     _run(dev, S.get_workload(name), batch, seed=batch + 3)
 
 
-def test_backward_small_bf16_head(dev):
-    # 15 rows and 2 bottleneck-row tiles of z: partial row tiles on the
-    # matrix-core path of the bf16 head (d = 96, H = 64, r = 32, V = 777)
+@pytest.mark.parametrize("batch", [3, 27])
+def test_backward_small_bf16_head(dev, batch):
+    # 15 rows (partial row tiles of z and dg) and 135 rows (dW1 on the matrix
+    # cores with every tile partial) of a small bf16 head (d = 96, H = 64,
+    # r = 32, V = 777)
     w = S.Workload(name="small_bf16", batch=3, block=5, d=96, vocab=777, gru_hidden=64, rank=32, dtype="bf16",
                    tied=False, temperature=0.0, init="fanin")
-    _run(dev, w, 3, seed=17)
+    _run(dev, w, batch, seed=17 + batch)
 
 
 def test_backward_repeatable_bf16(dev):
