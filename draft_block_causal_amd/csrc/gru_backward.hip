@@ -17,7 +17,9 @@
 //      every row of position i: da, dc and the direct part z dg of the carry)
 //      and gb_carry_kernel (W_hhᵀ dc, the rest of the gradient reaching
 //      g_{i-1}, its 3H terms split over P workgroups and their waves, the P
-//      partial sums added by the next gb_elem_kernel);
+//      partial sums added by the next gb_elem_kernel; bf16 heads:
+//      gb_carrym_kernel on the matrix cores against W_hh transposed once by
+//      gb_whht_kernel);
 //   4. gb_outer_kernel twice: dW_ih = Σ da eᵀ, db_ih = Σ da and
 //      dW_hh = Σ dc g_prevᵀ, db_hh = Σ dc over every row; bf16 heads from
 //      kGbMfmaRows rows on: the operands re-laid by gb_tsplit_kernel and the
@@ -191,6 +193,74 @@ __global__ void __launch_bounds__(kGbThreads) gb_carry_kernel(int B, int K, int 
     }
 }
 
+// bf16 heads: whhT[j][q] = W_hh[q][j] (once per call), 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(kGbThreads) gb_whht_kernel(int H, const uint16_t* __restrict__ w_hh,
+                                                             uint16_t* __restrict__ whhT) {
+  __shared__ uint16_t t[64][66];
+  const int G3 = 3 * H, j0 = blockIdx.x * 64, q0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int qq = (tid >> 6) + 4 * i, jj = tid & 63;
+    t[qq][jj] = q0 + qq < G3 && j0 + jj < H ? w_hh[(size_t)(q0 + qq) * H + j0 + jj] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int jj = (tid >> 6) + 4 * i, qq = tid & 63;
+    if (j0 + jj < H && q0 + qq < G3) whhT[(size_t)(j0 + jj) * G3 + q0 + qq] = t[qq][jj];
+  }
+}
+
+// bf16 heads: carry[1 + p][b][j] = Σ_q W_hh[q][j] dc[row(b, i)][q] over group
+// p (blockIdx.z) of the 3H terms on the matrix cores: 16 blocks (blockIdx.y)
+// x 64 units (16 per wave), dc split hi + lo, the group's K steps in order
+// with eight steps of loads in flight.  3H a multiple of 32 gridDim.z.
+__global__ void __launch_bounds__(kGbThreads) gb_carrym_kernel(int B, int K, int H, int i,
+                                                               const uint16_t* __restrict__ whhT,
+                                                               const float* __restrict__ dc,
+                                                               float* __restrict__ carry) {
+  const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int G3 = 3 * H, b0 = blockIdx.y * 16, j0 = blockIdx.x * 64 + wave * 16;
+  if (j0 >= H) return;  // (uniform over the wave; no barrier below)
+  const int steps = G3 / 32 / (int)gridDim.z, s_begin = (int)blockIdx.z * steps;
+  const int b = min(b0 + col, B - 1), jr = min(j0 + col, H - 1);
+  const float* arow = dc + ((size_t)b * K + i) * G3 + grp * 8;
+  const unsigned char* wrow = reinterpret_cast<const unsigned char*>(whhT + (size_t)jr * G3) + grp * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kU = 8;
+  for (int s0 = 0; s0 < steps; s0 += kU) {
+    u32x4 w[kU];
+    float x[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int st = s_begin + min(s0 + u, steps - 1);  // past the group: a repeated step, zeroed below
+      w[u] = ld16(wrow + (size_t)st * 64);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(arow + (size_t)st * 32);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(arow + (size_t)st * 32 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[u][e] = v0[e];
+        x[u][e + 4] = v1[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = s0 + u < steps ? x[u][e] : 0.f;
+      ActFrag<Bf16> a;
+      a.from_f32(xs);
+      acc = a.mma(acc, w[u]);
+    }
+  }
+  const int j = j0 + col;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bb = b0 + grp * 4 + q;
+    if (bb < B && j < H) carry[(1 + blockIdx.z) * (size_t)B * H + (size_t)bb * H + j] = acc[q];
+  }
+}
+
 // out[q][k] = Σ_rows A[row][q] X[row][k] for q0 .. q0 + 15 (X of type XE);
 // bias[q] = Σ_rows A[row][q] from the workgroups with blockIdx.x == 0.  The
 // A values of 64 rows at a time are staged in LDS (read as broadcasts).
@@ -357,13 +427,23 @@ static hipError_t gru_backward_t(const GruBackwardArgs& g, int num_cu, hipStream
                        static_cast<const E*>(g.w_hh), static_cast<const E*>(g.b_hh), x_g, c);
   }
   const int P = pl.carry_parts;
+  // bf16 heads: the carried gradient on the matrix cores against W_hh
+  // transposed once per call (Qwen3-8B, 32 blocks: 16.4 us a position with
+  // the float32 kernel)
+  uint16_t* whhT = pl.S > 0 && pl.whhT ? reinterpret_cast<uint16_t*>(ws + pl.whhT) : nullptr;
+  if (whhT)
+    hipLaunchKernelGGL(gb_whht_kernel, dim3((H + 63) / 64, (G3 + 63) / 64), dim3(kGbThreads), 0, s, H,
+                       static_cast<const uint16_t*>(g.w_hh), whhT);
   e = launch_fill_u64(reinterpret_cast<unsigned long long*>(carry), (int)(((size_t)(1 + P) * B * H + 1) / 2), s);
   if (e != hipSuccess) return e;
   const dim3 eg((H + 255) / 256, B);
   for (int i = K - 1; i >= 0; --i) {
     hipLaunchKernelGGL(gb_elem_kernel, eg, dim3(256), 0, s, B, K, H, i, i == K - 1 ? 0 : P, a, c, x_g, g.dg,
                        carry, da, dc);
-    if (i > 0)
+    if (i > 0 && whhT)
+      hipLaunchKernelGGL(gb_carrym_kernel, dim3((H + 63) / 64, (B + 15) / 16, P), dim3(kGbThreads), 0, s, B, K, H, i,
+                         whhT, dc, carry);
+    else if (i > 0)
       hipLaunchKernelGGL((B >= kGbCarryNB ? gb_carry_kernel<T, kGbCarryNB> : gb_carry_kernel<T, 1>),
                          dim3((H + 63) / 64, B >= kGbCarryNB ? (B + kGbCarryNB - 1) / kGbCarryNB : B, P),
                          dim3(kGbThreads), 0, s, B, K, H, i, static_cast<const E*>(g.w_hh), dc, carry);

@@ -269,6 +269,10 @@ struct GruBackwardPlan {
   // sums' per-64-row partials bpart [2][Rp / 64][3H]
   int Rp;
   size_t daT, eT, dcT, gT, bpart;
+  // bf16 heads with 3H a multiple of 32 carry_parts: W_hh transposed, whhT
+  // [H][3H] bf16, for the carried gradient W_hh^T dc on the matrix cores
+  // (0: the float32 kernel)
+  size_t whhT;
 };
 inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -291,8 +295,13 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
     // groups of the 3H terms of W_hh^T dc (the carry is [1 + P][B][H]: the
     // direct part, then one partial sum per group), about 256 workgroups
     const long wgs = ((long)H + 63) / 64 * (B >= kGruCarryBlocks ? (B + kGruCarryBlocks - 1) / kGruCarryBlocks : B);
-    const long P = 256 / wgs;
-    p.carry_parts = (int)(P < 1 ? 1 : P > 8 ? 8 : P);
+    long P = 256 / wgs;
+    P = P < 1 ? 1 : P > 8 ? 8 : P;
+    // bf16 heads: a power of two, so that the matrix-core carry kernel's K
+    // groups are whole 32-wide steps (3H a multiple of 32 P)
+    if (elem == 2)
+      while (P & (P - 1)) --P;
+    p.carry_parts = (int)P;
   }
   p.carry = off;
   off += up(((size_t)(1 + p.carry_parts) * B * H + 1) / 2 * 8);
@@ -322,6 +331,11 @@ inline GruBackwardPlan gru_backward_plan(int B, int K, int d, int H, int elem) {
     off += up((size_t)H * 3 * Rp * 2);
     p.bpart = off;
     off += up(2 * ((Rp + 63) / 64) * G3 * 4);
+    p.whhT = 0;
+    if (G3 % (32 * (size_t)p.carry_parts) == 0) {
+      p.whhT = off;
+      off += up((size_t)H * G3 * 2);
+    }
   }
   p.total = off;
   return p;
